@@ -1,0 +1,105 @@
+"""fp64 CPU oracle -- TEST INFRASTRUCTURE, not the product.
+
+Only the tests, the smoke check and the bench's CPU-baseline leg may import
+this package. The HIP library and its Python binding never do.
+
+* ``conv``               -- oracle.c's nested-loop convolution, returns float64.
+* ``conv3d_min_softmax`` -- conv (composed) -> min over one axis -> softmax over channels.
+* ``out_len``            -- the output-length formula of one axis.
+* ``brute``              -- a second, pure-Python statement of the same definition
+                           for tiny inputs (pins oracle.c by brute force).
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_LIB = None
+
+
+def _lib():
+    global _LIB
+    if _LIB is None:
+        path = _build.build()
+        lib = ctypes.CDLL(path)
+        i64p = ctypes.POINTER(ctypes.c_int64)
+        ip = ctypes.POINTER(ctypes.c_int)
+        fp = ctypes.c_void_p
+        lib.oracle_out_len.restype = ctypes.c_int64
+        lib.oracle_out_len.argtypes = [ctypes.c_int64] * 5
+        lib.oracle_num_threads.restype = ctypes.c_int
+        lib.oracle_conv.restype = ctypes.c_int
+        lib.oracle_conv.argtypes = [ctypes.c_int, fp, i64p, fp, i64p, fp, ip, ip, ip, ctypes.c_int, fp]
+        lib.oracle_conv3d_min_softmax.restype = ctypes.c_int
+        lib.oracle_conv3d_min_softmax.argtypes = [fp, i64p, fp, i64p, fp, ip, ip, ip, ctypes.c_int,
+                                                  ctypes.c_int, fp]
+        _LIB = lib
+    return _LIB
+
+
+def num_threads():
+    return _lib().oracle_num_threads()
+
+
+def out_len(L, k, s=1, d=1, p=0):
+    return int(_lib().oracle_out_len(L, k, s, d, p))
+
+
+def _i64(seq):
+    return (ctypes.c_int64 * len(seq))(*[int(v) for v in seq])
+
+
+def _i32(seq):
+    return (ctypes.c_int * len(seq))(*[int(v) for v in seq])
+
+
+def _vec(v, nd, name):
+    if isinstance(v, int):
+        return [v] * nd
+    v = list(v)
+    if len(v) != nd:
+        raise ValueError(f"{name} must have {nd} entries")
+    return v
+
+
+def conv(x, w, bias=None, stride=1, dilation=1, padding=0, groups=1):
+    """fp64 conv of fp32 numpy arrays; x [N,C,L] or [N,C,D,H,W]."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    nd = x.ndim - 2
+    stride, dilation, padding = (_vec(stride, nd, "stride"), _vec(dilation, nd, "dilation"),
+                                 _vec(padding, nd, "padding"))
+    out = [out_len(x.shape[2 + a], w.shape[2 + a], stride[a], dilation[a], padding[a]) for a in range(nd)]
+    if min(out) < 1:
+        raise ValueError(f"empty output {out}")
+    y = np.empty((x.shape[0], w.shape[0], *out), dtype=np.float64)
+    b = None
+    if bias is not None:
+        b = np.ascontiguousarray(bias, dtype=np.float32)
+    rc = _lib().oracle_conv(nd, x.ctypes.data, _i64(x.shape), w.ctypes.data, _i64(w.shape),
+                            b.ctypes.data if b is not None else None,
+                            _i32(stride), _i32(dilation), _i32(padding), groups, y.ctypes.data)
+    if rc != 0:
+        raise ValueError(f"oracle_conv rejected the arguments (code {rc})")
+    return y
+
+
+def conv3d_min_softmax(x, w, bias=None, stride=1, dilation=1, padding=0, groups=1, min_dim=2):
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    stride, dilation, padding = _vec(stride, 3, "stride"), _vec(dilation, 3, "dilation"), _vec(padding, 3, "padding")
+    o = [out_len(x.shape[2 + a], w.shape[2 + a], stride[a], dilation[a], padding[a]) for a in range(3)]
+    if min(o) < 1:
+        raise ValueError(f"empty output {o}")
+    keep = [o[a] for a in range(3) if a != min_dim - 2]
+    out = np.empty((x.shape[0], w.shape[0], *keep), dtype=np.float64)
+    b = np.ascontiguousarray(bias, dtype=np.float32) if bias is not None else None
+    rc = _lib().oracle_conv3d_min_softmax(x.ctypes.data, _i64(x.shape), w.ctypes.data, _i64(w.shape),
+                                          b.ctypes.data if b is not None else None,
+                                          _i32(stride), _i32(dilation), _i32(padding), groups, min_dim,
+                                          out.ctypes.data)
+    if rc != 0:
+        raise ValueError(f"oracle_conv3d_min_softmax rejected the arguments (code {rc})")
+    return out
