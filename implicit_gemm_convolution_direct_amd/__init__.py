@@ -1,0 +1,200 @@
+"""MI355X-native fp32 convolution: Python binding of the C-ABI library libconvhip.so.
+
+Argument marshalling only. Every step of the computation runs in the library's
+HIP kernels; there is no CPU or PyTorch fallback. If the library is not built,
+importing works but every call raises.
+
+Operations (POPCORNBENCH "Kimi-K2.6" pages l1_p60, l1_p76, l2_p24, opening turns):
+
+* ``conv_fwd(x, w, bias, stride, dilation, padding, groups)`` -- Conv1d / Conv3d forward.
+* ``conv3d_min_softmax(x, w, bias, stride, dilation, padding, groups, min_dim=2)`` --
+  softmax over channels of the minimum over depth of Conv3d, without writing the
+  5-D conv result.
+"""
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libconvhip.so")
+
+CONV_OK = 0
+STATUS_NAMES = {
+    0: "CONV_OK", -1: "CONV_ERR_NULL", -2: "CONV_ERR_RANK", -3: "CONV_ERR_SHAPE", -4: "CONV_ERR_GROUPS",
+    -5: "CONV_ERR_PARAM", -6: "CONV_ERR_EMPTY_OUTPUT", -7: "CONV_ERR_UNSUPPORTED", -8: "CONV_ERR_OVERFLOW",
+    -9: "CONV_ERR_HIP",
+}
+EXPORTED = ["conv_out_shape", "conv_fwd", "conv3d_min_softmax", "conv_status_string", "conv_plan_describe",
+            "convhip_synth_fill"]
+
+
+class ConvError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)}")
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"HIP library not built: {LIB_PATH} is missing "
+                               f"(run __graft_entry__.build() or python -m "
+                               f"implicit_gemm_convolution_direct_amd._build)")
+        L = ctypes.CDLL(LIB_PATH)
+        i64p = ctypes.POINTER(ctypes.c_int64)
+        ip = ctypes.POINTER(ctypes.c_int)
+        vp = ctypes.c_void_p
+        L.conv_out_shape.restype = ctypes.c_int
+        L.conv_out_shape.argtypes = [ctypes.c_int, i64p, i64p, ip, ip, ip, i64p]
+        L.conv_fwd.restype = ctypes.c_int
+        L.conv_fwd.argtypes = [ctypes.c_int, vp, i64p, vp, i64p, vp, ip, ip, ip, ctypes.c_int, vp, vp]
+        L.conv3d_min_softmax.restype = ctypes.c_int
+        L.conv3d_min_softmax.argtypes = [vp, i64p, vp, i64p, vp, ip, ip, ip, ctypes.c_int, ctypes.c_int, vp, vp]
+        L.conv_status_string.restype = ctypes.c_char_p
+        L.conv_status_string.argtypes = [ctypes.c_int]
+        L.conv_plan_describe.restype = ctypes.c_int
+        L.conv_plan_describe.argtypes = [ctypes.c_int, i64p, i64p, ip, ip, ip, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_char_p, ctypes.c_int]
+        L.convhip_synth_fill.restype = ctypes.c_int
+        L.convhip_synth_fill.argtypes = [vp, ctypes.c_int64, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int,
+                                         ctypes.c_float, ctypes.c_int, ctypes.c_int, vp]
+        _lib = L
+    return _lib
+
+
+def status_string(status):
+    try:
+        return lib().conv_status_string(int(status)).decode()
+    except RuntimeError:
+        return STATUS_NAMES.get(int(status), f"status {status}")
+
+
+def _i64(seq):
+    return (ctypes.c_int64 * len(seq))(*[int(v) for v in seq])
+
+
+def _i32(seq):
+    return (ctypes.c_int * len(seq))(*[int(v) for v in seq])
+
+
+def _vec(v, nd, name):
+    if isinstance(v, int):
+        return [v] * nd
+    v = [int(t) for t in v]
+    if len(v) != nd:
+        raise ValueError(f"{name} needs {nd} entries, got {len(v)}")
+    return v
+
+
+def out_shape(in_spatial, k_spatial, stride, dilation, padding):
+    """Output lengths via the library's conv_out_shape (host only)."""
+    nd = len(in_spatial)
+    out = (ctypes.c_int64 * nd)()
+    rc = lib().conv_out_shape(nd, _i64(in_spatial), _i64(k_spatial), _i32(_vec(stride, nd, "stride")),
+                              _i32(_vec(dilation, nd, "dilation")), _i32(_vec(padding, nd, "padding")), out)
+    return rc, [int(v) for v in out]
+
+
+def plan_describe(x_shape, w_shape, stride=1, dilation=1, padding=0, groups=1, fused=False):
+    nd = len(x_shape) - 2
+    buf = ctypes.create_string_buffer(1024)
+    rc = lib().conv_plan_describe(nd, _i64(x_shape), _i64(w_shape), _i32(_vec(stride, nd, "stride")),
+                                  _i32(_vec(dilation, nd, "dilation")), _i32(_vec(padding, nd, "padding")),
+                                  int(groups), 1 if fused else 0, buf, 1024)
+    if rc != CONV_OK:
+        raise ConvError(rc, "conv_plan_describe")
+    return buf.value.decode()
+
+
+def _check_tensor(t, name):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU (got {t.device}); there is no CPU path")
+    if t.dtype != torch.float32:
+        raise TypeError(f"{name} must be float32 (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream_handle(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def conv_fwd(x, w, bias=None, stride=1, dilation=1, padding=0, groups=1, out=None):
+    """y = Conv{1,3}d(x, w, bias) with zero padding; x [N,C,L] or [N,C,D,H,W] fp32 on the GPU."""
+    _check_tensor(x, "x")
+    _check_tensor(w, "w")
+    if bias is not None:
+        _check_tensor(bias, "bias")
+    nd = x.dim() - 2
+    if nd not in (1, 3) or w.dim() != x.dim():
+        raise ValueError("x and w must both be 3-D (Conv1d) or 5-D (Conv3d)")
+    stride, dilation, padding = (_vec(stride, nd, "stride"), _vec(dilation, nd, "dilation"),
+                                 _vec(padding, nd, "padding"))
+    rc, o = out_shape(list(x.shape[2:]), list(w.shape[2:]), stride, dilation, padding)
+    if rc != CONV_OK:
+        raise ConvError(rc, "conv_out_shape")
+    shape = (x.shape[0], w.shape[0], *o)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.float32, device=x.device)
+    else:
+        _check_tensor(out, "out")
+        if tuple(out.shape) != shape:
+            raise ValueError(f"out has shape {tuple(out.shape)}, expected {shape}")
+    rc = lib().conv_fwd(nd, x.data_ptr(), _i64(x.shape), w.data_ptr(), _i64(w.shape),
+                        bias.data_ptr() if bias is not None else None, _i32(stride), _i32(dilation),
+                        _i32(padding), int(groups), out.data_ptr(), _stream_handle(x.device))
+    if rc != CONV_OK:
+        raise ConvError(rc, "conv_fwd")
+    return out
+
+
+def conv3d_min_softmax(x, w, bias=None, stride=1, dilation=1, padding=0, groups=1, min_dim=2, out=None):
+    """softmax(min(Conv3d(x, w, bias), dim=min_dim), dim=1) without storing the conv result."""
+    _check_tensor(x, "x")
+    _check_tensor(w, "w")
+    if bias is not None:
+        _check_tensor(bias, "bias")
+    if x.dim() != 5 or w.dim() != 5:
+        raise ValueError("x and w must be 5-D")
+    stride, dilation, padding = _vec(stride, 3, "stride"), _vec(dilation, 3, "dilation"), _vec(padding, 3, "padding")
+    rc, o = out_shape(list(x.shape[2:]), list(w.shape[2:]), stride, dilation, padding)
+    if rc != CONV_OK:
+        raise ConvError(rc, "conv_out_shape")
+    if min_dim not in (2, 3, 4):
+        raise ValueError("min_dim must be 2, 3 or 4")
+    keep = [o[a] for a in range(3) if a != min_dim - 2]
+    shape = (x.shape[0], w.shape[0], *keep)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.float32, device=x.device)
+    else:
+        _check_tensor(out, "out")
+        if tuple(out.shape) != shape:
+            raise ValueError(f"out has shape {tuple(out.shape)}, expected {shape}")
+    rc = lib().conv3d_min_softmax(x.data_ptr(), _i64(x.shape), w.data_ptr(), _i64(w.shape),
+                                  bias.data_ptr() if bias is not None else None, _i32(stride), _i32(dilation),
+                                  _i32(padding), int(groups), int(min_dim), out.data_ptr(),
+                                  _stream_handle(x.device))
+    if rc != CONV_OK:
+        raise ConvError(rc, "conv3d_min_softmax")
+    return out
+
+
+KIND_UNIFORM01, KIND_SYMMETRIC, KIND_INT = 0, 1, 2
+
+
+def synth_fill(t, seed, kind=KIND_UNIFORM01, start=0, bound=1.0, lo=0, span=1):
+    """Fill a contiguous fp32 GPU tensor in place with the library's SplitMix64 generator."""
+    _check_tensor(t, "t")
+    rc = lib().convhip_synth_fill(t.data_ptr(), t.numel(), int(seed) & (2 ** 64 - 1), int(start), int(kind),
+                                  float(bound), int(lo), int(span), _stream_handle(t.device))
+    if rc != CONV_OK:
+        raise ConvError(rc, "convhip_synth_fill")
+    return t

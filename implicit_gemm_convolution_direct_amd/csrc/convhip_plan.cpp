@@ -1,0 +1,199 @@
+// Validation, output shapes and launch planning (host only).
+#include "convhip_plan.h"
+
+#include <algorithm>
+#include <cstdio>
+#include <limits>
+
+#include "../../include/convhip.h"
+
+namespace convhip {
+
+int64_t out_len(int64_t L, int64_t k, int64_t s, int64_t d, int64_t p) {
+  int64_t num = L + 2 * p - d * (k - 1) - 1;
+  int64_t q = num / s;
+  if (num % s != 0 && num < 0) q -= 1;  // floor, not truncation
+  return q + 1;
+}
+
+int make_geom(int nd, const int64_t* xs, const int64_t* ws, const int* stride, const int* dilation,
+              const int* padding, int groups, Geom* g) {
+  if (nd != 1 && nd != 3) return CONV_ERR_RANK;
+  if (!xs || !ws || !stride || !dilation || !padding || !g) return CONV_ERR_NULL;
+  for (int i = 0; i < nd + 2; i++)
+    if (xs[i] < 1 || ws[i] < 1) return CONV_ERR_SHAPE;
+  if (groups < 1) return CONV_ERR_GROUPS;
+  for (int a = 0; a < nd; a++)
+    if (stride[a] < 1 || dilation[a] < 1 || padding[a] < 0) return CONV_ERR_PARAM;
+  Geom r;
+  r.nd = nd;
+  r.N = xs[0];
+  r.Cin = xs[1];
+  r.Cout = ws[0];
+  r.G = groups;
+  if (r.Cin % groups != 0 || r.Cout % groups != 0) return CONV_ERR_GROUPS;
+  r.Cg = r.Cin / groups;
+  r.Coutg = r.Cout / groups;
+  if (ws[1] != r.Cg) return CONV_ERR_SHAPE;
+  for (int a = 0; a < nd; a++) {
+    int ax = 3 - nd + a;
+    r.L[ax] = xs[2 + a];
+    r.K[ax] = ws[2 + a];
+    r.S[ax] = stride[a];
+    r.Dl[ax] = dilation[a];
+    r.P[ax] = padding[a];
+  }
+  const int64_t kMax = std::numeric_limits<int32_t>::max();
+  for (int a = 0; a < 3; a++) {
+    if (r.L[a] > kMax || r.K[a] > kMax || r.S[a] > kMax || r.Dl[a] > kMax || r.P[a] > kMax)
+      return CONV_ERR_OVERFLOW;
+    r.O[a] = out_len(r.L[a], r.K[a], r.S[a], r.Dl[a], r.P[a]);
+    if (r.O[a] < 1) return CONV_ERR_EMPTY_OUTPUT;
+  }
+  // Per-tensor element counts must fit int64 comfortably; per-axis and per-plane
+  // indices are computed in 32 bits inside the kernels.
+  const double xe = double(r.N) * r.Cin * r.L[0] * r.L[1] * r.L[2];
+  const double ye = double(r.N) * r.Cout * r.O[0] * r.O[1] * r.O[2];
+  if (xe > 4.0e18 || ye > 4.0e18) return CONV_ERR_OVERFLOW;
+  if (r.N > kMax || r.Cin > kMax || r.Cout > kMax) return CONV_ERR_OVERFLOW;
+  if (double(r.O[1]) * r.O[2] > double(kMax)) return CONV_ERR_OVERFLOW;
+  if (double(r.Cg) * r.kvol() > double(kMax)) return CONV_ERR_OVERFLOW;
+  *g = r;
+  return CONV_OK;
+}
+
+CfgShape cfg_shape(int cfg) {
+  switch (cfg) {
+    case CFG_M16: return {1, 4, 1, 4};
+    case CFG_M32: return {2, 4, 1, 4};
+    case CFG_M64: return {4, 4, 1, 4};
+    default: return {4, 4, 2, 2};
+  }
+}
+
+static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Box geometry for a tiling mode with BN positions per tile.
+static void box_dims(const Geom& g, int mode, int BN, int* rows, int* bw, int64_t* tiles, int* row_tiles) {
+  if (mode == TILE_FLAT) {
+    int64_t rows_out = std::min<int64_t>(g.O[1], (g.O[2] + BN - 2) / g.O[2] + 1);
+    *rows = int((rows_out - 1) * g.S[1] + (g.K[1] - 1) * g.Dl[1] + 1);
+    *bw = int((g.O[2] - 1) * g.S[2] + (g.K[2] - 1) * g.Dl[2] + 1);
+    *tiles = ceil_div(g.plane_out(), BN);
+    *row_tiles = 0;
+  } else {
+    *rows = int((g.K[1] - 1) * g.Dl[1] + 1);
+    int64_t seg = std::min<int64_t>(BN, g.O[2]);
+    *bw = int((seg - 1) * g.S[2] + (g.K[2] - 1) * g.Dl[2] + 1);
+    *row_tiles = int(ceil_div(g.O[2], BN));
+    *tiles = g.O[1] * (*row_tiles);
+  }
+}
+
+int plan_conv(const Geom& g, ConvPlan* out) {
+  ConvPlan p;
+  if (g.Coutg <= 16) p.cfg = CFG_M16;
+  else if (g.Coutg <= 32) p.cfg = CFG_M32;
+  else if (g.Coutg <= 64) p.cfg = CFG_M64;
+  else p.cfg = CFG_M128;
+  CfgShape cs = cfg_shape(p.cfg);
+  p.BM = 16 * cs.MT * cs.WM;
+  p.BN = 16 * cs.NT * cs.WN;
+  // Flattened plane tiles when a tile covers at least two output rows; otherwise
+  // row segments, so the box never spans a full long row.
+  p.mode = (g.O[2] * 2 <= p.BN) ? TILE_FLAT : TILE_ROW;
+  box_dims(g, p.mode, p.BN, &p.rows, &p.bw, &p.tiles_per_plane, &p.row_tiles);
+  p.kdspan = int((g.K[0] - 1) * g.Dl[0] + 1);
+  const int64_t boxc = int64_t(p.kdspan) * p.rows * p.bw;
+  if (boxc > (int64_t(1) << 28)) return CONV_ERR_UNSUPPORTED;
+  p.boxc = int(boxc);
+  p.ldw = (p.BM % 32 == 16) ? p.BM : p.BM + 16;
+  // Channel chunk: among the chunk sizes whose staged box + weights fit the LDS
+  // budget, take the one with the least padded reduction work (chunks x padded
+  // taps per chunk), then the fewest chunks. The budget leaves room for two
+  // workgroups per CU.
+  const int64_t budget = 80 * 1024;
+  auto chunk_bytes = [&](int64_t cc) {
+    int64_t kcp = (cc * g.kvol() + 3) / 4 * 4;
+    return 4 * (cc * p.boxc + 4 + kcp + kcp * p.ldw);
+  };
+  int best = 0;
+  int64_t best_work = 0, best_chunks = 0;
+  for (int64_t cc = 1; cc <= std::min<int64_t>(g.Cg, 256); cc++) {
+    if (chunk_bytes(cc) > budget) break;
+    int64_t chunks = ceil_div(g.Cg, cc);
+    int64_t work = chunks * ((cc * g.kvol() + 3) / 4 * 4);
+    if (best == 0 || work < best_work || (work == best_work && chunks < best_chunks)) {
+      best = int(cc);
+      best_work = work;
+      best_chunks = chunks;
+    }
+  }
+  if (best == 0) {
+    if (chunk_bytes(1) > kLdsLimit) return CONV_ERR_UNSUPPORTED;
+    best = 1;
+  }
+  p.Cc = best;
+  int64_t kc = int64_t(p.Cc) * g.kvol();
+  p.kc_pad = int((kc + 3) / 4 * 4);
+  p.lds_bytes = 4 * (int64_t(p.Cc) * p.boxc + 4 + p.kc_pad + int64_t(p.kc_pad) * p.ldw);
+  p.ctiles = int(ceil_div(g.Coutg, p.BM));
+  p.grid[0] = p.tiles_per_plane;
+  p.grid[1] = g.N * g.O[0];
+  p.grid[2] = g.G * p.ctiles;
+  if (p.grid[0] > std::numeric_limits<int32_t>::max() || p.grid[1] > 65535 || p.grid[2] > 65535)
+    return CONV_ERR_OVERFLOW;
+  *out = p;
+  return CONV_OK;
+}
+
+int plan_fused(const Geom& g, int min_dim, FusedPlan* out) {
+  if (g.nd != 3) return CONV_ERR_RANK;
+  if (min_dim != 2 || g.G != 1 || g.Cout > 64) return CONV_ERR_UNSUPPORTED;
+  FusedPlan p;
+  p.cpad = int((g.Cout + 3) / 4 * 4);
+  p.ng = p.cpad / 4;
+  const int BN = 64;
+  p.mode = (g.O[2] * 2 <= BN) ? TILE_FLAT : TILE_ROW;
+  box_dims(g, p.mode, BN, &p.rows, &p.bw, &p.tiles_per_plane, &p.row_tiles);
+  p.dspan = int((g.O[0] - 1) * g.S[0] + (g.K[0] - 1) * g.Dl[0] + 1);
+  const int64_t boxc = int64_t(p.dspan) * p.rows * p.bw;
+  p.kfull = int(g.Cin * g.kvol());
+  const int64_t box = g.Cin * boxc;
+  const int64_t red = 4 * int64_t(p.cpad) * 64;  // per-wave minima, reuses the box space
+  const int64_t region = std::max(box + 4, red);
+  p.lds_bytes = 4 * (region + p.kfull + int64_t(p.kfull) * p.cpad);
+  if (p.lds_bytes > kLdsLimit || boxc > (int64_t(1) << 28)) return CONV_ERR_UNSUPPORTED;
+  p.boxc = int(boxc);
+  p.grid[0] = p.tiles_per_plane;
+  p.grid[1] = g.N;
+  p.grid[2] = 1;
+  if (p.grid[0] > std::numeric_limits<int32_t>::max() || p.grid[1] > 65535) return CONV_ERR_OVERFLOW;
+  *out = p;
+  return CONV_OK;
+}
+
+std::string describe(const Geom& g, const ConvPlan& p) {
+  char buf[512];
+  CfgShape cs = cfg_shape(p.cfg);
+  std::snprintf(buf, sizeof buf,
+                "kernel=conv_mfma16 cfg=%d MT=%d NT=%d WM=%d WN=%d BM=%d BN=%d mode=%s Cc=%d kc_pad=%d "
+                "box=%dx%dx%d grid=%lldx%lldx%lld lds=%lld macs=%lld",
+                p.cfg, cs.MT, cs.NT, cs.WM, cs.WN, p.BM, p.BN, p.mode == TILE_FLAT ? "flat" : "row", p.Cc,
+                p.kc_pad, p.kdspan, p.rows, p.bw, (long long)p.grid[0], (long long)p.grid[1],
+                (long long)p.grid[2], (long long)p.lds_bytes, (long long)g.macs());
+  return buf;
+}
+
+std::string describe(const Geom& g, const FusedPlan& p) {
+  char buf[512];
+  std::snprintf(buf, sizeof buf,
+                "kernel=fused_min_softmax_mfma4 ng=%d cpad=%d mode=%s box=%dx%dx%dx%d grid=%lldx%lldx%lld "
+                "lds=%lld macs=%lld",
+                p.ng, p.cpad, p.mode == TILE_FLAT ? "flat" : "row", int(g.Cin), p.dspan, p.rows, p.bw,
+                (long long)p.grid[0], (long long)p.grid[1], (long long)p.grid[2], (long long)p.lds_bytes,
+                (long long)g.macs());
+  return buf;
+}
+
+}  // namespace convhip

@@ -1,0 +1,125 @@
+/*
+ * convhip.h -- C ABI of the MI355X (gfx950) fp32 convolution library.
+ *
+ * Operations (the problem statements of the POPCORNBENCH "Kimi-K2.6" pages
+ * l1_p60 "Conv3d, asymmetric 3x5x7 kernel", l1_p76 "Conv1d, stride 3,
+ * dilation 4" and l2_p24 "Conv3d + min + softmax", each page's opening turn):
+ *
+ *   conv_fwd            y = Conv{1,3}d(x, w, bias; stride, dilation, zero padding, groups)
+ *   conv3d_min_softmax  y = softmax over channels of (min over depth of Conv3d(x, w, bias))
+ *
+ * Conventions shared by every entry point
+ *   - Tensors are fp32, contiguous, row-major (NCL / NCDHW). Pointers named x, w,
+ *     bias, y are DEVICE pointers on the current HIP device; shape and parameter
+ *     arrays are HOST pointers, read during the call only.
+ *   - The caller owns every buffer. The library allocates no device memory.
+ *   - Work is enqueued on `stream` (0 = the null stream); the call returns after
+ *     enqueue. The caller synchronises before reading y.
+ *   - Arguments are validated before anything is launched; a negative status is
+ *     returned and nothing runs. A failed launch returns CONV_ERR_HIP.
+ *   - y must not alias x, w or bias. Only zero padding exists.
+ *   - Results are computed in fp32 with fp32 accumulation (products of fp32
+ *     inputs summed by the matrix cores); no reduced-precision arithmetic.
+ */
+#ifndef CONVHIP_H
+#define CONVHIP_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* hipStream_t without including HIP headers: an opaque stream handle. */
+typedef struct ihipStream_t *convhip_stream_t;
+
+typedef enum {
+  CONV_OK = 0,
+  CONV_ERR_NULL = -1,         /* a required pointer is NULL */
+  CONV_ERR_RANK = -2,         /* nd not 1 or 3 */
+  CONV_ERR_SHAPE = -3,        /* non-positive dimension, or w's C_in/groups mismatch */
+  CONV_ERR_GROUPS = -4,       /* groups < 1, or C_in or C_out not divisible by groups */
+  CONV_ERR_PARAM = -5,        /* stride < 1, dilation < 1 or padding < 0 */
+  CONV_ERR_EMPTY_OUTPUT = -6, /* some output length <= 0 */
+  CONV_ERR_UNSUPPORTED = -7,  /* valid, but not handled by this build (stated per entry point) */
+  CONV_ERR_OVERFLOW = -8,     /* a size does not fit the index arithmetic */
+  CONV_ERR_HIP = -9           /* the HIP runtime reported an error at launch */
+} conv_status;
+
+/*
+ * Output length per spatial axis (the pages' formula, with floor division):
+ *   out[i] = floor((in[i] + 2*padding[i] - dilation[i]*(k[i]-1) - 1) / stride[i]) + 1
+ * nd in {1, 2, 3}. Writes out_spatial[0..nd-1] (which may be <= 0) and returns
+ * CONV_OK, or CONV_ERR_EMPTY_OUTPUT if any entry is <= 0 (the entries are still
+ * written), or CONV_ERR_PARAM / CONV_ERR_NULL / CONV_ERR_RANK. Host only.
+ */
+int conv_out_shape(int nd, const int64_t *in_spatial, const int64_t *k_spatial,
+                   const int *stride, const int *dilation, const int *padding,
+                   int64_t *out_spatial);
+
+/*
+ * Forward convolution (pages l1_p60 and l1_p76, opening turns: nn.Conv3d /
+ * nn.Conv1d forward).
+ *   nd = 1: x [N, C_in, L],       w [C_out, C_in/groups, k],            y [N, C_out, L_out]
+ *   nd = 3: x [N, C_in, D, H, W], w [C_out, C_in/groups, kD, kH, kW],   y [N, C_out, D_out, H_out, W_out]
+ *   y[n,co,o] = bias[co] + sum_{c', t} w[co,c',t] * x[n, g(co)*C_in/groups + c', o*stride + t*dilation - padding]
+ *   with out-of-range input reading as 0 and g(co) = co / (C_out/groups).
+ * x_shape / w_shape: nd+2 host entries. stride, dilation, padding: nd host
+ * entries each. bias: device pointer to C_out floats, or NULL for none.
+ * y: device buffer of N*C_out*prod(out) floats, preallocated by the caller.
+ */
+int conv_fwd(int nd,
+             const float *x, const int64_t *x_shape,
+             const float *w, const int64_t *w_shape,
+             const float *bias,
+             const int *stride, const int *dilation, const int *padding, int groups,
+             float *y, convhip_stream_t stream);
+
+/*
+ * Fused Conv3d -> min over depth -> softmax over channels (page l2_p24,
+ * opening turns: the module applies Conv3d, torch.min over dim 2, then
+ * torch.softmax over dim 1). The 5-D conv result is never written to memory.
+ *   x [N, C_in, D, H, W], w [C_out, C_in/groups, kD, kH, kW], bias [C_out] or NULL,
+ *   y [N, C_out, H_out, W_out] with
+ *   y[n,:,h,w] = softmax_c( min_{od} conv3d(x,w,bias)[n,c,od,h,w] ).
+ * Supported in this build: min_dim == 2, groups == 1, C_out <= 64; other valid
+ * arguments return CONV_ERR_UNSUPPORTED. Non-finite inputs: unspecified.
+ */
+int conv3d_min_softmax(const float *x, const int64_t *x_shape,
+                       const float *w, const int64_t *w_shape, const float *bias,
+                       const int *stride, const int *dilation, const int *padding, int groups,
+                       int min_dim, float *y, convhip_stream_t stream);
+
+/* Static text for a status code (never NULL). */
+const char *conv_status_string(int status);
+
+/*
+ * Describe the launch plan the library would use for these arguments (kernel
+ * variant, tile, grid, LDS bytes) as one line of text into buf (NUL-terminated,
+ * truncated to buflen). fused = 0 for conv_fwd, 1 for conv3d_min_softmax (then
+ * nd must be 3). Host only; launches nothing. Returns a conv_status.
+ */
+int conv_plan_describe(int nd, const int64_t *x_shape, const int64_t *w_shape,
+                       const int *stride, const int *dilation, const int *padding, int groups,
+                       int fused, char *buf, int buflen);
+
+/*
+ * Seeded synthetic input generator on the device (not part of the operation:
+ * it lets an input too large for the host be made in place). Writes
+ * dst[i] for i in [0, count) from element index (start + i) of the SplitMix64
+ * stream of `seed` (Steele, Lea & Flood, OOPSLA 2014): with
+ * m = (splitmix64 output) >> 40,
+ *   kind 0: m * 2^-24                        (uniform in [0,1))
+ *   kind 1: fp32(fp32(2*m*2^-24 - 1) * bound) (uniform in [-bound, bound))
+ *   kind 2: lo + ((m * span) >> 24)           (integers in [lo, lo+span))
+ * dst is a device pointer. Returns CONV_OK, CONV_ERR_NULL, CONV_ERR_PARAM
+ * (unknown kind, span < 1) or CONV_ERR_HIP.
+ */
+int convhip_synth_fill(float *dst, int64_t count, uint64_t seed, uint64_t start, int kind,
+                       float bound, int lo, int span, convhip_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CONVHIP_H */

@@ -1,0 +1,107 @@
+"""The C-ABI library loads, exports every declared symbol, and validates
+arguments on the host (no GPU needed: every case here returns before any
+launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import implicit_gemm_convolution_direct_amd as ch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "convhip.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|const char\s*\*)\s*\**\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_binding_names():
+    decl = _declared_functions()
+    assert set(decl) == set(ch.EXPORTED), decl
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ch.lib()
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    for code, name in ch.STATUS_NAMES.items():
+        assert ch.status_string(code).startswith(name)
+
+
+I64 = lambda *v: (ctypes.c_int64 * len(v))(*v)
+I32 = lambda *v: (ctypes.c_int * len(v))(*v)
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+
+
+def _fwd(nd, xs, ws, s, d, p, g, x=FAKE, w=FAKE, y=FAKE):
+    return ch.lib().conv_fwd(nd, x, I64(*xs), w, I64(*ws), None, I32(*s), I32(*d), I32(*p), g, y, None)
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((2, (1, 1, 4, 4), (1, 1, 3, 3), (1, 1), (1, 1), (0, 0), 1), -2),        # rank
+    ((3, (1, 4, 8, 8, 8), (4, 2, 3, 3, 3), (1,) * 3, (1,) * 3, (0,) * 3, 1), -3),  # C_in/groups mismatch
+    ((3, (1, 4, 8, 8, 8), (4, 4, 3, 3, 3), (1,) * 3, (1,) * 3, (0,) * 3, 0), -4),  # groups < 1
+    ((3, (1, 4, 8, 8, 8), (6, 1, 3, 3, 3), (1,) * 3, (1,) * 3, (0,) * 3, 4), -4),  # C_out % groups
+    ((3, (1, 6, 8, 8, 8), (4, 2, 3, 3, 3), (1,) * 3, (1,) * 3, (0,) * 3, 4), -4),  # C_in % groups
+    ((3, (1, 4, 8, 8, 8), (4, 4, 3, 3, 3), (0, 1, 1), (1,) * 3, (0,) * 3, 1), -5),  # stride
+    ((3, (1, 4, 8, 8, 8), (4, 4, 3, 3, 3), (1,) * 3, (1, 0, 1), (0,) * 3, 1), -5),  # dilation
+    ((3, (1, 4, 8, 8, 8), (4, 4, 3, 3, 3), (1,) * 3, (1,) * 3, (0, -1, 0), 1), -5),  # padding
+    ((1, (1, 4, 8), (4, 4, 3), (3,), (4,), (0,), 1), -6),                      # empty output (8 = d(k-1))
+    ((3, (1, 4, 8, 8, 2), (4, 4, 3, 3, 3), (1,) * 3, (1,) * 3, (0,) * 3, 1), -6),
+    ((3, (0, 4, 8, 8, 8), (4, 4, 3, 3, 3), (1,) * 3, (1,) * 3, (0,) * 3, 1), -3),  # zero batch
+])
+def test_conv_fwd_validation_errors(args, expect):
+    assert _fwd(*args) == expect
+
+
+def test_conv_fwd_null_pointers():
+    ok = (3, (1, 4, 8, 8, 8), (4, 4, 3, 3, 3), (1,) * 3, (1,) * 3, (0,) * 3, 1)
+    assert _fwd(*ok, x=None) == -1
+    assert _fwd(*ok, w=None) == -1
+    assert _fwd(*ok, y=None) == -1
+    lib = ch.lib()
+    assert lib.conv_fwd(3, FAKE, None, FAKE, I64(4, 4, 3, 3, 3), None, I32(1, 1, 1), I32(1, 1, 1),
+                        I32(0, 0, 0), 1, FAKE, None) == -1
+
+
+def test_conv3d_min_softmax_validation_errors():
+    lib = ch.lib()
+    xs, ws = I64(2, 3, 6, 6, 6), I64(5, 3, 3, 3, 3)
+    one, zero = I32(1, 1, 1), I32(0, 0, 0)
+    f = lambda **kw: lib.conv3d_min_softmax(kw.get("x", FAKE), kw.get("xs", xs), FAKE, kw.get("ws", ws), None,
+                                            kw.get("s", one), one, zero, kw.get("g", 1), kw.get("md", 2),
+                                            kw.get("y", FAKE), None)
+    assert f(y=None) == -1
+    assert f(md=5) == -5
+    assert f(md=3) == -7          # other axes: unsupported in this build
+    assert f(g=3) == -7 or f(g=3) == -4
+    assert f(ws=I64(6, 1, 3, 3, 3), xs=I64(2, 3, 6, 6, 6), g=3) == -7   # grouped fused: unsupported
+    assert f(ws=I64(65, 3, 3, 3, 3)) == -7                             # C_out > 64: unsupported
+    assert f(xs=I64(2, 3, 2, 6, 6)) == -6
+    assert f(s=I32(1, 0, 1)) == -5
+
+
+def test_conv_out_shape_matches_pages():
+    assert ch.out_shape([524280], [3], 3, 4, 0) == (0, [174758])
+    assert ch.out_shape([24, 32, 32], [3, 3, 3], 1, 1, 0) == (0, [22, 30, 30])
+    assert ch.out_shape([64, 64, 64], [3, 5, 7], 1, 1, 0) == (0, [62, 60, 58])
+    assert ch.out_shape([32, 32, 32], [3, 5, 7], (1, 2, 2), (1, 1, 2), (1, 2, 3)) == (0, [32, 16, 13])
+    assert ch.out_shape([8], [3], 3, 4, 0)[0] == -6
+
+
+def test_plans_fit_lds_and_cover_workloads():
+    import synth
+    for name, cfg in synth.WORKLOADS.items():
+        d = ch.plan_describe(cfg["x"], cfg["w"], cfg["stride"], cfg["dilation"], cfg["padding"], cfg["groups"],
+                             fused=cfg["fused"])
+        fields = dict(t.split("=", 1) for t in d.split() if "=" in t)
+        assert int(fields["lds"]) <= 160 * 1024, d
+        gx, gy, gz = (int(v) for v in fields["grid"].split("x"))
+        assert gx >= 1 and gy >= 1 and gz >= 1
