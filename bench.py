@@ -1,0 +1,266 @@
+"""Benchmark of the fp32 convolution hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAME] [--no-cpu]
+
+One "step" is one call of the library's entry point over one batch of the
+headline workload, the general-parameter Conv3d (x[4,16,32,32,32], w[32,8,3,5,7],
+groups 2, stride (1,2,2), padding (1,2,3), dilation (1,1,2)). The same run also
+times every other workload (tiny Conv3d, fused Conv3d+min+softmax, asymmetric
+Conv3d, long Conv1d) and reports them under "shapes". Inputs are seeded
+synthetic tensors already resident in device memory; the timed region is K
+back-to-back calls between two device synchronisations, timed with events on
+the stream the kernels are launched on.
+
+Prints one JSON line. Throughput = 2 * MACs / time (MACs count every kernel
+tap, padded ones included). Roofline fractions use MI355X's published peaks:
+fp32 matrix 157.3 TFLOP/s, HBM 8.0 TB/s.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+HEADLINE = "general_conv3d"
+ORDER = ["tiny_conv3d", "general_conv3d", "conv3d_min_softmax", "asym_conv3d", "long_conv1d"]
+KERNEL_SOURCES = [os.path.join(ROOT, "implicit_gemm_convolution_direct_amd", "csrc", f)
+                  for f in ("conv_kernels.hip", "convhip_plan.cpp", "convhip_plan.h")]
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def geometry(cfg):
+    """Output shape, MACs and algorithmic bytes (x, w, bias read once, y written once)."""
+    xs, ws = cfg["x"], cfg["w"]
+    nd = cfg["nd"]
+    out = []
+    for a in range(nd):
+        L, k, s, d, p = xs[2 + a], ws[2 + a], cfg["stride"][a], cfg["dilation"][a], cfg["padding"][a]
+        out.append((L + 2 * p - d * (k - 1) - 1) // s + 1)
+    kred = int(np.prod(ws[1:]))
+    conv_elems = xs[0] * ws[0] * int(np.prod(out))
+    macs = conv_elems * kred
+    if cfg["fused"]:
+        y_elems = xs[0] * ws[0] * int(np.prod(out[1:]))
+    else:
+        y_elems = conv_elems
+    nbytes = 4 * (int(np.prod(xs)) + int(np.prod(ws)) + (ws[0] if cfg["bias"] else 0) + y_elems)
+    return out, macs, nbytes, conv_elems, y_elems
+
+
+def read_traffic(name):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{name}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if "=" in line and not line.startswith("#"):
+                k, v = line.split("=", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_src_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def make_device_inputs(name, torch, ch, synth):
+    cfg = synth.WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    sx, sw, sb = cfg["seeds"]
+    x = torch.empty(cfg["x"], dtype=torch.float32, device=dev)
+    ch.synth_fill(x, sx, ch.KIND_UNIFORM01)
+    fan = synth.fan_in(cfg["w"])
+    w = torch.empty(cfg["w"], dtype=torch.float32, device=dev)
+    ch.synth_fill(w, sw, ch.KIND_SYMMETRIC, bound=synth.symmetric_bound(fan))
+    b = None
+    if cfg["bias"]:
+        b = torch.empty((cfg["w"][0],), dtype=torch.float32, device=dev)
+        ch.synth_fill(b, sb, ch.KIND_SYMMETRIC, bound=synth.symmetric_bound(fan))
+    return cfg, x, w, b
+
+
+def time_workload(name, steps, warmup, torch, ch, synth):
+    cfg, x, w, b = make_device_inputs(name, torch, ch, synth)
+    out, macs, nbytes, conv_elems, y_elems = geometry(cfg)
+    args = (cfg["stride"], cfg["dilation"], cfg["padding"], cfg["groups"])
+    if cfg["fused"]:
+        y = torch.empty((cfg["x"][0], cfg["w"][0], *out[1:]), dtype=torch.float32, device=x.device)
+        call = lambda: ch.conv3d_min_softmax(x, w, b, *args, min_dim=2, out=y)
+    else:
+        y = torch.empty((cfg["x"][0], cfg["w"][0], *out), dtype=torch.float32, device=x.device)
+        call = lambda: ch.conv_fwd(x, w, b, *args, out=y)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / steps
+    # Per-launch durations of a few isolated launches, for the spread.
+    singles = []
+    for _ in range(min(steps, 10)):
+        a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        call()
+        z.record(stream)
+        torch.cuda.synchronize()
+        singles.append(a.elapsed_time(z))
+    tflops = 2.0 * macs / (ms * 1e-3) / 1e12
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    rec = {
+        "workload": name,
+        "plan": ch.plan_describe(cfg["x"], cfg["w"], *args, fused=cfg["fused"]),
+        "ms": round(ms, 5),
+        "ms_single_min": round(min(singles), 5),
+        "ms_single_max": round(max(singles), 5),
+        "tflops": round(tflops, 3),
+        "gbs": round(gbs, 1),
+        "frac_fp32_peak": round(tflops / PEAK_FP32_TFLOPS, 4),
+        "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+        "macs": macs,
+        "alg_bytes": nbytes,
+        "wall_s": round(wall, 3),
+    }
+    if cfg["fused"]:
+        # Unfused chain: conv writes the 5-D result, min reads it and writes its
+        # result, softmax reads and writes that (algorithmic bytes).
+        unfused = 4 * (int(np.prod(cfg["x"])) + int(np.prod(cfg["w"])) + cfg["w"][0]
+                       + 2 * conv_elems + 3 * y_elems)
+        rec["unfused_alg_bytes"] = unfused
+        rec["fused_traffic_ratio_alg"] = round(unfused / nbytes, 2)
+    del x, w, b, y
+    torch.cuda.empty_cache()
+    return rec, macs
+
+
+def cpu_baseline(name):
+    """The fp64 oracle on the full headline workload, timed on the host cores."""
+    import oracle
+    import synth
+    cfg = synth.WORKLOADS[name]
+    x, w, b = synth.make_inputs(name)
+    _, macs, _, _, _ = geometry(cfg)
+    args = (cfg["stride"], cfg["dilation"], cfg["padding"], cfg["groups"])
+    oracle.conv(x[:1], w, b, *args)  # load the library, warm the threads
+    reps, t = 0, 0.0
+    t0 = time.perf_counter()
+    while reps < 1 or (time.perf_counter() - t0 < 10.0 and reps < 8):
+        ref = oracle.conv(x, w, b, *args)
+        reps += 1
+    t = (time.perf_counter() - t0) / reps
+    return {"value": round(2.0 * macs / t / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"full {name} workload (batch {cfg['x'][0]}), fp64 nested loops, {reps} pass(es), "
+                      f"{t:.3f} s per pass"}, ref
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--only", choices=ORDER, default=None, help="time one workload only (for profiling)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the convolution shards over the batch with no exchange; see DESIGN.md). Use --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import implicit_gemm_convolution_direct_amd as ch
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    ch.lib()
+
+    names = [args.only] if args.only else ORDER
+    shapes = {}
+    head = None
+    for name in names:
+        print(f"[bench] timing {name}", file=sys.stderr, flush=True)
+        rec, macs = time_workload(name, args.steps, args.warmup, torch, ch, synth)
+        shapes[name] = rec
+        print(f"[bench] {name}: {rec['ms']:.4f} ms  {rec['tflops']:.2f} TFLOP/s  "
+              f"({100 * rec['frac_fp32_peak']:.1f}% of fp32 peak)", file=sys.stderr, flush=True)
+    if args.only:
+        head = shapes[args.only]
+        head_name = args.only
+    else:
+        head = shapes[HEADLINE]
+        head_name = HEADLINE
+
+    cpu = None
+    parity = None
+    if not args.no_cpu and not args.only:
+        print("[bench] oracle CPU baseline", file=sys.stderr, flush=True)
+        cpu, ref = cpu_baseline(HEADLINE)
+        # Parity of the headline launch against the oracle on the same seeded inputs.
+        cfg, x, w, b = make_device_inputs(HEADLINE, torch, ch, synth)
+        y = ch.conv_fwd(x, w, b, cfg["stride"], cfg["dilation"], cfg["padding"], cfg["groups"])
+        torch.cuda.synchronize()
+        err = float(np.abs(y.cpu().numpy().astype(np.float64) - ref).max())
+        tol = 1e-4 * math.sqrt(int(np.prod(cfg["w"][1:]))) * float(np.abs(ref).max())
+        parity = {"max_abs_err": err, "tol": tol, "pass": err <= tol}
+
+    cfgh = synth.WORKLOADS[head_name]
+    traffic = read_traffic(head_name)
+    achieved = head["tflops"]
+    line = {
+        "metric": "conv fwd TFLOP/s (fp32) and % of MI355X FP32/HBM roofline per shape",
+        "value": achieved,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded SplitMix64: x~U[0,1), w,b~U(+-1/sqrt(fan_in)))",
+        "config": {"workload": head_name, "x": list(cfgh["x"]), "w": list(cfgh["w"]),
+                   "stride": list(cfgh["stride"]), "padding": list(cfgh["padding"]),
+                   "dilation": list(cfgh["dilation"]), "groups": cfgh["groups"], "bias": cfgh["bias"]},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_FP32_TFLOPS, 4), "traffic": traffic},
+        "cpu_baseline": cpu,
+        "parity": parity,
+        "shapes": shapes,
+        "kernel_src": kernel_source_hash(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
