@@ -22,6 +22,7 @@
 
 #include <cstdint>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <utility>
@@ -46,62 +47,104 @@ struct ConvArgs {
   int P0, P1, P2;
   int O0, O1, O2;
   int kvol, kfull;
-  int mode, Cc, kc_pad, ldw, kdspan, rows, bw, boxc;
-  int row_tiles, ctiles;
+  int mode, Cc, kc_pad, kdspan, rows, bw, boxc;
+  int xs_floats, koff_ints, ws_floats;
+  int row_tiles, ctiles, tiles_per_plane;
   int plane_out;
+  int nchunks;
+  int items;  // persistent kernel: (tile, plane) work items
 };
 
-// ---------------------------------------------------------------------------
-// conv_mfma16
-// ---------------------------------------------------------------------------
-template <int MT, int NT, int WM, int WN>
-__global__ __launch_bounds__(256) void conv_mfma16_kernel(ConvArgs a) {
-  constexpr int BM = 16 * MT * WM;
-  constexpr int BN = 16 * NT * WN;
-  extern __shared__ float smem[];
-  float* Xs = smem;
-  const int zero_idx = a.Cc * a.boxc;
-  int* koff = reinterpret_cast<int*>(smem + zero_idx + 4);
-  float* Ws = smem + zero_idx + 4 + a.kc_pad;
+// q = n / d and r = n % d for 0 <= n < 2^24, d >= 1, from a float reciprocal
+// with one correction step (the product is within one of the true quotient).
+__device__ __forceinline__ int divmod_small(int n, int d, float inv, int& r) {
+  int q = int(float(n) * inv);
+  r = n - q * d;
+  if (r < 0) { q -= 1; r += d; }
+  if (r >= d) { q += 1; r -= d; }
+  return q;
+}
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave / WN;
-  const int wn = wave - wm * WN;
-  const int kg = lane >> 4;   // k row of this lane inside a 4-deep MFMA step
-  const int li = lane & 15;   // m (A operand) or n (B operand) index of this lane
+template <int MT>
+struct AFrag;
+template <>
+struct AFrag<1> {
+  float v[1];
+  __device__ __forceinline__ void load(const float* __restrict__ p) { v[0] = p[0]; }
+};
+template <>
+struct AFrag<2> {
+  float v[2];
+  __device__ __forceinline__ void load(const float* __restrict__ p) {
+    const float2 t = *reinterpret_cast<const float2*>(p);
+    v[0] = t.x; v[1] = t.y;
+  }
+};
+template <>
+struct AFrag<4> {
+  float v[4];
+  __device__ __forceinline__ void load(const float* __restrict__ p) {
+    const float4 t = *reinterpret_cast<const float4*>(p);
+    v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+  }
+};
 
-  // Workgroup coordinates: position tile, (n, od) plane, (group, channel tile).
-  const int tile = blockIdx.x;
-  const int plane = blockIdx.y;
-  const int n = plane / a.O0;
-  const int od = plane - n * a.O0;
-  const int gz = blockIdx.z;
-  const int g = gz / a.ctiles;
-  const int m0 = (gz - g * a.ctiles) * BM;
+// A zero word in device memory: global->LDS copies of padding elements read it.
+__device__ const float kZeroWord[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 
-  int oh_first, oh_last, ow0 = 0, p0 = 0;
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima), emitted through the
+// builtin so the compiler's own wait-count tracking sees it.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Asynchronous copy of one float per lane from global memory into LDS: lane l
+// of the wave writes dst[l] (dst is the same for the whole wave).
+__device__ __forceinline__ void lds_dma_f32(const float* src, float* dst) {
+  __builtin_amdgcn_global_load_lds(src, dst, 4, 0, 0);
+}
+
+// Geometry of one output tile: BN positions of the (n, od) plane, BM channels
+// of group g starting at m0.
+struct TileGeo {
+  int n, od, g, m0;
+  int oh_first, ow0, p0, iwb;
+  int id0, ih0, iw0;
+  int rows_ld;  // input rows per plane in the staged box
+};
+
+__device__ __forceinline__ TileGeo tile_geo(const ConvArgs& a, int tile, int plane, int gz, int BM, int BN,
+                                            bool fixed_rows) {
+  TileGeo t;
+  t.n = plane / a.O0;
+  t.od = plane - t.n * a.O0;
+  t.g = gz / a.ctiles;
+  t.m0 = (gz - t.g * a.ctiles) * BM;
+  int oh_last;
   if (a.mode == TILE_FLAT) {
-    p0 = tile * BN;
-    const int p_last = min(p0 + BN, a.plane_out) - 1;
-    oh_first = p0 / a.O2;
+    t.p0 = tile * BN;
+    t.ow0 = 0;
+    const int p_last = min(t.p0 + BN, a.plane_out) - 1;
+    t.oh_first = t.p0 / a.O2;
     oh_last = p_last / a.O2;
   } else {
-    oh_first = oh_last = tile / a.row_tiles;
-    ow0 = (tile - oh_first * a.row_tiles) * BN;
+    t.p0 = 0;
+    t.oh_first = oh_last = tile / a.row_tiles;
+    t.ow0 = (tile - t.oh_first * a.row_tiles) * BN;
   }
-  const int iwb = ow0 * a.S2;  // box column 0 is input column iwb - P2
-  const int rows_needed = (oh_last - oh_first) * a.S1 + (a.K1 - 1) * a.D1 + 1;
-  const int id0 = od * a.S0 - a.P0;
-  const int ih0 = oh_first * a.S1 - a.P1;
-  const int iw0 = iwb - a.P2;
-  const int plane_stride = a.rows * a.bw;
+  t.iwb = t.ow0 * a.S2;  // box column 0 is input column iwb - P2
+  t.id0 = t.od * a.S0 - a.P0;
+  t.ih0 = t.oh_first * a.S1 - a.P1;
+  t.iw0 = t.iwb - a.P2;
+  t.rows_ld = fixed_rows ? a.rows : (oh_last - t.oh_first) * a.S1 + (a.K1 - 1) * a.D1 + 1;
+  return t;
+}
 
-  // Offset of every (channel, tap) of a chunk inside the staged box. Padding taps
-  // (k >= Cc*kvol) carry zero weights and point at the box start, so the value
-  // they multiply is a staged, finite input element.
-  for (int k = tid; k < a.kc_pad; k += 256) {
+// Offset of every (channel, tap) of a chunk inside a box with rows_ld rows per
+// plane. Padding taps (k >= Cc*kvol) carry zero weights and point at the box
+// start, a staged finite element; entries past kc_pad serve the prefetch.
+__device__ __forceinline__ void build_koff(const ConvArgs& a, int rows_ld, int* koff, int tid) {
+  const int plane_stride = rows_ld * a.bw;
+  const int boxc_t = a.kdspan * plane_stride;
+  for (int k = tid; k < a.koff_ints; k += 256) {
     int off = 0;
     if (k < a.Cc * a.kvol) {
       const int c = k / a.kvol;
@@ -110,31 +153,397 @@ __global__ __launch_bounds__(256) void conv_mfma16_kernel(ConvArgs a) {
       const int r2 = r - td * a.K1 * a.K2;
       const int th = r2 / a.K2;
       const int tw = r2 - th * a.K2;
-      off = c * a.boxc + td * a.D0 * plane_stride + th * a.D1 * a.bw + tw * a.D2;
+      off = c * boxc_t + td * a.D0 * plane_stride + th * a.D1 * a.bw + tw * a.D2;
     }
     koff[k] = off;
   }
+}
 
-  // Per-lane output positions of this wave's NT sub-tiles.
-  int noff[NT];
-  int pidx[NT];
+// Copy the box of channels [c0, c0+Cc) of a tile into dst, dense layout
+// [c][zd][zr < rows_ld][col]. Every lane writes its own LDS slot; slots whose
+// source lies outside the input (zero padding, channels past C_in/groups) read
+// the zero word.
+template <int NWAVES = 4>
+__device__ __forceinline__ void stage_box(const ConvArgs& a, const TileGeo& t, int c0, float* dst, int wave,
+                                          int lane) {
+  const int cc_count = min(a.Cc, a.Cg - c0);
+  const int rows_per_c = a.kdspan * t.rows_ld;
+  const int box_elems = a.Cc * rows_per_c * a.bw;
+  const float inv_bw = 1.0f / float(a.bw);
+  const float inv_rpc = 1.0f / float(rows_per_c);
+  const float inv_rn = 1.0f / float(t.rows_ld);
+  const int64_t x_n = (int64_t(t.n) * a.Cin + int64_t(t.g) * a.Cg + c0) * a.L0;
+  const int box_waves = (box_elems + 63) >> 6;
+  for (int wi = wave; wi < box_waves; wi += NWAVES) {
+    const int e = wi * 64 + lane;
+    int col, rem, zr;
+    const int row = divmod_small(e, a.bw, inv_bw, col);
+    const int c = divmod_small(row, rows_per_c, inv_rpc, rem);
+    const int zd = divmod_small(rem, t.rows_ld, inv_rn, zr);
+    const int id = t.id0 + zd, ih = t.ih0 + zr, iw = t.iw0 + col;
+    const bool ok = (e < box_elems) && (c < cc_count) && (unsigned(id) < unsigned(a.L0)) &&
+                    (unsigned(ih) < unsigned(a.L1)) && (unsigned(iw) < unsigned(a.L2));
+    const float* src = ok ? a.x + (((x_n + int64_t(c) * a.L0 + id) * a.L1 + ih) * a.L2 + iw) : kZeroWord;
+    lds_dma_f32(src, dst + wi * 64);
+  }
+}
+
+// Copy the weight fragments of channels [c0, c0+Cc) (k-steps 0..nsteps-1 of a
+// chunk) into dst, in the order the matrix core consumes them: for k-step s and
+// wave row wm, lane l holds W[m = wm*16*MT + 16*mi + (l%16)][k = 4s + l/16] for
+// mi = 0..MT-1 contiguously, so one vector LDS read delivers a lane's A operands.
+template <int MT, int WM, int NWAVES = 4>
+__device__ __forceinline__ void stage_wfrag(const ConvArgs& a, int g, int m0, int c0, int nsteps, float* dst,
+                                            int wave, int lane) {
+  const int cc_count = min(a.Cc, a.Cg - c0);
+  const int kvalid = cc_count * a.kvol;
+  const int64_t w_g = int64_t(g * a.Coutg + m0) * a.kfull + int64_t(c0) * a.kvol;
+  const int w_waves = (nsteps * WM * 64 * MT) >> 6;
+  for (int wi = wave; wi < w_waves; wi += NWAVES) {
+    const int f = wi * 64 + lane;
+    const int mi = f % MT;
+    const int q = f / MT;  // (s*WM + fwm)*64 + fl
+    const int fl = q & 63;
+    const int sw = q >> 6;
+    const int s = sw / WM;
+    const int fwm = sw - s * WM;
+    const int k = 4 * s + (fl >> 4);
+    const int m = fwm * 16 * MT + 16 * mi + (fl & 15);
+    const bool ok = (k < kvalid) && (m0 + m < a.Coutg);
+    const float* src = ok ? a.w + (w_g + int64_t(m) * a.kfull + k) : kZeroWord;
+    lds_dma_f32(src, dst + wi * 64);
+  }
+}
+
+// Per-lane output positions of a wave's NT sub-tiles: LDS offset inside the box
+// (row stride bw) and flattened index in the (n, co, od) output plane (-1: none).
+template <int NT>
+__device__ __forceinline__ void tile_positions(const ConvArgs& a, const TileGeo& t, int wn, int li, int noff[NT],
+                                               int pidx[NT]) {
 #pragma unroll
   for (int ni = 0; ni < NT; ni++) {
     const int q = wn * (16 * NT) + 16 * ni + li;
     int oh, ow, valid;
     if (a.mode == TILE_FLAT) {
-      const int p = p0 + q;
+      const int p = t.p0 + q;
       valid = p < a.plane_out;
       oh = p / a.O2;
       ow = p - oh * a.O2;
     } else {
-      oh = oh_first;
-      ow = ow0 + q;
+      oh = t.oh_first;
+      ow = t.ow0 + q;
       valid = ow < a.O2;
     }
-    noff[ni] = valid ? (oh - oh_first) * a.S1 * a.bw + ow * a.S2 - iwb : 0;
+    noff[ni] = valid ? (oh - t.oh_first) * a.S1 * a.bw + ow * a.S2 - t.iwb : 0;
     pidx[ni] = valid ? oh * a.O2 + ow : -1;
   }
+}
+
+// Reduction of one staged chunk: this wave takes k-steps ks, ks+KS, ... < nsteps,
+// software-pipelined (tap offsets two steps ahead, operands one step ahead of
+// the matrix-core instructions that use them).
+template <int MT, int NT, int WM, int KS>
+__device__ __forceinline__ void mma_chunk(const float* __restrict__ Xs, const float* __restrict__ Ws,
+                                          const int* __restrict__ koff, int nsteps, int ks, int wfrag_base,
+                                          const int (&noff)[NT], v4f (&acc)[MT][NT], int kg) {
+  constexpr int SSTRIDE = WM * 64 * MT;
+  int s = ks;
+  int ko_next = koff[4 * (s + KS) + kg];
+  AFrag<MT> af;
+  float bv[NT];
+  {
+    const int ko = koff[4 * s + kg];
+    af.load(Ws + s * SSTRIDE + wfrag_base);
+#pragma unroll
+    for (int ni = 0; ni < NT; ni++) bv[ni] = Xs[ko + noff[ni]];
+  }
+  for (; s < nsteps; s += KS) {
+    AFrag<MT> af_n;
+    float bv_n[NT];
+    const int ko = ko_next;
+    ko_next = koff[4 * (s + 2 * KS) + kg];
+    af_n.load(Ws + (s + KS) * SSTRIDE + wfrag_base);
+#pragma unroll
+    for (int ni = 0; ni < NT; ni++) bv_n[ni] = Xs[ko + noff[ni]];
+#pragma unroll
+    for (int mi = 0; mi < MT; mi++)
+#pragma unroll
+      for (int ni = 0; ni < NT; ni++)
+        acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x4f32(af.v[mi], bv[ni], acc[mi][ni], 0, 0, 0);
+    af = af_n;
+#pragma unroll
+    for (int ni = 0; ni < NT; ni++) bv[ni] = bv_n[ni];
+  }
+}
+
+// Bias of the channels this lane stores: register r of sub-tile mi holds channel
+// m0 + wm*16*MT + 16*mi + 4*kg + r. Loaded once, so no global load sits between
+// the output stores.
+template <int MT>
+__device__ __forceinline__ void load_bias(const ConvArgs& a, const TileGeo& t, int wm, int kg, float (&bias)[MT][4]) {
+#pragma unroll
+  for (int mi = 0; mi < MT; mi++)
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      const int ch = t.m0 + wm * 16 * MT + 16 * mi + 4 * kg + r;
+      bias[mi][r] = (a.bias && ch < a.Coutg) ? a.bias[t.g * a.Coutg + ch] : 0.0f;
+    }
+}
+
+// Store a wave tile (+ bias). D[m][n] of the matrix core sits in lane
+// n + 16*(m/4), register m%4.
+template <int MT, int NT>
+__device__ __forceinline__ void store_tile(const ConvArgs& a, const TileGeo& t, int wm, int kg,
+                                           const int (&pidx)[NT], const v4f (&acc)[MT][NT],
+                                           const float (&bias)[MT][4]) {
+  const int64_t out_plane = int64_t(a.O1) * a.O2;
+#pragma unroll
+  for (int mi = 0; mi < MT; mi++) {
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      const int ch = t.m0 + wm * 16 * MT + 16 * mi + 4 * kg + r;
+      if (ch < a.Coutg) {
+        const int co = t.g * a.Coutg + ch;
+        float* yp = a.y + ((int64_t(t.n) * a.Cout + co) * a.O0 + t.od) * out_plane;
+#pragma unroll
+        for (int ni = 0; ni < NT; ni++)
+          if (pidx[ni] >= 0) yp[pidx[ni]] = acc[mi][ni][r] + bias[mi][r];
+      }
+    }
+  }
+}
+
+// One pipeline stage of the streamed kernel: start the copies of the next chunk
+// into `nxt`, then reduce the chunk in `cur`. The buffers are distinct; the
+// restrict qualifiers let the compiler keep the copies in flight across the
+// reduction instead of waiting for them before every LDS read.
+template <int MT, int NT, int WM, int KS>
+__device__ __forceinline__ void stream_stage(const ConvArgs& a, const TileGeo& t, bool has_next, int c0_next,
+                                             const float* __restrict__ cur, float* __restrict__ nxt,
+                                             const int* __restrict__ koff, int nsteps, int ks, int wfrag_base,
+                                             const int (&noff)[NT], v4f (&acc)[MT][NT], int kg, int wave, int lane) {
+  if (has_next) {
+    stage_box(a, t, c0_next, nxt, wave, lane);
+    stage_wfrag<MT, WM>(a, t.g, t.m0, c0_next, nsteps, nxt + a.xs_floats, wave, lane);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  mma_chunk<MT, NT, WM, KS>(cur, cur + a.xs_floats, koff, nsteps, ks, wfrag_base, noff, acc, kg);
+}
+
+// ---------------------------------------------------------------------------
+// conv_mfma16 (streamed): one tile per workgroup; chunks of input channels
+// (box + weight fragments) are double-buffered in LDS.
+// LDS (floats): [ koff | buffer 0 | buffer 1 ], buffer = [ box | weights ].
+// ---------------------------------------------------------------------------
+template <int MT, int NT, int WM, int WN, int KS>
+__global__ __launch_bounds__(256) void conv_mfma16_kernel(ConvArgs a) {
+  constexpr int BM = 16 * MT * WM;
+  constexpr int BN = 16 * NT * WN;
+  extern __shared__ __align__(16) float smem[];
+  int* koff = reinterpret_cast<int*>(smem);
+  float* buf0 = smem + a.koff_ints;
+  float* buf1 = buf0 + a.xs_floats + a.ws_floats;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ks = wave % KS;
+  const int wt = wave / KS;
+  const int wm = wt / WN;
+  const int wn = wt - wm * WN;
+  const int kg = lane >> 4;
+  const int li = lane & 15;
+
+  const TileGeo t = tile_geo(a, blockIdx.x, blockIdx.y, blockIdx.z, BM, BN, false);
+  const int nsteps = a.kc_pad >> 2;
+  build_koff(a, t.rows_ld, koff, tid);
+  int noff[NT], pidx[NT];
+  tile_positions<NT>(a, t, wn, li, noff, pidx);
+  v4f acc[MT][NT];
+#pragma unroll
+  for (int mi = 0; mi < MT; mi++)
+#pragma unroll
+    for (int ni = 0; ni < NT; ni++) acc[mi][ni] = v4f{0.f, 0.f, 0.f, 0.f};
+  const int wfrag_base = wm * 64 * MT + lane * MT;
+  float bias[MT][4];
+  load_bias<MT>(a, t, wm, kg, bias);
+
+  stage_box(a, t, 0, buf0, wave, lane);
+  stage_wfrag<MT, WM>(a, t.g, t.m0, 0, nsteps, buf0 + a.xs_floats, wave, lane);
+  wait_vmem();
+  __syncthreads();
+  for (int ci = 0; ci < a.nchunks; ci++) {
+    const bool has_next = ci + 1 < a.nchunks;
+    if (ci & 1)
+      stream_stage<MT, NT, WM, KS>(a, t, has_next, (ci + 1) * a.Cc, buf1, buf0, koff, nsteps, ks, wfrag_base,
+                                   noff, acc, kg, wave, lane);
+    else
+      stream_stage<MT, NT, WM, KS>(a, t, has_next, (ci + 1) * a.Cc, buf0, buf1, koff, nsteps, ks, wfrag_base,
+                                   noff, acc, kg, wave, lane);
+    wait_vmem();       // this thread's copies of the next chunk have landed
+    __syncthreads();   // everyone's copies have landed; everyone is done with the current buffer
+  }
+
+  if constexpr (KS > 1) {
+    // Add the split-reduction partial sums through LDS (the buffers are free).
+    constexpr int TILE_F = MT * NT * 4 * 64;
+    float* red = buf0;
+    if (ks > 0) {
+      float* dstp = red + ((ks - 1) * (WM * WN) + wt) * TILE_F;
+#pragma unroll
+      for (int mi = 0; mi < MT; mi++)
+#pragma unroll
+        for (int ni = 0; ni < NT; ni++)
+#pragma unroll
+          for (int r = 0; r < 4; r++) dstp[((mi * NT + ni) * 4 + r) * 64 + lane] = acc[mi][ni][r];
+    }
+    __syncthreads();
+    if (ks != 0) return;
+#pragma unroll
+    for (int j = 1; j < KS; j++) {
+      const float* srcp = red + ((j - 1) * (WM * WN) + wt) * TILE_F;
+#pragma unroll
+      for (int mi = 0; mi < MT; mi++)
+#pragma unroll
+        for (int ni = 0; ni < NT; ni++)
+#pragma unroll
+          for (int r = 0; r < 4; r++) acc[mi][ni][r] += srcp[((mi * NT + ni) * 4 + r) * 64 + lane];
+    }
+  }
+  store_tile<MT, NT>(a, t, wm, kg, pidx, acc, bias);
+}
+
+// ---------------------------------------------------------------------------
+// conv_tap: the implicit GEMM specialised at build time for one geometry
+// (channel chunk, kernel taps, dilations, strides, staged box shape, tiling).
+// Every tap offset is a compile-time constant, so each matrix-core B operand is
+// one LDS read at (per-lane register + immediate offset): the register holds the
+// lane's output-position offset plus the lane's share of the 4-deep k-step, and
+// the few distinct per-step lane patterns are precomputed once per tile.
+// The kernel is persistent: each workgroup keeps the whole weight matrix in LDS
+// and walks work items (tile, plane) blockIdx.x, blockIdx.x + gridDim.x, ...;
+// chunks of the input box are double-buffered and copied by the DMA engine while
+// the previous chunk is reduced.
+// LDS (floats): [ box 0 | box 1 | weight fragments of all chunks (+1 step) ].
+// ---------------------------------------------------------------------------
+template <int KD, int KH, int KW, int DD, int DH, int DW, int CC, int KDSPAN, int ROWS, int BW>
+struct TapGeo {
+  static constexpr int CCH = CC;
+  static constexpr int KVOL = KD * KH * KW;
+  static constexpr int K = CC * KVOL;
+  static constexpr int NS = (K + 3) / 4;  // 4-deep k-steps per chunk
+  static constexpr int PLANE = ROWS * BW;
+  static constexpr int BOXC = KDSPAN * PLANE;
+  static constexpr int XS = (CC * BOXC + 255) / 256 * 256;  // floats per box buffer
+  // LDS offset (floats) of reduction index k = (channel, td, th, tw) of a chunk;
+  // padding indices (zero weights) point at the box start.
+  static constexpr int koff(int k) {
+    if (k >= K) return 0;
+    const int c = k / KVOL, r = k % KVOL, td = r / (KH * KW), r2 = r % (KH * KW), th = r2 / KW, tw = r2 % KW;
+    return c * BOXC + td * DD * PLANE + th * DH * BW + tw * DW;
+  }
+};
+
+// Distinct per-step lane patterns koff(4s + j) - koff(4s), j = 0..3.
+template <class G>
+struct TapPatterns {
+  int np = 0;
+  int pid[G::NS] = {};
+  int pat[G::NS][4] = {};
+  constexpr TapPatterns() {
+    for (int s = 0; s < G::NS; s++) {
+      int d[4] = {};
+      for (int j = 0; j < 4; j++) d[j] = G::koff(4 * s + j) - G::koff(4 * s);
+      int found = -1;
+      for (int q = 0; q < np && found < 0; q++) {
+        bool eq = true;
+        for (int j = 0; j < 4; j++) eq = eq && pat[q][j] == d[j];
+        if (eq) found = q;
+      }
+      if (found < 0) {
+        for (int j = 0; j < 4; j++) pat[np][j] = d[j];
+        found = np++;
+      }
+      pid[s] = found;
+    }
+  }
+};
+
+// Reduce one staged chunk: all k-steps unrolled, B operands read at
+// (lane register + immediate), A operands from the resident weight fragments
+// (wchunk already includes this lane's and wave row's offset).
+template <int MT, int NT, int WM, class G, int NP>
+__device__ __forceinline__ void tap_chunk(const float* __restrict__ box, const float* __restrict__ wchunk,
+                                          const int (&addr)[NP][NT], v4f (&acc)[MT][NT]) {
+  constexpr TapPatterns<G> P{};
+  const char* bb = reinterpret_cast<const char*>(box);
+#pragma unroll
+  for (int s = 0; s < G::NS; s++) {
+    AFrag<MT> af;
+    af.load(wchunk + s * (WM * 64 * MT));
+    float bv[NT];
+#pragma unroll
+    for (int ni = 0; ni < NT; ni++)
+      bv[ni] = *reinterpret_cast<const float*>(bb + addr[P.pid[s]][ni] + 4 * G::koff(4 * s));
+#pragma unroll
+    for (int mi = 0; mi < MT; mi++)
+#pragma unroll
+      for (int ni = 0; ni < NT; ni++)
+        acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x4f32(af.v[mi], bv[ni], acc[mi][ni], 0, 0, 0);
+  }
+}
+
+// One pipeline stage: start the copy of the next box into `nxt`, then reduce the
+// box in `cur` (distinct buffers; see stream_stage).
+template <int MT, int NT, int WM, int NWAVES, class G, int NP>
+__device__ __forceinline__ void tap_stage(const ConvArgs& a, const TileGeo& tn, bool has_next, int c0_next,
+                                          const float* __restrict__ cur, float* __restrict__ nxt,
+                                          const float* __restrict__ wchunk, const int (&addr)[NP][NT],
+                                          v4f (&acc)[MT][NT], int wave, int lane) {
+  if (has_next) stage_box<NWAVES>(a, tn, c0_next, nxt, wave, lane);
+  __builtin_amdgcn_sched_barrier(0);
+  tap_chunk<MT, NT, WM, G, NP>(cur, wchunk, addr, acc);
+}
+
+template <int MT, int NT, int WM, int WN, int NCH, class G>
+__global__ __launch_bounds__(64 * WM * WN) void conv_tap_kernel(ConvArgs a) {
+  constexpr int NWAVES = WM * WN;
+  constexpr int BM = 16 * MT * WM;
+  constexpr int BN = 16 * NT * WN;
+  constexpr int SSTRIDE = WM * 64 * MT;  // floats per k-step of the weight fragments
+  constexpr TapPatterns<G> P{};
+  constexpr int NP = P.np;
+  extern __shared__ __align__(16) float smem[];
+  float* box0 = smem;
+  float* box1 = smem + G::XS;
+  float* Wres = smem + 2 * G::XS;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN;
+  const int wn = wave - wm * WN;
+  const int kg = lane >> 4;
+  const int li = lane & 15;
+
+  int item = blockIdx.x;
+  if (item >= a.items) return;
+#pragma unroll
+  for (int c = 0; c < NCH; c++)
+    stage_wfrag<MT, WM, NWAVES>(a, 0, 0, c * G::CCH, G::NS, Wres + c * G::NS * SSTRIDE, wave, lane);
+  TileGeo t = tile_geo(a, item % a.tiles_per_plane, item / a.tiles_per_plane, 0, BM, BN, true);
+  stage_box<NWAVES>(a, t, 0, box0, wave, lane);
+  wait_vmem();
+  __syncthreads();
+
+  // This lane's share of each distinct k-step pattern (row kg of the step).
+  int dpat[NP];
+#pragma unroll
+  for (int q = 0; q < NP; q++)
+    dpat[q] = kg == 0 ? P.pat[q][0] : kg == 1 ? P.pat[q][1] : kg == 2 ? P.pat[q][2] : P.pat[q][3];
+  const float* wlane = Wres + wm * 64 * MT + lane * MT;
+  float bias[MT][4];
+  load_bias<MT>(a, t, wm, kg, bias);  // one channel tile: the same for every item
 
   v4f acc[MT][NT];
 #pragma unroll
@@ -142,78 +551,46 @@ __global__ __launch_bounds__(256) void conv_mfma16_kernel(ConvArgs a) {
 #pragma unroll
     for (int ni = 0; ni < NT; ni++) acc[mi][ni] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  const int64_t x_n = (int64_t(n) * a.Cin + int64_t(g) * a.Cg) * a.L0;
-  const int wrow = wm * 16 * MT + li;
-
-  for (int c0 = 0; c0 < a.Cg; c0 += a.Cc) {
-    const int cc_count = min(a.Cc, a.Cg - c0);
-    __syncthreads();  // previous chunk's reads are complete (and the koff table is written)
-
-    // Stage the input box of this chunk: rows of bw contiguous input columns.
-    const int rows_per_c = a.kdspan * rows_needed;
-    const int nrows = a.Cc * rows_per_c;
-    for (int r = wave; r < nrows; r += 4) {
-      const int c = r / rows_per_c;
-      const int rem = r - c * rows_per_c;
-      const int zd = rem / rows_needed;
-      const int zr = rem - zd * rows_needed;
-      const int id = id0 + zd;
-      const int ih = ih0 + zr;
-      const bool rv = (c < cc_count) && (id >= 0) && (id < a.L0) && (ih >= 0) && (ih < a.L1);
-      const float* src = a.x + ((x_n + int64_t(c0 + c) * a.L0 + (rv ? id : 0)) * a.L1 + (rv ? ih : 0)) * a.L2;
-      float* dst = Xs + c * a.boxc + zd * plane_stride + zr * a.bw;
-      for (int col = lane; col < a.bw; col += 64) {
-        const int iw = iw0 + col;
-        float v = 0.0f;
-        if (rv && iw >= 0 && iw < a.L2) v = src[iw];
-        dst[col] = v;
+  int parity = 0;  // buffer holding chunk 0 of the current item
+  for (;;) {
+    int noff[NT], pidx[NT];
+    tile_positions<NT>(a, t, wn, li, noff, pidx);
+    int addr[NP][NT];
+#pragma unroll
+    for (int q = 0; q < NP; q++)
+#pragma unroll
+      for (int ni = 0; ni < NT; ni++) addr[q][ni] = 4 * (noff[ni] + dpat[q]);
+    const int next_item = item + gridDim.x;
+    const bool more = next_item < a.items;
+    TileGeo tn = t;
+    if (more) tn = tile_geo(a, next_item % a.tiles_per_plane, next_item / a.tiles_per_plane, 0, BM, BN, true);
+#pragma unroll
+    for (int c = 0; c < NCH; c++) {
+      const bool last = c + 1 == NCH;
+      const bool has_next = !last || more;
+      const int c0n = last ? 0 : (c + 1) * G::CCH;
+      const bool odd = ((c & 1) != 0) != (parity != 0);
+      const float* wchunk = wlane + c * G::NS * SSTRIDE;
+      if (odd)
+        tap_stage<MT, NT, WM, NWAVES, G, NP>(a, last ? tn : t, has_next, c0n, box1, box0, wchunk, addr, acc, wave,
+                                             lane);
+      else
+        tap_stage<MT, NT, WM, NWAVES, G, NP>(a, last ? tn : t, has_next, c0n, box0, box1, wchunk, addr, acc, wave,
+                                             lane);
+      if (last) {
+        store_tile<MT, NT>(a, t, wm, kg, pidx, acc, bias);
+#pragma unroll
+        for (int mi = 0; mi < MT; mi++)
+#pragma unroll
+          for (int ni = 0; ni < NT; ni++) acc[mi][ni] = v4f{0.f, 0.f, 0.f, 0.f};
       }
+      wait_vmem();
+      __syncthreads();
     }
-    // Stage the weight chunk transposed to [k][m] (zero beyond the valid k and m).
-    const int kvalid = cc_count * a.kvol;
-    for (int idx = tid; idx < a.kc_pad * BM; idx += 256) {
-      const int m = idx / a.kc_pad;
-      const int k = idx - m * a.kc_pad;
-      const int co = m0 + m;
-      float v = 0.0f;
-      if (k < kvalid && co < a.Coutg) v = a.w[int64_t(g * a.Coutg + co) * a.kfull + c0 * a.kvol + k];
-      Ws[k * a.ldw + m] = v;
-    }
-    __syncthreads();
-
-    const int nsteps = a.kc_pad >> 2;
-    for (int s = 0; s < nsteps; s++) {
-      const int kk = 4 * s + kg;
-      const int ko = koff[kk];
-      float av[MT], bv[NT];
-#pragma unroll
-      for (int mi = 0; mi < MT; mi++) av[mi] = Ws[kk * a.ldw + wrow + 16 * mi];
-#pragma unroll
-      for (int ni = 0; ni < NT; ni++) bv[ni] = Xs[ko + noff[ni]];
-#pragma unroll
-      for (int mi = 0; mi < MT; mi++)
-#pragma unroll
-        for (int ni = 0; ni < NT; ni++)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[mi], bv[ni], acc[mi][ni], 0, 0, 0);
-    }
-  }
-
-  // Epilogue: D[m][n] sits in lane n + 16*(m/4), register m%4.
-  const int64_t out_plane = int64_t(a.O1) * a.O2;
-#pragma unroll
-  for (int mi = 0; mi < MT; mi++) {
-#pragma unroll
-    for (int r = 0; r < 4; r++) {
-      const int ch = m0 + wm * 16 * MT + 16 * mi + 4 * kg + r;
-      if (ch < a.Coutg) {
-        const int co = g * a.Coutg + ch;
-        const float b = a.bias ? a.bias[co] : 0.0f;
-        float* yp = a.y + ((int64_t(n) * a.Cout + co) * a.O0 + od) * out_plane;
-#pragma unroll
-        for (int ni = 0; ni < NT; ni++)
-          if (pidx[ni] >= 0) yp[pidx[ni]] = acc[mi][ni][r] + b;
-      }
-    }
+    if (!more) break;
+    if (NCH & 1) parity ^= 1;
+    item = next_item;
+    t = tn;
   }
 }
 
@@ -424,19 +801,47 @@ __global__ void synth_fill_kernel(float* __restrict__ dst, int64_t count, uint64
 // ---------------------------------------------------------------------------
 typedef void (*ConvKernelFn)(ConvArgs);
 
-template <int MT, int NT, int WM, int WN>
-static int launch_conv_cfg(const ConvArgs& args, const ConvPlan& p, hipStream_t stream) {
-  auto fn = conv_mfma16_kernel<MT, NT, WM, WN>;
-  static std::once_flag once;
-  static hipError_t attr_err = hipSuccess;
+template <typename Fn>
+static int set_lds_limit_once(Fn fn, std::once_flag& once, hipError_t& err) {
   std::call_once(once, [&] {
-    attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
-                                   hipFuncAttributeMaxDynamicSharedMemorySize, int(kLdsLimit));
+    err = hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
+                              int(kLdsLimit));
   });
-  if (attr_err != hipSuccess) return CONV_ERR_HIP;
+  return err == hipSuccess ? CONV_OK : CONV_ERR_HIP;
+}
+
+template <int MT, int NT, int WM, int WN, int KS>
+static int launch_conv_cfg(const ConvArgs& args, const ConvPlan& p, hipStream_t stream) {
+  static std::once_flag once;
+  static hipError_t err = hipSuccess;
+  auto fn = conv_mfma16_kernel<MT, NT, WM, WN, KS>;
+  if (set_lds_limit_once(fn, once, err) != CONV_OK) return CONV_ERR_HIP;
   dim3 grid(unsigned(p.grid[0]), unsigned(p.grid[1]), unsigned(p.grid[2]));
   hipLaunchKernelGGL(fn, grid, dim3(256), size_t(p.lds_bytes), stream, args);
   return hipGetLastError() == hipSuccess ? CONV_OK : CONV_ERR_HIP;
+}
+
+template <int MT, int NT, int WM, int WN, int NCH, int KD, int KH, int KW, int DD, int DH, int DW, int CC, int KDSPAN,
+          int ROWS, int BW>
+static int launch_tap(const ConvArgs& args, const ConvPlan& p, hipStream_t stream) {
+  using G = TapGeo<KD, KH, KW, DD, DH, DW, CC, KDSPAN, ROWS, BW>;
+  static std::once_flag once;
+  static hipError_t err = hipSuccess;
+  auto fn = conv_tap_kernel<MT, NT, WM, WN, NCH, G>;
+  if (set_lds_limit_once(fn, once, err) != CONV_OK) return CONV_ERR_HIP;
+  hipLaunchKernelGGL(fn, dim3(unsigned(p.grid[0])), dim3(64 * WM * WN), size_t(p.lds_bytes), stream, args);
+  return hipGetLastError() == hipSuccess ? CONV_OK : CONV_ERR_HIP;
+}
+
+static int launch_tap_spec(const ConvArgs& args, const ConvPlan& p, hipStream_t stream) {
+  switch (p.tap_spec) {
+#define CONVHIP_TAP_CASE(id, MT, NT, WM, WN, NCH, KD, KH, KW, DD, DH, DW, CC, KDSPAN, ROWS, BW) \
+  case id:                                                                                        \
+    return launch_tap<MT, NT, WM, WN, NCH, KD, KH, KW, DD, DH, DW, CC, KDSPAN, ROWS, BW>(args, p, stream);
+    CONVHIP_TAP_SPECS(CONVHIP_TAP_CASE)
+#undef CONVHIP_TAP_CASE
+    default: return CONV_ERR_UNSUPPORTED;
+  }
 }
 
 template <int NG>
@@ -466,7 +871,9 @@ static ConvArgs conv_args(const Geom& g, const ConvPlan& p, const float* x, cons
   a.P0 = int(g.P[0]); a.P1 = int(g.P[1]); a.P2 = int(g.P[2]);
   a.O0 = int(g.O[0]); a.O1 = int(g.O[1]); a.O2 = int(g.O[2]);
   a.kvol = int(g.kvol()); a.kfull = int(g.kred());
-  a.mode = p.mode; a.Cc = p.Cc; a.kc_pad = p.kc_pad; a.ldw = p.ldw; a.kdspan = p.kdspan;
+  a.mode = p.mode; a.Cc = p.Cc; a.kc_pad = p.kc_pad; a.kdspan = p.kdspan;
+  a.xs_floats = p.xs_floats; a.koff_ints = p.koff_ints; a.ws_floats = p.ws_floats;
+  a.tiles_per_plane = int(p.tiles_per_plane); a.nchunks = p.nchunks; a.items = int(p.items);
   a.rows = p.rows; a.bw = p.bw; a.boxc = p.boxc; a.row_tiles = p.row_tiles; a.ctiles = p.ctiles;
   a.plane_out = int(g.plane_out());
   return a;
@@ -475,6 +882,35 @@ static ConvArgs conv_args(const Geom& g, const ConvPlan& p, const float* x, cons
 }  // namespace convhip
 
 using namespace convhip;
+
+// CONVHIP_CONV_CFG=<n> forces tile configuration n of conv_fwd (used by the tests
+// to run every configuration on every case); unset or out of range = planner's choice.
+static int forced_conv_cfg() {
+  const char* s = std::getenv("CONVHIP_CONV_CFG");
+  if (!s || !*s) return -1;
+  const int v = std::atoi(s);
+  return (v >= 0 && v < CFG_COUNT) ? v : -1;
+}
+
+// CONVHIP_TAP=0 keeps conv_fwd off the build-time specialised kernels.
+static int use_tap() {
+  const char* s = std::getenv("CONVHIP_TAP");
+  if (!s || !*s) return -1;
+  return std::atoi(s) ? -1 : 0;
+}
+
+// Compute units of the current device (cached per device id).
+static int device_num_cu() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
 
 extern "C" {
 
@@ -524,7 +960,7 @@ int conv_plan_describe(int nd, const int64_t* x_shape, const int64_t* w_shape, c
     s = describe(g, p);
   } else {
     ConvPlan p;
-    rc = plan_conv(g, &p);
+    rc = plan_conv(g, &p, forced_conv_cfg(), 256, use_tap());
     if (rc != CONV_OK) return rc;
     s = describe(g, p);
   }
@@ -540,18 +976,22 @@ int conv_fwd(int nd, const float* x, const int64_t* x_shape, const float* w, con
   if (rc != CONV_OK) return rc;
   if (!x || !w || !y) return CONV_ERR_NULL;
   ConvPlan p;
-  rc = plan_conv(g, &p);
+  rc = plan_conv(g, &p, forced_conv_cfg(), device_num_cu(), use_tap());
   if (rc != CONV_OK) return rc;
   ConvArgs a = conv_args(g, p, x, w, bias, y);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (p.tap_spec >= 0) return launch_tap_spec(a, p, s);
   switch (p.cfg) {
-    case CFG_M16: return launch_conv_cfg<1, 4, 1, 4>(a, p, s);
-    case CFG_M32: return launch_conv_cfg<2, 4, 1, 4>(a, p, s);
-    case CFG_M64: return launch_conv_cfg<4, 4, 1, 4>(a, p, s);
-    default: return launch_conv_cfg<4, 4, 2, 2>(a, p, s);
+    case CFG_M64: return launch_conv_cfg<4, 4, 1, 4, 1>(a, p, s);
+    case CFG_M128: return launch_conv_cfg<4, 4, 2, 2, 1>(a, p, s);
+    case CFG_M32: return launch_conv_cfg<2, 4, 1, 4, 1>(a, p, s);
+    case CFG_M16: return launch_conv_cfg<1, 4, 1, 4, 1>(a, p, s);
+    case CFG_M16_N64_K4: return launch_conv_cfg<1, 4, 1, 1, 4>(a, p, s);
+    case CFG_M16_N128_K4: return launch_conv_cfg<1, 8, 1, 1, 4>(a, p, s);
+    case CFG_M16_N208_K4: return launch_conv_cfg<1, 13, 1, 1, 4>(a, p, s);
+    default: return launch_conv_cfg<1, 16, 1, 1, 4>(a, p, s);
   }
 }
-
 int conv3d_min_softmax(const float* x, const int64_t* x_shape, const float* w, const int64_t* w_shape,
                        const float* bias, const int* stride, const int* dilation, const int* padding, int groups,
                        int min_dim, float* y, convhip_stream_t stream) {

@@ -64,10 +64,14 @@ int make_geom(int nd, const int64_t* xs, const int64_t* ws, const int* stride, c
 
 CfgShape cfg_shape(int cfg) {
   switch (cfg) {
-    case CFG_M16: return {1, 4, 1, 4};
-    case CFG_M32: return {2, 4, 1, 4};
-    case CFG_M64: return {4, 4, 1, 4};
-    default: return {4, 4, 2, 2};
+    case CFG_M64: return {4, 4, 1, 4, 1};
+    case CFG_M128: return {4, 4, 2, 2, 1};
+    case CFG_M32: return {2, 4, 1, 4, 1};
+    case CFG_M16: return {1, 4, 1, 4, 1};
+    case CFG_M16_N64_K4: return {1, 4, 1, 1, 4};
+    case CFG_M16_N128_K4: return {1, 8, 1, 1, 4};
+    case CFG_M16_N208_K4: return {1, 13, 1, 1, 4};
+    default: return {1, 16, 1, 1, 4};
   }
 }
 
@@ -90,13 +94,96 @@ static void box_dims(const Geom& g, int mode, int BN, int* rows, int* bw, int64_
   }
 }
 
-int plan_conv(const Geom& g, ConvPlan* out) {
+const TapSpecDesc* tap_specs(int* count) {
+#define CONVHIP_TAP_DESC(id, MT, NT, WM, WN, NCH, KD, KH, KW, DD, DH, DW, CC, KDSPAN, ROWS, BW) \
+  {id, MT, NT, WM, WN, NCH, KD, KH, KW, DD, DH, DW, CC, KDSPAN, ROWS, BW},
+  static const TapSpecDesc specs[] = {CONVHIP_TAP_SPECS(CONVHIP_TAP_DESC)};
+#undef CONVHIP_TAP_DESC
+  *count = int(sizeof(specs) / sizeof(specs[0]));
+  return specs;
+}
+
+// Plan of a tap specialisation if the geometry is exactly the one it was built for.
+static bool plan_tap(const Geom& g, const TapSpecDesc& d, int num_cu, ConvPlan* p) {
+  const int BM = 16 * d.MT * d.WM, BN = 16 * d.NT * d.WN;
+  if (g.G != 1 || g.Coutg > BM || g.Cg != int64_t(d.CC) * d.NCH) return false;
+  if (g.K[0] != d.KD || g.K[1] != d.KH || g.K[2] != d.KW) return false;
+  if (g.Dl[0] != d.DD || g.Dl[1] != d.DH || g.Dl[2] != d.DW) return false;
+  const int mode = (g.O[2] * 2 <= BN) ? TILE_FLAT : TILE_ROW;
+  int rows, bw, row_tiles;
+  int64_t tiles;
+  box_dims(g, mode, BN, &rows, &bw, &tiles, &row_tiles);
+  const int kdspan = int((g.K[0] - 1) * g.Dl[0] + 1);
+  if (rows != d.ROWS || bw != d.BW || kdspan != d.KDSPAN) return false;
+  const int64_t items = tiles * g.N * g.O[0];
+  if (items > std::numeric_limits<int32_t>::max()) return false;
+  const int64_t kvol = int64_t(d.KD) * d.KH * d.KW;
+  const int64_t ns = (d.CC * kvol + 3) / 4;
+  const int64_t xs = (int64_t(d.CC) * kdspan * rows * bw + 255) / 256 * 256;
+  const int64_t wf = (d.NCH * ns + 1) * d.WM * 64 * d.MT;
+  const int64_t bytes = 4 * (2 * xs + wf);
+  if (bytes > kLdsLimit) return false;
+  ConvPlan q;
+  q.cfg = -1;
+  q.tap_spec = d.id;
+  q.threads = 64 * d.WM * d.WN;
+  q.BM = BM;
+  q.BN = BN;
+  q.mode = mode;
+  q.Cc = d.CC;
+  q.kc_pad = int(ns * 4);
+  q.kdspan = kdspan;
+  q.rows = rows;
+  q.bw = bw;
+  q.boxc = kdspan * rows * bw;
+  q.xs_floats = int(xs);
+  q.koff_ints = 0;
+  q.ws_floats = int(wf);
+  q.tiles_per_plane = tiles;
+  q.row_tiles = row_tiles;
+  q.ctiles = 1;
+  q.nchunks = d.NCH;
+  q.items = items;
+  q.lds_bytes = bytes;
+  const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(2, kLdsLimit / bytes));
+  q.grid[0] = std::min<int64_t>(items, per_cu * num_cu);
+  q.grid[1] = 1;
+  q.grid[2] = 1;
+  *p = q;
+  return true;
+}
+
+int plan_conv(const Geom& g, ConvPlan* out, int force_cfg, int num_cu, int use_tap) {
+  if (use_tap != 0 && force_cfg < 0) {
+    int n = 0;
+    const TapSpecDesc* specs = tap_specs(&n);
+    for (int i = 0; i < n; i++)
+      if (plan_tap(g, specs[i], num_cu, out)) return CONV_OK;
+  }
   ConvPlan p;
-  if (g.Coutg <= 16) p.cfg = CFG_M16;
-  else if (g.Coutg <= 32) p.cfg = CFG_M32;
-  else if (g.Coutg <= 64) p.cfg = CFG_M64;
-  else p.cfg = CFG_M128;
-  CfgShape cs = cfg_shape(p.cfg);
+  if (force_cfg >= 0 && force_cfg < CFG_COUNT) {
+    p.cfg = force_cfg;
+  } else if (g.Coutg > 64) {
+    p.cfg = CFG_M128;
+  } else if (g.Coutg > 32) {
+    p.cfg = CFG_M64;
+  } else if (g.Coutg > 16) {
+    p.cfg = CFG_M32;
+  } else {
+    // Few output channels: the reduction is split over the 4 waves of a block and
+    // a tile covers a whole (n, od) plane when it fits, so no lanes idle on a
+    // ragged plane tail. Large planes with many tiles take the unsplit tile.
+    const int64_t plane = g.plane_out();
+    if (plane <= 64) p.cfg = CFG_M16_N64_K4;
+    else if (plane <= 128) p.cfg = CFG_M16_N128_K4;
+    else if (plane <= 208) p.cfg = CFG_M16_N208_K4;
+    else if (plane <= 256) p.cfg = CFG_M16_N256_K4;
+    else {
+      const int64_t tiles = g.N * g.O[0] * ceil_div(plane, 256) * g.G;
+      p.cfg = tiles >= 2048 ? CFG_M16 : CFG_M16_N256_K4;
+    }
+  }
+  const CfgShape cs = cfg_shape(p.cfg);
   p.BM = 16 * cs.MT * cs.WM;
   p.BN = 16 * cs.NT * cs.WN;
   // Flattened plane tiles when a tile covers at least two output rows; otherwise
@@ -105,24 +192,34 @@ int plan_conv(const Geom& g, ConvPlan* out) {
   box_dims(g, p.mode, p.BN, &p.rows, &p.bw, &p.tiles_per_plane, &p.row_tiles);
   p.kdspan = int((g.K[0] - 1) * g.Dl[0] + 1);
   const int64_t boxc = int64_t(p.kdspan) * p.rows * p.bw;
-  if (boxc > (int64_t(1) << 28)) return CONV_ERR_UNSUPPORTED;
+  if (boxc > (int64_t(1) << 26)) return CONV_ERR_UNSUPPORTED;
   p.boxc = int(boxc);
-  p.ldw = (p.BM % 32 == 16) ? p.BM : p.BM + 16;
+  const int64_t red = cs.KS > 1 ? int64_t(cs.KS - 1) * cs.WM * cs.WN * cs.MT * cs.NT * 4 * 64 : 0;
+  auto r4 = [](int64_t v) { return (v + 3) / 4 * 4; };
+  // LDS: [koff table | 2 x (box | weight fragments)]. The box region is padded to
+  // whole 256-float blocks (the DMA writes whole wave-wide rows of 64 slots); the
+  // split-K partial sums reuse the two buffers after the reduction.
+  auto r256 = [](int64_t v) { return (v + 255) / 256 * 256; };
+  auto layout = [&](int64_t cc, int64_t* xs, int64_t* ko, int64_t* ws) {
+    const int64_t kcp = r4(cc * g.kvol());
+    *xs = r256(cc * p.boxc);
+    *ko = r4(kcp + 8 * cs.KS);
+    *ws = (kcp / 4 + cs.KS) * cs.WM * 64 * cs.MT;
+    if (2 * (*xs + *ws) < red) *xs = r256(red / 2);
+    return 4 * (*ko + 2 * (*xs + *ws));
+  };
   // Channel chunk: among the chunk sizes whose staged box + weights fit the LDS
   // budget, take the one with the least padded reduction work (chunks x padded
-  // taps per chunk), then the fewest chunks. The budget leaves room for two
-  // workgroups per CU.
-  const int64_t budget = 80 * 1024;
-  auto chunk_bytes = [&](int64_t cc) {
-    int64_t kcp = (cc * g.kvol() + 3) / 4 * 4;
-    return 4 * (cc * p.boxc + 4 + kcp + kcp * p.ldw);
-  };
+  // taps per chunk), then the fewest chunks. Unsplit tiles keep room for two
+  // workgroups per CU; split tiles are used where the grid is small.
+  const int64_t budget = cs.KS > 1 ? kLdsLimit : 80 * 1024;  // double-buffered chunks
   int best = 0;
   int64_t best_work = 0, best_chunks = 0;
-  for (int64_t cc = 1; cc <= std::min<int64_t>(g.Cg, 256); cc++) {
-    if (chunk_bytes(cc) > budget) break;
-    int64_t chunks = ceil_div(g.Cg, cc);
-    int64_t work = chunks * ((cc * g.kvol() + 3) / 4 * 4);
+  for (int64_t cc = 1; cc <= std::min<int64_t>(g.Cg, 1024); cc++) {
+    int64_t xs, ko, ws;
+    if (layout(cc, &xs, &ko, &ws) > budget) break;
+    const int64_t chunks = ceil_div(g.Cg, cc);
+    const int64_t work = chunks * r4(cc * g.kvol());
     if (best == 0 || work < best_work || (work == best_work && chunks < best_chunks)) {
       best = int(cc);
       best_work = work;
@@ -130,17 +227,23 @@ int plan_conv(const Geom& g, ConvPlan* out) {
     }
   }
   if (best == 0) {
-    if (chunk_bytes(1) > kLdsLimit) return CONV_ERR_UNSUPPORTED;
+    int64_t xs, ko, ws;
+    if (layout(1, &xs, &ko, &ws) > kLdsLimit) return CONV_ERR_UNSUPPORTED;
     best = 1;
   }
   p.Cc = best;
-  int64_t kc = int64_t(p.Cc) * g.kvol();
-  p.kc_pad = int((kc + 3) / 4 * 4);
-  p.lds_bytes = 4 * (int64_t(p.Cc) * p.boxc + 4 + p.kc_pad + int64_t(p.kc_pad) * p.ldw);
+  int64_t xs, ko, ws;
+  p.lds_bytes = layout(p.Cc, &xs, &ko, &ws);
+  p.xs_floats = int(xs);
+  p.koff_ints = int(ko);
+  p.ws_floats = int(ws);
+  p.kc_pad = int(r4(int64_t(p.Cc) * g.kvol()));
+  p.nchunks = int(ceil_div(g.Cg, p.Cc));
   p.ctiles = int(ceil_div(g.Coutg, p.BM));
   p.grid[0] = p.tiles_per_plane;
   p.grid[1] = g.N * g.O[0];
   p.grid[2] = g.G * p.ctiles;
+
   if (p.grid[0] > std::numeric_limits<int32_t>::max() || p.grid[1] > 65535 || p.grid[2] > 65535)
     return CONV_ERR_OVERFLOW;
   *out = p;
@@ -176,10 +279,16 @@ int plan_fused(const Geom& g, int min_dim, FusedPlan* out) {
 std::string describe(const Geom& g, const ConvPlan& p) {
   char buf[512];
   CfgShape cs = cfg_shape(p.cfg);
+  if (p.tap_spec >= 0) {
+    int n = 0;
+    const TapSpecDesc& d = tap_specs(&n)[p.tap_spec];
+    cs = CfgShape{d.MT, d.NT, d.WM, d.WN, 1};
+  }
   std::snprintf(buf, sizeof buf,
-                "kernel=conv_mfma16 cfg=%d MT=%d NT=%d WM=%d WN=%d BM=%d BN=%d mode=%s Cc=%d kc_pad=%d "
+                "kernel=%s cfg=%d MT=%d NT=%d WM=%d WN=%d KS=%d BM=%d BN=%d mode=%s Cc=%d kc_pad=%d "
                 "box=%dx%dx%d grid=%lldx%lldx%lld lds=%lld macs=%lld",
-                p.cfg, cs.MT, cs.NT, cs.WM, cs.WN, p.BM, p.BN, p.mode == TILE_FLAT ? "flat" : "row", p.Cc,
+                p.tap_spec >= 0 ? "conv_tap" : "conv_mfma16", p.tap_spec >= 0 ? p.tap_spec : p.cfg, cs.MT, cs.NT,
+                cs.WM, cs.WN, cs.KS, p.BM, p.BN, p.mode == TILE_FLAT ? "flat" : "row", p.Cc,
                 p.kc_pad, p.kdspan, p.rows, p.bw, (long long)p.grid[0], (long long)p.grid[1],
                 (long long)p.grid[2], (long long)p.lds_bytes, (long long)g.macs());
   return buf;

@@ -34,15 +34,20 @@ int make_geom(int nd, const int64_t* x_shape, const int64_t* w_shape, const int*
 
 // Tile configurations of the fp32 MFMA implicit-GEMM conv kernel. Each wave
 // owns MT x NT tiles of 16 (output channels) x 16 (output positions); the block
-// is WM x WN waves.
+// holds WM x WN such wave tiles, and KS waves split the reduction of each wave
+// tile (their partial sums are added through LDS). WM * WN * KS = 4 waves.
+struct CfgShape { int MT, NT, WM, WN, KS; };
 enum ConvCfg : int {
-  CFG_M16 = 0,   // MT=1 NT=4 WM=1 WN=4 : 16 channels x 256 positions
-  CFG_M32 = 1,   // MT=2 NT=4 WM=1 WN=4 : 32 x 256
-  CFG_M64 = 2,   // MT=4 NT=4 WM=1 WN=4 : 64 x 256
-  CFG_M128 = 3,  // MT=4 NT=4 WM=2 WN=2 : 128 x 128
-  CFG_COUNT = 4
+  CFG_M64 = 0,       // 64 x 256, no split     (64 < C_out/g)
+  CFG_M128 = 1,      // 128 x 128, no split    (C_out/g > 64)
+  CFG_M32 = 2,       // 32 x 256, no split
+  CFG_M16 = 3,       // 16 x 256, no split
+  CFG_M16_N64_K4 = 4,    // 16 x 64, reduction split over 4 waves
+  CFG_M16_N128_K4 = 5,   // 16 x 128, split 4
+  CFG_M16_N208_K4 = 6,   // 16 x 208, split 4
+  CFG_M16_N256_K4 = 7,   // 16 x 256, split 4
+  CFG_COUNT = 8
 };
-struct CfgShape { int MT, NT, WM, WN; };
 CfgShape cfg_shape(int cfg);
 
 // Tiling of output positions inside one (n, od) plane of H_out x W_out outputs.
@@ -57,20 +62,43 @@ struct ConvPlan {
   int mode = TILE_FLAT;
   int Cc = 0;          // input channels staged per chunk
   int kc_pad = 0;      // Cc * kvol rounded up to a multiple of 4
-  int ldw = 0;         // LDS row stride (floats) of the staged weight chunk [k][m]
   int kdspan = 0;      // input planes in the box: (kD-1)*dD + 1
   int rows = 0;        // input rows in the box (maximum over tiles)
   int bw = 0;          // input columns in the box
   int boxc = 0;        // floats per channel in the box: kdspan * rows * bw
+  int xs_floats = 0;   // LDS floats of the box region (box, or the split-K partial sums if larger)
+  int koff_ints = 0;   // LDS ints of the tap-offset table (padded for prefetch)
+  int ws_floats = 0;   // LDS floats of the weight fragments (padded for prefetch)
   int64_t tiles_per_plane = 0;
   int row_tiles = 0;   // TILE_ROW: tiles per output row
   int ctiles = 0;      // channel tiles per group
+  int nchunks = 0;      // chunks of Cc input channels per tile
+  int tap_spec = -1;    // >= 0: build-time specialised persistent kernel (grid[0] workgroups walk `items`)
+  int threads = 256;    // workgroup size
+  int64_t items = 0;    // tap kernel: work items (tile, plane)
   int64_t grid[3] = {0, 0, 0};
   int64_t lds_bytes = 0;
 };
 
 // Plan for conv_fwd. Returns a conv_status (CONV_ERR_UNSUPPORTED if nothing fits).
-int plan_conv(const Geom& g, ConvPlan* p);
+// force_cfg >= 0 selects a tile configuration (tests cover every configuration).
+// Build-time specialisations of the persistent tap-unrolled kernel: each fixes
+// the tiling, the channel chunk, the kernel taps and dilations, and the staged
+// box shape. X(id, MT, NT, WM, WN, NCH, KD, KH, KW, DD, DH, DW, CC, KDSPAN, ROWS, BW)
+#define CONVHIP_TAP_SPECS(X)                                                      \
+  /* Conv3d 3->64, kernel 3x5x7, 64^3 input: 64 ch x 256 positions, 8 waves */ \
+  X(0, 4, 2, 1, 8, 1, 3, 5, 7, 1, 1, 1, 3, 3, 10, 64)                            \
+  /* Conv1d 64->128, k=3, stride 3, dilation 4: 128 ch x 256 positions */       \
+  X(1, 4, 4, 2, 4, 8, 1, 1, 3, 1, 1, 4, 8, 1, 1, 774)
+
+struct TapSpecDesc {
+  int id, MT, NT, WM, WN, NCH, KD, KH, KW, DD, DH, DW, CC, KDSPAN, ROWS, BW;
+};
+const TapSpecDesc* tap_specs(int* count);
+
+// num_cu: compute units of the device (sizes the persistent grid).
+// use_tap: -1 planner's choice, 0 never use a tap specialisation.
+int plan_conv(const Geom& g, ConvPlan* p, int force_cfg = -1, int num_cu = 256, int use_tap = -1);
 
 // Plan of the fused conv -> min over depth -> softmax over channels kernel.
 struct FusedPlan {

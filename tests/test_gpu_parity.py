@@ -240,3 +240,70 @@ def test_synth_device_matches_host():
         host = synth.fill(kind, 0xABCDEF, t.numel(), start=12345, bound=kw.get("bound", 1.0),
                           lo=kw.get("lo", 0), span=kw.get("span", 1))
         np.testing.assert_array_equal(t.cpu().numpy(), host)
+
+
+CFG_CASES = [
+    ((2, 3, 9, 10, 11), (8, 3, 3, 3, 3), 1, 1, 0, 1),
+    ((1, 4, 7, 9, 10), (6, 2, 2, 3, 2), (1, 2, 2), (1, 1, 2), (1, 2, 3), 2),
+    ((1, 3, 40), (5, 3, 3), 3, 4, 0, 1),
+    ((1, 4, 3, 12, 13), (16, 2, 2, 3, 3), 1, (1, 1, 2), 1, 2),
+    ((2, 3, 4, 14, 14), (70, 3, 3, 3, 3), 1, 1, 0, 1),
+    ((1, 5, 900), (33, 5, 3), 3, 4, 1, 1),
+]
+
+
+@pytest.mark.parametrize("cfg", range(8))
+def test_every_tile_config_integer_exact(cfg, monkeypatch):
+    """Each tile configuration of the conv kernel (forced through CONVHIP_CONV_CFG)
+    gives the exact oracle result on shapes with ragged tiles and chunk tails."""
+    monkeypatch.setenv("CONVHIP_CONV_CFG", str(cfg))
+    r = np.random.default_rng(77 + cfg)
+    for xs, ws, s, d, p, g in CFG_CASES:
+        x, w, b = _int_inputs(r, xs, ws, bias=True)
+        say(f"cfg {cfg}: x={xs} w={ws}: " + ch.plan_describe(xs, ws, s, d, p, g))
+        y = gpu_conv(x, w, b, s, d, p, g)
+        np.testing.assert_array_equal(y.astype(np.float64), oracle.conv(x, w, b, s, d, p, g))
+
+
+# Shapes that keep the geometry of a build-time specialisation (channel chunk,
+# taps, dilations, staged box) with fewer samples / shorter extents, so the
+# specialised persistent kernel runs on sizes the oracle checks in full.
+TAP_CASES = [
+    ((2, 3, 8, 64, 64), (64, 3, 3, 5, 7), 1, 1, 0, True),
+    ((2, 3, 5, 64, 64), (40, 3, 3, 5, 7), 1, 1, 0, False),   # fewer output channels, one sample per item
+    ((3, 3, 9, 64, 64), (64, 3, 3, 5, 7), 1, 1, 0, True),    # odd item count per workgroup
+    ((2, 64, 3000), (128, 64, 3), 3, 4, 0, False),
+    ((1, 64, 5000), (100, 64, 3), 3, 4, 2, True),            # padding, ragged last tile
+    ((4, 64, 200000), (128, 64, 3), 3, 4, 0, False),         # several items per workgroup
+]
+
+
+@pytest.mark.parametrize("case", range(len(TAP_CASES)))
+def test_tap_specialised_kernel_integer_exact(case):
+    xs, ws, s, d, p, bias = TAP_CASES[case]
+    desc = ch.plan_describe(xs, ws, s, d, p, 1)
+    assert "kernel=conv_tap" in desc, desc
+    r = np.random.default_rng(400 + case)
+    x, w, b = _int_inputs(r, xs, ws, bias=bias)
+    say(f"tap case {case}: x={xs} w={ws}: {desc}")
+    y = gpu_conv(x, w, b, s, d, p, 1)
+    np.testing.assert_array_equal(y.astype(np.float64), oracle.conv(x, w, b, s, d, p, 1))
+
+
+def test_tap_disabled_falls_back_to_streamed(monkeypatch):
+    monkeypatch.setenv("CONVHIP_TAP", "0")
+    xs, ws, s, d, p, _ = TAP_CASES[0]
+    desc = ch.plan_describe(xs, ws, s, d, p, 1)
+    assert "kernel=conv_mfma16 " in desc + " ", desc
+    r = np.random.default_rng(5)
+    x, w, b = _int_inputs(r, xs, ws, bias=True)
+    y = gpu_conv(x, w, b, s, d, p, 1)
+    np.testing.assert_array_equal(y.astype(np.float64), oracle.conv(x, w, b, s, d, p, 1))
+
+
+def test_workloads_use_expected_kernels():
+    for name, kernel in [("asym_conv3d", "conv_tap"), ("long_conv1d", "conv_tap"),
+                         ("general_conv3d", "conv_mfma16 "), ("tiny_conv3d", "conv_mfma16 ")]:
+        cfg = synth.WORKLOADS[name]
+        d = ch.plan_describe(cfg["x"], cfg["w"], *_cfg_args(cfg)) + " "
+        assert f"kernel={kernel}" in d, d
