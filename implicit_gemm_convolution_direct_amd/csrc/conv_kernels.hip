@@ -90,7 +90,7 @@ struct AFrag<4> {
 };
 
 // A zero word in device memory: global->LDS copies of padding elements read it.
-__device__ const float kZeroWord[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+__device__ __align__(16) const float kZeroWord[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima), emitted through the
 // builtin so the compiler's own wait-count tracking sees it.
@@ -160,31 +160,37 @@ __device__ __forceinline__ void build_koff(const ConvArgs& a, int rows_ld, int* 
 }
 
 // Copy the box of channels [c0, c0+Cc) of a tile into dst, dense layout
-// [c][zd][zr < rows_ld][col]. Every lane writes its own LDS slot; slots whose
-// source lies outside the input (zero padding, channels past C_in/groups) read
-// the zero word.
+// [c][zd][zr < rows_ld][col]. Rows are spread over the waves; a row's channel,
+// plane and input row are wave-uniform (scalar arithmetic) and its lanes copy
+// consecutive columns, so each copy instruction moves up to 64 contiguous
+// floats. Slots whose source lies outside the input (zero padding, channels
+// past C_in/groups) read the zero word.
 template <int NWAVES = 4>
 __device__ __forceinline__ void stage_box(const ConvArgs& a, const TileGeo& t, int c0, float* dst, int wave,
                                           int lane) {
   const int cc_count = min(a.Cc, a.Cg - c0);
-  const int rows_per_c = a.kdspan * t.rows_ld;
-  const int box_elems = a.Cc * rows_per_c * a.bw;
-  const float inv_bw = 1.0f / float(a.bw);
-  const float inv_rpc = 1.0f / float(rows_per_c);
-  const float inv_rn = 1.0f / float(t.rows_ld);
-  const int64_t x_n = (int64_t(t.n) * a.Cin + int64_t(t.g) * a.Cg + c0) * a.L0;
-  const int box_waves = (box_elems + 63) >> 6;
-  for (int wi = wave; wi < box_waves; wi += NWAVES) {
-    const int e = wi * 64 + lane;
-    int col, rem, zr;
-    const int row = divmod_small(e, a.bw, inv_bw, col);
-    const int c = divmod_small(row, rows_per_c, inv_rpc, rem);
-    const int zd = divmod_small(rem, t.rows_ld, inv_rn, zr);
-    const int id = t.id0 + zd, ih = t.ih0 + zr, iw = t.iw0 + col;
-    const bool ok = (e < box_elems) && (c < cc_count) && (unsigned(id) < unsigned(a.L0)) &&
-                    (unsigned(ih) < unsigned(a.L1)) && (unsigned(iw) < unsigned(a.L2));
-    const float* src = ok ? a.x + (((x_n + int64_t(c) * a.L0 + id) * a.L1 + ih) * a.L2 + iw) : kZeroWord;
-    lds_dma_f32(src, dst + wi * 64);
+  const int rows_total = a.Cc * a.kdspan * t.rows_ld;
+  const int64_t x_c0 = (int64_t(t.n) * a.Cin + int64_t(t.g) * a.Cg + c0) * a.L0;
+  // (c, zd, zr) of row r = wave, advanced by NWAVES rows per iteration.
+  int c = 0, zd = 0, zr = wave;
+  while (zr >= t.rows_ld) { zr -= t.rows_ld; zd++; }
+  while (zd >= a.kdspan) { zd -= a.kdspan; c++; }
+  for (int r = wave; r < rows_total; r += NWAVES) {
+    const int id = t.id0 + zd, ih = t.ih0 + zr;
+    const bool row_ok = (c < cc_count) && (unsigned(id) < unsigned(a.L0)) && (unsigned(ih) < unsigned(a.L1));
+    const float* srow = a.x + ((x_c0 + int64_t(c) * a.L0 + (row_ok ? id : 0)) * a.L1 + (row_ok ? ih : 0)) * a.L2;
+    float* drow = dst + r * a.bw;
+    for (int j = 0; j < a.bw; j += 64) {
+      const int col = j + lane;
+      if (col < a.bw) {
+        const int iw = t.iw0 + col;
+        const bool ok = row_ok && (unsigned(iw) < unsigned(a.L2));
+        lds_dma_f32(ok ? srow + iw : kZeroWord, drow + j);
+      }
+    }
+    zr += NWAVES;
+    while (zr >= t.rows_ld) { zr -= t.rows_ld; zd++; }
+    while (zd >= a.kdspan) { zd -= a.kdspan; c++; }
   }
 }
 
@@ -435,6 +441,8 @@ struct TapGeo {
   static constexpr int PLANE = ROWS * BW;
   static constexpr int BOXC = KDSPAN * PLANE;
   static constexpr int XS = (CC * BOXC + 255) / 256 * 256;  // floats per box buffer
+  template <int NCH, int WM, int MT>
+  static constexpr int lds_floats() { return 2 * XS + (NCH * NS + 1) * WM * 64 * MT; }
   // LDS offset (floats) of reduction index k = (channel, td, th, tw) of a chunk;
   // padding indices (zero weights) point at the box start.
   static constexpr int koff(int k) {
@@ -469,6 +477,19 @@ struct TapPatterns {
   }
 };
 
+// Lane kg's share of distinct step pattern Q, selected among compile-time
+// constants (no table in memory).
+template <class G, int Q>
+__device__ __forceinline__ int pat_delta(int kg) {
+  constexpr TapPatterns<G> P{};
+  constexpr int d0 = P.pat[Q][0], d1 = P.pat[Q][1], d2 = P.pat[Q][2], d3 = P.pat[Q][3];
+  return kg == 0 ? d0 : kg == 1 ? d1 : kg == 2 ? d2 : d3;
+}
+template <class G, int... Q>
+__device__ __forceinline__ void fill_pat_deltas(int* dp, int kg, std::integer_sequence<int, Q...>) {
+  ((dp[Q] = pat_delta<G, Q>(kg)), ...);
+}
+
 // Reduce one staged chunk: all k-steps unrolled, B operands read at
 // (lane register + immediate), A operands from the resident weight fragments
 // (wchunk already includes this lane's and wave row's offset).
@@ -477,19 +498,32 @@ __device__ __forceinline__ void tap_chunk(const float* __restrict__ box, const f
                                           const int (&addr)[NP][NT], v4f (&acc)[MT][NT]) {
   constexpr TapPatterns<G> P{};
   const char* bb = reinterpret_cast<const char*>(box);
+  // Operands of step s+1 are read while the matrix core works on step s.
+  AFrag<MT> af[2];
+  float bv[2][NT];
+  af[0].load(wchunk);
+#pragma unroll
+  for (int ni = 0; ni < NT; ni++) bv[0][ni] = *reinterpret_cast<const float*>(bb + addr[P.pid[0]][ni]);
 #pragma unroll
   for (int s = 0; s < G::NS; s++) {
-    AFrag<MT> af;
-    af.load(wchunk + s * (WM * 64 * MT));
-    float bv[NT];
+    const int cu = s & 1, nx = cu ^ 1;
+    if (s + 1 < G::NS) {
+      af[nx].load(wchunk + (s + 1) * (WM * 64 * MT));
 #pragma unroll
-    for (int ni = 0; ni < NT; ni++)
-      bv[ni] = *reinterpret_cast<const float*>(bb + addr[P.pid[s]][ni] + 4 * G::koff(4 * s));
+      for (int ni = 0; ni < NT; ni++)
+        bv[nx][ni] = *reinterpret_cast<const float*>(bb + addr[P.pid[s + 1]][ni] + 4 * G::koff(4 * (s + 1)));
+    }
 #pragma unroll
     for (int mi = 0; mi < MT; mi++)
 #pragma unroll
       for (int ni = 0; ni < NT; ni++)
-        acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x4f32(af.v[mi], bv[ni], acc[mi][ni], 0, 0, 0);
+        acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[cu].v[mi], bv[cu][ni], acc[mi][ni], 0, 0, 0);
+    // Interleave the next step's LDS reads with this step's matrix-core work.
+#pragma unroll
+    for (int i = 0; i < NT + 1; i++) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, MT * NT / (NT + 1) > 0 ? MT * NT / (NT + 1) : 1, 0);
+    }
   }
 }
 
@@ -513,7 +547,9 @@ __global__ __launch_bounds__(64 * WM * WN) void conv_tap_kernel(ConvArgs a) {
   constexpr int SSTRIDE = WM * 64 * MT;  // floats per k-step of the weight fragments
   constexpr TapPatterns<G> P{};
   constexpr int NP = P.np;
-  extern __shared__ __align__(16) float smem[];
+  // Static LDS: its address is known when compiling, so box offsets fold into
+  // the LDS read's immediate.
+  __shared__ __align__(16) float smem[G::template lds_floats<NCH, WM, MT>()];
   float* box0 = smem;
   float* box1 = smem + G::XS;
   float* Wres = smem + 2 * G::XS;
@@ -538,9 +574,7 @@ __global__ __launch_bounds__(64 * WM * WN) void conv_tap_kernel(ConvArgs a) {
 
   // This lane's share of each distinct k-step pattern (row kg of the step).
   int dpat[NP];
-#pragma unroll
-  for (int q = 0; q < NP; q++)
-    dpat[q] = kg == 0 ? P.pat[q][0] : kg == 1 ? P.pat[q][1] : kg == 2 ? P.pat[q][2] : P.pat[q][3];
+  fill_pat_deltas<G>(dpat, kg, std::make_integer_sequence<int, NP>{});
   const float* wlane = Wres + wm * 64 * MT + lane * MT;
   float bias[MT][4];
   load_bias<MT>(a, t, wm, kg, bias);  // one channel tile: the same for every item
@@ -591,6 +625,229 @@ __global__ __launch_bounds__(64 * WM * WN) void conv_tap_kernel(ConvArgs a) {
     if (NCH & 1) parity ^= 1;
     item = next_item;
     t = tn;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// conv_tap_split: one workgroup per (n, od) plane and group, for few output
+// channels (<= 16) and small planes (<= 16*NT positions). Each of the NW waves
+// owns one input channel of the group and reduces it against the group's
+// weights; the NW partial tiles are summed through LDS at the end.
+// - The group's weight matrix (C_out/g rows of C_in/g * kvol floats) is copied
+//   once per workgroup with 16-byte DMA copies into a shared LDS region.
+// - Each wave copies its channel's input box into its own LDS region, one kernel
+//   depth tap (input plane) at a time, so the reduction of the first taps starts
+//   while the rest is in flight. The box keeps every F-th input column: with
+//   stride and dilation along W both multiples of F no other column is read.
+// ---------------------------------------------------------------------------
+// s_waitcnt vmcnt(V) with expcnt and lgkmcnt left at their maxima (gfx9 encoding:
+// vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+template <int V>
+__device__ __forceinline__ void wait_vmem_le() {
+  static_assert(V >= 0 && V < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((V & 15) | ((V >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Asynchronous 16-byte copy per lane: lane l writes dst[4l .. 4l+3].
+__device__ __forceinline__ void lds_dma_f32x4(const float* src, float* dst) {
+  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+}
+
+template <int KD, int KH, int KW, int DD, int DH, int DW, int F, int ROWS, int BW, int NW>
+struct SplitGeo {
+  static constexpr int FF = F;
+  static constexpr int NROWS = ROWS;
+  static constexpr int BWC = BW;
+  static constexpr int KVOL = KD * KH * KW;
+  static constexpr int K = KVOL;          // one channel per wave
+  static constexpr int NS = (K + 3) / 4;
+  static constexpr int KDT = KD;          // depth taps: staged one at a time
+  static constexpr int KPP = KH * KW;     // reduction indices per depth tap
+  static constexpr int PLANE = ROWS * BW;
+  static constexpr int BOX = KD * PLANE;  // only the planes the depth taps read
+  static constexpr int XSW = (BOX + 3) / 4 * 4;           // floats of a wave's box region
+  static constexpr int PLANE_INSTR = (PLANE + 63) / 64;   // copies per box plane
+  // Shared weights: 16 rows of WROW = NW * KVOL floats (the group's reduction
+  // length), stored contiguously (the LDS copy writes consecutive addresses per
+  // lane), plus a tail read by the last row's padding taps.
+  static constexpr int WROW = NW * KVOL;
+  static constexpr bool W4 = WROW % 4 == 0;               // 16-byte copies, else 4-byte
+  static constexpr int WCW = W4 ? 4 : 1;                   // floats per copy per lane
+  static constexpr int WCH = 16 * WROW / WCW;              // copies of the weight block
+  static constexpr int WSH = (16 * WROW + 4 + 3) / 4 * 4;
+  static constexpr int W_INSTR = (WCH + 64 * NW - 1) / (64 * NW);  // copies per wave
+  static_assert((KDT - 1) * PLANE_INSTR < 64, "vmcnt range");
+  // Highest depth tap read by k-step s (its 4 reduction indices).
+  static constexpr int td_of(int s) { return (4 * s + 3 < K ? 4 * s + 3 : K - 1) / KPP; }
+  // LDS offset (floats) of reduction index k = (td, th, tw) of the box; padding
+  // indices (zero weights) point at the box start.
+  static constexpr int koff(int k) {
+    if (k >= K) return 0;
+    const int td = k / (KH * KW), r2 = k % (KH * KW), th = r2 / KW, tw = r2 % KW;
+    return td * PLANE + th * DH * BW + tw * (DW / F);
+  }
+};
+
+template <int NT, int NW, class G>
+__global__ __launch_bounds__(64 * NW) void conv_tap_split_kernel(ConvArgs a) {
+  constexpr TapPatterns<G> P{};
+  constexpr int NP = P.np;
+  constexpr int RED = NW * NT * 4 * 64;
+  constexpr int STAGE = G::WSH + NW * G::XSW;
+  constexpr int LDS = (STAGE > RED) ? STAGE : RED;
+  __shared__ __align__(16) float smem[LDS];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kg = lane >> 4;
+  const int li = lane & 15;
+  // Workgroups are dispatched round-robin over the 8 XCDs; give each XCD a
+  // contiguous run of (plane, group) items so the input planes that
+  // neighbouring output depths share stay in that XCD's L2.
+  int item = blockIdx.x + gridDim.x * blockIdx.y;
+  const int items = gridDim.x * gridDim.y;
+  if ((items & 7) == 0) item = (item & 7) * (items >> 3) + (item >> 3);
+  const int plane = item % gridDim.x;
+  const int g = item / gridDim.x;
+  const int n = plane / a.O0;
+  const int od = plane - n * a.O0;
+  const int c = wave;  // this wave's input channel within the group
+  float* wsh = smem;
+  float* box = smem + G::WSH + wave * G::XSW;
+
+  float b4[4];
+#pragma unroll
+  for (int r = 0; r < 4; r++) {
+    const int ch = 4 * kg + r;
+    b4[r] = (a.bias && ch < a.Coutg) ? a.bias[g * a.Coutg + ch] : 0.0f;
+  }
+  {
+    // The group's weights [16][WROW] (rows past C_out/g read as zero); copy j
+    // moves floats WCW*j .. WCW*j + WCW-1 of the block.
+    const float* wg = a.w + int64_t(g) * a.Coutg * G::WROW;
+#pragma unroll
+    for (int i = 0; i < G::W_INSTR; i++) {
+      const int j0 = (i * NW + wave) * 64;
+      const int j = j0 + lane;
+      if (j < G::WCH) {
+        const bool ok = (G::WCW * j) / G::WROW < a.Coutg;
+        if constexpr (G::W4) lds_dma_f32x4(ok ? wg + 4 * j : kZeroWord, wsh + 4 * j0);
+        else lds_dma_f32(ok ? wg + j : kZeroWord, wsh + j0);
+      }
+    }
+    // Box: element e = ((td * ROWS) + zr) * BW + j <- input
+    // (od*S0 - P0 + td*DD, zr - P1, F*j - P2) of channel g*Cg + c.
+    const float* xc = a.x + (int64_t(n) * a.Cin + int64_t(g) * a.Cg + c) * (int64_t(a.L0) * a.L1 * a.L2);
+#pragma unroll
+    for (int td = 0; td < G::KDT; td++) {
+      const int id = od * a.S0 - a.P0 + td * a.D0;
+      const bool pok = unsigned(id) < unsigned(a.L0);
+#pragma unroll
+      for (int i = 0; i < G::PLANE_INSTR; i++) {
+        const int e = i * 64 + lane;  // element of this plane
+        if (e < G::PLANE) {
+          const int zr = e / G::BWC, j = e - zr * G::BWC;
+          const int ih = zr - a.P1, iw = G::FF * j - a.P2;
+          const bool ok = pok && (unsigned(ih) < unsigned(a.L1)) && (unsigned(iw) < unsigned(a.L2));
+          lds_dma_f32(ok ? xc + ((int64_t(id) * a.L1 + ih) * a.L2 + iw) : kZeroWord, box + td * G::PLANE + i * 64);
+        }
+      }
+    }
+  }
+  // Output positions of the plane (whole plane, flattened (oh, ow)).
+  int noff[NT], pidx[NT];
+#pragma unroll
+  for (int ni = 0; ni < NT; ni++) {
+    const int p = 16 * ni + li;
+    const int oh = p / a.O2, ow = p - (p / a.O2) * a.O2;
+    const bool valid = p < a.plane_out;
+    noff[ni] = valid ? oh * a.S1 * G::BWC + ow * (a.S2 / G::FF) : 0;
+    pidx[ni] = valid ? p : -1;
+  }
+  int dpat[NP];
+  fill_pat_deltas<G>(dpat, kg, std::make_integer_sequence<int, NP>{});
+  // Byte offsets: position part per sub-tile, pattern part per distinct step shape.
+  const int base_b = int(reinterpret_cast<uintptr_t>(box) - reinterpret_cast<uintptr_t>(smem));
+  int nb[NT], dp[NP];
+#pragma unroll
+  for (int ni = 0; ni < NT; ni++) nb[ni] = base_b + 4 * noff[ni];
+#pragma unroll
+  for (int q = 0; q < NP; q++) dp[q] = 4 * dpat[q];
+
+  v4f acc[NT];
+#pragma unroll
+  for (int ni = 0; ni < NT; ni++) acc[ni] = v4f{0.f, 0.f, 0.f, 0.f};
+  // Weights (copied by every wave) and this wave's first plane have landed. A
+  // plain barrier: a workgroup-scope fence would also wait for the later planes.
+  wait_vmem_le<(G::KDT - 1) * G::PLANE_INSTR>();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+
+  {
+    const char* bb = reinterpret_cast<const char*>(smem);
+    const float* wl = wsh + li * G::WROW + c * G::KVOL + kg;  // A[m = li][k = 4s + kg] at wl[4s]
+    // Operands of step s+1 are read while the matrix core works on step s. The
+    // reduction indices past the channel's kernel volume (last step) take a zero
+    // weight: what lies there in LDS belongs to the next channel.
+    float av[2];
+    float bv[2][NT];
+    av[0] = (G::KVOL >= 4 || kg < G::KVOL) ? wl[0] : 0.0f;
+#pragma unroll
+    for (int ni = 0; ni < NT; ni++)
+      bv[0][ni] = *reinterpret_cast<const float*>(bb + nb[ni] + dp[P.pid[0]] + 4 * G::koff(0));
+#pragma unroll
+    for (int s = 0; s < G::NS; s++) {
+      const int cu = s & 1, nx = cu ^ 1;
+      if (s + 1 < G::NS) {
+        // Step s+1 reads taps up to depth tap td_of(s+1): wait for its plane.
+        if (G::td_of(s + 1) != G::td_of(s)) {
+          if (G::td_of(s + 1) == 1) wait_vmem_le<(G::KDT > 2 ? (G::KDT - 2) * G::PLANE_INSTR : 0)>();
+          else wait_vmem_le<0>();
+        }
+        av[nx] = wl[4 * (s + 1)];
+        if (4 * (s + 1) + 3 >= G::KVOL) av[nx] = (4 * (s + 1) + kg < G::KVOL) ? av[nx] : 0.0f;
+#pragma unroll
+        for (int ni = 0; ni < NT; ni++)
+          bv[nx][ni] = *reinterpret_cast<const float*>(bb + nb[ni] + dp[P.pid[s + 1]] + 4 * G::koff(4 * (s + 1)));
+      }
+#pragma unroll
+      for (int ni = 0; ni < NT; ni++)
+        acc[ni] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[cu], bv[cu][ni], acc[ni], 0, 0, 0);
+      // Interleave the next step's LDS reads with this step's matrix-core work.
+#pragma unroll
+      for (int i = 0; i < NT; i++) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
+    }
+  }
+
+  // Sum the NW partial tiles: every wave parks its tile, then wave w adds up the
+  // (sub-tile, register) pairs p with p % NW == w and stores them.
+  __syncthreads();
+#pragma unroll
+  for (int ni = 0; ni < NT; ni++)
+#pragma unroll
+    for (int r = 0; r < 4; r++) smem[((wave * NT + ni) * 4 + r) * 64 + lane] = acc[ni][r];
+  __syncthreads();
+  const int64_t out_plane = int64_t(a.O1) * a.O2;
+  for (int pr = wave; pr < NT * 4; pr += NW) {
+    const int ni = pr >> 2, r = pr & 3;
+    float v = 0.0f;
+#pragma unroll
+    for (int w2 = 0; w2 < NW; w2++) v += smem[((w2 * NT + ni) * 4 + r) * 64 + lane];
+    const int ch = 4 * kg + r;
+    int pi = -1;
+#pragma unroll
+    for (int q = 0; q < NT; q++)
+      if (q == ni) pi = pidx[q];
+    const float b = r == 0 ? b4[0] : r == 1 ? b4[1] : r == 2 ? b4[2] : b4[3];
+    if (ch < a.Coutg && pi >= 0) {
+      const int co = g * a.Coutg + ch;
+      a.y[((int64_t(n) * a.Cout + co) * a.O0 + od) * out_plane + pi] = v + b;
+    }
   }
 }
 
@@ -828,9 +1085,31 @@ static int launch_tap(const ConvArgs& args, const ConvPlan& p, hipStream_t strea
   static std::once_flag once;
   static hipError_t err = hipSuccess;
   auto fn = conv_tap_kernel<MT, NT, WM, WN, NCH, G>;
-  if (set_lds_limit_once(fn, once, err) != CONV_OK) return CONV_ERR_HIP;
-  hipLaunchKernelGGL(fn, dim3(unsigned(p.grid[0])), dim3(64 * WM * WN), size_t(p.lds_bytes), stream, args);
+  static_assert(4 * G::template lds_floats<NCH, WM, MT>() <= kLdsLimit, "tap specialisation exceeds LDS");
+  if (4 * int64_t(G::template lds_floats<NCH, WM, MT>()) != p.lds_bytes) return CONV_ERR_UNSUPPORTED;
+  (void)once;
+  (void)err;
+  hipLaunchKernelGGL(fn, dim3(unsigned(p.grid[0])), dim3(64 * WM * WN), 0, stream, args);
   return hipGetLastError() == hipSuccess ? CONV_OK : CONV_ERR_HIP;
+}
+
+template <int NT, int NW, int KD, int KH, int KW, int DD, int DH, int DW, int F, int ROWS, int BW>
+static int launch_split(const ConvArgs& args, const ConvPlan& p, hipStream_t stream) {
+  using G = SplitGeo<KD, KH, KW, DD, DH, DW, F, ROWS, BW, NW>;
+  hipLaunchKernelGGL((conv_tap_split_kernel<NT, NW, G>), dim3(unsigned(p.grid[0]), unsigned(p.grid[1]), 1),
+                     dim3(64 * NW), 0, stream, args);
+  return hipGetLastError() == hipSuccess ? CONV_OK : CONV_ERR_HIP;
+}
+
+static int launch_split_spec(const ConvArgs& args, const ConvPlan& p, hipStream_t stream) {
+  switch (p.split_spec) {
+#define CONVHIP_SPLIT_CASE(id, NT, NW, KD, KH, KW, DD, DH, DW, F, ROWS, BW) \
+  case id:                                                                  \
+    return launch_split<NT, NW, KD, KH, KW, DD, DH, DW, F, ROWS, BW>(args, p, stream);
+    CONVHIP_SPLIT_SPECS(CONVHIP_SPLIT_CASE)
+#undef CONVHIP_SPLIT_CASE
+    default: return CONV_ERR_UNSUPPORTED;
+  }
 }
 
 static int launch_tap_spec(const ConvArgs& args, const ConvPlan& p, hipStream_t stream) {
@@ -981,6 +1260,7 @@ int conv_fwd(int nd, const float* x, const int64_t* x_shape, const float* w, con
   ConvArgs a = conv_args(g, p, x, w, bias, y);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (p.tap_spec >= 0) return launch_tap_spec(a, p, s);
+  if (p.split_spec >= 0) return launch_split_spec(a, p, s);
   switch (p.cfg) {
     case CFG_M64: return launch_conv_cfg<4, 4, 1, 4, 1>(a, p, s);
     case CFG_M128: return launch_conv_cfg<4, 4, 2, 2, 1>(a, p, s);

@@ -103,6 +103,53 @@ const TapSpecDesc* tap_specs(int* count) {
   return specs;
 }
 
+const SplitSpecDesc* split_specs(int* count) {
+#define CONVHIP_SPLIT_DESC(id, NT, NW, KD, KH, KW, DD, DH, DW, F, ROWS, BW) \
+  {id, NT, NW, KD, KH, KW, DD, DH, DW, F, ROWS, BW},
+  static const SplitSpecDesc specs[] = {CONVHIP_SPLIT_SPECS(CONVHIP_SPLIT_DESC)};
+#undef CONVHIP_SPLIT_DESC
+  *count = int(sizeof(specs) / sizeof(specs[0]));
+  return specs;
+}
+
+static bool plan_split(const Geom& g, const SplitSpecDesc& d, ConvPlan* p) {
+  if (g.Coutg > 16 || g.Cg != d.NW) return false;
+  if (g.K[0] != d.KD || g.K[1] != d.KH || g.K[2] != d.KW) return false;
+  if (g.Dl[0] != d.DD || g.Dl[1] != d.DH || g.Dl[2] != d.DW) return false;
+  if (g.S[2] % d.F != 0 || g.Dl[2] % d.F != 0) return false;
+  if (g.plane_out() > 16 * d.NT || g.plane_out() <= 16 * (d.NT - 1)) return false;
+  const int64_t kvol = int64_t(d.KD) * d.KH * d.KW;
+  const int64_t rows = (g.O[1] - 1) * g.S[1] + (g.K[1] - 1) * g.Dl[1] + 1;
+  const int64_t bw = ((g.O[2] - 1) * g.S[2] + (g.K[2] - 1) * g.Dl[2]) / d.F + 1;
+  if (rows != d.ROWS || bw != d.BW) return false;
+  if (g.N * g.O[0] > std::numeric_limits<int32_t>::max() || g.G > 65535) return false;
+  ConvPlan q;
+  q.cfg = -1;
+  q.split_spec = d.id;
+  q.threads = 64 * d.NW;
+  q.BM = 16;
+  q.BN = 16 * d.NT;
+  q.mode = TILE_FLAT;
+  q.Cc = 1;
+  q.kc_pad = int((kvol + 3) / 4 * 4);
+  q.kdspan = d.KD;
+  q.rows = int(rows);
+  q.bw = int(bw);
+  q.boxc = int(d.KD * rows * bw);
+  q.tiles_per_plane = 1;
+  q.ctiles = 1;
+  q.nchunks = 1;
+  const int64_t xsw = (int64_t(q.boxc) + 3) / 4 * 4;
+  const int64_t wsh = (16 * d.NW * kvol + 4 + 3) / 4 * 4;
+  q.lds_bytes = 4 * std::max<int64_t>(wsh + int64_t(d.NW) * xsw, int64_t(d.NW) * d.NT * 4 * 64);
+  if (q.lds_bytes > kLdsLimit) return false;
+  q.grid[0] = g.N * g.O[0];
+  q.grid[1] = g.G;
+  q.grid[2] = 1;
+  *p = q;
+  return true;
+}
+
 // Plan of a tap specialisation if the geometry is exactly the one it was built for.
 static bool plan_tap(const Geom& g, const TapSpecDesc& d, int num_cu, ConvPlan* p) {
   const int BM = 16 * d.MT * d.WM, BN = 16 * d.NT * d.WN;
@@ -159,6 +206,9 @@ int plan_conv(const Geom& g, ConvPlan* out, int force_cfg, int num_cu, int use_t
     const TapSpecDesc* specs = tap_specs(&n);
     for (int i = 0; i < n; i++)
       if (plan_tap(g, specs[i], num_cu, out)) return CONV_OK;
+    const SplitSpecDesc* ss = split_specs(&n);
+    for (int i = 0; i < n; i++)
+      if (plan_split(g, ss[i], out)) return CONV_OK;
   }
   ConvPlan p;
   if (force_cfg >= 0 && force_cfg < CFG_COUNT) {
@@ -283,11 +333,16 @@ std::string describe(const Geom& g, const ConvPlan& p) {
     int n = 0;
     const TapSpecDesc& d = tap_specs(&n)[p.tap_spec];
     cs = CfgShape{d.MT, d.NT, d.WM, d.WN, 1};
+  } else if (p.split_spec >= 0) {
+    int n = 0;
+    const SplitSpecDesc& d = split_specs(&n)[p.split_spec];
+    cs = CfgShape{1, d.NT, 1, 1, d.NW};
   }
   std::snprintf(buf, sizeof buf,
                 "kernel=%s cfg=%d MT=%d NT=%d WM=%d WN=%d KS=%d BM=%d BN=%d mode=%s Cc=%d kc_pad=%d "
                 "box=%dx%dx%d grid=%lldx%lldx%lld lds=%lld macs=%lld",
-                p.tap_spec >= 0 ? "conv_tap" : "conv_mfma16", p.tap_spec >= 0 ? p.tap_spec : p.cfg, cs.MT, cs.NT,
+                p.tap_spec >= 0 ? "conv_tap" : p.split_spec >= 0 ? "conv_tap_split" : "conv_mfma16",
+                p.tap_spec >= 0 ? p.tap_spec : p.split_spec >= 0 ? p.split_spec : p.cfg, cs.MT, cs.NT,
                 cs.WM, cs.WN, cs.KS, p.BM, p.BN, p.mode == TILE_FLAT ? "flat" : "row", p.Cc,
                 p.kc_pad, p.kdspan, p.rows, p.bw, (long long)p.grid[0], (long long)p.grid[1],
                 (long long)p.grid[2], (long long)p.lds_bytes, (long long)g.macs());

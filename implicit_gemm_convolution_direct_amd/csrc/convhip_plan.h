@@ -74,6 +74,7 @@ struct ConvPlan {
   int ctiles = 0;      // channel tiles per group
   int nchunks = 0;      // chunks of Cc input channels per tile
   int tap_spec = -1;    // >= 0: build-time specialised persistent kernel (grid[0] workgroups walk `items`)
+  int split_spec = -1;  // >= 0: build-time specialised channel-split kernel
   int threads = 256;    // workgroup size
   int64_t items = 0;    // tap kernel: work items (tile, plane)
   int64_t grid[3] = {0, 0, 0};
@@ -90,6 +91,21 @@ struct ConvPlan {
   X(0, 4, 2, 1, 8, 1, 3, 5, 7, 1, 1, 1, 3, 3, 10, 64)                            \
   /* Conv1d 64->128, k=3, stride 3, dilation 4: 128 ch x 256 positions */       \
   X(1, 4, 4, 2, 4, 8, 1, 1, 3, 1, 1, 4, 8, 1, 1, 774)
+
+// Build-time specialisations of the channel-split kernel (one input channel per
+// wave, whole (n, od) plane per workgroup, <= 16 output channels per group).
+// X(id, NT, NW, KD, KH, KW, DD, DH, DW, F, ROWS, BW): the staged box keeps every
+// F-th input column; ROWS input rows and BW kept columns per plane.
+#define CONVHIP_SPLIT_SPECS(X)                                                     \
+  /* Conv3d 16->32, groups 2, kernel 3x5x7, stride (1,2,2), dilation (1,1,2) */  \
+  X(0, 13, 8, 3, 5, 7, 1, 1, 2, 2, 35, 19)                                        \
+  /* Conv3d 3->8, kernel 3x3x3 on 16^3 */                                         \
+  X(1, 13, 3, 3, 3, 3, 1, 1, 1, 1, 16, 16)
+
+struct SplitSpecDesc {
+  int id, NT, NW, KD, KH, KW, DD, DH, DW, F, ROWS, BW;
+};
+const SplitSpecDesc* split_specs(int* count);
 
 struct TapSpecDesc {
   int id, MT, NT, WM, WN, NCH, KD, KH, KW, DD, DH, DW, CC, KDSPAN, ROWS, BW;

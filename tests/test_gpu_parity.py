@@ -290,6 +290,29 @@ def test_tap_specialised_kernel_integer_exact(case):
     np.testing.assert_array_equal(y.astype(np.float64), oracle.conv(x, w, b, s, d, p, 1))
 
 
+SPLIT_CASES = [
+    # general Conv3d geometry (groups 2, stride (1,2,2), dilation (1,1,2)) with fewer planes
+    ((1, 16, 6, 32, 32), (32, 8, 3, 5, 7), (1, 2, 2), (1, 1, 2), (1, 2, 3), 2),
+    ((2, 16, 3, 32, 32), (20, 8, 3, 5, 7), (1, 2, 2), (1, 1, 2), (0, 2, 3), 2),
+    ((1, 8, 4, 32, 32), (16, 8, 3, 5, 7), (1, 2, 2), (1, 1, 2), (1, 2, 3), 1),
+    # tiny Conv3d geometry
+    ((2, 3, 4, 16, 16), (8, 3, 3, 3, 3), 1, 1, 0, 1),
+    ((1, 3, 5, 16, 16), (5, 3, 3, 3, 3), 1, 1, 0, 1),
+]
+
+
+@pytest.mark.parametrize("case", range(len(SPLIT_CASES)))
+def test_split_specialised_kernel_integer_exact(case):
+    xs, ws, s, d, p, g = SPLIT_CASES[case]
+    desc = ch.plan_describe(xs, ws, s, d, p, g)
+    assert "kernel=conv_tap_split" in desc, desc
+    r = np.random.default_rng(500 + case)
+    x, w, b = _int_inputs(r, xs, ws, bias=True)
+    say(f"split case {case}: x={xs} w={ws}: {desc}")
+    y = gpu_conv(x, w, b, s, d, p, g)
+    np.testing.assert_array_equal(y.astype(np.float64), oracle.conv(x, w, b, s, d, p, g))
+
+
 def test_tap_disabled_falls_back_to_streamed(monkeypatch):
     monkeypatch.setenv("CONVHIP_TAP", "0")
     xs, ws, s, d, p, _ = TAP_CASES[0]
@@ -303,7 +326,7 @@ def test_tap_disabled_falls_back_to_streamed(monkeypatch):
 
 def test_workloads_use_expected_kernels():
     for name, kernel in [("asym_conv3d", "conv_tap"), ("long_conv1d", "conv_tap"),
-                         ("general_conv3d", "conv_mfma16 "), ("tiny_conv3d", "conv_mfma16 ")]:
+                         ("general_conv3d", "conv_tap_split"), ("tiny_conv3d", "conv_tap_split")]:
         cfg = synth.WORKLOADS[name]
         d = ch.plan_describe(cfg["x"], cfg["w"], *_cfg_args(cfg)) + " "
         assert f"kernel={kernel}" in d, d
