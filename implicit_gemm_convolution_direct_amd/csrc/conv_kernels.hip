@@ -1028,6 +1028,211 @@ __global__ __launch_bounds__(256) void fused_min_softmax_mfma4_kernel(FusedArgs 
 }
 
 // ---------------------------------------------------------------------------
+// fused_stream: Conv3d -> min over depth -> softmax over channels for a fixed
+// small geometry (stride 1, dilation 1, groups 1, kD = 3), streaming the input
+// depth planes once.
+// - One wave owns 64 consecutive output positions (h, w) of one sample and every
+//   output depth; the waves of a workgroup are independent (no barriers).
+// - Input plane z feeds output depths z, z-1, z-2 (depth taps 0, 1, 2): each
+//   staged value is read from LDS once and multiplied into three rolling sets of
+//   accumulators; the set of depth z-2 is complete after plane z and is folded
+//   into the running minimum.
+// - Planes are copied into a ring of three LDS slots two planes ahead.
+// - Matrix core: 4x4x1 MFMA with 16 blocks, the weight operand broadcast from
+//   one block (cbsz 4, abid b): lane l accumulates channels 4g..4g+3 of position
+//   l, so C_out is covered in steps of 4 channels with no padding, and every
+//   weight (channel group, reduction index) pair sits in one of 16 lane quads of
+//   a resident register.
+// - The depth minimum, bias, and the softmax over all channels stay inside the
+//   lane: nothing of the conv result leaves the registers.
+// ---------------------------------------------------------------------------
+template <int N, class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl<N>(f, std::make_integer_sequence<int, N>{});
+}
+
+template <int CIN, int KH, int KW_, int NG, int O2, int ROWS>
+struct StreamGeo {
+  static constexpr int CIN_ = CIN, NG_ = NG, O2_ = O2, KW = KW_;
+  static constexpr int KD = 3;
+  static constexpr int BW = O2 + KW_ - 1;       // input columns per staged row
+  static constexpr int CH = ROWS * BW;           // floats per channel of a plane
+  static constexpr int PLANE = CIN * CH;         // floats of one staged plane
+  static constexpr int PI = (PLANE + 63) / 64;   // 64-lane copies per plane
+  static constexpr int SLOT = PI * 64;           // slot floats (every copy lane lands inside)
+  static constexpr int NSLOT = 3;
+  static constexpr int KHW = KH * KW_;
+  static constexpr int KVOL = KD * KHW;
+  static constexpr int KRED = CIN * KVOL;
+  static constexpr int NT = CIN * KHW;           // staged values read per plane
+  static constexpr int NPAIR = NG * KRED;        // (channel group, reduction index) pairs
+  static constexpr int NAREG = (NPAIR + 15) / 16;
+  static_assert(2 * PI < 64, "vmcnt range");
+};
+
+struct StreamArgs {
+  const float* __restrict__ x;
+  const float* __restrict__ w;
+  const float* __restrict__ bias;
+  float* __restrict__ y;
+  int Cout;
+  int L0, L1, L2;
+  int P0, P1, P2;
+  int O0, O1;
+  int plane_out;
+  int tiles_per_plane;
+  int units;  // N * tiles_per_plane
+};
+
+template <class G>
+__global__ __launch_bounds__(256, 2) void fused_stream_kernel(StreamArgs a) {
+  constexpr int NG = G::NG_;
+  __shared__ __align__(16) float smem[4 * G::NSLOT * G::SLOT];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int unit = blockIdx.x * 4 + wave;
+  if (unit >= a.units) return;  // wave-uniform; the waves share no barrier
+  const int n = unit / a.tiles_per_plane;
+  const int p0 = (unit - n * a.tiles_per_plane) * 64;
+  float* ring = smem + wave * (G::NSLOT * G::SLOT);
+
+  // Weights: register r, lane 4b + i holds w[4g + i][k] for pair 16r + b = g * KRED + k.
+  float aw[G::NAREG];
+#pragma unroll
+  for (int r = 0; r < G::NAREG; r++) {
+    const int pair = 16 * r + (lane >> 2);
+    const int gq = pair / G::KRED, k = pair - gq * G::KRED;
+    const int co = 4 * gq + (lane & 3);
+    aw[r] = (pair < G::NPAIR && co < a.Cout) ? a.w[co * G::KRED + k] : 0.0f;
+  }
+
+  // Copy sources: copy i, lane l moves slot element e = 64i + l = (c, row, col)
+  // from input (c, ih0 + row, col - P2) of the plane being staged.
+  const int oh_first = p0 / G::O2_;
+  const int ih0 = oh_first - a.P1;
+  const int64_t chan_stride = int64_t(a.L0) * a.L1 * a.L2;
+  const float* xn = a.x + int64_t(n) * G::CIN_ * chan_stride;
+  int soff[G::PI];
+  uint32_t sok = 0;
+#pragma unroll
+  for (int i = 0; i < G::PI; i++) {
+    const int e = 64 * i + lane;
+    const int c = e / G::CH, rem = e - (e / G::CH) * G::CH;
+    const int r = rem / G::BW, col = rem - (rem / G::BW) * G::BW;
+    const int ih = ih0 + r, iw = col - a.P2;
+    const bool ok = (e < G::PLANE) && unsigned(ih) < unsigned(a.L1) && unsigned(iw) < unsigned(a.L2);
+    soff[i] = ok ? int(c * chan_stride) + ih * a.L2 + iw : 0;
+    sok |= uint32_t(ok) << i;
+  }
+  const int plane_elems = a.L1 * a.L2;
+  const int Z = a.O0 + G::KD - 1;  // staged planes: input depths -P0 .. O0 + 1 - P0
+  auto stage = [&](int z, int slot) {
+    const int id = z - a.P0;
+    const bool pok = (z < Z) && unsigned(id) < unsigned(a.L0);
+    const float* xp = xn + int64_t(pok ? id : 0) * plane_elems;
+#pragma unroll
+    for (int i = 0; i < G::PI; i++) {
+      const bool ok = pok && ((sok >> i) & 1);
+      lds_dma_f32(ok ? xp + soff[i] : kZeroWord, ring + slot * G::SLOT + 64 * i);
+    }
+  };
+
+  // This lane's output position and its offset inside a slot.
+  const int p = p0 + lane;
+  const bool valid = p < a.plane_out;
+  const int oh = p / G::O2_, ow = p - (p / G::O2_) * G::O2_;
+  const int lbase = valid ? (oh - oh_first) * G::BW + ow : 0;
+  const char* bbase = reinterpret_cast<const char*>(ring) + 4 * lbase;
+
+  v4f acc[3][NG];
+  v4f mn[NG];
+#pragma unroll
+  for (int q = 0; q < NG; q++) mn[q] = v4f{INFINITY, INFINITY, INFINITY, INFINITY};
+
+  stage(0, 0);
+  stage(1, 1);
+  for (int z0 = 0; z0 < Z; z0 += 3) {
+    static_for<3>([&](auto JJ) {
+      constexpr int J = decltype(JJ)::value;
+      const int z = z0 + J;
+      if (z < Z) {
+        // Plane z + 2 goes into the slot plane z - 1 used, once those reads
+        // have returned.
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        asm volatile("" ::: "memory");
+        stage(z + 2, (J + 2) % 3);
+        wait_vmem_le<2 * G::PI>();
+        asm volatile("" ::: "memory");
+        float bv[G::NT];
+        static_for<G::NT>([&](auto TT) {
+          constexpr int t = decltype(TT)::value;
+          constexpr int c = t / G::KHW, kh = (t % G::KHW) / G::KW, kw = t % G::KW;
+          bv[t] = *reinterpret_cast<const float*>(bbase + 4 * (J * G::SLOT + c * G::CH + kh * G::BW + kw));
+        });
+        static_for<3>([&](auto KK) {
+          constexpr int kd = decltype(KK)::value;
+          constexpr int set = (J - kd + 3) % 3;
+          const int od = z - kd;
+          if (od >= 0 && od < a.O0) {
+            static_for<G::NT>([&](auto TT) {
+              constexpr int t = decltype(TT)::value;
+              constexpr int c = t / G::KHW, hw = t % G::KHW;
+              constexpr int k = c * G::KVOL + kd * G::KHW + hw;
+              static_for<NG>([&](auto QQ) {
+                constexpr int q = decltype(QQ)::value;
+                constexpr int pair = q * G::KRED + k;
+                constexpr int r = pair / 16, ab = pair % 16;
+                if constexpr (kd == 0 && t == 0)
+                  acc[set][q] = __builtin_amdgcn_mfma_f32_4x4x1f32(aw[r], bv[t], v4f{0.f, 0.f, 0.f, 0.f}, 4, ab, 0);
+                else
+                  acc[set][q] = __builtin_amdgcn_mfma_f32_4x4x1f32(aw[r], bv[t], acc[set][q], 4, ab, 0);
+              });
+            });
+            if constexpr (kd == 2) {
+#pragma unroll
+              for (int q = 0; q < NG; q++)
+#pragma unroll
+                for (int i = 0; i < 4; i++) mn[q][i] = fminf(mn[q][i], acc[set][q][i]);
+            }
+          }
+        });
+      }
+    });
+  }
+
+  // Softmax over the channels of this lane's position. fp32 addition is
+  // monotone, so adding the bias after the minimum equals adding it before.
+  if (valid) {
+    float m[4 * NG];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < NG; q++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const int c = 4 * q + i;
+        m[c] = c < a.Cout ? mn[q][i] + (a.bias ? a.bias[c] : 0.0f) : -INFINITY;
+        mx = fmaxf(mx, m[c]);
+      }
+    float sum = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 4 * NG; c++) {
+      const float e = c < a.Cout ? expf(m[c] - mx) : 0.0f;
+      m[c] = e;
+      sum += e;
+    }
+    const float inv = 1.0f / sum;
+    float* yp = a.y + int64_t(n) * a.Cout * a.plane_out + p;
+#pragma unroll
+    for (int c = 0; c < 4 * NG; c++)
+      if (c < a.Cout) yp[int64_t(c) * a.plane_out] = m[c] * inv;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Device-side synthetic input generator (SplitMix64, one output per element).
 // ---------------------------------------------------------------------------
 __global__ void synth_fill_kernel(float* __restrict__ dst, int64_t count, uint64_t seed, uint64_t start,
@@ -1138,6 +1343,25 @@ static int launch_fused_ng(const FusedArgs& args, const FusedPlan& p, hipStream_
   return hipGetLastError() == hipSuccess ? CONV_OK : CONV_ERR_HIP;
 }
 
+template <int CIN, int KH, int KW, int NG, int O2, int ROWS>
+static int launch_stream(const StreamArgs& args, const FusedPlan& p, hipStream_t stream) {
+  using G = StreamGeo<CIN, KH, KW, NG, O2, ROWS>;
+  if (int64_t(4) * 4 * G::NSLOT * G::SLOT != p.lds_bytes) return CONV_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL(fused_stream_kernel<G>, dim3(unsigned(p.grid[0])), dim3(256), 0, stream, args);
+  return hipGetLastError() == hipSuccess ? CONV_OK : CONV_ERR_HIP;
+}
+
+static int launch_stream_spec(const StreamArgs& args, const FusedPlan& p, hipStream_t stream) {
+  switch (p.spec) {
+#define CONVHIP_FUSED_CASE(id, CIN, KH, KW, NG, O2, ROWS) \
+  case id:                                              \
+    return launch_stream<CIN, KH, KW, NG, O2, ROWS>(args, p, stream);
+    CONVHIP_FUSED_SPECS(CONVHIP_FUSED_CASE)
+#undef CONVHIP_FUSED_CASE
+    default: return CONV_ERR_UNSUPPORTED;
+  }
+}
+
 static ConvArgs conv_args(const Geom& g, const ConvPlan& p, const float* x, const float* w, const float* bias,
                           float* y) {
   ConvArgs a;
@@ -1171,7 +1395,8 @@ static int forced_conv_cfg() {
   return (v >= 0 && v < CFG_COUNT) ? v : -1;
 }
 
-// CONVHIP_TAP=0 keeps conv_fwd off the build-time specialised kernels.
+// CONVHIP_TAP=0 keeps conv_fwd and conv3d_min_softmax off the build-time
+// specialised kernels.
 static int use_tap() {
   const char* s = std::getenv("CONVHIP_TAP");
   if (!s || !*s) return -1;
@@ -1234,7 +1459,7 @@ int conv_plan_describe(int nd, const int64_t* x_shape, const int64_t* w_shape, c
   std::string s;
   if (fused) {
     FusedPlan p;
-    rc = plan_fused(g, 2, &p);
+    rc = plan_fused(g, 2, &p, use_tap() != 0);
     if (rc != CONV_OK) return rc;
     s = describe(g, p);
   } else {
@@ -1281,8 +1506,21 @@ int conv3d_min_softmax(const float* x, const int64_t* x_shape, const float* w, c
   if (!x || !w || !y) return CONV_ERR_NULL;
   if (min_dim < 2 || min_dim > 4) return CONV_ERR_PARAM;
   FusedPlan p;
-  rc = plan_fused(g, min_dim, &p);
+  rc = plan_fused(g, min_dim, &p, use_tap() != 0);
   if (rc != CONV_OK) return rc;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (p.spec >= 0) {
+    StreamArgs sa;
+    sa.x = x; sa.w = w; sa.bias = bias; sa.y = y;
+    sa.Cout = int(g.Cout);
+    sa.L0 = int(g.L[0]); sa.L1 = int(g.L[1]); sa.L2 = int(g.L[2]);
+    sa.P0 = int(g.P[0]); sa.P1 = int(g.P[1]); sa.P2 = int(g.P[2]);
+    sa.O0 = int(g.O[0]); sa.O1 = int(g.O[1]);
+    sa.plane_out = int(g.plane_out());
+    sa.tiles_per_plane = int(p.tiles_per_plane);
+    sa.units = int(p.units);
+    return launch_stream_spec(sa, p, s);
+  }
   FusedArgs a;
   a.x = x; a.w = w; a.bias = bias; a.y = y;
   a.Cin = int(g.Cin); a.Cout = int(g.Cout);
@@ -1295,7 +1533,6 @@ int conv3d_min_softmax(const float* x, const int64_t* x_shape, const float* w, c
   a.kvol = int(g.kvol()); a.kfull = p.kfull; a.cpad = p.cpad;
   a.mode = p.mode; a.dspan = p.dspan; a.rows = p.rows; a.bw = p.bw; a.boxc = p.boxc; a.row_tiles = p.row_tiles;
   a.plane_out = int(g.plane_out());
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   switch (p.ng) {
     case 1: return launch_fused_ng<1>(a, p, s);
     case 2: return launch_fused_ng<2>(a, p, s);

@@ -300,9 +300,60 @@ int plan_conv(const Geom& g, ConvPlan* out, int force_cfg, int num_cu, int use_t
   return CONV_OK;
 }
 
-int plan_fused(const Geom& g, int min_dim, FusedPlan* out) {
+#define CONVHIP_FUSED_DESC(id, CIN, KH, KW, NG, O2, ROWS) {id, CIN, KH, KW, NG, O2, ROWS},
+static const FusedSpecDesc kFusedSpecs[] = {CONVHIP_FUSED_SPECS(CONVHIP_FUSED_DESC)};
+#undef CONVHIP_FUSED_DESC
+
+const FusedSpecDesc* fused_specs(int* count) {
+  *count = int(sizeof(kFusedSpecs) / sizeof(kFusedSpecs[0]));
+  return kFusedSpecs;
+}
+
+// Plan of a depth-streamed specialisation if the geometry is the one it was built for.
+static bool plan_fused_stream(const Geom& g, const FusedSpecDesc& d, FusedPlan* p) {
+  if (g.Cin != d.CIN || g.K[0] != 3 || g.K[1] != d.KH || g.K[2] != d.KW) return false;
+  for (int i = 0; i < 3; i++)
+    if (g.S[i] != 1 || g.Dl[i] != 1) return false;
+  if ((g.Cout + 3) / 4 != d.NG || g.O[2] != d.O2) return false;
+  const int64_t plane_out = g.plane_out();
+  const int64_t tiles = (plane_out + 63) / 64;
+  for (int64_t t = 0; t < tiles; t++) {
+    const int64_t p0 = 64 * t, p1 = std::min(p0 + 63, plane_out - 1);
+    if (p1 / g.O[2] - p0 / g.O[2] + d.KH > d.ROWS) return false;
+  }
+  if (g.Cin * g.L[0] * g.L[1] * g.L[2] > std::numeric_limits<int32_t>::max()) return false;
+  const int64_t units = g.N * tiles;
+  if ((units + 3) / 4 > std::numeric_limits<int32_t>::max()) return false;
+  FusedPlan q;
+  q.spec = d.id;
+  q.units = units;
+  q.ng = d.NG;
+  q.cpad = 4 * d.NG;
+  q.mode = TILE_FLAT;
+  q.dspan = int(g.O[0] + 2);
+  q.rows = d.ROWS;
+  q.bw = d.O2 + d.KW - 1;
+  q.kfull = int(g.Cin * g.kvol());
+  q.tiles_per_plane = tiles;
+  const int64_t slot = (int64_t(d.CIN) * d.ROWS * q.bw + 63) / 64 * 64;
+  q.boxc = int(slot);
+  q.lds_bytes = 4 * 4 * 3 * slot;
+  q.grid[0] = (units + 3) / 4;
+  q.grid[1] = 1;
+  q.grid[2] = 1;
+  *p = q;
+  return true;
+}
+
+int plan_fused(const Geom& g, int min_dim, FusedPlan* out, bool allow_spec) {
   if (g.nd != 3) return CONV_ERR_RANK;
   if (min_dim != 2 || g.G != 1 || g.Cout > 64) return CONV_ERR_UNSUPPORTED;
+  if (allow_spec) {
+    int ns = 0;
+    const FusedSpecDesc* specs = fused_specs(&ns);
+    for (int i = 0; i < ns; i++)
+      if (plan_fused_stream(g, specs[i], out)) return CONV_OK;
+  }
   FusedPlan p;
   p.cpad = int((g.Cout + 3) / 4 * 4);
   p.ng = p.cpad / 4;
@@ -351,6 +402,15 @@ std::string describe(const Geom& g, const ConvPlan& p) {
 
 std::string describe(const Geom& g, const FusedPlan& p) {
   char buf[512];
+  if (p.spec >= 0) {
+    std::snprintf(buf, sizeof buf,
+                  "kernel=fused_stream spec=%d ng=%d cpad=%d planes=%d rows=%d bw=%d tiles=%lld units=%lld "
+                  "grid=%lldx%lldx%lld lds=%lld macs=%lld",
+                  p.spec, p.ng, p.cpad, p.dspan, p.rows, p.bw, (long long)p.tiles_per_plane, (long long)p.units,
+                  (long long)p.grid[0], (long long)p.grid[1], (long long)p.grid[2], (long long)p.lds_bytes,
+                  (long long)g.macs());
+    return buf;
+  }
   std::snprintf(buf, sizeof buf,
                 "kernel=fused_min_softmax_mfma4 ng=%d cpad=%d mode=%s box=%dx%dx%dx%d grid=%lldx%lldx%lld "
                 "lds=%lld macs=%lld",

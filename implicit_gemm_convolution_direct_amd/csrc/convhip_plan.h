@@ -116,8 +116,23 @@ const TapSpecDesc* tap_specs(int* count);
 // use_tap: -1 planner's choice, 0 never use a tap specialisation.
 int plan_conv(const Geom& g, ConvPlan* p, int force_cfg = -1, int num_cu = 256, int use_tap = -1);
 
+// Build-time specialisations of the depth-streamed fused kernel (stride 1,
+// dilation 1, groups 1, kD = 3, min over depth): X(id, CIN, KH, KW, NG, O2, ROWS)
+// with NG groups of 4 output channels, W_out = O2 and at most ROWS staged input
+// rows per 64-position tile.
+#define CONVHIP_FUSED_SPECS(X)                                 \
+  /* Conv3d 3->24, kernel 3x3x3, 32x32 planes (W_out 30) */ \
+  X(0, 3, 3, 3, 6, 30, 6)
+
+struct FusedSpecDesc {
+  int id, CIN, KH, KW, NG, O2, ROWS;
+};
+const FusedSpecDesc* fused_specs(int* count);
+
 // Plan of the fused conv -> min over depth -> softmax over channels kernel.
 struct FusedPlan {
+  int spec = -1;       // >= 0: depth-streamed specialisation (one wave per 64 positions)
+  int64_t units = 0;   // streamed: N * tiles_per_plane waves
   int ng = 0;          // channel groups of 4 handled by one lane
   int cpad = 0;        // C_out rounded up to 4
   int mode = TILE_FLAT;
@@ -129,7 +144,8 @@ struct FusedPlan {
   int64_t grid[3] = {0, 0, 0};
   int64_t lds_bytes = 0;
 };
-int plan_fused(const Geom& g, int min_dim, FusedPlan* p);
+// allow_spec: false skips the build-time specialisations (tests of the generic kernel).
+int plan_fused(const Geom& g, int min_dim, FusedPlan* p, bool allow_spec = true);
 
 std::string describe(const Geom& g, const ConvPlan& p);
 std::string describe(const Geom& g, const FusedPlan& p);

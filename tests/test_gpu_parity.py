@@ -223,6 +223,44 @@ def test_fused_cases(case):
     assert err <= FUSED_ATOL
 
 
+STREAM_CASES = [
+    # depth-streamed kernel geometry: C_in 3, kernel 3x3x3, stride 1, W_out 30
+    ("full_planes", (2, 3, 6, 32, 32), (24, 3, 3, 3, 3), 0, True),
+    ("short_plane", (1, 3, 5, 10, 32), (24, 3, 3, 3, 3), 0, True),
+    ("padded_cout22", (1, 3, 4, 9, 30), (22, 3, 3, 3, 3), (1, 2, 1), False),
+    ("cout21_depth1", (2, 3, 3, 7, 32), (21, 3, 3, 3, 3), (0, 1, 0), True),
+    ("ragged_units", (3, 3, 8, 21, 32), (24, 3, 3, 3, 3), 0, True),
+]
+
+
+@pytest.mark.parametrize("case", STREAM_CASES, ids=[c[0] for c in STREAM_CASES])
+def test_fused_stream_cases(case):
+    name, xs, ws, p, bias = case
+    desc = ch.plan_describe(xs, ws, 1, 1, p, 1, fused=True)
+    assert "kernel=fused_stream" in desc, desc
+    r = np.random.default_rng(900 + len(name))
+    x, w, b = _float_inputs(r, xs, ws, bias)
+    say(f"stream {name}: {desc}")
+    y = gpu_fused(x, w, b, 1, 1, p)
+    ref = oracle.conv3d_min_softmax(x, w, b, 1, 1, p)
+    err = float(np.abs(y - ref).max())
+    say(f"  max|err| = {err:.3e}")
+    assert err <= FUSED_ATOL
+
+
+def test_fused_generic_kernel_on_workload_slice(monkeypatch):
+    """With the specialisations off, the workload geometry runs on the generic
+    fused kernel and agrees with the oracle too."""
+    monkeypatch.setenv("CONVHIP_TAP", "0")
+    cfg = synth.WORKLOADS["conv3d_min_softmax"]
+    desc = ch.plan_describe(cfg["x"], cfg["w"], fused=True)
+    assert "kernel=fused_min_softmax_mfma4" in desc, desc
+    x, w, b = synth.make_inputs("conv3d_min_softmax", n_samples=3)
+    y = gpu_fused(x, w, b)
+    ref = oracle.conv3d_min_softmax(x, w, b)
+    assert float(np.abs(y - ref).max()) <= FUSED_ATOL
+
+
 def test_fused_integer_inputs_exact_minimum():
     """Integer inputs make every conv value exact, so the minimum is exact and only
     exp/division rounding remains."""
@@ -325,6 +363,9 @@ def test_tap_disabled_falls_back_to_streamed(monkeypatch):
 
 
 def test_workloads_use_expected_kernels():
+    cfg = synth.WORKLOADS["conv3d_min_softmax"]
+    d = ch.plan_describe(cfg["x"], cfg["w"], fused=True)
+    assert "kernel=fused_stream" in d, d
     for name, kernel in [("asym_conv3d", "conv_tap"), ("long_conv1d", "conv_tap"),
                          ("general_conv3d", "conv_tap_split"), ("tiny_conv3d", "conv_tap_split")]:
         cfg = synth.WORKLOADS[name]
