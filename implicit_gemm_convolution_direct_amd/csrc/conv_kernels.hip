@@ -1030,21 +1030,20 @@ __global__ __launch_bounds__(256) void fused_min_softmax_mfma4_kernel(FusedArgs 
 // ---------------------------------------------------------------------------
 // fused_stream: Conv3d -> min over depth -> softmax over channels for a fixed
 // small geometry (stride 1, dilation 1, groups 1, kD = 3), streaming the input
-// depth planes once.
-// - One wave owns 64 consecutive output positions (h, w) of one sample and every
-//   output depth; the waves of a workgroup are independent (no barriers).
-// - Input plane z feeds output depths z, z-1, z-2 (depth taps 0, 1, 2): each
-//   staged value is read from LDS once and multiplied into three rolling sets of
-//   accumulators; the set of depth z-2 is complete after plane z and is folded
-//   into the running minimum.
-// - Planes are copied into a ring of three LDS slots two planes ahead.
+// depth planes through LDS.
+// - One wave owns 64 consecutive output positions (h, w) of one sample and a
+//   contiguous range of output depths (the depth range is split over DSPLIT
+//   waves); the waves of a workgroup are independent (no barriers).
+// - Output depth od reads input planes od, od+1, od+2; planes sit in a ring of
+//   four LDS slots and the plane three ahead is copied while od is reduced.
 // - Matrix core: 4x4x1 MFMA with 16 blocks, the weight operand broadcast from
 //   one block (cbsz 4, abid b): lane l accumulates channels 4g..4g+3 of position
 //   l, so C_out is covered in steps of 4 channels with no padding, and every
 //   weight (channel group, reduction index) pair sits in one of 16 lane quads of
 //   a resident register.
 // - The depth minimum, bias, and the softmax over all channels stay inside the
-//   lane: nothing of the conv result leaves the registers.
+//   lane: nothing of the conv result leaves the registers. With DSPLIT > 1 the
+//   partial minima of the depth ranges meet in LDS first.
 // ---------------------------------------------------------------------------
 template <int N, class F, int... I>
 __device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
@@ -1062,16 +1061,20 @@ struct StreamGeo {
   static constexpr int BW = O2 + KW_ - 1;       // input columns per staged row
   static constexpr int CH = ROWS * BW;           // floats per channel of a plane
   static constexpr int PLANE = CIN * CH;         // floats of one staged plane
-  static constexpr int PI = (PLANE + 63) / 64;   // 64-lane copies per plane
-  static constexpr int SLOT = PI * 64;           // slot floats (every copy lane lands inside)
-  static constexpr int NSLOT = 3;
+  static_assert(BW % 4 == 0, "rows are copied in 16-byte chunks");
+  static constexpr int CHUNKS = PLANE / 4;       // 16-byte chunks per plane
+  static constexpr int PI = (CHUNKS + 63) / 64;  // 64-lane copies per plane (the last one partial)
+  static constexpr int SLOT = PLANE;
+  static constexpr int NSLOT = 4;
   static constexpr int KHW = KH * KW_;
   static constexpr int KVOL = KD * KHW;
   static constexpr int KRED = CIN * KVOL;
   static constexpr int NT = CIN * KHW;           // staged values read per plane
   static constexpr int NPAIR = NG * KRED;        // (channel group, reduction index) pairs
   static constexpr int NAREG = (NPAIR + 15) / 16;
-  static_assert(2 * PI < 64, "vmcnt range");
+  static constexpr int WAVES = 4;                // waves per workgroup
+  static constexpr int LDS_FLOATS = WAVES * NSLOT * SLOT;
+  static_assert(PI < 64, "vmcnt range");
 };
 
 struct StreamArgs {
@@ -1085,19 +1088,27 @@ struct StreamArgs {
   int O0, O1;
   int plane_out;
   int tiles_per_plane;
-  int units;  // N * tiles_per_plane
+  int dsplit;      // waves per (sample, tile): the depth range is split over them
+  int ods;         // output depths per wave (the last range may be shorter)
+  int units;       // N * tiles_per_plane * dsplit
 };
 
 template <class G>
-__global__ __launch_bounds__(256, 2) void fused_stream_kernel(StreamArgs a) {
+__global__ __launch_bounds__(256, 4) void fused_stream_kernel(StreamArgs a) {
   constexpr int NG = G::NG_;
-  __shared__ __align__(16) float smem[4 * G::NSLOT * G::SLOT];
+  __shared__ __align__(16) float smem[G::LDS_FLOATS];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int unit = blockIdx.x * 4 + wave;
-  if (unit >= a.units) return;  // wave-uniform; the waves share no barrier
-  const int n = unit / a.tiles_per_plane;
-  const int p0 = (unit - n * a.tiles_per_plane) * 64;
+  // Waves of one (sample, tile) are consecutive units, so they share a workgroup
+  // when dsplit divides the workgroup's wave count.
+  const int unit = blockIdx.x * G::WAVES + wave;
+  const bool live = unit < a.units;
+  const int tu = unit / a.dsplit;
+  const int part = unit - tu * a.dsplit;
+  const int n = tu / a.tiles_per_plane;
+  const int p0 = (tu - n * a.tiles_per_plane) * 64;
+  const int od0 = part * a.ods;
+  const int od1 = live ? min(a.O0, od0 + a.ods) : od0;
   float* ring = smem + wave * (G::NSLOT * G::SLOT);
 
   // Weights: register r, lane 4b + i holds w[4g + i][k] for pair 16r + b = g * KRED + k.
@@ -1107,11 +1118,12 @@ __global__ __launch_bounds__(256, 2) void fused_stream_kernel(StreamArgs a) {
     const int pair = 16 * r + (lane >> 2);
     const int gq = pair / G::KRED, k = pair - gq * G::KRED;
     const int co = 4 * gq + (lane & 3);
-    aw[r] = (pair < G::NPAIR && co < a.Cout) ? a.w[co * G::KRED + k] : 0.0f;
+    aw[r] = (live && pair < G::NPAIR && co < a.Cout) ? a.w[co * G::KRED + k] : 0.0f;
   }
 
-  // Copy sources: copy i, lane l moves slot element e = 64i + l = (c, row, col)
-  // from input (c, ih0 + row, col - P2) of the plane being staged.
+  // Copy sources: copy i, lane l moves 16-byte chunk e = 64i + l = (c, row, q) of
+  // the slot from input (c, ih0 + row, 4q .. 4q+3) of the plane being staged
+  // (input rows are exactly BW wide: no padding along W).
   const int oh_first = p0 / G::O2_;
   const int ih0 = oh_first - a.P1;
   const int64_t chan_stride = int64_t(a.L0) * a.L1 * a.L2;
@@ -1121,87 +1133,118 @@ __global__ __launch_bounds__(256, 2) void fused_stream_kernel(StreamArgs a) {
 #pragma unroll
   for (int i = 0; i < G::PI; i++) {
     const int e = 64 * i + lane;
-    const int c = e / G::CH, rem = e - (e / G::CH) * G::CH;
-    const int r = rem / G::BW, col = rem - (rem / G::BW) * G::BW;
-    const int ih = ih0 + r, iw = col - a.P2;
-    const bool ok = (e < G::PLANE) && unsigned(ih) < unsigned(a.L1) && unsigned(iw) < unsigned(a.L2);
-    soff[i] = ok ? int(c * chan_stride) + ih * a.L2 + iw : 0;
+    const int c = e / (G::CH / 4), rem = e - c * (G::CH / 4);
+    const int r = rem / (G::BW / 4), q = rem - r * (G::BW / 4);
+    const int ih = ih0 + r;
+    const bool ok = unsigned(ih) < unsigned(a.L1);
+    soff[i] = ok ? int(c * chan_stride) + ih * G::BW + 4 * q : 0;
     sok |= uint32_t(ok) << i;
   }
-  const int plane_elems = a.L1 * a.L2;
-  const int Z = a.O0 + G::KD - 1;  // staged planes: input depths -P0 .. O0 + 1 - P0
-  auto stage = [&](int z, int slot) {
+  const int plane_elems = a.L1 * G::BW;
+  // Plane z (input depth z - P0) -> slot z % 4. Planes past od1 + 1 are copied
+  // as zeros so every wave issues the same number of copies per step; lanes
+  // past the plane's last chunk copy nothing.
+  auto stage = [&](int z) {
     const int id = z - a.P0;
-    const bool pok = (z < Z) && unsigned(id) < unsigned(a.L0);
+    const bool pok = live && (z < od1 + G::KD - 1) && unsigned(id) < unsigned(a.L0);
     const float* xp = xn + int64_t(pok ? id : 0) * plane_elems;
+    float* dst = ring + (z & 3) * G::SLOT;
 #pragma unroll
     for (int i = 0; i < G::PI; i++) {
       const bool ok = pok && ((sok >> i) & 1);
-      lds_dma_f32(ok ? xp + soff[i] : kZeroWord, ring + slot * G::SLOT + 64 * i);
+      if (64 * i + lane < G::CHUNKS) lds_dma_f32x4(ok ? xp + soff[i] : kZeroWord, dst + 256 * i);
     }
   };
 
-  // This lane's output position and its offset inside a slot.
+  // This lane's output position and its byte offset inside a slot.
   const int p = p0 + lane;
-  const bool valid = p < a.plane_out;
+  const bool valid = live && p < a.plane_out;
   const int oh = p / G::O2_, ow = p - (p / G::O2_) * G::O2_;
   const int lbase = valid ? (oh - oh_first) * G::BW + ow : 0;
-  const char* bbase = reinterpret_cast<const char*>(ring) + 4 * lbase;
+  const char* bbase = reinterpret_cast<const char*>(ring + lbase);
 
-  v4f acc[3][NG];
   v4f mn[NG];
 #pragma unroll
   for (int q = 0; q < NG; q++) mn[q] = v4f{INFINITY, INFINITY, INFINITY, INFINITY};
 
-  stage(0, 0);
-  stage(1, 1);
-  for (int z0 = 0; z0 < Z; z0 += 3) {
-    static_for<3>([&](auto JJ) {
-      constexpr int J = decltype(JJ)::value;
-      const int z = z0 + J;
-      if (z < Z) {
-        // Plane z + 2 goes into the slot plane z - 1 used, once those reads
-        // have returned.
-        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-        asm volatile("" ::: "memory");
-        stage(z + 2, (J + 2) % 3);
-        wait_vmem_le<2 * G::PI>();
-        asm volatile("" ::: "memory");
-        float bv[G::NT];
-        static_for<G::NT>([&](auto TT) {
-          constexpr int t = decltype(TT)::value;
-          constexpr int c = t / G::KHW, kh = (t % G::KHW) / G::KW, kw = t % G::KW;
-          bv[t] = *reinterpret_cast<const float*>(bbase + 4 * (J * G::SLOT + c * G::CH + kh * G::BW + kw));
-        });
-        static_for<3>([&](auto KK) {
-          constexpr int kd = decltype(KK)::value;
-          constexpr int set = (J - kd + 3) % 3;
-          const int od = z - kd;
-          if (od >= 0 && od < a.O0) {
-            static_for<G::NT>([&](auto TT) {
-              constexpr int t = decltype(TT)::value;
-              constexpr int c = t / G::KHW, hw = t % G::KHW;
-              constexpr int k = c * G::KVOL + kd * G::KHW + hw;
-              static_for<NG>([&](auto QQ) {
-                constexpr int q = decltype(QQ)::value;
-                constexpr int pair = q * G::KRED + k;
-                constexpr int r = pair / 16, ab = pair % 16;
-                if constexpr (kd == 0 && t == 0)
-                  acc[set][q] = __builtin_amdgcn_mfma_f32_4x4x1f32(aw[r], bv[t], v4f{0.f, 0.f, 0.f, 0.f}, 4, ab, 0);
-                else
-                  acc[set][q] = __builtin_amdgcn_mfma_f32_4x4x1f32(aw[r], bv[t], acc[set][q], 4, ab, 0);
-              });
-            });
-            if constexpr (kd == 2) {
+  stage(od0);
+  stage(od0 + 1);
+  stage(od0 + 2);
+  wait_vmem_le<3 * G::PI>();  // the weights (loaded before the copies)
+  for (int od = od0; od < od1; od++) {
+    // Plane od + 3 goes into the slot plane od - 1 used, once those reads have
+    // returned; then planes od .. od + 2 are complete.
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    stage(od + 3);
+    wait_vmem_le<G::PI>();
+    asm volatile("" ::: "memory");
+    // Reduction in groups of one (depth tap, channel): the KH*KW staged values
+    // of group g+1 are read while the matrix core works through group g.
+    constexpr int NGRP = G::KD * G::CIN_;
+    const char* bps[G::KD];
 #pragma unroll
-              for (int q = 0; q < NG; q++)
-#pragma unroll
-                for (int i = 0; i < 4; i++) mn[q][i] = fminf(mn[q][i], acc[set][q][i]);
-            }
-          }
+    for (int kd = 0; kd < G::KD; kd++) bps[kd] = bbase + ((od + kd) & 3) * (4 * G::SLOT);
+    float bv[2][G::KHW];
+    auto load_group = [&](auto GG, float* dst) {
+      constexpr int g = decltype(GG)::value;
+      constexpr int kd = g / G::CIN_, c = g % G::CIN_;
+      static_for<G::KHW>([&](auto HH) {
+        constexpr int hw = decltype(HH)::value;
+        constexpr int kh = hw / G::KW, kw = hw % G::KW;
+        dst[hw] = *reinterpret_cast<const float*>(bps[kd] + 4 * (c * G::CH + kh * G::BW + kw));
+      });
+    };
+    load_group(std::integral_constant<int, 0>{}, bv[0]);
+    v4f acc[NG];
+    static_for<NGRP>([&](auto GG) {
+      constexpr int g = decltype(GG)::value;
+      constexpr int kd = g / G::CIN_, c = g % G::CIN_;
+      constexpr int cur = g & 1;
+      // Issue the next group's reads, then this group's products (the barriers
+      // keep the scheduler from sinking the reads next to their uses).
+      if constexpr (g + 1 < NGRP) load_group(std::integral_constant<int, g + 1>{}, bv[cur ^ 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      static_for<G::KHW>([&](auto HH) {
+        constexpr int hw = decltype(HH)::value;
+        constexpr int k = c * G::KVOL + kd * G::KHW + hw;
+        static_for<NG>([&](auto QQ) {
+          constexpr int q = decltype(QQ)::value;
+          constexpr int pair = q * G::KRED + k;
+          constexpr int r = pair / 16, ab = pair % 16;
+          if constexpr (g == 0 && hw == 0)
+            acc[q] = __builtin_amdgcn_mfma_f32_4x4x1f32(aw[r], bv[cur][hw], v4f{0.f, 0.f, 0.f, 0.f}, 4, ab, 0);
+          else
+            acc[q] = __builtin_amdgcn_mfma_f32_4x4x1f32(aw[r], bv[cur][hw], acc[q], 4, ab, 0);
         });
-      }
+      });
+      __builtin_amdgcn_sched_barrier(0);
     });
+#pragma unroll
+    for (int q = 0; q < NG; q++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) mn[q][i] = fminf(mn[q][i], acc[q][i]);
+  }
+
+  float* yp = a.y + int64_t(n) * a.Cout * a.plane_out + p;
+  if (a.dsplit > 1) {
+    // The parts of one (sample, tile) are consecutive waves of this workgroup:
+    // part 0 takes the minimum over the others' partial minima. The ring is
+    // reused once every wave's last (zero) copies have landed.
+    wait_vmem_le<0>();
+    __syncthreads();
+    float* red = smem;
+#pragma unroll
+    for (int q = 0; q < NG; q++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) red[((wave * NG + q) * 4 + i) * 64 + lane] = mn[q][i];
+    __syncthreads();
+    if (part != 0) return;
+    for (int o = 1; o < a.dsplit; o++)
+#pragma unroll
+      for (int q = 0; q < NG; q++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) mn[q][i] = fminf(mn[q][i], red[(((wave + o) * NG + q) * 4 + i) * 64 + lane]);
   }
 
   // Softmax over the channels of this lane's position. fp32 addition is
@@ -1225,7 +1268,6 @@ __global__ __launch_bounds__(256, 2) void fused_stream_kernel(StreamArgs a) {
       sum += e;
     }
     const float inv = 1.0f / sum;
-    float* yp = a.y + int64_t(n) * a.Cout * a.plane_out + p;
 #pragma unroll
     for (int c = 0; c < 4 * NG; c++)
       if (c < a.Cout) yp[int64_t(c) * a.plane_out] = m[c] * inv;
@@ -1346,8 +1388,8 @@ static int launch_fused_ng(const FusedArgs& args, const FusedPlan& p, hipStream_
 template <int CIN, int KH, int KW, int NG, int O2, int ROWS>
 static int launch_stream(const StreamArgs& args, const FusedPlan& p, hipStream_t stream) {
   using G = StreamGeo<CIN, KH, KW, NG, O2, ROWS>;
-  if (int64_t(4) * 4 * G::NSLOT * G::SLOT != p.lds_bytes) return CONV_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL(fused_stream_kernel<G>, dim3(unsigned(p.grid[0])), dim3(256), 0, stream, args);
+  if (int64_t(4) * G::LDS_FLOATS != p.lds_bytes || G::WAVES % p.dsplit != 0) return CONV_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL(fused_stream_kernel<G>, dim3(unsigned(p.grid[0])), dim3(64 * G::WAVES), 0, stream, args);
   return hipGetLastError() == hipSuccess ? CONV_OK : CONV_ERR_HIP;
 }
 
@@ -1480,7 +1522,10 @@ int conv_fwd(int nd, const float* x, const int64_t* x_shape, const float* w, con
   if (rc != CONV_OK) return rc;
   if (!x || !w || !y) return CONV_ERR_NULL;
   ConvPlan p;
-  rc = plan_conv(g, &p, forced_conv_cfg(), device_num_cu(), use_tap());
+  // The specialised kernels copy weights in 16-byte chunks: they need a 16-byte
+  // aligned weight pointer (any tensor allocation is; a sliced view may not be).
+  const bool aligned = (reinterpret_cast<uintptr_t>(w) & 15) == 0;
+  rc = plan_conv(g, &p, forced_conv_cfg(), device_num_cu(), aligned ? use_tap() : 0);
   if (rc != CONV_OK) return rc;
   ConvArgs a = conv_args(g, p, x, w, bias, y);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -1506,7 +1551,9 @@ int conv3d_min_softmax(const float* x, const int64_t* x_shape, const float* w, c
   if (!x || !w || !y) return CONV_ERR_NULL;
   if (min_dim < 2 || min_dim > 4) return CONV_ERR_PARAM;
   FusedPlan p;
-  rc = plan_fused(g, min_dim, &p, use_tap() != 0);
+  // The depth-streamed kernel copies input rows in 16-byte chunks.
+  const bool aligned = (reinterpret_cast<uintptr_t>(x) & 15) == 0;
+  rc = plan_fused(g, min_dim, &p, use_tap() != 0 && aligned);
   if (rc != CONV_OK) return rc;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (p.spec >= 0) {
@@ -1518,6 +1565,8 @@ int conv3d_min_softmax(const float* x, const int64_t* x_shape, const float* w, c
     sa.O0 = int(g.O[0]); sa.O1 = int(g.O[1]);
     sa.plane_out = int(g.plane_out());
     sa.tiles_per_plane = int(p.tiles_per_plane);
+    sa.dsplit = p.dsplit;
+    sa.ods = int((g.O[0] + p.dsplit - 1) / p.dsplit);
     sa.units = int(p.units);
     return launch_stream_spec(sa, p, s);
   }

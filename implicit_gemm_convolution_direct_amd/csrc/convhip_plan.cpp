@@ -315,6 +315,8 @@ static bool plan_fused_stream(const Geom& g, const FusedSpecDesc& d, FusedPlan* 
   for (int i = 0; i < 3; i++)
     if (g.S[i] != 1 || g.Dl[i] != 1) return false;
   if ((g.Cout + 3) / 4 != d.NG || g.O[2] != d.O2) return false;
+  // Input rows are copied whole in 16-byte chunks: no padding along W.
+  if (g.P[2] != 0 || g.L[2] != d.O2 + d.KW - 1 || g.L[2] % 4 != 0) return false;
   const int64_t plane_out = g.plane_out();
   const int64_t tiles = (plane_out + 63) / 64;
   for (int64_t t = 0; t < tiles; t++) {
@@ -322,10 +324,14 @@ static bool plan_fused_stream(const Geom& g, const FusedSpecDesc& d, FusedPlan* 
     if (p1 / g.O[2] - p0 / g.O[2] + d.KH > d.ROWS) return false;
   }
   if (g.Cin * g.L[0] * g.L[1] * g.L[2] > std::numeric_limits<int32_t>::max()) return false;
-  const int64_t units = g.N * tiles;
-  if ((units + 3) / 4 > std::numeric_limits<int32_t>::max()) return false;
+  // Two waves split the output depths of each tile: twice the waves in flight,
+  // at the cost of staging two extra input planes per tile.
+  const int dsplit = g.O[0] >= 2 ? 2 : 1;
+  const int64_t units = g.N * tiles * dsplit;
+  if (units > std::numeric_limits<int32_t>::max() - 4) return false;
   FusedPlan q;
   q.spec = d.id;
+  q.dsplit = dsplit;
   q.units = units;
   q.ng = d.NG;
   q.cpad = 4 * d.NG;
@@ -335,9 +341,9 @@ static bool plan_fused_stream(const Geom& g, const FusedSpecDesc& d, FusedPlan* 
   q.bw = d.O2 + d.KW - 1;
   q.kfull = int(g.Cin * g.kvol());
   q.tiles_per_plane = tiles;
-  const int64_t slot = (int64_t(d.CIN) * d.ROWS * q.bw + 63) / 64 * 64;
+  const int64_t slot = int64_t(d.CIN) * d.ROWS * q.bw;
   q.boxc = int(slot);
-  q.lds_bytes = 4 * 4 * 3 * slot;
+  q.lds_bytes = 4 * 4 * 4 * slot;  // 4 waves x 4 ring slots
   q.grid[0] = (units + 3) / 4;
   q.grid[1] = 1;
   q.grid[2] = 1;
@@ -404,9 +410,9 @@ std::string describe(const Geom& g, const FusedPlan& p) {
   char buf[512];
   if (p.spec >= 0) {
     std::snprintf(buf, sizeof buf,
-                  "kernel=fused_stream spec=%d ng=%d cpad=%d planes=%d rows=%d bw=%d tiles=%lld units=%lld "
+                  "kernel=fused_stream spec=%d ng=%d cpad=%d planes=%d rows=%d bw=%d tiles=%lld dsplit=%d units=%lld "
                   "grid=%lldx%lldx%lld lds=%lld macs=%lld",
-                  p.spec, p.ng, p.cpad, p.dspan, p.rows, p.bw, (long long)p.tiles_per_plane, (long long)p.units,
+                  p.spec, p.ng, p.cpad, p.dspan, p.rows, p.bw, (long long)p.tiles_per_plane, p.dsplit, (long long)p.units,
                   (long long)p.grid[0], (long long)p.grid[1], (long long)p.grid[2], (long long)p.lds_bytes,
                   (long long)g.macs());
     return buf;

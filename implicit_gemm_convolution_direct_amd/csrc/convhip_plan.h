@@ -132,7 +132,8 @@ const FusedSpecDesc* fused_specs(int* count);
 // Plan of the fused conv -> min over depth -> softmax over channels kernel.
 struct FusedPlan {
   int spec = -1;       // >= 0: depth-streamed specialisation (one wave per 64 positions)
-  int64_t units = 0;   // streamed: N * tiles_per_plane waves
+  int dsplit = 1;      // streamed: waves sharing the output depths of one 64-position tile
+  int64_t units = 0;   // streamed: N * tiles_per_plane * dsplit waves
   int ng = 0;          // channel groups of 4 handled by one lane
   int cpad = 0;        // C_out rounded up to 4
   int mode = TILE_FLAT;

@@ -207,6 +207,8 @@ FUSED_CASES = [
     ("cout_64", (1, 2, 6, 10, 12), (64, 2, 3, 3, 3), 1, 1, 1),
     ("depth_out_1", (2, 3, 3, 12, 13), (24, 3, 3, 3, 3), 1, 1, 0),
     ("depth_out_2", (1, 3, 4, 12, 13), (24, 3, 3, 3, 3), 1, 1, 0),
+    # the streamed kernel's channel/kernel geometry with padding along W: generic kernel
+    ("stream_geometry_w_padded", (1, 3, 4, 9, 30), (22, 3, 3, 3, 3), 1, 1, (1, 2, 1)),
 ]
 
 
@@ -227,7 +229,7 @@ STREAM_CASES = [
     # depth-streamed kernel geometry: C_in 3, kernel 3x3x3, stride 1, W_out 30
     ("full_planes", (2, 3, 6, 32, 32), (24, 3, 3, 3, 3), 0, True),
     ("short_plane", (1, 3, 5, 10, 32), (24, 3, 3, 3, 3), 0, True),
-    ("padded_cout22", (1, 3, 4, 9, 30), (22, 3, 3, 3, 3), (1, 2, 1), False),
+    ("padded_cout22", (1, 3, 4, 9, 32), (22, 3, 3, 3, 3), (1, 2, 0), False),
     ("cout21_depth1", (2, 3, 3, 7, 32), (21, 3, 3, 3, 3), (0, 1, 0), True),
     ("ragged_units", (3, 3, 8, 21, 32), (24, 3, 3, 3, 3), 0, True),
 ]
@@ -246,6 +248,26 @@ def test_fused_stream_cases(case):
     err = float(np.abs(y - ref).max())
     say(f"  max|err| = {err:.3e}")
     assert err <= FUSED_ATOL
+
+
+def test_misaligned_pointers_take_generic_kernels():
+    """Views that start 4 bytes past an allocation keep the specialised kernels
+    (16-byte copies) out and still give the oracle's results."""
+    cfg = synth.WORKLOADS["conv3d_min_softmax"]
+    x, w, b = synth.make_inputs("conv3d_min_softmax", n_samples=2)
+    xd = torch.empty(x.size + 1, dtype=torch.float32, device=dev())[1:].view(x.shape)
+    xd.copy_(torch.from_numpy(x))
+    assert xd.data_ptr() % 16 != 0
+    y = ch.conv3d_min_softmax(xd, to_dev(w), to_dev(b), 1, 1, 0, 1, min_dim=2).cpu().numpy()
+    assert float(np.abs(y - oracle.conv3d_min_softmax(x, w, b)).max()) <= FUSED_ATOL
+    name = "general_conv3d"
+    cfg = synth.WORKLOADS[name]
+    x, w, b = synth.make_inputs(name, n_samples=1)
+    wd = torch.empty(w.size + 1, dtype=torch.float32, device=dev())[1:].view(w.shape)
+    wd.copy_(torch.from_numpy(w))
+    assert wd.data_ptr() % 16 != 0
+    y = ch.conv_fwd(to_dev(x), wd, to_dev(b), *_cfg_args(cfg)).cpu().numpy()
+    assert_conv_close(y, oracle.conv(x, w, b, *_cfg_args(cfg)), w.shape, "misaligned w")
 
 
 def test_fused_generic_kernel_on_workload_slice(monkeypatch):
