@@ -169,9 +169,10 @@ def cpu_baseline(name):
     _, macs, _, _, _ = geometry(cfg)
     args = (cfg["stride"], cfg["dilation"], cfg["padding"], cfg["groups"])
     oracle.conv(x[:1], w, b, *args)  # load the library, warm the threads
+    # Repeat the whole-workload pass for about 10 s of CPU work.
     reps, t = 0, 0.0
     t0 = time.perf_counter()
-    while reps < 1 or (time.perf_counter() - t0 < 10.0 and reps < 8):
+    while reps < 1 or time.perf_counter() - t0 < 10.0:
         ref = oracle.conv(x, w, b, *args)
         reps += 1
     t = (time.perf_counter() - t0) / reps
@@ -188,6 +189,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--only", choices=ORDER, default=None, help="time one workload only (for profiling)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many bytes per step "
+                         "(calibrates rocprofv3's FETCH_SIZE / WRITE_SIZE against a known traffic)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -203,6 +207,16 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     ch.lib()
+
+    if args.copy_bytes:
+        n = args.copy_bytes // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup + args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": 4 * n, "steps": args.warmup + args.steps}), flush=True)
+        return
 
     names = [args.only] if args.only else ORDER
     shapes = {}

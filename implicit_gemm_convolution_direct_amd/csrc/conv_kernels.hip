@@ -1100,8 +1100,12 @@ __global__ __launch_bounds__(256, 4) void fused_stream_kernel(StreamArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // Waves of one (sample, tile) are consecutive units, so they share a workgroup
-  // when dsplit divides the workgroup's wave count.
-  const int unit = blockIdx.x * G::WAVES + wave;
+  // when dsplit divides the workgroup's wave count. Workgroups are dispatched
+  // round-robin over the 8 XCDs: give each XCD a contiguous run of workgroups so
+  // the input rows that neighbouring tiles share are fetched into one L2.
+  int blk = blockIdx.x;
+  if ((gridDim.x & 7) == 0) blk = (blk & 7) * (gridDim.x >> 3) + (blk >> 3);
+  const int unit = blk * G::WAVES + wave;
   const bool live = unit < a.units;
   const int tu = unit / a.dsplit;
   const int part = unit - tu * a.dsplit;
