@@ -1,20 +1,25 @@
 // fp32 convolution kernels for gfx950 (MI355X) and the C-ABI entry points.
 //
-// conv_mfma16: implicit-GEMM direct convolution. Per workgroup, an output tile
-//   of BM channels x BN positions is a GEMM  Y[m][n] = sum_k W[m][k] * Xhat[k][n]
-//   with k = (input channel, kernel tap). Xhat is never formed: the input halo
-//   box of a chunk of input channels is staged in LDS once, and each matrix-core
-//   operand is gathered from it through a per-k offset table (koff) plus a
-//   per-position offset (noff), so one LDS copy of every input element serves
-//   all taps and all BM output channels. The contraction runs on
-//   v_mfma_f32_16x16x4_f32 (fp32 in, fp32 accumulate).
+// Every conv kernel here is an implicit GEMM  Y[m][n] = sum_k W[m][k] * Xhat[k][n]
+// with m = output channel, n = output position and k = (input channel, kernel
+// tap). Xhat is never formed: the input halo box is copied into LDS once (by the
+// LDS DMA path, global_load_lds) and each matrix-core B operand is read from it
+// at (position offset + tap offset), so one LDS copy of every input element
+// serves all taps and all output channels. Products run on the fp32 matrix
+// cores (fp32 in, fp32 accumulate).
 //
-// fused_min_softmax_mfma4: Conv3d -> min over depth -> softmax over channels.
-//   One lane owns one output column (n, oh, ow) and all its channels, using the
-//   4x4x1 matrix-core form with the weight operand broadcast from one 4-lane
-//   block (cbsz=4): each instruction updates 4 channels x 64 columns. The
-//   running minimum over output depth and the softmax over channels both stay
-//   in the lane's registers; only the final [N, C_out, H_out, W_out] is stored.
+// conv_mfma16       any geometry: tile of BM channels x BN positions per
+//                   workgroup, chunks of input channels double-buffered, tap
+//                   offsets from an LDS table; v_mfma_f32_16x16x4_f32.
+// conv_tap          build-time specialised geometries (every tap offset an
+//                   immediate), persistent grid, weights resident in LDS.
+// conv_tap_split    build-time specialised, few output channels per group: one
+//                   wave per input channel of the group, partial tiles summed in
+//                   LDS; the whole (n, od) output plane per workgroup.
+// fused_stream      Conv3d -> min over depth -> softmax over channels for a
+//                   build-time geometry: depth planes streamed through a 4-slot
+//                   LDS ring, 4x4x1 MFMA with the weight operand broadcast.
+// fused_min_softmax_mfma4  the same fused op for any geometry (min over depth).
 //
 // Problem statements: POPCORNBENCH "Kimi-K2.6" pages l1_p60 (Conv3d), l1_p76
 // (Conv1d), l2_p24 (Conv3d + min + softmax), opening turns.
