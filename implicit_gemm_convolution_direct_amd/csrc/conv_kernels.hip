@@ -39,6 +39,17 @@ namespace convhip {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 
+// f(integral_constant<int, 0>) ... f(integral_constant<int, N-1>): loops whose
+// index must be a compile-time constant (immediate offsets, register indices).
+template <int N, class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl<N>(f, std::make_integer_sequence<int, N>{});
+}
+
 struct ConvArgs {
   const float* __restrict__ x;
   const float* __restrict__ w;
@@ -684,6 +695,13 @@ struct SplitGeo {
   static_assert((KDT - 1) * PLANE_INSTR < 64, "vmcnt range");
   // Highest depth tap read by k-step s (its 4 reduction indices).
   static constexpr int td_of(int s) { return (4 * s + 3 < K ? 4 * s + 3 : K - 1) / KPP; }
+  // First k-step that reads depth tap 1.
+  static constexpr int first_td1() {
+    for (int s = 0; s < NS; s++)
+      if (td_of(s) >= 1) return s;
+    return NS;
+  }
+  static constexpr int FIRST_TD1 = first_td1();
   // LDS offset (floats) of reduction index k = (td, th, tw) of the box; padding
   // indices (zero weights) point at the box start.
   static constexpr int koff(int k) {
@@ -741,25 +759,31 @@ __global__ __launch_bounds__(64 * NW) void conv_tap_split_kernel(ConvArgs a) {
         else lds_dma_f32(ok ? wg + j : kZeroWord, wsh + j0);
       }
     }
-    // Box: element e = ((td * ROWS) + zr) * BW + j <- input
-    // (od*S0 - P0 + td*DD, zr - P1, F*j - P2) of channel g*Cg + c.
-    const float* xc = a.x + (int64_t(n) * a.Cin + int64_t(g) * a.Cg + c) * (int64_t(a.L0) * a.L1 * a.L2);
-#pragma unroll
-    for (int td = 0; td < G::KDT; td++) {
-      const int id = od * a.S0 - a.P0 + td * a.D0;
-      const bool pok = unsigned(id) < unsigned(a.L0);
-#pragma unroll
-      for (int i = 0; i < G::PLANE_INSTR; i++) {
-        const int e = i * 64 + lane;  // element of this plane
-        if (e < G::PLANE) {
-          const int zr = e / G::BWC, j = e - zr * G::BWC;
-          const int ih = zr - a.P1, iw = G::FF * j - a.P2;
-          const bool ok = pok && (unsigned(ih) < unsigned(a.L1)) && (unsigned(iw) < unsigned(a.L2));
-          lds_dma_f32(ok ? xc + ((int64_t(id) * a.L1 + ih) * a.L2 + iw) : kZeroWord, box + td * G::PLANE + i * 64);
-        }
-      }
-    }
   }
+  // Box: element e = ((td * ROWS) + zr) * BW + j <- input
+  // (od*S0 - P0 + td*DD, zr - P1, F*j - P2) of channel g*Cg + c. Copy i of a
+  // plane moves elements 64i .. 64i + 63; the in-plane part of each lane's
+  // source is the same for every plane.
+  const float* xc = a.x + (int64_t(n) * a.Cin + int64_t(g) * a.Cg + c) * (int64_t(a.L0) * a.L1 * a.L2);
+  int soff[G::PLANE_INSTR];
+  uint32_t sok = 0;
+#pragma unroll
+  for (int i = 0; i < G::PLANE_INSTR; i++) {
+    const int e = i * 64 + lane;
+    const int zr = e / G::BWC, j = e - zr * G::BWC;
+    const int ih = zr - a.P1, iw = G::FF * j - a.P2;
+    const bool ok = e < G::PLANE && unsigned(ih) < unsigned(a.L1) && unsigned(iw) < unsigned(a.L2);
+    soff[i] = ok ? ih * a.L2 + iw : 0;
+    sok |= uint32_t(ok) << i;
+  }
+  auto stage_copy = [&](int td, int i) {
+    const int id = od * a.S0 - a.P0 + td * a.D0;
+    const bool ok = unsigned(id) < unsigned(a.L0) && ((sok >> i) & 1);
+    if (i * 64 + lane < G::PLANE)
+      lds_dma_f32(ok ? xc + (int64_t(id) * a.L1 * a.L2 + soff[i]) : kZeroWord, box + td * G::PLANE + i * 64);
+  };
+#pragma unroll
+  for (int i = 0; i < G::PLANE_INSTR; i++) stage_copy(0, i);
   // Output positions of the plane (whole plane, flattened (oh, ow)).
   int noff[NT], pidx[NT];
 #pragma unroll
@@ -784,8 +808,9 @@ __global__ __launch_bounds__(64 * NW) void conv_tap_split_kernel(ConvArgs a) {
 #pragma unroll
   for (int ni = 0; ni < NT; ni++) acc[ni] = v4f{0.f, 0.f, 0.f, 0.f};
   // Weights (copied by every wave) and this wave's first plane have landed. A
-  // plain barrier: a workgroup-scope fence would also wait for the later planes.
-  wait_vmem_le<(G::KDT - 1) * G::PLANE_INSTR>();
+  // plain barrier: the later planes are copied during the reduction and each
+  // wave waits for its own copies of them.
+  wait_vmem_le<0>();
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
@@ -802,9 +827,15 @@ __global__ __launch_bounds__(64 * NW) void conv_tap_split_kernel(ConvArgs a) {
 #pragma unroll
     for (int ni = 0; ni < NT; ni++)
       bv[0][ni] = *reinterpret_cast<const float*>(bb + nb[ni] + dp[P.pid[0]] + 4 * G::koff(0));
+    // Copies of planes 1 .. KDT-1 (in order), DPS per step, all issued before
+    // the first step that reads plane 1.
+    constexpr int TCOPY = (G::KDT - 1) * G::PLANE_INSTR;
+    constexpr int DPS = G::FIRST_TD1 > 0 ? (TCOPY + G::FIRST_TD1 - 1) / G::FIRST_TD1 : TCOPY;
 #pragma unroll
     for (int s = 0; s < G::NS; s++) {
       const int cu = s & 1, nx = cu ^ 1;
+#pragma unroll
+      for (int q = DPS * s; q < DPS * (s + 1) && q < TCOPY; q++) stage_copy(1 + q / G::PLANE_INSTR, q % G::PLANE_INSTR);
       if (s + 1 < G::NS) {
         // Step s+1 reads taps up to depth tap td_of(s+1): wait for its plane.
         if (G::td_of(s + 1) != G::td_of(s)) {
@@ -1050,14 +1081,6 @@ __global__ __launch_bounds__(256) void fused_min_softmax_mfma4_kernel(FusedArgs 
 //   lane: nothing of the conv result leaves the registers. With DSPLIT > 1 the
 //   partial minima of the depth ranges meet in LDS first.
 // ---------------------------------------------------------------------------
-template <int N, class F, int... I>
-__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
-  (f(std::integral_constant<int, I>{}), ...);
-}
-template <int N, class F>
-__device__ __forceinline__ void static_for(F&& f) {
-  static_for_impl<N>(f, std::make_integer_sequence<int, N>{});
-}
 
 template <int CIN, int KH, int KW_, int NG, int O2, int ROWS>
 struct StreamGeo {
