@@ -118,6 +118,20 @@ __device__ __forceinline__ void lds_dma_f32(const float* src, float* dst) {
   __builtin_amdgcn_global_load_lds(src, dst, 4, 0, 0);
 }
 
+// s_waitcnt vmcnt(V) with expcnt and lgkmcnt left at their maxima (gfx9 encoding:
+// vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+template <int V>
+__device__ __forceinline__ void wait_vmem_le() {
+  static_assert(V >= 0 && V < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((V & 15) | ((V >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Asynchronous 16-byte copy per lane: lane l writes dst[4l .. 4l+3].
+__device__ __forceinline__ void lds_dma_f32x4(const float* src, float* dst) {
+  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+}
+
+
 // Geometry of one output tile: BN positions of the (n, od) plane, BM channels
 // of group g starting at m0.
 struct TileGeo {
@@ -457,6 +471,9 @@ struct TapGeo {
   static constexpr int PLANE = ROWS * BW;
   static constexpr int BOXC = KDSPAN * PLANE;
   static constexpr int XS = (CC * BOXC + 255) / 256 * 256;  // floats per box buffer
+  // One input row per channel and a row length that is a multiple of 4: the
+  // box is copied row by row in 16-byte chunks (the planner checks alignment).
+  static constexpr bool ROWCOPY = ROWS == 1 && KDSPAN == 1 && BW % 4 == 0;
   template <int NCH, int WM, int MT>
   static constexpr int lds_floats() { return 2 * XS + (NCH * NS + 1) * WM * 64 * MT; }
   // LDS offset (floats) of reduction index k = (channel, td, th, tw) of a chunk;
@@ -506,6 +523,39 @@ __device__ __forceinline__ void fill_pat_deltas(int* dp, int kg, std::integer_se
   ((dp[Q] = pat_delta<G, Q>(kg)), ...);
 }
 
+// Box of one chunk when it is a single input row per channel (ROWCOPY): row r
+// (channel c0 + r) of the chunk holds input columns iw0 .. iw0 + BW - 1, copied
+// in 16-byte chunks (iw0, the row length and the input pointer are multiples of
+// 4 floats, so a chunk lies wholly inside or wholly outside the input).
+template <class G, int NWAVES>
+__device__ __forceinline__ void stage_rows16(const ConvArgs& a, const TileGeo& t, int c0, float* dst, int wave,
+                                             int lane) {
+  constexpr int Q = G::BOXC / 4;  // chunks per row
+  const bool plane_ok = unsigned(t.id0) < unsigned(a.L0) && unsigned(t.ih0) < unsigned(a.L1);
+#pragma unroll
+  for (int r = wave; r < G::CCH; r += NWAVES) {
+    const float* srow = a.x + ((int64_t(t.n) * a.Cin + int64_t(t.g) * a.Cg + c0 + r) * a.L0 + (plane_ok ? t.id0 : 0)) *
+                                  int64_t(a.L1) * a.L2 +
+                        int64_t(plane_ok ? t.ih0 : 0) * a.L2;
+#pragma unroll
+    for (int i = 0; i < (Q + 63) / 64; i++) {
+      const int q = 64 * i + lane;
+      if (q < Q) {
+        const int iw = t.iw0 + 4 * q;
+        const bool ok = plane_ok && unsigned(iw) < unsigned(a.L2);
+        lds_dma_f32x4(ok ? srow + iw : kZeroWord, dst + r * G::BOXC + 256 * i);
+      }
+    }
+  }
+}
+
+template <class G, int NWAVES>
+__device__ __forceinline__ void stage_tap_box(const ConvArgs& a, const TileGeo& t, int c0, float* dst, int wave,
+                                              int lane) {
+  if constexpr (G::ROWCOPY) stage_rows16<G, NWAVES>(a, t, c0, dst, wave, lane);
+  else stage_box<NWAVES>(a, t, c0, dst, wave, lane);
+}
+
 // Reduce one staged chunk: all k-steps unrolled, B operands read at
 // (lane register + immediate), A operands from the resident weight fragments
 // (wchunk already includes this lane's and wave row's offset).
@@ -550,7 +600,7 @@ __device__ __forceinline__ void tap_stage(const ConvArgs& a, const TileGeo& tn, 
                                           const float* __restrict__ cur, float* __restrict__ nxt,
                                           const float* __restrict__ wchunk, const int (&addr)[NP][NT],
                                           v4f (&acc)[MT][NT], int wave, int lane) {
-  if (has_next) stage_box<NWAVES>(a, tn, c0_next, nxt, wave, lane);
+  if (has_next) stage_tap_box<G, NWAVES>(a, tn, c0_next, nxt, wave, lane);
   __builtin_amdgcn_sched_barrier(0);
   tap_chunk<MT, NT, WM, G, NP>(cur, wchunk, addr, acc);
 }
@@ -584,7 +634,7 @@ __global__ __launch_bounds__(64 * WM * WN) void conv_tap_kernel(ConvArgs a) {
   for (int c = 0; c < NCH; c++)
     stage_wfrag<MT, WM, NWAVES>(a, 0, 0, c * G::CCH, G::NS, Wres + c * G::NS * SSTRIDE, wave, lane);
   TileGeo t = tile_geo(a, item % a.tiles_per_plane, item / a.tiles_per_plane, 0, BM, BN, true);
-  stage_box<NWAVES>(a, t, 0, box0, wave, lane);
+  stage_tap_box<G, NWAVES>(a, t, 0, box0, wave, lane);
   wait_vmem();
   __syncthreads();
 
@@ -656,19 +706,6 @@ __global__ __launch_bounds__(64 * WM * WN) void conv_tap_kernel(ConvArgs a) {
 //   while the rest is in flight. The box keeps every F-th input column: with
 //   stride and dilation along W both multiples of F no other column is read.
 // ---------------------------------------------------------------------------
-// s_waitcnt vmcnt(V) with expcnt and lgkmcnt left at their maxima (gfx9 encoding:
-// vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
-template <int V>
-__device__ __forceinline__ void wait_vmem_le() {
-  static_assert(V >= 0 && V < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((V & 15) | ((V >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// Asynchronous 16-byte copy per lane: lane l writes dst[4l .. 4l+3].
-__device__ __forceinline__ void lds_dma_f32x4(const float* src, float* dst) {
-  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
-}
-
 template <int KD, int KH, int KW, int DD, int DH, int DW, int F, int ROWS, int BW, int NW>
 struct SplitGeo {
   static constexpr int FF = F;
@@ -1554,9 +1591,10 @@ int conv_fwd(int nd, const float* x, const int64_t* x_shape, const float* w, con
   if (rc != CONV_OK) return rc;
   if (!x || !w || !y) return CONV_ERR_NULL;
   ConvPlan p;
-  // The specialised kernels copy weights in 16-byte chunks: they need a 16-byte
-  // aligned weight pointer (any tensor allocation is; a sliced view may not be).
-  const bool aligned = (reinterpret_cast<uintptr_t>(w) & 15) == 0;
+  // The specialised kernels copy weights (and 1-D input rows) in 16-byte chunks:
+  // they need 16-byte aligned pointers (any tensor allocation is; a sliced view
+  // may not be).
+  const bool aligned = ((reinterpret_cast<uintptr_t>(w) | reinterpret_cast<uintptr_t>(x)) & 15) == 0;
   rc = plan_conv(g, &p, forced_conv_cfg(), device_num_cu(), aligned ? use_tap() : 0);
   if (rc != CONV_OK) return rc;
   ConvArgs a = conv_args(g, p, x, w, bias, y);

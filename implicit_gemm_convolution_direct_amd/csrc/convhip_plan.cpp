@@ -161,7 +161,15 @@ static bool plan_tap(const Geom& g, const TapSpecDesc& d, int num_cu, ConvPlan* 
   int64_t tiles;
   box_dims(g, mode, BN, &rows, &bw, &tiles, &row_tiles);
   const int kdspan = int((g.K[0] - 1) * g.Dl[0] + 1);
-  if (rows != d.ROWS || bw != d.BW || kdspan != d.KDSPAN) return false;
+  if (rows != d.ROWS || kdspan != d.KDSPAN) return false;
+  if (d.ROWS == 1 && d.KDSPAN == 1 && d.BW % 4 == 0) {
+    // Row-copy specialisation: input rows copied in 16-byte chunks starting at
+    // column ow0*S - P, so the row, its start and its length are multiples of 4.
+    if (mode != TILE_ROW || bw > d.BW || g.L[2] % 4 != 0 || g.P[2] % 4 != 0 || (g.S[2] * BN) % 4 != 0) return false;
+    bw = d.BW;
+  } else if (bw != d.BW) {
+    return false;
+  }
   const int64_t items = tiles * g.N * g.O[0];
   if (items > std::numeric_limits<int32_t>::max()) return false;
   const int64_t kvol = int64_t(d.KD) * d.KH * d.KW;

@@ -89,8 +89,9 @@ struct ConvPlan {
 #define CONVHIP_TAP_SPECS(X)                                                      \
   /* Conv3d 3->64, kernel 3x5x7, 64^3 input: 64 ch x 256 positions, 8 waves */ \
   X(0, 4, 2, 1, 8, 1, 3, 5, 7, 1, 1, 1, 3, 3, 10, 64)                            \
-  /* Conv1d 64->128, k=3, stride 3, dilation 4: 128 ch x 256 positions */       \
-  X(1, 4, 4, 2, 4, 8, 1, 1, 3, 1, 1, 4, 8, 1, 1, 774)
+  /* Conv1d 64->128, k=3, stride 3, dilation 4: 128 ch x 256 positions; the   \
+     774-float input segment is copied as 776 (16-byte chunks) */               \
+  X(1, 4, 4, 2, 4, 8, 1, 1, 3, 1, 1, 4, 8, 1, 1, 776)
 
 // Build-time specialisations of the channel-split kernel (one input channel per
 // wave, whole (n, od) plane per workgroup, <= 16 output channels per group).

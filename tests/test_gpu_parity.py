@@ -91,6 +91,9 @@ EDGE_CASES = [
     ("conv1d_k1", (1, 8, 1000), (24, 8, 1), 2, 1, 0, 1),
     ("wide_rows_3d", (1, 2, 3, 4, 600), (8, 2, 2, 2, 3), 1, 1, 1, 1),
     ("many_input_channels", (1, 200, 4, 4, 40), (16, 200, 1, 1, 3), 1, 1, 0, 1),
+    # the long Conv1d's channel/kernel geometry where 16-byte row copies do not
+    # apply (padding 2, length not a multiple of 4): generic kernel
+    ("conv1d_unaligned_rows", (1, 64, 3001), (128, 64, 3), 3, 4, 2, 1),
 ]
 
 
@@ -333,7 +336,7 @@ TAP_CASES = [
     ((2, 3, 5, 64, 64), (40, 3, 3, 5, 7), 1, 1, 0, False),   # fewer output channels, one sample per item
     ((3, 3, 9, 64, 64), (64, 3, 3, 5, 7), 1, 1, 0, True),    # odd item count per workgroup
     ((2, 64, 3000), (128, 64, 3), 3, 4, 0, False),
-    ((1, 64, 5000), (100, 64, 3), 3, 4, 2, True),            # padding, ragged last tile
+    ((1, 64, 5000), (100, 64, 3), 3, 4, 4, True),            # padding, ragged last tile
     ((4, 64, 200000), (128, 64, 3), 3, 4, 0, False),         # several items per workgroup
 ]
 
