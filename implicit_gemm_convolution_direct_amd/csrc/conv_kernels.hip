@@ -471,9 +471,10 @@ struct TapGeo {
   static constexpr int PLANE = ROWS * BW;
   static constexpr int BOXC = KDSPAN * PLANE;
   static constexpr int XS = (CC * BOXC + 255) / 256 * 256;  // floats per box buffer
-  // One input row per channel and a row length that is a multiple of 4: the
-  // box is copied row by row in 16-byte chunks (the planner checks alignment).
-  static constexpr bool ROWCOPY = ROWS == 1 && KDSPAN == 1 && BW % 4 == 0;
+  // Box rows a multiple of 4 floats long: copied in 16-byte chunks (the planner
+  // checks the alignment of the rows' first input column).
+  static constexpr bool ROWCOPY = BW % 4 == 0;
+  static constexpr int BW_ = BW, ROWS_ = ROWS, KDSPAN_ = KDSPAN;
   template <int NCH, int WM, int MT>
   static constexpr int lds_floats() { return 2 * XS + (NCH * NS + 1) * WM * 64 * MT; }
   // LDS offset (floats) of reduction index k = (channel, td, th, tw) of a chunk;
@@ -523,28 +524,32 @@ __device__ __forceinline__ void fill_pat_deltas(int* dp, int kg, std::integer_se
   ((dp[Q] = pat_delta<G, Q>(kg)), ...);
 }
 
-// Box of one chunk when it is a single input row per channel (ROWCOPY): row r
-// (channel c0 + r) of the chunk holds input columns iw0 .. iw0 + BW - 1, copied
-// in 16-byte chunks (iw0, the row length and the input pointer are multiples of
-// 4 floats, so a chunk lies wholly inside or wholly outside the input).
+// Box of one chunk as whole 16-byte chunks (ROWCOPY). The box is CC*KDSPAN*ROWS
+// rows of BW floats, row (c, zd, zr) <- input row (c0 + c, id0 + zd, ih0 + zr),
+// columns iw0 .. iw0 + BW - 1. The rows are contiguous in LDS, so copy i of wave
+// w moves box chunks u = (i*NWAVES + w)*64 + lane as one contiguous 1 KB run.
+// iw0, the input row length and the input pointer are multiples of 4 floats
+// (the planner checks), so a chunk lies wholly inside or wholly outside a row.
 template <class G, int NWAVES>
 __device__ __forceinline__ void stage_rows16(const ConvArgs& a, const TileGeo& t, int c0, float* dst, int wave,
                                              int lane) {
-  constexpr int Q = G::BOXC / 4;  // chunks per row
-  const bool plane_ok = unsigned(t.id0) < unsigned(a.L0) && unsigned(t.ih0) < unsigned(a.L1);
+  constexpr int Q = G::BW_ / 4;                                  // chunks per row
+  constexpr int NROWS = G::CCH * G::KDSPAN_ * G::ROWS_;
+  constexpr int NCHUNK = NROWS * Q;
+  constexpr int NI = (NCHUNK + 64 * NWAVES - 1) / (64 * NWAVES);  // copies per wave
+  const int64_t chan0 = int64_t(t.n) * a.Cin + int64_t(t.g) * a.Cg + c0;
 #pragma unroll
-  for (int r = wave; r < G::CCH; r += NWAVES) {
-    const float* srow = a.x + ((int64_t(t.n) * a.Cin + int64_t(t.g) * a.Cg + c0 + r) * a.L0 + (plane_ok ? t.id0 : 0)) *
-                                  int64_t(a.L1) * a.L2 +
-                        int64_t(plane_ok ? t.ih0 : 0) * a.L2;
-#pragma unroll
-    for (int i = 0; i < (Q + 63) / 64; i++) {
-      const int q = 64 * i + lane;
-      if (q < Q) {
-        const int iw = t.iw0 + 4 * q;
-        const bool ok = plane_ok && unsigned(iw) < unsigned(a.L2);
-        lds_dma_f32x4(ok ? srow + iw : kZeroWord, dst + r * G::BOXC + 256 * i);
-      }
+  for (int i = 0; i < NI; i++) {
+    const int u0 = (i * NWAVES + wave) * 64;
+    const int u = u0 + lane;
+    if (u < NCHUNK) {
+      const int row = u / Q, q = u - row * Q;
+      const int c = row / (G::KDSPAN_ * G::ROWS_), rr = row - c * (G::KDSPAN_ * G::ROWS_);
+      const int zd = rr / G::ROWS_, zr = rr - zd * G::ROWS_;
+      const int id = t.id0 + zd, ih = t.ih0 + zr, iw = t.iw0 + 4 * q;
+      const bool ok = unsigned(id) < unsigned(a.L0) && unsigned(ih) < unsigned(a.L1) && unsigned(iw) < unsigned(a.L2);
+      const float* src = a.x + (((chan0 + c) * a.L0 + id) * a.L1 + ih) * a.L2 + iw;
+      lds_dma_f32x4(ok ? src : kZeroWord, dst + 4 * u0);
     }
   }
 }

@@ -162,10 +162,16 @@ static bool plan_tap(const Geom& g, const TapSpecDesc& d, int num_cu, ConvPlan* 
   box_dims(g, mode, BN, &rows, &bw, &tiles, &row_tiles);
   const int kdspan = int((g.K[0] - 1) * g.Dl[0] + 1);
   if (rows != d.ROWS || kdspan != d.KDSPAN) return false;
-  if (d.ROWS == 1 && d.KDSPAN == 1 && d.BW % 4 == 0) {
-    // Row-copy specialisation: input rows copied in 16-byte chunks starting at
-    // column ow0*S - P, so the row, its start and its length are multiples of 4.
-    if (mode != TILE_ROW || bw > d.BW || g.L[2] % 4 != 0 || g.P[2] % 4 != 0 || (g.S[2] * BN) % 4 != 0) return false;
+  // Specialisations with rows of a multiple of 4 floats copy the box in 16-byte
+  // chunks starting at input column ow0*S - P: the input rows, that column and
+  // the row length must be multiples of 4. A single-row box (1-D) may be staged
+  // wider than needed.
+  if (d.BW % 4 == 0) {
+    if (g.L[2] % 4 != 0 || g.P[2] % 4 != 0) return false;
+    if (mode == TILE_ROW && (g.S[2] * BN) % 4 != 0) return false;
+  }
+  if (d.ROWS == 1 && d.KDSPAN == 1 && d.BW % 4 == 0 && mode == TILE_ROW) {
+    if (bw > d.BW) return false;
     bw = d.BW;
   } else if (bw != d.BW) {
     return false;
