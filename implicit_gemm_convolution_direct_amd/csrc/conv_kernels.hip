@@ -1294,10 +1294,12 @@ __global__ __launch_bounds__(256, 4) void fused_stream_kernel(StreamArgs a) {
       });
       __builtin_amdgcn_sched_barrier(0);
     });
+    // Running minimum as compare-and-select: a NaN product is dropped, as fminf
+    // drops it, without fminf's operand canonicalisation.
 #pragma unroll
     for (int q = 0; q < NG; q++)
 #pragma unroll
-      for (int i = 0; i < 4; i++) mn[q][i] = fminf(mn[q][i], acc[q][i]);
+      for (int i = 0; i < 4; i++) mn[q][i] = acc[q][i] < mn[q][i] ? acc[q][i] : mn[q][i];
   }
 
   float* yp = a.y + int64_t(n) * a.Cout * a.plane_out + p;
@@ -1318,7 +1320,10 @@ __global__ __launch_bounds__(256, 4) void fused_stream_kernel(StreamArgs a) {
 #pragma unroll
       for (int q = 0; q < NG; q++)
 #pragma unroll
-        for (int i = 0; i < 4; i++) mn[q][i] = fminf(mn[q][i], red[(((wave + o) * NG + q) * 4 + i) * 64 + lane]);
+        for (int i = 0; i < 4; i++) {
+          const float v = red[(((wave + o) * NG + q) * 4 + i) * 64 + lane];
+          mn[q][i] = v < mn[q][i] ? v : mn[q][i];
+        }
   }
 
   // Softmax over the channels of this lane's position. fp32 addition is
