@@ -947,6 +947,11 @@ struct FusedArgs {
   int kvol, kfull, cpad;
   int mode, dspan, rows, bw, boxc, row_tiles;
   int plane_out;
+  // Element strides of x (per sample, per input channel, per spatial axis) and of
+  // w (per kernel axis), in the kernel's axis order: the minimum is always taken
+  // over axis 0, and the host permutes the axes for a minimum over H or W.
+  int64_t xs_n, xs_c, xs0, xs1, xs2;
+  int ws0, ws1, ws2;
 };
 
 template <int A>
@@ -1000,16 +1005,21 @@ __global__ __launch_bounds__(256) void fused_min_softmax_mfma4_kernel(FusedArgs 
     const int tw = r2 - th * a.K2;
     koff[k] = c * a.boxc + td * a.D0 * plane_stride + th * a.D1 * a.bw + tw * a.D2;
   }
-  // Weights transposed to [k][c_out] so lane c reads channel c of tap k.
+  // Weights transposed to [k][c_out] so lane c reads channel c of tap k
+  // (k = (input channel, td, th, tw) in the kernel's axis order).
   for (int idx = tid; idx < a.kfull * a.cpad; idx += 256) {
     const int c = idx / a.kfull;
     const int k = idx - c * a.kfull;
-    Wt[k * a.cpad + c] = (c < a.Cout) ? a.w[int64_t(c) * a.kfull + k] : 0.0f;
+    const int ci = k / a.kvol, r = k - ci * a.kvol;
+    const int td = r / (a.K1 * a.K2), r2 = r - td * a.K1 * a.K2;
+    const int th = r2 / a.K2, tw = r2 - th * a.K2;
+    Wt[k * a.cpad + c] =
+        (c < a.Cout) ? a.w[int64_t(c) * a.kfull + ci * a.kvol + td * a.ws0 + th * a.ws1 + tw * a.ws2] : 0.0f;
   }
   // Input box: all input planes the output depths read, rows of this tile.
   const int rows_per_c = a.dspan * rows_needed;
   const int nrows = a.Cin * rows_per_c;
-  const int64_t x_n = int64_t(n) * a.Cin * a.L0;
+  const float* x_n = a.x + int64_t(n) * a.xs_n;
   for (int r = wave; r < nrows; r += 4) {
     const int c = r / rows_per_c;
     const int rem = r - c * rows_per_c;
@@ -1018,12 +1028,12 @@ __global__ __launch_bounds__(256) void fused_min_softmax_mfma4_kernel(FusedArgs 
     const int id = zd - a.P0;
     const int ih = ih0 + zr;
     const bool rv = (id >= 0) && (id < a.L0) && (ih >= 0) && (ih < a.L1);
-    const float* src = a.x + ((x_n + int64_t(c) * a.L0 + (rv ? id : 0)) * a.L1 + (rv ? ih : 0)) * a.L2;
+    const float* src = x_n + c * a.xs_c + (rv ? id : 0) * a.xs0 + (rv ? ih : 0) * a.xs1;
     float* dst = Xs + c * a.boxc + zd * plane_stride + zr * a.bw;
     for (int col = lane; col < a.bw; col += 64) {
       const int iw = iw0 + col;
       float v = 0.0f;
-      if (rv && iw >= 0 && iw < a.L2) v = src[iw];
+      if (rv && iw >= 0 && iw < a.L2) v = src[iw * a.xs2];
       dst[col] = v;
     }
   }
@@ -1630,10 +1640,28 @@ int conv3d_min_softmax(const float* x, const int64_t* x_shape, const float* w, c
   if (rc != CONV_OK) return rc;
   if (!x || !w || !y) return CONV_ERR_NULL;
   if (min_dim < 2 || min_dim > 4) return CONV_ERR_PARAM;
+  // The kernels take the minimum over their axis 0. For a minimum over H or W the
+  // spatial axes are permuted (conv commutes with a permutation of the spatial
+  // axes applied to x, w, stride, dilation and padding alike); the remaining two
+  // axes keep their order, so the output [N, C_out, rest...] is contiguous in the
+  // permuted order too.
+  static const int kPerm[3][3] = {{0, 1, 2}, {1, 0, 2}, {2, 0, 1}};
+  const int* perm = kPerm[min_dim - 2];
+  const Geom g0 = g;
+  for (int i = 0; i < 3; i++) {
+    g.L[i] = g0.L[perm[i]];
+    g.K[i] = g0.K[perm[i]];
+    g.S[i] = g0.S[perm[i]];
+    g.Dl[i] = g0.Dl[perm[i]];
+    g.P[i] = g0.P[perm[i]];
+    g.O[i] = g0.O[perm[i]];
+  }
+  const int64_t xst[3] = {g0.L[1] * g0.L[2], g0.L[2], 1};
+  const int64_t wst[3] = {g0.K[1] * g0.K[2], g0.K[2], 1};
   FusedPlan p;
   // The depth-streamed kernel copies input rows in 16-byte chunks.
   const bool aligned = (reinterpret_cast<uintptr_t>(x) & 15) == 0;
-  rc = plan_fused(g, min_dim, &p, use_tap() != 0 && aligned);
+  rc = plan_fused(g, min_dim, &p, use_tap() != 0 && aligned && min_dim == 2);
   if (rc != CONV_OK) return rc;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (p.spec >= 0) {
@@ -1662,6 +1690,14 @@ int conv3d_min_softmax(const float* x, const int64_t* x_shape, const float* w, c
   a.kvol = int(g.kvol()); a.kfull = p.kfull; a.cpad = p.cpad;
   a.mode = p.mode; a.dspan = p.dspan; a.rows = p.rows; a.bw = p.bw; a.boxc = p.boxc; a.row_tiles = p.row_tiles;
   a.plane_out = int(g.plane_out());
+  a.xs_c = g0.L[0] * g0.L[1] * g0.L[2];
+  a.xs_n = g0.Cin * a.xs_c;
+  a.xs0 = xst[perm[0]];
+  a.xs1 = xst[perm[1]];
+  a.xs2 = xst[perm[2]];
+  a.ws0 = int(wst[perm[0]]);
+  a.ws1 = int(wst[perm[1]]);
+  a.ws2 = int(wst[perm[2]]);
   switch (p.ng) {
     case 1: return launch_fused_ng<1>(a, p, s);
     case 2: return launch_fused_ng<2>(a, p, s);

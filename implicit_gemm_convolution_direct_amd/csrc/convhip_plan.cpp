@@ -367,7 +367,8 @@ static bool plan_fused_stream(const Geom& g, const FusedSpecDesc& d, FusedPlan* 
 
 int plan_fused(const Geom& g, int min_dim, FusedPlan* out, bool allow_spec) {
   if (g.nd != 3) return CONV_ERR_RANK;
-  if (min_dim != 2 || g.G != 1 || g.Cout > 64) return CONV_ERR_UNSUPPORTED;
+  // g is in the kernels' axis order (the minimum over axis 0).
+  if (min_dim < 2 || min_dim > 4 || g.G != 1 || g.Cout > 64) return CONV_ERR_UNSUPPORTED;
   if (allow_spec) {
     int ns = 0;
     const FusedSpecDesc* specs = fused_specs(&ns);

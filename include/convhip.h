@@ -76,14 +76,18 @@ int conv_fwd(int nd,
              float *y, convhip_stream_t stream);
 
 /*
- * Fused Conv3d -> min over depth -> softmax over channels (page l2_p24,
- * opening turns: the module applies Conv3d, torch.min over dim 2, then
- * torch.softmax over dim 1). The 5-D conv result is never written to memory.
+ * Fused Conv3d -> min over one spatial axis -> softmax over channels (page
+ * l2_p24, opening turns: the module applies Conv3d, torch.min over dim 2, then
+ * torch.softmax over dim 1; its `dim` argument names the min axis). The 5-D
+ * conv result is never written to memory.
  *   x [N, C_in, D, H, W], w [C_out, C_in/groups, kD, kH, kW], bias [C_out] or NULL,
- *   y [N, C_out, H_out, W_out] with
- *   y[n,:,h,w] = softmax_c( min_{od} conv3d(x,w,bias)[n,c,od,h,w] ).
- * Supported in this build: min_dim == 2, groups == 1, C_out <= 64; other valid
- * arguments return CONV_ERR_UNSUPPORTED. Non-finite inputs: unspecified.
+ *   min_dim 2, 3 or 4 (D, H or W); y holds the two other output axes in order:
+ *   min_dim 2: y [N, C_out, H_out, W_out],
+ *              y[n,:,h,w] = softmax_c( min_{od} conv3d(x,w,bias)[n,c,od,h,w] );
+ *   min_dim 3: y [N, C_out, D_out, W_out];  min_dim 4: y [N, C_out, D_out, H_out].
+ * Supported in this build: groups == 1, C_out <= 64, and the input box of one
+ * output tile over the whole min axis must fit in LDS; other valid arguments
+ * return CONV_ERR_UNSUPPORTED. Non-finite inputs: unspecified.
  */
 int conv3d_min_softmax(const float *x, const int64_t *x_shape,
                        const float *w, const int64_t *w_shape, const float *bias,

@@ -80,7 +80,8 @@ def test_conv3d_min_softmax_validation_errors():
                                             kw.get("y", FAKE), None)
     assert f(y=None) == -1
     assert f(md=5) == -5
-    assert f(md=3) == -7          # other axes: unsupported in this build
+    assert f(md=3, ws=I64(65, 3, 3, 3, 3)) == -7   # min over H: supported, but not C_out > 64
+    assert f(md=4, xs=I64(2, 3, 6, 6, 2)) == -6    # min over W of an empty output
     assert f(g=3) == -7 or f(g=3) == -4
     assert f(ws=I64(6, 1, 3, 3, 3), xs=I64(2, 3, 6, 6, 6), g=3) == -7   # grouped fused: unsupported
     assert f(ws=I64(65, 3, 3, 3, 3)) == -7                             # C_out > 64: unsupported

@@ -253,6 +253,44 @@ def test_fused_stream_cases(case):
     assert err <= FUSED_ATOL
 
 
+MIN_AXIS_CASES = [
+    # name, x, w, stride, dilation, padding, min_dim
+    ("min_h_workload_like", (2, 3, 6, 12, 10), (24, 3, 3, 3, 3), 1, 1, 0, 3),
+    ("min_w_workload_like", (2, 3, 6, 10, 12), (24, 3, 3, 3, 3), 1, 1, 0, 4),
+    ("min_h_strided_padded", (1, 2, 7, 9, 11), (10, 2, 2, 3, 2), (2, 1, 2), (1, 2, 1), (1, 1, 2), 3),
+    ("min_w_strided_padded", (1, 2, 7, 9, 13), (7, 2, 2, 3, 3), (1, 2, 2), (2, 1, 1), (1, 1, 2), 4),
+    ("min_w_asym_kernel", (2, 3, 5, 6, 9), (5, 3, 1, 2, 4), 1, (1, 1, 2), (0, 1, 1), 4),
+    ("min_h_single_row", (1, 3, 4, 3, 8), (6, 3, 2, 3, 3), 1, 1, 0, 3),
+]
+
+
+@pytest.mark.parametrize("case", MIN_AXIS_CASES, ids=[c[0] for c in MIN_AXIS_CASES])
+def test_fused_min_over_h_or_w(case):
+    """Minimum over H or W (min_dim 3, 4): the generic fused kernel with permuted
+    axes, against the oracle's own minimum over that axis."""
+    name, xs, ws, s, d, p, md = case
+    r = np.random.default_rng(1300 + len(name))
+    x, w, b = _float_inputs(r, xs, ws, True)
+    y = gpu_fused(x, w, b, s, d, p, 1, md)
+    ref = oracle.conv3d_min_softmax(x, w, b, s, d, p, 1, md)
+    assert y.shape == ref.shape, (y.shape, ref.shape)
+    err = float(np.abs(y - ref).max())
+    say(f"  {name}: max|err| = {err:.3e}")
+    assert err <= FUSED_ATOL
+
+
+def test_fused_min_axes_integer_exact_minimum():
+    """Integer inputs make every conv value exact: the minimum over each axis is
+    exact and only exp/division rounding remains."""
+    r = np.random.default_rng(77)
+    x, w, b = _int_inputs(r, (2, 3, 6, 7, 8), (8, 3, 3, 3, 3), bias=True)
+    w = (w * 0.125).astype(np.float32)
+    for md in (2, 3, 4):
+        y = gpu_fused(x, w, b, 1, 1, 1, 1, md)
+        ref = oracle.conv3d_min_softmax(x, w, b, 1, 1, 1, 1, md)
+        assert float(np.abs(y - ref).max()) <= 1e-6, md
+
+
 def test_misaligned_pointers_take_generic_kernels():
     """Views that start 4 bytes past an allocation keep the specialised kernels
     (16-byte copies) out and still give the oracle's results."""
