@@ -134,8 +134,8 @@ def conv_fwd(x, w, bias=None, stride=1, dilation=1, padding=0, groups=1, out=Non
     if bias is not None:
         _check_tensor(bias, "bias")
     nd = x.dim() - 2
-    if nd not in (1, 3) or w.dim() != x.dim():
-        raise ValueError("x and w must both be 3-D (Conv1d) or 5-D (Conv3d)")
+    if nd not in (1, 2, 3) or w.dim() != x.dim():
+        raise ValueError("x and w must both be 3-D (Conv1d), 4-D (Conv2d) or 5-D (Conv3d)")
     stride, dilation, padding = (_vec(stride, nd, "stride"), _vec(dilation, nd, "dilation"),
                                  _vec(padding, nd, "padding"))
     rc, o = out_shape(list(x.shape[2:]), list(w.shape[2:]), stride, dilation, padding)

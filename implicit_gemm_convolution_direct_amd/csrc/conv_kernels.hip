@@ -952,6 +952,7 @@ struct FusedArgs {
   // over axis 0, and the host permutes the axes for a minimum over H or W.
   int64_t xs_n, xs_c, xs0, xs1, xs2;
   int ws0, ws1, ws2;
+  int Cg, Coutg;  // groups: input / output channels per group
 };
 
 template <int A>
@@ -1006,15 +1007,19 @@ __global__ __launch_bounds__(256) void fused_min_softmax_mfma4_kernel(FusedArgs 
     koff[k] = c * a.boxc + td * a.D0 * plane_stride + th * a.D1 * a.bw + tw * a.D2;
   }
   // Weights transposed to [k][c_out] so lane c reads channel c of tap k
-  // (k = (input channel, td, th, tw) in the kernel's axis order).
+  // (k = (input channel, td, th, tw) in the kernel's axis order, over all C_in
+  // input channels: with groups the matrix is block-diagonal, zero where the
+  // input channel lies outside output channel c's group).
   for (int idx = tid; idx < a.kfull * a.cpad; idx += 256) {
     const int c = idx / a.kfull;
     const int k = idx - c * a.kfull;
     const int ci = k / a.kvol, r = k - ci * a.kvol;
     const int td = r / (a.K1 * a.K2), r2 = r - td * a.K1 * a.K2;
     const int th = r2 / a.K2, tw = r2 - th * a.K2;
+    const int cl = ci - (c / a.Coutg) * a.Cg;  // input channel within c's group
+    const bool in_group = c < a.Cout && cl >= 0 && cl < a.Cg;
     Wt[k * a.cpad + c] =
-        (c < a.Cout) ? a.w[int64_t(c) * a.kfull + ci * a.kvol + td * a.ws0 + th * a.ws1 + tw * a.ws2] : 0.0f;
+        in_group ? a.w[int64_t(c) * a.Cg * a.kvol + cl * a.kvol + td * a.ws0 + th * a.ws1 + tw * a.ws2] : 0.0f;
   }
   // Input box: all input planes the output depths read, rows of this tile.
   const int rows_per_c = a.dspan * rows_needed;
@@ -1698,6 +1703,8 @@ int conv3d_min_softmax(const float* x, const int64_t* x_shape, const float* w, c
   a.ws0 = int(wst[perm[0]]);
   a.ws1 = int(wst[perm[1]]);
   a.ws2 = int(wst[perm[2]]);
+  a.Cg = int(g.Cg);
+  a.Coutg = int(g.Coutg);
   switch (p.ng) {
     case 1: return launch_fused_ng<1>(a, p, s);
     case 2: return launch_fused_ng<2>(a, p, s);

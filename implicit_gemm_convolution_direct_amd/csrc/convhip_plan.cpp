@@ -18,7 +18,7 @@ int64_t out_len(int64_t L, int64_t k, int64_t s, int64_t d, int64_t p) {
 
 int make_geom(int nd, const int64_t* xs, const int64_t* ws, const int* stride, const int* dilation,
               const int* padding, int groups, Geom* g) {
-  if (nd != 1 && nd != 3) return CONV_ERR_RANK;
+  if (nd < 1 || nd > 3) return CONV_ERR_RANK;
   if (!xs || !ws || !stride || !dilation || !padding || !g) return CONV_ERR_NULL;
   for (int i = 0; i < nd + 2; i++)
     if (xs[i] < 1 || ws[i] < 1) return CONV_ERR_SHAPE;
@@ -325,7 +325,7 @@ const FusedSpecDesc* fused_specs(int* count) {
 
 // Plan of a depth-streamed specialisation if the geometry is the one it was built for.
 static bool plan_fused_stream(const Geom& g, const FusedSpecDesc& d, FusedPlan* p) {
-  if (g.Cin != d.CIN || g.K[0] != 3 || g.K[1] != d.KH || g.K[2] != d.KW) return false;
+  if (g.G != 1 || g.Cin != d.CIN || g.K[0] != 3 || g.K[1] != d.KH || g.K[2] != d.KW) return false;
   for (int i = 0; i < 3; i++)
     if (g.S[i] != 1 || g.Dl[i] != 1) return false;
   if ((g.Cout + 3) / 4 != d.NG || g.O[2] != d.O2) return false;
@@ -368,7 +368,7 @@ static bool plan_fused_stream(const Geom& g, const FusedSpecDesc& d, FusedPlan* 
 int plan_fused(const Geom& g, int min_dim, FusedPlan* out, bool allow_spec) {
   if (g.nd != 3) return CONV_ERR_RANK;
   // g is in the kernels' axis order (the minimum over axis 0).
-  if (min_dim < 2 || min_dim > 4 || g.G != 1 || g.Cout > 64) return CONV_ERR_UNSUPPORTED;
+  if (min_dim < 2 || min_dim > 4 || g.Cout > 64) return CONV_ERR_UNSUPPORTED;
   if (allow_spec) {
     int ns = 0;
     const FusedSpecDesc* specs = fused_specs(&ns);

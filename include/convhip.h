@@ -36,7 +36,7 @@ typedef struct ihipStream_t *convhip_stream_t;
 typedef enum {
   CONV_OK = 0,
   CONV_ERR_NULL = -1,         /* a required pointer is NULL */
-  CONV_ERR_RANK = -2,         /* nd not 1 or 3 */
+  CONV_ERR_RANK = -2,         /* nd not 1, 2 or 3 */
   CONV_ERR_SHAPE = -3,        /* non-positive dimension, or w's C_in/groups mismatch */
   CONV_ERR_GROUPS = -4,       /* groups < 1, or C_in or C_out not divisible by groups */
   CONV_ERR_PARAM = -5,        /* stride < 1, dilation < 1 or padding < 0 */
@@ -61,7 +61,10 @@ int conv_out_shape(int nd, const int64_t *in_spatial, const int64_t *k_spatial,
  * Forward convolution (pages l1_p60 and l1_p76, opening turns: nn.Conv3d /
  * nn.Conv1d forward).
  *   nd = 1: x [N, C_in, L],       w [C_out, C_in/groups, k],            y [N, C_out, L_out]
+ *   nd = 2: x [N, C_in, H, W],    w [C_out, C_in/groups, kH, kW],       y [N, C_out, H_out, W_out]
  *   nd = 3: x [N, C_in, D, H, W], w [C_out, C_in/groups, kD, kH, kW],   y [N, C_out, D_out, H_out, W_out]
+ *   (nd = 2 is the 3-D case with D = kD = 1: the pages' rank-generic loops
+ *   cover it; it is the rank between their Conv1d and Conv3d.)
  *   y[n,co,o] = bias[co] + sum_{c', t} w[co,c',t] * x[n, g(co)*C_in/groups + c', o*stride + t*dilation - padding]
  *   with out-of-range input reading as 0 and g(co) = co / (C_out/groups).
  * x_shape / w_shape: nd+2 host entries. stride, dilation, padding: nd host
@@ -85,9 +88,10 @@ int conv_fwd(int nd,
  *   min_dim 2: y [N, C_out, H_out, W_out],
  *              y[n,:,h,w] = softmax_c( min_{od} conv3d(x,w,bias)[n,c,od,h,w] );
  *   min_dim 3: y [N, C_out, D_out, W_out];  min_dim 4: y [N, C_out, D_out, H_out].
- * Supported in this build: groups == 1, C_out <= 64, and the input box of one
- * output tile over the whole min axis must fit in LDS; other valid arguments
- * return CONV_ERR_UNSUPPORTED. Non-finite inputs: unspecified.
+ * Supported in this build: C_out <= 64, and the input box of one output tile
+ * over the whole min axis must fit in LDS (groups > 1 run as a block-diagonal
+ * dense conv); other valid arguments return CONV_ERR_UNSUPPORTED. Non-finite
+ * inputs: unspecified.
  */
 int conv3d_min_softmax(const float *x, const int64_t *x_shape,
                        const float *w, const int64_t *w_shape, const float *bias,

@@ -60,15 +60,17 @@ int oracle_num_threads(void) {
 #endif
 }
 
-/* nd = 1: x [N,C_in,L], w [C_out,C_g,k]; nd = 3: x [N,C_in,D,H,W], w [C_out,C_g,kD,kH,kW].
+/* nd = 1: x [N,C_in,L], w [C_out,C_g,k]; nd = 2: x [N,C_in,H,W], w [C_out,C_g,kH,kW];
+   nd = 3: x [N,C_in,D,H,W], w [C_out,C_g,kD,kH,kW].
  * y (double) is [N, C_out, out...]. bias may be NULL. Returns OR_OK or a negative code. */
 int oracle_conv(int nd, const float *x, const int64_t *xs, const float *w, const int64_t *ws,
                 const float *bias, const int *stride, const int *dilation, const int *padding,
                 int groups, double *y) {
-    if (nd != 1 && nd != 3) return OR_ERR_ARG;
+    if (nd < 1 || nd > 3) return OR_ERR_ARG;
     if (!x || !xs || !w || !ws || !stride || !dilation || !padding || !y) return OR_ERR_ARG;
     if (groups < 1) return OR_ERR_ARG;
-    /* View every case as 3 spatial axes; a 1-D conv has D = H = 1 and kD = kH = 1. */
+    /* View every case as 3 spatial axes; a 1-D conv has D = H = 1 and kD = kH = 1,
+       a 2-D conv D = 1 and kD = 1. */
     int64_t N = xs[0], Cin = xs[1], Cout = ws[0], Cg = ws[1];
     int64_t L[3], K[3], S[3], Dl[3], P[3], O[3];
     for (int a = 0; a < 3; a++) { L[a] = 1; K[a] = 1; S[a] = 1; Dl[a] = 1; P[a] = 0; }

@@ -45,7 +45,9 @@ def _fwd(nd, xs, ws, s, d, p, g, x=FAKE, w=FAKE, y=FAKE):
 
 
 @pytest.mark.parametrize("args,expect", [
-    ((2, (1, 1, 4, 4), (1, 1, 3, 3), (1, 1), (1, 1), (0, 0), 1), -2),        # rank
+    ((4, (1, 1, 4, 4, 4, 4), (1, 1, 3, 3, 3, 3), (1,) * 4, (1,) * 4, (0,) * 4, 1), -2),  # rank
+    ((0, (1, 1), (1, 1), (0,), (0,), (0,), 1), -2),                            # rank
+    ((2, (1, 4, 2, 8), (4, 4, 3, 3), (1, 1), (1, 1), (0, 0), 1), -6),          # Conv2d, empty output
     ((3, (1, 4, 8, 8, 8), (4, 2, 3, 3, 3), (1,) * 3, (1,) * 3, (0,) * 3, 1), -3),  # C_in/groups mismatch
     ((3, (1, 4, 8, 8, 8), (4, 4, 3, 3, 3), (1,) * 3, (1,) * 3, (0,) * 3, 0), -4),  # groups < 1
     ((3, (1, 4, 8, 8, 8), (6, 1, 3, 3, 3), (1,) * 3, (1,) * 3, (0,) * 3, 4), -4),  # C_out % groups
@@ -82,8 +84,8 @@ def test_conv3d_min_softmax_validation_errors():
     assert f(md=5) == -5
     assert f(md=3, ws=I64(65, 3, 3, 3, 3)) == -7   # min over H: supported, but not C_out > 64
     assert f(md=4, xs=I64(2, 3, 6, 6, 2)) == -6    # min over W of an empty output
-    assert f(g=3) == -7 or f(g=3) == -4
-    assert f(ws=I64(6, 1, 3, 3, 3), xs=I64(2, 3, 6, 6, 6), g=3) == -7   # grouped fused: unsupported
+    assert f(g=3) == -4                                                # C_out % groups
+    assert f(ws=I64(66, 1, 3, 3, 3), xs=I64(2, 3, 6, 6, 6), g=3) == -7  # grouped, C_out > 64
     assert f(ws=I64(65, 3, 3, 3, 3)) == -7                             # C_out > 64: unsupported
     assert f(xs=I64(2, 3, 2, 6, 6)) == -6
     assert f(s=I32(1, 0, 1)) == -5

@@ -46,13 +46,13 @@ def _random_geometry(r, nd):
     Ls = []
     for a in range(nd):
         lo = max(1, d[a] * (ks[a] - 1) + 1 - 2 * p[a])
-        span = 700 if nd == 1 else 20
+        span = {1: 700, 2: 60, 3: 20}[nd]
         Ls.append(int(r.integers(lo, lo + span)))
     N = int(r.integers(1, 3))
     return (N, g * cg, *Ls), (g * coutg, cg, *ks), s, d, p, g
 
 
-RANDOM_CASES = [(nd, seed) for nd in (1, 3) for seed in range(14)]
+RANDOM_CASES = [(nd, seed) for nd in (1, 2, 3) for seed in range(14)]
 
 
 @pytest.mark.parametrize("nd,seed", RANDOM_CASES)
@@ -277,6 +277,43 @@ def test_fused_min_over_h_or_w(case):
     err = float(np.abs(y - ref).max())
     say(f"  {name}: max|err| = {err:.3e}")
     assert err <= FUSED_ATOL
+
+
+GROUPED_FUSED_CASES = [
+    ("groups2_min_d", (2, 4, 6, 8, 9), (6, 2, 3, 3, 3), 1, 1, 0, 2, 2),
+    ("groups3_min_h_strided", (1, 6, 5, 9, 8), (9, 2, 2, 3, 2), (1, 2, 1), 1, (1, 1, 0), 3, 3),
+    ("depthwise_min_w", (2, 4, 4, 6, 10), (4, 1, 2, 2, 3), 1, (1, 1, 2), 1, 4, 4),
+]
+
+
+@pytest.mark.parametrize("case", GROUPED_FUSED_CASES, ids=[c[0] for c in GROUPED_FUSED_CASES])
+def test_fused_grouped(case):
+    """Grouped convolutions in the fused op (block-diagonal weights)."""
+    name, xs, ws, s, d, p, g, md = case
+    r = np.random.default_rng(1700 + len(name))
+    x, w, b = _float_inputs(r, xs, ws, True)
+    y = gpu_fused(x, w, b, s, d, p, g, md)
+    ref = oracle.conv3d_min_softmax(x, w, b, s, d, p, g, md)
+    err = float(np.abs(y - ref).max())
+    say(f"  {name}: max|err| = {err:.3e}")
+    assert err <= FUSED_ATOL
+
+
+CONV2D_CASES = [
+    ("conv2d_workload_like", (2, 16, 32, 32), (32, 8, 5, 7), (2, 2), (1, 2), (2, 3), 2),
+    ("conv2d_3x3", (1, 3, 40, 50), (8, 3, 3, 3), 1, 1, 1, 1),
+    ("conv2d_1x1_strided", (2, 12, 17, 19), (20, 12, 1, 1), 2, 1, 0, 1),
+]
+
+
+@pytest.mark.parametrize("case", CONV2D_CASES, ids=[c[0] for c in CONV2D_CASES])
+def test_conv2d_integer_exact(case):
+    name, xs, ws, s, d, p, g = case
+    r = np.random.default_rng(1900 + len(name))
+    x, w, b = _int_inputs(r, xs, ws, bias=True)
+    say(f"conv2d {name}: " + ch.plan_describe(xs, ws, s, d, p, g))
+    y = gpu_conv(x, w, b, s, d, p, g)
+    np.testing.assert_array_equal(y.astype(np.float64), oracle.conv(x, w, b, s, d, p, g))
 
 
 def test_fused_min_axes_integer_exact_minimum():

@@ -92,14 +92,14 @@ def _random_case(r, nd):
     Ls = []
     for a in range(nd):
         lo = max(1, d[a] * (ks[a] - 1) + 1 - 2 * p[a])
-        Ls.append(int(r.integers(lo, lo + (7 if nd == 1 else 4))))
+        Ls.append(int(r.integers(lo, lo + {1: 7, 2: 5, 3: 4}[nd])))
     x = r.standard_normal((N, groups * cg, *Ls)).astype(np.float32)
     w = r.standard_normal((groups * cout_g, cg, *ks)).astype(np.float32)
     b = r.standard_normal(groups * cout_g).astype(np.float32) if r.random() < 0.5 else None
     return x, w, b, s, d, p, groups
 
 
-@pytest.mark.parametrize("nd", [1, 3])
+@pytest.mark.parametrize("nd", [1, 2, 3])
 def test_oracle_matches_brute_force(nd):
     r = _rng(100 + nd)
     ncases = 150 if nd == 1 else 60
@@ -111,11 +111,11 @@ def test_oracle_matches_brute_force(nd):
         np.testing.assert_allclose(yo, yb, rtol=1e-12, atol=1e-12)
 
 
-@pytest.mark.parametrize("nd", [1, 3])
+@pytest.mark.parametrize("nd", [1, 2, 3])
 def test_oracle_matches_torch_float64(nd):
     """The definition is what torch's float64 CPU convolution computes."""
     r = _rng(200 + nd)
-    conv = F.conv1d if nd == 1 else F.conv3d
+    conv = {1: F.conv1d, 2: F.conv2d, 3: F.conv3d}[nd]
     for _ in range(25):
         x, w, b, s, d, p, g = _random_case(r, nd)
         yo = oracle.conv(x, w, b, s, d, p, g)
