@@ -732,8 +732,14 @@ struct SplitGeo {
   static constexpr bool W4 = WROW % 4 == 0;               // 16-byte copies, else 4-byte
   static constexpr int WCW = W4 ? 4 : 1;                   // floats per copy per lane
   static constexpr int WCH = 16 * WROW / WCW;              // copies of the weight block
-  static constexpr int WSH = (16 * WROW + 4 + 3) / 4 * 4;
-  static constexpr int W_INSTR = (WCH + 64 * NW - 1) / (64 * NW);  // copies per wave
+  // 16-byte copies go row by row into rows of WLD floats, with WLD/4 odd so the
+  // 16 rows of one A-operand read fall on distinct bank groups; 4-byte copies
+  // fill the block contiguously (WLD = WROW).
+  static constexpr int WQ = WROW / 4;                      // 16-byte chunks per row
+  static constexpr int WLD = W4 ? ((WQ % 2) ? WROW : WROW + 4) : WROW;
+  static constexpr int WRI = (WQ + 63) / 64;               // copies per row (16-byte path)
+  static constexpr int WSH = (16 * WLD + 4 + 3) / 4 * 4;
+  static constexpr int W_INSTR = W4 ? (16 * WRI + NW - 1) / NW : (WCH + 64 * NW - 1) / (64 * NW);
   static_assert((KDT - 1) * PLANE_INSTR < 64, "vmcnt range");
   // Highest depth tap read by k-step s (its 4 reduction indices).
   static constexpr int td_of(int s) { return (4 * s + 3 < K ? 4 * s + 3 : K - 1) / KPP; }
@@ -788,17 +794,30 @@ __global__ __launch_bounds__(64 * NW) void conv_tap_split_kernel(ConvArgs a) {
     b4[r] = (a.bias && ch < a.Coutg) ? a.bias[g * a.Coutg + ch] : 0.0f;
   }
   {
-    // The group's weights [16][WROW] (rows past C_out/g read as zero); copy j
-    // moves floats WCW*j .. WCW*j + WCW-1 of the block.
+    // The group's weights, 16 rows (rows past C_out/g read as zero).
     const float* wg = a.w + int64_t(g) * a.Coutg * G::WROW;
+    if constexpr (G::W4) {
+      // Copy (m, i) moves chunks 64i .. 64i+63 of row m into row m of stride WLD.
 #pragma unroll
-    for (int i = 0; i < G::W_INSTR; i++) {
-      const int j0 = (i * NW + wave) * 64;
-      const int j = j0 + lane;
-      if (j < G::WCH) {
-        const bool ok = (G::WCW * j) / G::WROW < a.Coutg;
-        if constexpr (G::W4) lds_dma_f32x4(ok ? wg + 4 * j : kZeroWord, wsh + 4 * j0);
-        else lds_dma_f32(ok ? wg + j : kZeroWord, wsh + j0);
+      for (int it = 0; it < G::W_INSTR; it++) {
+        const int ci = it * NW + wave;  // = m * WRI + i
+        if (ci < 16 * G::WRI) {
+          const int m = ci / G::WRI, i = ci - m * G::WRI;
+          const int q = 64 * i + lane;
+          const bool ok = m < a.Coutg;
+          if (q < G::WQ) lds_dma_f32x4(ok ? wg + m * G::WROW + 4 * q : kZeroWord, wsh + m * G::WLD + 256 * i);
+        }
+      }
+    } else {
+      // Copy j moves float j of the contiguous [16][WROW] block.
+#pragma unroll
+      for (int i = 0; i < G::W_INSTR; i++) {
+        const int j0 = (i * NW + wave) * 64;
+        const int j = j0 + lane;
+        if (j < G::WCH) {
+          const bool ok = j / G::WROW < a.Coutg;
+          lds_dma_f32(ok ? wg + j : kZeroWord, wsh + j0);
+        }
       }
     }
   }
@@ -859,7 +878,7 @@ __global__ __launch_bounds__(64 * NW) void conv_tap_split_kernel(ConvArgs a) {
 
   {
     const char* bb = reinterpret_cast<const char*>(smem);
-    const float* wl = wsh + li * G::WROW + c * G::KVOL + kg;  // A[m = li][k = 4s + kg] at wl[4s]
+    const float* wl = wsh + li * G::WLD + c * G::KVOL + kg;  // A[m = li][k = 4s + kg] at wl[4s]
     // Operands of step s+1 are read while the matrix core works on step s. The
     // reduction indices past the channel's kernel volume (last step) take a zero
     // weight: what lies there in LDS belongs to the next channel.

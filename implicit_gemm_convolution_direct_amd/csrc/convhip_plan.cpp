@@ -121,7 +121,7 @@ static bool plan_split(const Geom& g, const SplitSpecDesc& d, ConvPlan* p) {
   const int64_t kvol = int64_t(d.KD) * d.KH * d.KW;
   const int64_t rows = (g.O[1] - 1) * g.S[1] + (g.K[1] - 1) * g.Dl[1] + 1;
   const int64_t bw = ((g.O[2] - 1) * g.S[2] + (g.K[2] - 1) * g.Dl[2]) / d.F + 1;
-  if (rows != d.ROWS || bw != d.BW) return false;
+  if (rows != d.ROWS || bw > d.BW) return false;  // rows may be staged wider (bank spread)
   if (g.N * g.O[0] > std::numeric_limits<int32_t>::max() || g.G > 65535) return false;
   ConvPlan q;
   q.cfg = -1;
@@ -134,13 +134,15 @@ static bool plan_split(const Geom& g, const SplitSpecDesc& d, ConvPlan* p) {
   q.kc_pad = int((kvol + 3) / 4 * 4);
   q.kdspan = d.KD;
   q.rows = int(rows);
-  q.bw = int(bw);
-  q.boxc = int(d.KD * rows * bw);
+  q.bw = d.BW;
+  q.boxc = int(d.KD * rows * d.BW);
   q.tiles_per_plane = 1;
   q.ctiles = 1;
   q.nchunks = 1;
   const int64_t xsw = (int64_t(q.boxc) + 3) / 4 * 4;
-  const int64_t wsh = (16 * d.NW * kvol + 4 + 3) / 4 * 4;
+  const int64_t wrow = d.NW * kvol;
+  const int64_t wld = (wrow % 4 == 0 && (wrow / 4) % 2 == 0) ? wrow + 4 : wrow;
+  const int64_t wsh = (16 * wld + 4 + 3) / 4 * 4;
   q.lds_bytes = 4 * std::max<int64_t>(wsh + int64_t(d.NW) * xsw, int64_t(d.NW) * d.NT * 4 * 64);
   if (q.lds_bytes > kLdsLimit) return false;
   q.grid[0] = g.N * g.O[0];

@@ -99,7 +99,7 @@ struct ConvPlan {
 // F-th input column; ROWS input rows and BW kept columns per plane.
 #define CONVHIP_SPLIT_SPECS(X)                                                     \
   /* Conv3d 16->32, groups 2, kernel 3x5x7, stride (1,2,2), dilation (1,1,2) */  \
-  X(0, 13, 8, 3, 5, 7, 1, 1, 2, 2, 35, 19)                                        \
+  X(0, 13, 8, 3, 5, 7, 1, 1, 2, 2, 35, 20)                                        \
   /* Conv3d 3->8, kernel 3x3x3 on 16^3 */                                         \
   X(1, 13, 3, 3, 3, 3, 1, 1, 1, 1, 16, 16)
 
