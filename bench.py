@@ -12,7 +12,8 @@ back-to-back calls between two device synchronisations, timed with events on
 the stream the kernels are launched on.
 
 Prints one JSON line. Throughput = 2 * MACs / time (MACs count every kernel
-tap, padded ones included). Roofline fractions use MI355X's published peaks:
+tap, padded ones included). Each workload also reports the median of single
+launches after a 512 MiB write that evicts L2 and the MALL (ms_cold_median). Roofline fractions use MI355X's published peaks:
 fp32 matrix 157.3 TFLOP/s, HBM 8.0 TB/s.
 """
 import argparse
@@ -99,7 +100,7 @@ def make_device_inputs(name, torch, ch, synth):
     return cfg, x, w, b
 
 
-def time_workload(name, steps, warmup, torch, ch, synth):
+def time_workload(name, steps, warmup, torch, ch, synth, flush=None):
     cfg, x, w, b = make_device_inputs(name, torch, ch, synth)
     out, macs, nbytes, conv_elems, y_elems = geometry(cfg)
     args = (cfg["stride"], cfg["dilation"], cfg["padding"], cfg["groups"])
@@ -132,6 +133,17 @@ def time_workload(name, steps, warmup, torch, ch, synth):
         z.record(stream)
         torch.cuda.synchronize()
         singles.append(a.elapsed_time(z))
+    # Cold caches: a 512 MiB write (more than L2 + MALL) before each timed launch.
+    colds = []
+    if flush is not None:
+        for _ in range(min(steps, 10)):
+            flush.fill_(1.0)
+            a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            call()
+            z.record(stream)
+            torch.cuda.synchronize()
+            colds.append(a.elapsed_time(z))
     tflops = 2.0 * macs / (ms * 1e-3) / 1e12
     gbs = nbytes / (ms * 1e-3) / 1e9
     rec = {
@@ -140,6 +152,7 @@ def time_workload(name, steps, warmup, torch, ch, synth):
         "ms": round(ms, 5),
         "ms_single_min": round(min(singles), 5),
         "ms_single_max": round(max(singles), 5),
+        "ms_cold_median": round(float(np.median(colds)), 5) if colds else None,
         "tflops": round(tflops, 3),
         "gbs": round(gbs, 1),
         "frac_fp32_peak": round(tflops / PEAK_FP32_TFLOPS, 4),
@@ -221,12 +234,14 @@ def main():
     names = [args.only] if args.only else ORDER
     shapes = {}
     head = None
+    flush = torch.empty(128 << 20, dtype=torch.float32, device="cuda:0")
     for name in names:
         print(f"[bench] timing {name}", file=sys.stderr, flush=True)
-        rec, macs = time_workload(name, args.steps, args.warmup, torch, ch, synth)
+        rec, macs = time_workload(name, args.steps, args.warmup, torch, ch, synth, flush=flush)
         shapes[name] = rec
         print(f"[bench] {name}: {rec['ms']:.4f} ms  {rec['tflops']:.2f} TFLOP/s  "
-              f"({100 * rec['frac_fp32_peak']:.1f}% of fp32 peak)", file=sys.stderr, flush=True)
+              f"({100 * rec['frac_fp32_peak']:.1f}% of fp32 peak); cold caches {rec['ms_cold_median']} ms",
+              file=sys.stderr, flush=True)
     if args.only:
         head = shapes[args.only]
         head_name = args.only
