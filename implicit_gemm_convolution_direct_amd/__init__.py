@@ -115,7 +115,7 @@ def plan_describe(x_shape, w_shape, stride=1, dilation=1, padding=0, groups=1, f
 def _check_tensor(t, name):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if t.device.type != "cuda":
+    if not t.is_cuda:
         raise ValueError(f"{name} must be on the GPU (got {t.device}); there is no CPU path")
     if t.dtype != torch.float32:
         raise TypeError(f"{name} must be float32 (got {t.dtype})")
@@ -123,12 +123,43 @@ def _check_tensor(t, name):
         raise ValueError(f"{name} must be contiguous")
 
 
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream_handle(device):
+    """The caller's current stream on `device` (torch's), as the C ABI's stream handle."""
+    if _raw_stream is not None:
+        return ctypes.c_void_p(_raw_stream(device.index if device.index is not None else torch.cuda.current_device()))
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+# Marshalled shape/parameter arguments per call signature (the arrays are only
+# read by the library during the call, so they can be reused).
+_ARGS_CACHE = {}
+
+
+def _conv_args(x_shape, w_shape, stride, dilation, padding, drop_axis=None):
+    key = (x_shape, w_shape, stride if isinstance(stride, int) else tuple(stride),
+           dilation if isinstance(dilation, int) else tuple(dilation),
+           padding if isinstance(padding, int) else tuple(padding), drop_axis)
+    hit = _ARGS_CACHE.get(key)
+    if hit is not None:
+        return hit
+    nd = len(x_shape) - 2
+    s, d, p = _vec(stride, nd, "stride"), _vec(dilation, nd, "dilation"), _vec(padding, nd, "padding")
+    rc, o = out_shape(list(x_shape[2:]), list(w_shape[2:]), s, d, p)
+    if rc != CONV_OK:
+        raise ConvError(rc, "conv_out_shape")
+    keep = o if drop_axis is None else [o[a] for a in range(nd) if a != drop_axis]
+    val = (nd, _i64(x_shape), _i64(w_shape), _i32(s), _i32(d), _i32(p), (x_shape[0], w_shape[0], *keep))
+    if len(_ARGS_CACHE) > 256:
+        _ARGS_CACHE.clear()
+    _ARGS_CACHE[key] = val
+    return val
+
+
 def conv_fwd(x, w, bias=None, stride=1, dilation=1, padding=0, groups=1, out=None):
-    """y = Conv{1,3}d(x, w, bias) with zero padding; x [N,C,L] or [N,C,D,H,W] fp32 on the GPU."""
+    """y = Conv{1,2,3}d(x, w, bias) with zero padding; x [N,C,L], [N,C,H,W] or [N,C,D,H,W] fp32 on the GPU."""
     _check_tensor(x, "x")
     _check_tensor(w, "w")
     if bias is not None:
@@ -136,21 +167,15 @@ def conv_fwd(x, w, bias=None, stride=1, dilation=1, padding=0, groups=1, out=Non
     nd = x.dim() - 2
     if nd not in (1, 2, 3) or w.dim() != x.dim():
         raise ValueError("x and w must both be 3-D (Conv1d), 4-D (Conv2d) or 5-D (Conv3d)")
-    stride, dilation, padding = (_vec(stride, nd, "stride"), _vec(dilation, nd, "dilation"),
-                                 _vec(padding, nd, "padding"))
-    rc, o = out_shape(list(x.shape[2:]), list(w.shape[2:]), stride, dilation, padding)
-    if rc != CONV_OK:
-        raise ConvError(rc, "conv_out_shape")
-    shape = (x.shape[0], w.shape[0], *o)
+    nd, xs, ws, s, d, p, shape = _conv_args(tuple(x.shape), tuple(w.shape), stride, dilation, padding)
     if out is None:
         out = torch.empty(shape, dtype=torch.float32, device=x.device)
     else:
         _check_tensor(out, "out")
         if tuple(out.shape) != shape:
             raise ValueError(f"out has shape {tuple(out.shape)}, expected {shape}")
-    rc = lib().conv_fwd(nd, x.data_ptr(), _i64(x.shape), w.data_ptr(), _i64(w.shape),
-                        bias.data_ptr() if bias is not None else None, _i32(stride), _i32(dilation),
-                        _i32(padding), int(groups), out.data_ptr(), _stream_handle(x.device))
+    rc = lib().conv_fwd(nd, x.data_ptr(), xs, w.data_ptr(), ws, bias.data_ptr() if bias is not None else None,
+                        s, d, p, int(groups), out.data_ptr(), _stream_handle(x.device))
     if rc != CONV_OK:
         raise ConvError(rc, "conv_fwd")
     return out
@@ -164,24 +189,18 @@ def conv3d_min_softmax(x, w, bias=None, stride=1, dilation=1, padding=0, groups=
         _check_tensor(bias, "bias")
     if x.dim() != 5 or w.dim() != 5:
         raise ValueError("x and w must be 5-D")
-    stride, dilation, padding = _vec(stride, 3, "stride"), _vec(dilation, 3, "dilation"), _vec(padding, 3, "padding")
-    rc, o = out_shape(list(x.shape[2:]), list(w.shape[2:]), stride, dilation, padding)
-    if rc != CONV_OK:
-        raise ConvError(rc, "conv_out_shape")
     if min_dim not in (2, 3, 4):
         raise ValueError("min_dim must be 2, 3 or 4")
-    keep = [o[a] for a in range(3) if a != min_dim - 2]
-    shape = (x.shape[0], w.shape[0], *keep)
+    _, xs, ws, s, d, p, shape = _conv_args(tuple(x.shape), tuple(w.shape), stride, dilation, padding,
+                                           drop_axis=min_dim - 2)
     if out is None:
         out = torch.empty(shape, dtype=torch.float32, device=x.device)
     else:
         _check_tensor(out, "out")
         if tuple(out.shape) != shape:
             raise ValueError(f"out has shape {tuple(out.shape)}, expected {shape}")
-    rc = lib().conv3d_min_softmax(x.data_ptr(), _i64(x.shape), w.data_ptr(), _i64(w.shape),
-                                  bias.data_ptr() if bias is not None else None, _i32(stride), _i32(dilation),
-                                  _i32(padding), int(groups), int(min_dim), out.data_ptr(),
-                                  _stream_handle(x.device))
+    rc = lib().conv3d_min_softmax(x.data_ptr(), xs, w.data_ptr(), ws, bias.data_ptr() if bias is not None else None,
+                                  s, d, p, int(groups), int(min_dim), out.data_ptr(), _stream_handle(x.device))
     if rc != CONV_OK:
         raise ConvError(rc, "conv3d_min_softmax")
     return out
