@@ -845,11 +845,11 @@ __global__ __launch_bounds__(64 * NW) void conv_tap_split_kernel(ConvArgs a) {
   };
 #pragma unroll
   for (int i = 0; i < G::PLANE_INSTR; i++) stage_copy(0, i);
-  // Output positions of the plane (whole plane, flattened (oh, ow)).
+  // Output positions: tiles blockIdx.z*NT .. of the plane (flattened (oh, ow)).
   int noff[NT], pidx[NT];
 #pragma unroll
   for (int ni = 0; ni < NT; ni++) {
-    const int p = 16 * ni + li;
+    const int p = 16 * (int(blockIdx.z) * NT + ni) + li;
     const int oh = p / a.O2, ow = p - (p / a.O2) * a.O2;
     const bool valid = p < a.plane_out;
     noff[ni] = valid ? oh * a.S1 * G::BWC + ow * (a.S2 / G::FF) : 0;
@@ -1456,14 +1456,15 @@ static int launch_tap(const ConvArgs& args, const ConvPlan& p, hipStream_t strea
 template <int NT, int NW, int KD, int KH, int KW, int DD, int DH, int DW, int F, int ROWS, int BW>
 static int launch_split(const ConvArgs& args, const ConvPlan& p, hipStream_t stream) {
   using G = SplitGeo<KD, KH, KW, DD, DH, DW, F, ROWS, BW, NW>;
-  hipLaunchKernelGGL((conv_tap_split_kernel<NT, NW, G>), dim3(unsigned(p.grid[0]), unsigned(p.grid[1]), 1),
+  hipLaunchKernelGGL((conv_tap_split_kernel<NT, NW, G>),
+                     dim3(unsigned(p.grid[0]), unsigned(p.grid[1]), unsigned(p.grid[2])),
                      dim3(64 * NW), 0, stream, args);
   return hipGetLastError() == hipSuccess ? CONV_OK : CONV_ERR_HIP;
 }
 
 static int launch_split_spec(const ConvArgs& args, const ConvPlan& p, hipStream_t stream) {
   switch (p.split_spec) {
-#define CONVHIP_SPLIT_CASE(id, NT, NW, KD, KH, KW, DD, DH, DW, F, ROWS, BW) \
+#define CONVHIP_SPLIT_CASE(id, NT, NW, KD, KH, KW, DD, DH, DW, F, ROWS, BW, TS) \
   case id:                                                                  \
     return launch_split<NT, NW, KD, KH, KW, DD, DH, DW, F, ROWS, BW>(args, p, stream);
     CONVHIP_SPLIT_SPECS(CONVHIP_SPLIT_CASE)

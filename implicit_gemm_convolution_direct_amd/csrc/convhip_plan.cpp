@@ -104,8 +104,8 @@ const TapSpecDesc* tap_specs(int* count) {
 }
 
 const SplitSpecDesc* split_specs(int* count) {
-#define CONVHIP_SPLIT_DESC(id, NT, NW, KD, KH, KW, DD, DH, DW, F, ROWS, BW) \
-  {id, NT, NW, KD, KH, KW, DD, DH, DW, F, ROWS, BW},
+#define CONVHIP_SPLIT_DESC(id, NT, NW, KD, KH, KW, DD, DH, DW, F, ROWS, BW, TS) \
+  {id, NT, NW, KD, KH, KW, DD, DH, DW, F, ROWS, BW, TS},
   static const SplitSpecDesc specs[] = {CONVHIP_SPLIT_SPECS(CONVHIP_SPLIT_DESC)};
 #undef CONVHIP_SPLIT_DESC
   *count = int(sizeof(specs) / sizeof(specs[0]));
@@ -117,7 +117,8 @@ static bool plan_split(const Geom& g, const SplitSpecDesc& d, ConvPlan* p) {
   if (g.K[0] != d.KD || g.K[1] != d.KH || g.K[2] != d.KW) return false;
   if (g.Dl[0] != d.DD || g.Dl[1] != d.DH || g.Dl[2] != d.DW) return false;
   if (g.S[2] % d.F != 0 || g.Dl[2] % d.F != 0) return false;
-  if (g.plane_out() > 16 * d.NT || g.plane_out() <= 16 * (d.NT - 1)) return false;
+  // The plane's 16-position tiles fill TS groups of NT (the last group partly).
+  if (g.plane_out() > 16 * d.NT * d.TS || g.plane_out() <= 16 * (d.NT * d.TS - d.NT)) return false;
   const int64_t kvol = int64_t(d.KD) * d.KH * d.KW;
   const int64_t rows = (g.O[1] - 1) * g.S[1] + (g.K[1] - 1) * g.Dl[1] + 1;
   const int64_t bw = ((g.O[2] - 1) * g.S[2] + (g.K[2] - 1) * g.Dl[2]) / d.F + 1;
@@ -147,7 +148,7 @@ static bool plan_split(const Geom& g, const SplitSpecDesc& d, ConvPlan* p) {
   if (q.lds_bytes > kLdsLimit) return false;
   q.grid[0] = g.N * g.O[0];
   q.grid[1] = g.G;
-  q.grid[2] = 1;
+  q.grid[2] = d.TS;
   *p = q;
   return true;
 }

@@ -94,17 +94,18 @@ struct ConvPlan {
   X(1, 4, 4, 2, 4, 8, 1, 1, 3, 1, 1, 4, 8, 1, 1, 776)
 
 // Build-time specialisations of the channel-split kernel (one input channel per
-// wave, whole (n, od) plane per workgroup, <= 16 output channels per group).
-// X(id, NT, NW, KD, KH, KW, DD, DH, DW, F, ROWS, BW): the staged box keeps every
-// F-th input column; ROWS input rows and BW kept columns per plane.
+// wave, <= 16 output channels per group).
+// X(id, NT, NW, KD, KH, KW, DD, DH, DW, F, ROWS, BW, TS): the staged box keeps
+// every F-th input column, ROWS input rows and BW kept columns per plane; each
+// (n, od) output plane is split into TS workgroups of NT 16-position tiles.
 #define CONVHIP_SPLIT_SPECS(X)                                                     \
   /* Conv3d 16->32, groups 2, kernel 3x5x7, stride (1,2,2), dilation (1,1,2) */  \
-  X(0, 13, 8, 3, 5, 7, 1, 1, 2, 2, 35, 20)                                        \
-  /* Conv3d 3->8, kernel 3x3x3 on 16^3 */                                         \
-  X(1, 13, 3, 3, 3, 3, 1, 1, 1, 1, 16, 16)
+  X(0, 13, 8, 3, 5, 7, 1, 1, 2, 2, 35, 20, 1)                                     \
+  /* Conv3d 3->8, kernel 3x3x3 on 16^3: 4 workgroups per plane */                \
+  X(1, 4, 3, 3, 3, 3, 1, 1, 1, 1, 16, 16, 4)
 
 struct SplitSpecDesc {
-  int id, NT, NW, KD, KH, KW, DD, DH, DW, F, ROWS, BW;
+  int id, NT, NW, KD, KH, KW, DD, DH, DW, F, ROWS, BW, TS;
 };
 const SplitSpecDesc* split_specs(int* count);
 
