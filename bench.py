@@ -7,9 +7,10 @@ headline workload, the general-parameter Conv3d (x[4,16,32,32,32], w[32,8,3,5,7]
 groups 2, stride (1,2,2), padding (1,2,3), dilation (1,1,2)). The same run also
 times every other workload (tiny Conv3d, fused Conv3d+min+softmax, asymmetric
 Conv3d, long Conv1d) and reports them under "shapes". Inputs are seeded
-synthetic tensors already resident in device memory; the timed region is K
-back-to-back calls between two device synchronisations, timed with events on
-the stream the kernels are launched on.
+synthetic tensors already resident in device memory; each workload is first run
+back to back for at least 0.5 s (the GPU's clocks ramp up from idle over
+that time), then the timed region is K back-to-back calls between two device
+synchronisations, timed with events on the stream the kernels are launched on.
 
 Prints one JSON line. Throughput = 2 * MACs / time (MACs count every kernel
 tap, padded ones included). Each workload also reports the median of single
@@ -30,6 +31,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_FP32_TFLOPS = 157.3
+WARM_S = 0.5  # seconds of warm-up calls per workload
 PEAK_HBM_GBS = 8000.0
 HEADLINE = "general_conv3d"
 ORDER = ["tiny_conv3d", "general_conv3d", "conv3d_min_softmax", "asym_conv3d", "long_conv1d"]
@@ -110,8 +112,15 @@ def time_workload(name, steps, warmup, torch, ch, synth, flush=None):
     else:
         y = torch.empty((cfg["x"][0], cfg["w"][0], *out), dtype=torch.float32, device=x.device)
         call = lambda: ch.conv_fwd(x, w, b, *args, out=y)
-    for _ in range(warmup):
-        call()
+    # Warm-up: at least `warmup` calls and WARM_S seconds of back-to-back calls, so
+    # the GPU's clocks have left their idle state before the timed region.
+    t_w = time.perf_counter()
+    done = 0
+    while done < warmup or time.perf_counter() - t_w < WARM_S:
+        for _ in range(8):
+            call()
+        done += 8
+        torch.cuda.synchronize()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     e0 = torch.cuda.Event(enable_timing=True)

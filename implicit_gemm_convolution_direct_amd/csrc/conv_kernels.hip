@@ -38,6 +38,7 @@
 namespace convhip {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 
 // f(integral_constant<int, 0>) ... f(integral_constant<int, N-1>): loops whose
 // index must be a compile-time constant (immediate offsets, register indices).
@@ -1174,7 +1175,14 @@ struct StreamGeo {
   static constexpr int KVOL = KD * KHW;
   static constexpr int KRED = CIN * KVOL;
   static constexpr int NT = CIN * KHW;           // staged values read per plane
-  static constexpr int NPAIR = NG * KRED;        // (channel group, reduction index) pairs
+  // With 16 or more output channels, channels 0..15 run on the 16x16x1 4-block
+  // form (A broadcast from one block: one instruction per input value) and the
+  // rest on the 4x4x1 16-block form; else every channel on the 4x4x1 form.
+  static constexpr bool MIX = NG >= 4;
+  static constexpr int NA16 = (KRED + 3) / 4;     // 16x16 weights: register j holds k = 4j .. 4j+3
+  static constexpr int NG4 = MIX ? NG - 4 : NG;   // 4-channel groups on the 4x4x1 form
+  static constexpr int CO4 = MIX ? 16 : 0;        // their first channel
+  static constexpr int NPAIR = NG4 * KRED;        // (channel group, reduction index) pairs
   static constexpr int NAREG = (NPAIR + 15) / 16;
   static constexpr int WAVES = 4;                // waves per workgroup
   static constexpr int LDS_FLOATS = WAVES * NSLOT * SLOT;
@@ -1219,14 +1227,24 @@ __global__ __launch_bounds__(256, 4) void fused_stream_kernel(StreamArgs a) {
   const int od1 = live ? min(a.O0, od0 + a.ods) : od0;
   float* ring = smem + wave * (G::NSLOT * G::SLOT);
 
-  // Weights: register r, lane 4b + i holds w[4g + i][k] for pair 16r + b = g * KRED + k.
+  // Weights of the 4x4x1 form: register r, lane 4b + i holds w[CO4 + 4g + i][k]
+  // for pair 16r + b = g * KRED + k.
   float aw[G::NAREG];
 #pragma unroll
   for (int r = 0; r < G::NAREG; r++) {
     const int pair = 16 * r + (lane >> 2);
     const int gq = pair / G::KRED, k = pair - gq * G::KRED;
-    const int co = 4 * gq + (lane & 3);
+    const int co = G::CO4 + 4 * gq + (lane & 3);
     aw[r] = (live && pair < G::NPAIR && co < a.Cout) ? a.w[co * G::KRED + k] : 0.0f;
+  }
+  // Weights of the 16x16x1 form: register j, lane 16b + m holds w[m][4j + b].
+  float a16[G::MIX ? G::NA16 : 1];
+  if constexpr (G::MIX) {
+#pragma unroll
+    for (int j = 0; j < G::NA16; j++) {
+      const int k = 4 * j + (lane >> 4), m = lane & 15;
+      a16[j] = (live && k < G::KRED && m < a.Cout) ? a.w[m * G::KRED + k] : 0.0f;
+    }
   }
 
   // Copy sources: copy i, lane l moves 16-byte chunk e = 64i + l = (c, row, q) of
@@ -1304,7 +1322,8 @@ __global__ __launch_bounds__(256, 4) void fused_stream_kernel(StreamArgs a) {
       });
     };
     load_group(std::integral_constant<int, 0>{}, bv[0]);
-    v4f acc[NG];
+    v4f acc[G::NG4];
+    v16f acc16;
     static_for<NGRP>([&](auto GG) {
       constexpr int g = decltype(GG)::value;
       constexpr int kd = g / G::CIN_, c = g % G::CIN_;
@@ -1316,7 +1335,13 @@ __global__ __launch_bounds__(256, 4) void fused_stream_kernel(StreamArgs a) {
       static_for<G::KHW>([&](auto HH) {
         constexpr int hw = decltype(HH)::value;
         constexpr int k = c * G::KVOL + kd * G::KHW + hw;
-        static_for<NG>([&](auto QQ) {
+        if constexpr (G::MIX) {
+          if constexpr (g == 0 && hw == 0)
+            acc16 = __builtin_amdgcn_mfma_f32_16x16x1f32(a16[k / 4], bv[cur][hw], v16f{}, 2, k % 4, 0);
+          else
+            acc16 = __builtin_amdgcn_mfma_f32_16x16x1f32(a16[k / 4], bv[cur][hw], acc16, 2, k % 4, 0);
+        }
+        static_for<G::NG4>([&](auto QQ) {
           constexpr int q = decltype(QQ)::value;
           constexpr int pair = q * G::KRED + k;
           constexpr int r = pair / 16, ab = pair % 16;
@@ -1330,10 +1355,18 @@ __global__ __launch_bounds__(256, 4) void fused_stream_kernel(StreamArgs a) {
     });
     // Running minimum as compare-and-select: a NaN product is dropped, as fminf
     // drops it, without fminf's operand canonicalisation.
+    // mn[q], q < 4 (16x16x1 form): registers 4q .. 4q+3 of its output, lane l
+    // holding channel 4(l/16) + i of position 16q + l%16; mn[q] otherwise: the
+    // 4x4x1 form, lane l holding channel 4q + i of position l.
 #pragma unroll
     for (int q = 0; q < NG; q++)
 #pragma unroll
-      for (int i = 0; i < 4; i++) mn[q][i] = acc[q][i] < mn[q][i] ? acc[q][i] : mn[q][i];
+      for (int i = 0; i < 4; i++) {
+        float v;
+        if constexpr (G::MIX) v = q < 4 ? acc16[4 * q + i] : acc[q < 4 ? 0 : q - 4][i];
+        else v = acc[q][i];
+        mn[q][i] = v < mn[q][i] ? v : mn[q][i];
+      }
   }
 
   float* yp = a.y + int64_t(n) * a.Cout * a.plane_out + p;
@@ -1360,19 +1393,40 @@ __global__ __launch_bounds__(256, 4) void fused_stream_kernel(StreamArgs a) {
         }
   }
 
+  // Channels 0..15 of the 16x16x1 form: through LDS to the lane of their
+  // position. The region lies past the partial-minimum slots and is this
+  // wave's own (every copy into the rings has landed).
+  float m[4 * NG];
+  if constexpr (G::MIX) {
+    if (a.dsplit == 1) wait_vmem_le<0>();
+    float* xch = a.dsplit > 1 ? smem + 4 * NG * 64 * G::WAVES + (wave / a.dsplit) * 1024 : ring;
+#pragma unroll
+    for (int q = 0; q < 4; q++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) xch[(4 * (lane >> 4) + i) * 64 + 16 * q + (lane & 15)] = mn[q][i];
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the wave's writes are done
+#pragma unroll
+    for (int c = 0; c < 16; c++) m[c] = xch[c * 64 + lane];
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4 && q < NG; q++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) m[4 * q + i] = mn[q][i];
+  }
+#pragma unroll
+  for (int q = 4; q < NG; q++)
+#pragma unroll
+    for (int i = 0; i < 4; i++) m[4 * q + i] = mn[q][i];
+
   // Softmax over the channels of this lane's position. fp32 addition is
   // monotone, so adding the bias after the minimum equals adding it before.
   if (valid) {
-    float m[4 * NG];
     float mx = -INFINITY;
 #pragma unroll
-    for (int q = 0; q < NG; q++)
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const int c = 4 * q + i;
-        m[c] = c < a.Cout ? mn[q][i] + (a.bias ? a.bias[c] : 0.0f) : -INFINITY;
-        mx = fmaxf(mx, m[c]);
-      }
+    for (int c = 0; c < 4 * NG; c++) {
+      m[c] = c < a.Cout ? m[c] + (a.bias ? a.bias[c] : 0.0f) : -INFINITY;
+      mx = fmaxf(mx, m[c]);
+    }
     float sum = 0.0f;
 #pragma unroll
     for (int c = 0; c < 4 * NG; c++) {
