@@ -31,7 +31,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_FP32_TFLOPS = 157.3
-WARM_S = 0.5  # seconds of warm-up calls per workload
+WARM_S = 0.5  # default seconds of warm-up calls per workload (--warm-seconds)
 PEAK_HBM_GBS = 8000.0
 HEADLINE = "general_conv3d"
 ORDER = ["tiny_conv3d", "general_conv3d", "conv3d_min_softmax", "asym_conv3d", "long_conv1d"]
@@ -102,7 +102,7 @@ def make_device_inputs(name, torch, ch, synth):
     return cfg, x, w, b
 
 
-def time_workload(name, steps, warmup, torch, ch, synth, flush=None):
+def time_workload(name, steps, warmup, torch, ch, synth, flush=None, warm_s=WARM_S):
     cfg, x, w, b = make_device_inputs(name, torch, ch, synth)
     out, macs, nbytes, conv_elems, y_elems = geometry(cfg)
     args = (cfg["stride"], cfg["dilation"], cfg["padding"], cfg["groups"])
@@ -116,7 +116,7 @@ def time_workload(name, steps, warmup, torch, ch, synth, flush=None):
     # the GPU's clocks have left their idle state before the timed region.
     t_w = time.perf_counter()
     done = 0
-    while done < warmup or time.perf_counter() - t_w < WARM_S:
+    while done < warmup or time.perf_counter() - t_w < warm_s:
         for _ in range(8):
             call()
         done += 8
@@ -211,6 +211,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--only", choices=ORDER, default=None, help="time one workload only (for profiling)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--warm-seconds", type=float, default=WARM_S,
+                    help="minimum seconds of back-to-back warm-up calls per workload")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device-to-device copy of this many bytes per step "
                          "(calibrates rocprofv3's FETCH_SIZE / WRITE_SIZE against a known traffic)")
@@ -246,7 +248,8 @@ def main():
     flush = torch.empty(128 << 20, dtype=torch.float32, device="cuda:0")
     for name in names:
         print(f"[bench] timing {name}", file=sys.stderr, flush=True)
-        rec, macs = time_workload(name, args.steps, args.warmup, torch, ch, synth, flush=flush)
+        rec, macs = time_workload(name, args.steps, args.warmup, torch, ch, synth, flush=flush,
+                                  warm_s=args.warm_seconds)
         shapes[name] = rec
         print(f"[bench] {name}: {rec['ms']:.4f} ms  {rec['tflops']:.2f} TFLOP/s  "
               f"({100 * rec['frac_fp32_peak']:.1f}% of fp32 peak); cold caches {rec['ms_cold_median']} ms",
