@@ -847,14 +847,12 @@ __global__ __launch_bounds__(64 * NW) void conv_tap_split_kernel(ConvArgs a) {
 #pragma unroll
   for (int i = 0; i < G::PLANE_INSTR; i++) stage_copy(0, i);
   // Output positions: tiles blockIdx.z*NT .. of the plane (flattened (oh, ow)).
-  int noff[NT], pidx[NT];
+  int noff[NT];
 #pragma unroll
   for (int ni = 0; ni < NT; ni++) {
     const int p = 16 * (int(blockIdx.z) * NT + ni) + li;
     const int oh = p / a.O2, ow = p - (p / a.O2) * a.O2;
-    const bool valid = p < a.plane_out;
-    noff[ni] = valid ? oh * a.S1 * G::BWC + ow * (a.S2 / G::FF) : 0;
-    pidx[ni] = valid ? p : -1;
+    noff[ni] = p < a.plane_out ? oh * a.S1 * G::BWC + ow * (a.S2 / G::FF) : 0;
   }
   int dpat[NP];
   fill_pat_deltas<G>(dpat, kg, std::make_integer_sequence<int, NP>{});
@@ -930,22 +928,29 @@ __global__ __launch_bounds__(64 * NW) void conv_tap_split_kernel(ConvArgs a) {
 #pragma unroll
     for (int r = 0; r < 4; r++) smem[((wave * NT + ni) * 4 + r) * 64 + lane] = acc[ni][r];
   __syncthreads();
+  // All of this wave's partial reads are issued before the sums and stores.
   const int64_t out_plane = int64_t(a.O1) * a.O2;
-  for (int pr = wave; pr < NT * 4; pr += NW) {
+  constexpr int NPR = (NT * 4 + NW - 1) / NW;  // (tile, register) pairs per wave
+  float part[NPR][NW];
+#pragma unroll
+  for (int j = 0; j < NPR; j++) {
+    const int pr = wave + NW * j;
+#pragma unroll
+    for (int w2 = 0; w2 < NW; w2++)
+      part[j][w2] = pr < NT * 4 ? smem[((w2 * NT + (pr >> 2)) * 4 + (pr & 3)) * 64 + lane] : 0.0f;
+  }
+  float* yg = a.y + (int64_t(n) * a.Cout + int64_t(g) * a.Coutg) * a.O0 * out_plane + int64_t(od) * out_plane;
+#pragma unroll
+  for (int j = 0; j < NPR; j++) {
+    const int pr = wave + NW * j;
     const int ni = pr >> 2, r = pr & 3;
     float v = 0.0f;
 #pragma unroll
-    for (int w2 = 0; w2 < NW; w2++) v += smem[((w2 * NT + ni) * 4 + r) * 64 + lane];
+    for (int w2 = 0; w2 < NW; w2++) v += part[j][w2];
     const int ch = 4 * kg + r;
-    int pi = -1;
-#pragma unroll
-    for (int q = 0; q < NT; q++)
-      if (q == ni) pi = pidx[q];
+    const int p = 16 * (int(blockIdx.z) * NT + ni) + li;
     const float b = r == 0 ? b4[0] : r == 1 ? b4[1] : r == 2 ? b4[2] : b4[3];
-    if (ch < a.Coutg && pi >= 0) {
-      const int co = g * a.Coutg + ch;
-      a.y[((int64_t(n) * a.Cout + co) * a.O0 + od) * out_plane + pi] = v + b;
-    }
+    if (pr < NT * 4 && ch < a.Coutg && p < a.plane_out) yg[int64_t(ch) * a.O0 * out_plane + p] = v + b;
   }
 }
 
