@@ -6,7 +6,9 @@ importing works but every call raises.
 
 Operations (POPCORNBENCH "Kimi-K2.6" pages l1_p60, l1_p76, l2_p24, opening turns):
 
-* ``conv_fwd(x, w, bias, stride, dilation, padding, groups)`` -- Conv1d / Conv3d forward.
+* ``conv_fwd(x, w, bias, stride, dilation, padding, groups)`` -- Conv1d / Conv2d / Conv3d forward.
+* ``conv_fwd_channels_last(x, w, ...)`` -- the same on channels-last tensors:
+  x [N, spatial..., C_in] -> y [N, out..., C_out] (w keeps [C_out, C_in/groups, k...]).
 * ``conv3d_min_softmax(x, w, bias, stride, dilation, padding, groups, min_dim=2)`` --
   softmax over channels of the minimum over depth of Conv3d, without writing the
   5-D conv result.
@@ -25,8 +27,8 @@ STATUS_NAMES = {
     -5: "CONV_ERR_PARAM", -6: "CONV_ERR_EMPTY_OUTPUT", -7: "CONV_ERR_UNSUPPORTED", -8: "CONV_ERR_OVERFLOW",
     -9: "CONV_ERR_HIP",
 }
-EXPORTED = ["conv_out_shape", "conv_fwd", "conv3d_min_softmax", "conv_status_string", "conv_plan_describe",
-            "convhip_synth_fill"]
+EXPORTED = ["conv_out_shape", "conv_fwd", "conv_fwd_channels_last", "conv3d_min_softmax", "conv_status_string",
+            "conv_plan_describe", "convhip_synth_fill"]
 
 
 class ConvError(RuntimeError):
@@ -54,6 +56,8 @@ def lib():
         L.conv_out_shape.argtypes = [ctypes.c_int, i64p, i64p, ip, ip, ip, i64p]
         L.conv_fwd.restype = ctypes.c_int
         L.conv_fwd.argtypes = [ctypes.c_int, vp, i64p, vp, i64p, vp, ip, ip, ip, ctypes.c_int, vp, vp]
+        L.conv_fwd_channels_last.restype = ctypes.c_int
+        L.conv_fwd_channels_last.argtypes = [ctypes.c_int, vp, i64p, vp, i64p, vp, ip, ip, ip, ctypes.c_int, vp, vp]
         L.conv3d_min_softmax.restype = ctypes.c_int
         L.conv3d_min_softmax.argtypes = [vp, i64p, vp, i64p, vp, ip, ip, ip, ctypes.c_int, ctypes.c_int, vp, vp]
         L.conv_status_string.restype = ctypes.c_char_p
@@ -101,12 +105,14 @@ def out_shape(in_spatial, k_spatial, stride, dilation, padding):
     return rc, [int(v) for v in out]
 
 
-def plan_describe(x_shape, w_shape, stride=1, dilation=1, padding=0, groups=1, fused=False):
+def plan_describe(x_shape, w_shape, stride=1, dilation=1, padding=0, groups=1, fused=False, channels_last=False):
+    """The library's launch plan; channels_last=True takes x_shape as [N, spatial..., C_in]."""
     nd = len(x_shape) - 2
     buf = ctypes.create_string_buffer(1024)
+    mode = 2 if channels_last else (1 if fused else 0)
     rc = lib().conv_plan_describe(nd, _i64(x_shape), _i64(w_shape), _i32(_vec(stride, nd, "stride")),
                                   _i32(_vec(dilation, nd, "dilation")), _i32(_vec(padding, nd, "padding")),
-                                  int(groups), 1 if fused else 0, buf, 1024)
+                                  int(groups), mode, buf, 1024)
     if rc != CONV_OK:
         raise ConvError(rc, "conv_plan_describe")
     return buf.value.decode()
@@ -178,6 +184,34 @@ def conv_fwd(x, w, bias=None, stride=1, dilation=1, padding=0, groups=1, out=Non
                         s, d, p, int(groups), out.data_ptr(), _stream_handle(x.device))
     if rc != CONV_OK:
         raise ConvError(rc, "conv_fwd")
+    return out
+
+
+def conv_fwd_channels_last(x, w, bias=None, stride=1, dilation=1, padding=0, groups=1, out=None):
+    """Channels-last convolution: x [N, L, C], [N, H, W, C] or [N, D, H, W, C] fp32 on the GPU
+    (contiguous in that order), w [C_out, C_in/groups, k...]; returns y [N, out..., C_out]."""
+    _check_tensor(x, "x")
+    _check_tensor(w, "w")
+    if bias is not None:
+        _check_tensor(bias, "bias")
+    nd = x.dim() - 2
+    if nd not in (1, 2, 3) or w.dim() != x.dim():
+        raise ValueError("x and w must both be 3-D, 4-D or 5-D")
+    xs_cl = tuple(x.shape)
+    logical = (xs_cl[0], xs_cl[-1], *xs_cl[1:-1])
+    nd, _, ws, s, d, p, shape = _conv_args(logical, tuple(w.shape), stride, dilation, padding)
+    shape = (shape[0], *shape[2:], shape[1])
+    if out is None:
+        out = torch.empty(shape, dtype=torch.float32, device=x.device)
+    else:
+        _check_tensor(out, "out")
+        if tuple(out.shape) != shape:
+            raise ValueError(f"out has shape {tuple(out.shape)}, expected {shape}")
+    rc = lib().conv_fwd_channels_last(nd, x.data_ptr(), _i64(xs_cl), w.data_ptr(), ws,
+                                      bias.data_ptr() if bias is not None else None, s, d, p, int(groups),
+                                      out.data_ptr(), _stream_handle(x.device))
+    if rc != CONV_OK:
+        raise ConvError(rc, "conv_fwd_channels_last")
     return out
 
 

@@ -70,6 +70,8 @@ struct ConvArgs {
   int plane_out;
   int nchunks;
   int items;  // persistent kernel: (tile, plane) work items
+  int ccp;        // channels-last box: LDS floats per (plane, row, column) site
+  int vec_store;  // channels-last output: 4 consecutive channels stored as one 16-byte write
 };
 
 // q = n / d and r = n % d for 0 <= n < 2^24, d >= 1, from a float reciprocal
@@ -172,6 +174,9 @@ __device__ __forceinline__ TileGeo tile_geo(const ConvArgs& a, int tile, int pla
 // Offset of every (channel, tap) of a chunk inside a box with rows_ld rows per
 // plane. Padding taps (k >= Cc*kvol) carry zero weights and point at the box
 // start, a staged finite element; entries past kc_pad serve the prefetch.
+// Channels-last boxes (CL) hold the channels of a site contiguously, so a tap
+// moves by whole sites of ccp floats and a channel by one float.
+template <bool CL = false>
 __device__ __forceinline__ void build_koff(const ConvArgs& a, int rows_ld, int* koff, int tid) {
   const int plane_stride = rows_ld * a.bw;
   const int boxc_t = a.kdspan * plane_stride;
@@ -184,7 +189,8 @@ __device__ __forceinline__ void build_koff(const ConvArgs& a, int rows_ld, int* 
       const int r2 = r - td * a.K1 * a.K2;
       const int th = r2 / a.K2;
       const int tw = r2 - th * a.K2;
-      off = c * boxc_t + td * a.D0 * plane_stride + th * a.D1 * a.bw + tw * a.D2;
+      const int site = td * a.D0 * plane_stride + th * a.D1 * a.bw + tw * a.D2;
+      off = CL ? c + site * a.ccp : c * boxc_t + site;
     }
     koff[k] = off;
   }
@@ -225,6 +231,37 @@ __device__ __forceinline__ void stage_box(const ConvArgs& a, const TileGeo& t, i
   }
 }
 
+// Channels-last input x [N, D, H, W, C_in]: copy the box of channels [c0, c0+Cc)
+// of a tile into dst, layout [zd][zr < rows_ld][col][c < ccp]. The LDS slots are
+// walked in order, 64 per copy instruction, so consecutive lanes read the
+// consecutive channels of a site and then the next site along W: runs of Cc
+// contiguous input floats. Slots outside the input (zero padding, channels past
+// the chunk, the pitch padding c >= Cc) read the zero word.
+template <int NWAVES = 4>
+__device__ __forceinline__ void stage_box_cl(const ConvArgs& a, const TileGeo& t, int c0, float* dst, int wave,
+                                             int lane) {
+  const int cc_count = min(a.Cc, a.Cg - c0);
+  const int total = a.kdspan * t.rows_ld * a.bw * a.ccp;
+  const float inv_ccp = 1.0f / float(a.ccp);
+  const float inv_bw = 1.0f / float(a.bw);
+  const float inv_rows = 1.0f / float(t.rows_ld);
+  const float* xn = a.x + int64_t(t.n) * a.L0 * a.L1 * a.L2 * a.Cin + (int64_t(t.g) * a.Cg + c0);
+  for (int r = wave; r * 64 < total; r += NWAVES) {
+    const int s = r * 64 + lane;
+    if (s < total) {
+      int c, col, zr;
+      const int site = divmod_small(s, a.ccp, inv_ccp, c);
+      const int zz = divmod_small(site, a.bw, inv_bw, col);
+      const int zd = divmod_small(zz, t.rows_ld, inv_rows, zr);
+      const int id = t.id0 + zd, ih = t.ih0 + zr, iw = t.iw0 + col;
+      const bool ok = (c < cc_count) && (unsigned(id) < unsigned(a.L0)) && (unsigned(ih) < unsigned(a.L1)) &&
+                      (unsigned(iw) < unsigned(a.L2));
+      const float* src = ok ? xn + ((int64_t(id) * a.L1 + ih) * a.L2 + iw) * a.Cin + c : kZeroWord;
+      lds_dma_f32(src, dst + r * 64);
+    }
+  }
+}
+
 // Copy the weight fragments of channels [c0, c0+Cc) (k-steps 0..nsteps-1 of a
 // chunk) into dst, in the order the matrix core consumes them: for k-step s and
 // wave row wm, lane l holds W[m = wm*16*MT + 16*mi + (l%16)][k = 4s + l/16] for
@@ -254,7 +291,7 @@ __device__ __forceinline__ void stage_wfrag(const ConvArgs& a, int g, int m0, in
 
 // Per-lane output positions of a wave's NT sub-tiles: LDS offset inside the box
 // (row stride bw) and flattened index in the (n, co, od) output plane (-1: none).
-template <int NT>
+template <int NT, bool CL = false>
 __device__ __forceinline__ void tile_positions(const ConvArgs& a, const TileGeo& t, int wn, int li, int noff[NT],
                                                int pidx[NT]) {
 #pragma unroll
@@ -271,7 +308,8 @@ __device__ __forceinline__ void tile_positions(const ConvArgs& a, const TileGeo&
       ow = t.ow0 + q;
       valid = ow < a.O2;
     }
-    noff[ni] = valid ? (oh - t.oh_first) * a.S1 * a.bw + ow * a.S2 - t.iwb : 0;
+    const int site = (oh - t.oh_first) * a.S1 * a.bw + ow * a.S2 - t.iwb;
+    noff[ni] = valid ? (CL ? site * a.ccp : site) : 0;
     pidx[ni] = valid ? oh * a.O2 + ow : -1;
   }
 }
@@ -328,12 +366,35 @@ __device__ __forceinline__ void load_bias(const ConvArgs& a, const TileGeo& t, i
 }
 
 // Store a wave tile (+ bias). D[m][n] of the matrix core sits in lane
-// n + 16*(m/4), register m%4.
-template <int MT, int NT>
+// n + 16*(m/4), register m%4: a lane holds 4 consecutive channels of one
+// position, which channels-last output y [N, D_out, H_out, W_out, C_out] takes
+// as one 16-byte store.
+template <int MT, int NT, bool CL = false>
 __device__ __forceinline__ void store_tile(const ConvArgs& a, const TileGeo& t, int wm, int kg,
                                            const int (&pidx)[NT], const v4f (&acc)[MT][NT],
                                            const float (&bias)[MT][4]) {
   const int64_t out_plane = int64_t(a.O1) * a.O2;
+  if constexpr (CL) {
+    float* yplane = a.y + (int64_t(t.n) * a.O0 + t.od) * out_plane * a.Cout + int64_t(t.g) * a.Coutg;
+#pragma unroll
+    for (int mi = 0; mi < MT; mi++) {
+      const int ch0 = t.m0 + wm * 16 * MT + 16 * mi + 4 * kg;
+#pragma unroll
+      for (int ni = 0; ni < NT; ni++) {
+        if (pidx[ni] < 0 || ch0 >= a.Coutg) continue;
+        float* yp = yplane + int64_t(pidx[ni]) * a.Cout + ch0;
+        if (a.vec_store) {
+          *reinterpret_cast<float4*>(yp) = make_float4(acc[mi][ni][0] + bias[mi][0], acc[mi][ni][1] + bias[mi][1],
+                                                       acc[mi][ni][2] + bias[mi][2], acc[mi][ni][3] + bias[mi][3]);
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; r++)
+            if (ch0 + r < a.Coutg) yp[r] = acc[mi][ni][r] + bias[mi][r];
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int mi = 0; mi < MT; mi++) {
 #pragma unroll
@@ -354,13 +415,14 @@ __device__ __forceinline__ void store_tile(const ConvArgs& a, const TileGeo& t, 
 // into `nxt`, then reduce the chunk in `cur`. The buffers are distinct; the
 // restrict qualifiers let the compiler keep the copies in flight across the
 // reduction instead of waiting for them before every LDS read.
-template <int MT, int NT, int WM, int KS>
+template <int MT, int NT, int WM, int KS, bool CL>
 __device__ __forceinline__ void stream_stage(const ConvArgs& a, const TileGeo& t, bool has_next, int c0_next,
                                              const float* __restrict__ cur, float* __restrict__ nxt,
                                              const int* __restrict__ koff, int nsteps, int ks, int wfrag_base,
                                              const int (&noff)[NT], v4f (&acc)[MT][NT], int kg, int wave, int lane) {
   if (has_next) {
-    stage_box(a, t, c0_next, nxt, wave, lane);
+    if constexpr (CL) stage_box_cl(a, t, c0_next, nxt, wave, lane);
+    else stage_box(a, t, c0_next, nxt, wave, lane);
     stage_wfrag<MT, WM>(a, t.g, t.m0, c0_next, nsteps, nxt + a.xs_floats, wave, lane);
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -372,7 +434,7 @@ __device__ __forceinline__ void stream_stage(const ConvArgs& a, const TileGeo& t
 // (box + weight fragments) are double-buffered in LDS.
 // LDS (floats): [ koff | buffer 0 | buffer 1 ], buffer = [ box | weights ].
 // ---------------------------------------------------------------------------
-template <int MT, int NT, int WM, int WN, int KS>
+template <int MT, int NT, int WM, int WN, int KS, bool CL>
 __global__ __launch_bounds__(256) void conv_mfma16_kernel(ConvArgs a) {
   constexpr int BM = 16 * MT * WM;
   constexpr int BN = 16 * NT * WN;
@@ -393,9 +455,9 @@ __global__ __launch_bounds__(256) void conv_mfma16_kernel(ConvArgs a) {
 
   const TileGeo t = tile_geo(a, blockIdx.x, blockIdx.y, blockIdx.z, BM, BN, false);
   const int nsteps = a.kc_pad >> 2;
-  build_koff(a, t.rows_ld, koff, tid);
+  build_koff<CL>(a, t.rows_ld, koff, tid);
   int noff[NT], pidx[NT];
-  tile_positions<NT>(a, t, wn, li, noff, pidx);
+  tile_positions<NT, CL>(a, t, wn, li, noff, pidx);
   v4f acc[MT][NT];
 #pragma unroll
   for (int mi = 0; mi < MT; mi++)
@@ -405,17 +467,18 @@ __global__ __launch_bounds__(256) void conv_mfma16_kernel(ConvArgs a) {
   float bias[MT][4];
   load_bias<MT>(a, t, wm, kg, bias);
 
-  stage_box(a, t, 0, buf0, wave, lane);
+  if constexpr (CL) stage_box_cl(a, t, 0, buf0, wave, lane);
+  else stage_box(a, t, 0, buf0, wave, lane);
   stage_wfrag<MT, WM>(a, t.g, t.m0, 0, nsteps, buf0 + a.xs_floats, wave, lane);
   wait_vmem();
   __syncthreads();
   for (int ci = 0; ci < a.nchunks; ci++) {
     const bool has_next = ci + 1 < a.nchunks;
     if (ci & 1)
-      stream_stage<MT, NT, WM, KS>(a, t, has_next, (ci + 1) * a.Cc, buf1, buf0, koff, nsteps, ks, wfrag_base,
+      stream_stage<MT, NT, WM, KS, CL>(a, t, has_next, (ci + 1) * a.Cc, buf1, buf0, koff, nsteps, ks, wfrag_base,
                                    noff, acc, kg, wave, lane);
     else
-      stream_stage<MT, NT, WM, KS>(a, t, has_next, (ci + 1) * a.Cc, buf0, buf1, koff, nsteps, ks, wfrag_base,
+      stream_stage<MT, NT, WM, KS, CL>(a, t, has_next, (ci + 1) * a.Cc, buf0, buf1, koff, nsteps, ks, wfrag_base,
                                    noff, acc, kg, wave, lane);
     wait_vmem();       // this thread's copies of the next chunk have landed
     __syncthreads();   // everyone's copies have landed; everyone is done with the current buffer
@@ -447,7 +510,7 @@ __global__ __launch_bounds__(256) void conv_mfma16_kernel(ConvArgs a) {
           for (int r = 0; r < 4; r++) acc[mi][ni][r] += srcp[((mi * NT + ni) * 4 + r) * 64 + lane];
     }
   }
-  store_tile<MT, NT>(a, t, wm, kg, pidx, acc, bias);
+  store_tile<MT, NT, CL>(a, t, wm, kg, pidx, acc, bias);
 }
 
 // ---------------------------------------------------------------------------
@@ -1486,11 +1549,11 @@ static int set_lds_limit_once(Fn fn, std::once_flag& once, hipError_t& err) {
   return err == hipSuccess ? CONV_OK : CONV_ERR_HIP;
 }
 
-template <int MT, int NT, int WM, int WN, int KS>
+template <int MT, int NT, int WM, int WN, int KS, bool CL = false>
 static int launch_conv_cfg(const ConvArgs& args, const ConvPlan& p, hipStream_t stream) {
   static std::once_flag once;
   static hipError_t err = hipSuccess;
-  auto fn = conv_mfma16_kernel<MT, NT, WM, WN, KS>;
+  auto fn = conv_mfma16_kernel<MT, NT, WM, WN, KS, CL>;
   if (set_lds_limit_once(fn, once, err) != CONV_OK) return CONV_ERR_HIP;
   dim3 grid(unsigned(p.grid[0]), unsigned(p.grid[1]), unsigned(p.grid[2]));
   hipLaunchKernelGGL(fn, grid, dim3(256), size_t(p.lds_bytes), stream, args);
@@ -1577,6 +1640,21 @@ static int launch_stream_spec(const StreamArgs& args, const FusedPlan& p, hipStr
   }
 }
 
+// The generic implicit-GEMM kernel in the plan's tile configuration.
+template <bool CL>
+static int launch_generic(const ConvArgs& a, const ConvPlan& p, hipStream_t s) {
+  switch (p.cfg) {
+    case CFG_M64: return launch_conv_cfg<4, 4, 1, 4, 1, CL>(a, p, s);
+    case CFG_M128: return launch_conv_cfg<4, 4, 2, 2, 1, CL>(a, p, s);
+    case CFG_M32: return launch_conv_cfg<2, 4, 1, 4, 1, CL>(a, p, s);
+    case CFG_M16: return launch_conv_cfg<1, 4, 1, 4, 1, CL>(a, p, s);
+    case CFG_M16_N64_K4: return launch_conv_cfg<1, 4, 1, 1, 4, CL>(a, p, s);
+    case CFG_M16_N128_K4: return launch_conv_cfg<1, 8, 1, 1, 4, CL>(a, p, s);
+    case CFG_M16_N208_K4: return launch_conv_cfg<1, 13, 1, 1, 4, CL>(a, p, s);
+    default: return launch_conv_cfg<1, 16, 1, 1, 4, CL>(a, p, s);
+  }
+}
+
 static ConvArgs conv_args(const Geom& g, const ConvPlan& p, const float* x, const float* w, const float* bias,
                           float* y) {
   ConvArgs a;
@@ -1594,6 +1672,8 @@ static ConvArgs conv_args(const Geom& g, const ConvPlan& p, const float* x, cons
   a.tiles_per_plane = int(p.tiles_per_plane); a.nchunks = p.nchunks; a.items = int(p.items);
   a.rows = p.rows; a.bw = p.bw; a.boxc = p.boxc; a.row_tiles = p.row_tiles; a.ctiles = p.ctiles;
   a.plane_out = int(g.plane_out());
+  a.ccp = p.ccp;
+  a.vec_store = 0;
   return a;
 }
 
@@ -1652,7 +1732,7 @@ const char* conv_status_string(int status) {
   switch (status) {
     case CONV_OK: return "CONV_OK";
     case CONV_ERR_NULL: return "CONV_ERR_NULL: a required pointer is NULL";
-    case CONV_ERR_RANK: return "CONV_ERR_RANK: nd must be 1 or 3";
+    case CONV_ERR_RANK: return "CONV_ERR_RANK: nd must be 1, 2 or 3";
     case CONV_ERR_SHAPE: return "CONV_ERR_SHAPE: bad dimension or weight shape";
     case CONV_ERR_GROUPS: return "CONV_ERR_GROUPS: groups < 1 or channels not divisible by groups";
     case CONV_ERR_PARAM: return "CONV_ERR_PARAM: stride/dilation < 1 or padding < 0";
@@ -1668,18 +1748,20 @@ int conv_plan_describe(int nd, const int64_t* x_shape, const int64_t* w_shape, c
                        const int* dilation, const int* padding, int groups, int fused, char* buf, int buflen) {
   if (!buf || buflen < 1) return CONV_ERR_NULL;
   buf[0] = 0;
+  if (fused < 0 || fused > 2) return CONV_ERR_PARAM;
   Geom g;
-  int rc = make_geom(nd, x_shape, w_shape, stride, dilation, padding, groups, &g);
+  int rc = fused == 2 ? make_geom_channels_last(nd, x_shape, w_shape, stride, dilation, padding, groups, &g)
+                      : make_geom(nd, x_shape, w_shape, stride, dilation, padding, groups, &g);
   if (rc != CONV_OK) return rc;
   std::string s;
-  if (fused) {
+  if (fused == 1) {
     FusedPlan p;
     rc = plan_fused(g, 2, &p, use_tap() != 0);
     if (rc != CONV_OK) return rc;
     s = describe(g, p);
   } else {
     ConvPlan p;
-    rc = plan_conv(g, &p, forced_conv_cfg(), 256, use_tap());
+    rc = plan_conv(g, &p, forced_conv_cfg(), 256, fused == 2 ? 0 : use_tap());
     if (rc != CONV_OK) return rc;
     s = describe(g, p);
   }
@@ -1705,16 +1787,22 @@ int conv_fwd(int nd, const float* x, const int64_t* x_shape, const float* w, con
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (p.tap_spec >= 0) return launch_tap_spec(a, p, s);
   if (p.split_spec >= 0) return launch_split_spec(a, p, s);
-  switch (p.cfg) {
-    case CFG_M64: return launch_conv_cfg<4, 4, 1, 4, 1>(a, p, s);
-    case CFG_M128: return launch_conv_cfg<4, 4, 2, 2, 1>(a, p, s);
-    case CFG_M32: return launch_conv_cfg<2, 4, 1, 4, 1>(a, p, s);
-    case CFG_M16: return launch_conv_cfg<1, 4, 1, 4, 1>(a, p, s);
-    case CFG_M16_N64_K4: return launch_conv_cfg<1, 4, 1, 1, 4>(a, p, s);
-    case CFG_M16_N128_K4: return launch_conv_cfg<1, 8, 1, 1, 4>(a, p, s);
-    case CFG_M16_N208_K4: return launch_conv_cfg<1, 13, 1, 1, 4>(a, p, s);
-    default: return launch_conv_cfg<1, 16, 1, 1, 4>(a, p, s);
-  }
+  return launch_generic<false>(a, p, s);
+}
+
+int conv_fwd_channels_last(int nd, const float* x, const int64_t* x_shape, const float* w, const int64_t* w_shape,
+                           const float* bias, const int* stride, const int* dilation, const int* padding,
+                           int groups, float* y, convhip_stream_t stream) {
+  Geom g;
+  int rc = make_geom_channels_last(nd, x_shape, w_shape, stride, dilation, padding, groups, &g);
+  if (rc != CONV_OK) return rc;
+  if (!x || !w || !y) return CONV_ERR_NULL;
+  ConvPlan p;
+  rc = plan_conv(g, &p, forced_conv_cfg(), device_num_cu(), 0);
+  if (rc != CONV_OK) return rc;
+  ConvArgs a = conv_args(g, p, x, w, bias, y);
+  a.vec_store = (g.Cout % 4 == 0 && g.Coutg % 4 == 0 && (reinterpret_cast<uintptr_t>(y) & 15) == 0) ? 1 : 0;
+  return launch_generic<true>(a, p, reinterpret_cast<hipStream_t>(stream));
 }
 int conv3d_min_softmax(const float* x, const int64_t* x_shape, const float* w, const int64_t* w_shape,
                        const float* bias, const int* stride, const int* dilation, const int* padding, int groups,

@@ -62,6 +62,19 @@ int make_geom(int nd, const int64_t* xs, const int64_t* ws, const int* stride, c
   return CONV_OK;
 }
 
+int make_geom_channels_last(int nd, const int64_t* xs, const int64_t* ws, const int* stride, const int* dilation,
+                            const int* padding, int groups, Geom* g) {
+  if (nd < 1 || nd > 3) return CONV_ERR_RANK;
+  if (!xs) return CONV_ERR_NULL;
+  int64_t logical[5];
+  logical[0] = xs[0];
+  logical[1] = xs[nd + 1];
+  for (int a = 0; a < nd; a++) logical[2 + a] = xs[1 + a];
+  const int rc = make_geom(nd, logical, ws, stride, dilation, padding, groups, g);
+  if (rc == CONV_OK) g->cl = true;
+  return rc;
+}
+
 CfgShape cfg_shape(int cfg) {
   switch (cfg) {
     case CFG_M64: return {4, 4, 1, 4, 1};
@@ -217,7 +230,17 @@ static bool plan_tap(const Geom& g, const TapSpecDesc& d, int num_cu, ConvPlan* 
   return true;
 }
 
+// Channels-last box pitch: Cc floats per site unless the 16 position lanes of a
+// matrix-core operand read (stride W * Cc floats apart) would share LDS banks;
+// then one float of padding per site.
+static int cl_pitch(int64_t cc, int64_t stride_w) {
+  int64_t v = cc * stride_w, gcd = 64;
+  while (v % gcd != 0) gcd /= 2;
+  return int(gcd <= 4 ? cc : cc + 1);
+}
+
 int plan_conv(const Geom& g, ConvPlan* out, int force_cfg, int num_cu, int use_tap) {
+  if (g.cl) use_tap = 0;
   if (use_tap != 0 && force_cfg < 0) {
     int n = 0;
     const TapSpecDesc* specs = tap_specs(&n);
@@ -269,7 +292,7 @@ int plan_conv(const Geom& g, ConvPlan* out, int force_cfg, int num_cu, int use_t
   auto r256 = [](int64_t v) { return (v + 255) / 256 * 256; };
   auto layout = [&](int64_t cc, int64_t* xs, int64_t* ko, int64_t* ws) {
     const int64_t kcp = r4(cc * g.kvol());
-    *xs = r256(cc * p.boxc);
+    *xs = r256((g.cl ? cl_pitch(cc, g.S[2]) : cc) * p.boxc);
     *ko = r4(kcp + 8 * cs.KS);
     *ws = (kcp / 4 + cs.KS) * cs.WM * 64 * cs.MT;
     if (2 * (*xs + *ws) < red) *xs = r256(red / 2);
@@ -299,6 +322,7 @@ int plan_conv(const Geom& g, ConvPlan* out, int force_cfg, int num_cu, int use_t
     best = 1;
   }
   p.Cc = best;
+  p.ccp = g.cl ? cl_pitch(best, g.S[2]) : 0;
   int64_t xs, ko, ws;
   p.lds_bytes = layout(p.Cc, &xs, &ko, &ws);
   p.xs_floats = int(xs);
@@ -414,9 +438,10 @@ std::string describe(const Geom& g, const ConvPlan& p) {
     cs = CfgShape{1, d.NT, 1, 1, d.NW};
   }
   std::snprintf(buf, sizeof buf,
-                "kernel=%s cfg=%d MT=%d NT=%d WM=%d WN=%d KS=%d BM=%d BN=%d mode=%s Cc=%d kc_pad=%d "
+                "kernel=%s%s cfg=%d MT=%d NT=%d WM=%d WN=%d KS=%d BM=%d BN=%d mode=%s Cc=%d kc_pad=%d "
                 "box=%dx%dx%d grid=%lldx%lldx%lld lds=%lld macs=%lld",
                 p.tap_spec >= 0 ? "conv_tap" : p.split_spec >= 0 ? "conv_tap_split" : "conv_mfma16",
+                g.cl ? " layout=channels_last" : "",
                 p.tap_spec >= 0 ? p.tap_spec : p.split_spec >= 0 ? p.split_spec : p.cfg, cs.MT, cs.NT,
                 cs.WM, cs.WN, cs.KS, p.BM, p.BN, p.mode == TILE_FLAT ? "flat" : "row", p.Cc,
                 p.kc_pad, p.kdspan, p.rows, p.bw, (long long)p.grid[0], (long long)p.grid[1],

@@ -12,6 +12,7 @@ namespace convhip {
 // the case D = H = 1, kD = kH = 1 with its length on the W axis.
 struct Geom {
   int nd = 3;
+  bool cl = false;            // channels-last tensors: x [N, D, H, W, C_in], y [N, D_out, H_out, W_out, C_out]
   int64_t N = 0, Cin = 0, Cout = 0, G = 1, Cg = 0, Coutg = 0;
   int64_t L[3] = {1, 1, 1};   // input D, H, W
   int64_t K[3] = {1, 1, 1};   // kernel kD, kH, kW
@@ -31,6 +32,9 @@ int64_t out_len(int64_t L, int64_t k, int64_t s, int64_t d, int64_t p);
 // Validate the user's arguments and fill g. Returns a conv_status value.
 int make_geom(int nd, const int64_t* x_shape, const int64_t* w_shape, const int* stride,
               const int* dilation, const int* padding, int groups, Geom* g);
+// The same for a channels-last input, x_shape = [N, spatial..., C_in]; sets g->cl.
+int make_geom_channels_last(int nd, const int64_t* x_shape, const int64_t* w_shape, const int* stride,
+                            const int* dilation, const int* padding, int groups, Geom* g);
 
 // Tile configurations of the fp32 MFMA implicit-GEMM conv kernel. Each wave
 // owns MT x NT tiles of 16 (output channels) x 16 (output positions); the block
@@ -65,7 +69,8 @@ struct ConvPlan {
   int kdspan = 0;      // input planes in the box: (kD-1)*dD + 1
   int rows = 0;        // input rows in the box (maximum over tiles)
   int bw = 0;          // input columns in the box
-  int boxc = 0;        // floats per channel in the box: kdspan * rows * bw
+  int boxc = 0;        // floats per channel in the box: kdspan * rows * bw (channels-last: sites)
+  int ccp = 0;         // channels-last: LDS floats per box site (Cc, or Cc + 1 against bank conflicts)
   int xs_floats = 0;   // LDS floats of the box region (box, or the split-K partial sums if larger)
   int koff_ints = 0;   // LDS ints of the tap-offset table (padded for prefetch)
   int ws_floats = 0;   // LDS floats of the weight fragments (padded for prefetch)
@@ -115,7 +120,8 @@ struct TapSpecDesc {
 const TapSpecDesc* tap_specs(int* count);
 
 // num_cu: compute units of the device (sizes the persistent grid).
-// use_tap: -1 planner's choice, 0 never use a tap specialisation.
+// use_tap: -1 planner's choice, 0 never use a tap specialisation. Channels-last
+// geometries (g.cl) always take the generic kernel.
 int plan_conv(const Geom& g, ConvPlan* p, int force_cfg = -1, int num_cu = 256, int use_tap = -1);
 
 // Build-time specialisations of the depth-streamed fused kernel (stride 1,

@@ -79,6 +79,28 @@ int conv_fwd(int nd,
              float *y, convhip_stream_t stream);
 
 /*
+ * Forward convolution on channels-last tensors (page l1_p60, opening turn: the
+ * NDHWC layout is weighed there for coalesced input reads). The same operation
+ * as conv_fwd; only the memory order of x and y differs:
+ *   nd = 1: x [N, L, C_in],       y [N, L_out, C_out]
+ *   nd = 2: x [N, H, W, C_in],    y [N, H_out, W_out, C_out]
+ *   nd = 3: x [N, D, H, W, C_in], y [N, D_out, H_out, W_out, C_out]
+ *   y[n,o,co] = bias[co] + sum_{c', t} w[co,c',t] * x[n, o*stride + t*dilation - padding, g(co)*C_in/groups + c']
+ * x_shape: nd+2 host entries in the channels-last order above ([N, spatial..., C_in]).
+ * w keeps the conv_fwd layout [C_out, C_in/groups, k...] (w_shape likewise);
+ * bias [C_out] or NULL. y: device buffer of N*prod(out)*C_out floats. Status
+ * codes, ownership and stream semantics as conv_fwd. Any pointer alignment is
+ * accepted (16-byte aligned y with C_out and C_out/groups multiples of 4 takes
+ * vector stores).
+ */
+int conv_fwd_channels_last(int nd,
+                           const float *x, const int64_t *x_shape,
+                           const float *w, const int64_t *w_shape,
+                           const float *bias,
+                           const int *stride, const int *dilation, const int *padding, int groups,
+                           float *y, convhip_stream_t stream);
+
+/*
  * Fused Conv3d -> min over one spatial axis -> softmax over channels (page
  * l2_p24, opening turns: the module applies Conv3d, torch.min over dim 2, then
  * torch.softmax over dim 1; its `dim` argument names the min axis). The 5-D
@@ -105,7 +127,9 @@ const char *conv_status_string(int status);
  * Describe the launch plan the library would use for these arguments (kernel
  * variant, tile, grid, LDS bytes) as one line of text into buf (NUL-terminated,
  * truncated to buflen). fused = 0 for conv_fwd, 1 for conv3d_min_softmax (then
- * nd must be 3). Host only; launches nothing. Returns a conv_status.
+ * nd must be 3), 2 for conv_fwd_channels_last (x_shape in its channels-last
+ * order); other values give CONV_ERR_PARAM. Host only; launches nothing.
+ * Returns a conv_status.
  */
 int conv_plan_describe(int nd, const int64_t *x_shape, const int64_t *w_shape,
                        const int *stride, const int *dilation, const int *padding, int groups,

@@ -4,6 +4,9 @@ Only the tests, the smoke check and the bench's CPU-baseline leg may import
 this package. The HIP library and its Python binding never do.
 
 * ``conv``               -- oracle.c's nested-loop convolution, returns float64.
+* ``conv_channels_last`` -- the same convolution on channels-last tensors
+                           (x [N, spatial..., C_in] -> y [N, out..., C_out]): a
+                           pure change of memory order around ``conv``.
 * ``conv3d_min_softmax`` -- conv (composed) -> min over one axis -> softmax over channels.
 * ``out_len``            -- the output-length formula of one axis.
 * ``brute``              -- a second, pure-Python statement of the same definition
@@ -84,6 +87,14 @@ def conv(x, w, bias=None, stride=1, dilation=1, padding=0, groups=1):
     if rc != 0:
         raise ValueError(f"oracle_conv rejected the arguments (code {rc})")
     return y
+
+
+def conv_channels_last(x_cl, w, bias=None, stride=1, dilation=1, padding=0, groups=1):
+    """fp64 conv of a channels-last input (page l1_p60, opening turn: the NDHWC
+    layout). The operation is conv's; the channel axis moves to the end on the
+    way in and on the way out."""
+    x = np.moveaxis(np.asarray(x_cl, dtype=np.float32), -1, 1)
+    return np.ascontiguousarray(np.moveaxis(conv(x, w, bias, stride, dilation, padding, groups), 1, -1))
 
 
 def conv3d_min_softmax(x, w, bias=None, stride=1, dilation=1, padding=0, groups=1, min_dim=2):

@@ -43,6 +43,35 @@ def conv(x, w, bias, stride, dilation, padding, groups):
     return y
 
 
+def conv_channels_last(x, w, bias, stride, dilation, padding, groups):
+    """The same sum with channels-last indexing: x[n, position..., channel] and
+    y[n, position..., output channel]; w[co, c', tap...] as in conv."""
+    import numpy as np
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    nd = x.ndim - 2
+    N, Cin = x.shape[0], x.shape[-1]
+    Cout, Cg = w.shape[:2]
+    ks = w.shape[2:]
+    Ls = x.shape[1:-1]
+    outs = [out_len(Ls[a], ks[a], stride[a], dilation[a], padding[a]) for a in range(nd)]
+    y = np.zeros((N, *outs, Cout), dtype=np.float64)
+    per_group_out = Cout // groups
+    for n in range(N):
+        for o in itertools.product(*[range(v) for v in outs]):
+            for co in range(Cout):
+                g = co // per_group_out
+                s = float(bias[co]) if bias is not None else 0.0
+                for t in itertools.product(*[range(v) for v in ks]):
+                    pos = [o[a] * stride[a] + t[a] * dilation[a] - padding[a] for a in range(nd)]
+                    if not all(0 <= pos[a] < Ls[a] for a in range(nd)):
+                        continue
+                    for cc in range(Cg):
+                        s += float(w[(co, cc) + t]) * float(x[(n,) + tuple(pos) + (g * Cg + cc,)])
+                y[(n,) + o + (co,)] = s
+    return y
+
+
 def conv3d_min_softmax(x, w, bias, stride, dilation, padding, groups, min_dim=2):
     import numpy as np
     y = conv(x, w, bias, stride, dilation, padding, groups)

@@ -73,6 +73,33 @@ def test_conv_fwd_null_pointers():
                         I32(0, 0, 0), 1, FAKE, None) == -1
 
 
+def test_conv_fwd_channels_last_validation_errors():
+    lib = ch.lib()
+    one, zero = I32(1, 1, 1), I32(0, 0, 0)
+    f = lambda nd=3, xs=(1, 8, 8, 8, 4), ws=(4, 4, 3, 3, 3), g=1, x=FAKE, y=FAKE, s=one: \
+        lib.conv_fwd_channels_last(nd, x, I64(*xs) if xs else None, FAKE, I64(*ws), None, s, one, zero, g, y, None)
+    assert f(nd=4) == -2
+    assert f(xs=None) == -1
+    assert f(x=None) == -1 and f(y=None) == -1
+    assert f(xs=(1, 8, 8, 8, 2)) == -3                     # channel axis is the last entry
+    assert f(xs=(1, 8, 8, 8, 6), ws=(4, 2, 3, 3, 3), g=4) == -4
+    assert f(xs=(1, 8, 8, 2, 4)) == -6                     # W = 2 < kW
+    assert f(s=I32(1, 0, 1)) == -5
+    assert f(nd=1, xs=(1, 8, 4), ws=(4, 4, 9)) == -6
+    buf = ctypes.create_string_buffer(256)
+    assert lib.conv_plan_describe(3, I64(1, 8, 8, 8, 4), I64(4, 4, 3, 3, 3), one, one, zero, 1, 3, buf, 256) == -5
+
+
+def test_channels_last_plans_take_the_generic_kernel():
+    for xs, ws, s, d, p, g in [((4, 32, 32, 32, 16), (32, 8, 3, 5, 7), (1, 2, 2), (1, 1, 2), (1, 2, 3), 2),
+                               ((2, 16, 16, 16, 3), (8, 3, 3, 3, 3), 1, 1, 0, 1),
+                               ((4, 4096, 64), (128, 64, 3), 3, 4, 0, 1)]:
+        desc = ch.plan_describe(xs, ws, s, d, p, g, channels_last=True)
+        fields = dict(t.split("=", 1) for t in desc.split() if "=" in t)
+        assert fields["kernel"] == "conv_mfma16" and fields["layout"] == "channels_last", desc
+        assert int(fields["lds"]) <= 160 * 1024, desc
+
+
 def test_conv3d_min_softmax_validation_errors():
     lib = ch.lib()
     xs, ws = I64(2, 3, 6, 6, 6), I64(5, 3, 3, 3, 3)

@@ -1,0 +1,193 @@
+"""GPU parity of the channels-last convolution (x [N, spatial..., C_in] ->
+y [N, out..., C_out]) against the fp64 oracle on the same seeded inputs.
+
+Integer-valued inputs keep every partial sum an exact fp32 integer, so those
+cases compare bit for bit; uniform inputs use the conv tolerance
+1e-4 * sqrt(K_red) * max|y_ref|.
+"""
+import numpy as np
+import pytest
+import torch
+
+import implicit_gemm_convolution_direct_amd as ch
+import oracle
+import synth
+from gpu_util import assert_conv_close, dev, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _int_inputs(r, xs_cl, ws, bias):
+    x = r.integers(0, 4, size=xs_cl).astype(np.float32)
+    w = r.integers(-2, 3, size=ws).astype(np.float32)
+    b = r.integers(-4, 5, size=ws[0]).astype(np.float32) if bias else None
+    return x, w, b
+
+
+def _float_inputs(r, xs_cl, ws, bias):
+    x = r.random(xs_cl, dtype=np.float32)
+    fan = int(np.prod(ws[1:]))
+    w = ((r.random(ws, dtype=np.float32) * 2 - 1) / np.sqrt(fan)).astype(np.float32)
+    b = ((r.random(ws[0], dtype=np.float32) * 2 - 1) / np.sqrt(fan)).astype(np.float32) if bias else None
+    return x, w, b
+
+
+def gpu_conv_cl(x, w, b, s, d, p, g, out=None):
+    y = ch.conv_fwd_channels_last(to_dev(x), to_dev(w), to_dev(b), s, d, p, g, out=out)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+def _random_geometry(r, nd):
+    g = int(r.choice([1, 1, 2, 4]))
+    cg = int(r.choice([1, 2, 3, 5, 8, 16, 24]))
+    coutg = int(r.choice([1, 3, 4, 8, 16, 20, 33, 64, 70, 128]))
+    if g > 1:
+        coutg = min(coutg, 40)
+    ks = [int(r.integers(1, 6)) for _ in range(nd)]
+    s = [int(r.integers(1, 4)) for _ in range(nd)]
+    d = [int(r.integers(1, 4)) for _ in range(nd)]
+    p = [int(r.integers(0, 4)) for _ in range(nd)]
+    Ls = []
+    for a in range(nd):
+        lo = max(1, d[a] * (ks[a] - 1) + 1 - 2 * p[a])
+        Ls.append(int(r.integers(lo, lo + {1: 500, 2: 40, 3: 14}[nd])))
+    N = int(r.integers(1, 3))
+    return (N, *Ls, g * cg), (g * coutg, cg, *ks), s, d, p, g
+
+
+RANDOM_CASES = [(nd, seed) for nd in (1, 2, 3) for seed in range(8)]
+
+
+@pytest.mark.parametrize("nd,seed", RANDOM_CASES)
+def test_channels_last_random_integer_exact(nd, seed):
+    r = np.random.default_rng(7000 + 100 * nd + seed)
+    xs, ws, s, d, p, g = _random_geometry(r, nd)
+    x, w, b = _int_inputs(r, xs, ws, bias=bool(seed % 2))
+    say(f"cl case nd={nd} seed={seed} x={xs} w={ws} s={s} d={d} p={p} g={g}: "
+        + ch.plan_describe(xs, ws, s, d, p, g, channels_last=True))
+    y = gpu_conv_cl(x, w, b, s, d, p, g)
+    ref = oracle.conv_channels_last(x, w, b, s, d, p, g)
+    assert np.abs(ref).max() < 2 ** 24
+    np.testing.assert_array_equal(y.astype(np.float64), ref)
+
+
+@pytest.mark.parametrize("nd,seed", RANDOM_CASES[::3])
+def test_channels_last_random_float(nd, seed):
+    r = np.random.default_rng(7500 + 100 * nd + seed)
+    xs, ws, s, d, p, g = _random_geometry(r, nd)
+    x, w, b = _float_inputs(r, xs, ws, bias=True)
+    say(f"cl float nd={nd} seed={seed} x={xs} w={ws}")
+    y = gpu_conv_cl(x, w, b, s, d, p, g)
+    assert_conv_close(y, oracle.conv_channels_last(x, w, b, s, d, p, g), ws, f"cl float nd={nd} seed={seed}")
+
+
+EDGE_CASES = [
+    # name, x shape (channels last), w shape, stride, dilation, padding, groups
+    ("cout_odd_scalar_stores", (2, 5, 6, 7, 3), (5, 3, 3, 3, 3), 1, 1, 1, 1),
+    ("coutg_2_scalar_stores", (1, 6, 7, 8, 4), (4, 2, 2, 3, 3), 1, 1, 0, 2),
+    ("depthwise", (2, 5, 9, 11, 6), (6, 1, 3, 3, 3), 1, 1, 1, 6),
+    ("kernel_1x1x1", (2, 4, 6, 7, 5), (7, 5, 1, 1, 1), 1, 1, 0, 1),
+    ("single_output", (1, 3, 4, 5, 2), (3, 2, 3, 4, 5), 1, 1, 0, 1),
+    ("padding_wider_than_kernel", (1, 3, 3, 3, 2), (4, 2, 2, 2, 2), 1, 1, 3, 1),
+    ("stride_gt_kernel", (1, 9, 17, 33, 3), (5, 3, 2, 2, 2), (4, 3, 5), 1, 0, 1),
+    ("many_input_channels", (1, 4, 4, 40, 200), (16, 200, 1, 1, 3), 1, 1, 0, 1),
+    ("cin64_conv1d_geometry", (2, 3001, 64), (128, 64, 3), 3, 4, 2, 1),
+    ("cout_129_two_channel_tiles", (1, 300, 4), (129, 4, 3), 3, 4, 0, 1),
+    ("conv1d_long_row_tiles", (2, 5000, 3), (16, 3, 5), 1, 2, 2, 1),
+    ("conv2d", (2, 32, 32, 16), (32, 8, 5, 7), (2, 2), (1, 2), (2, 3), 2),
+]
+
+
+@pytest.mark.parametrize("case", EDGE_CASES, ids=[c[0] for c in EDGE_CASES])
+def test_channels_last_edge_cases_integer_exact(case):
+    name, xs, ws, s, d, p, g = case
+    r = np.random.default_rng(sum(map(ord, name)))
+    x, w, b = _int_inputs(r, xs, ws, bias=True)
+    say(f"cl edge {name}: " + ch.plan_describe(xs, ws, s, d, p, g, channels_last=True))
+    y = gpu_conv_cl(x, w, b, s, d, p, g)
+    np.testing.assert_array_equal(y.astype(np.float64), oracle.conv_channels_last(x, w, b, s, d, p, g))
+
+
+def test_channels_last_misaligned_output_and_input():
+    """Views 4 bytes past an allocation: y takes the scalar stores, x the same
+    copies; results unchanged."""
+    r = np.random.default_rng(11)
+    xs, ws = (2, 6, 7, 8, 4), (8, 4, 3, 3, 3)
+    x, w, b = _int_inputs(r, xs, ws, bias=True)
+    xd = torch.empty(x.size + 1, dtype=torch.float32, device=dev())[1:].view(xs)
+    xd.copy_(torch.from_numpy(x))
+    ys = (2, 4, 5, 6, 8)
+    yd = torch.empty(int(np.prod(ys)) + 1, dtype=torch.float32, device=dev())[1:].view(ys)
+    assert xd.data_ptr() % 16 != 0 and yd.data_ptr() % 16 != 0
+    ch.conv_fwd_channels_last(xd, to_dev(w), to_dev(b), 1, 1, 0, 1, out=yd)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(yd.cpu().numpy().astype(np.float64),
+                                  oracle.conv_channels_last(x, w, b, 1, 1, 0, 1))
+
+
+CFG_CASES = [
+    ((2, 9, 10, 11, 3), (8, 3, 3, 3, 3), 1, 1, 0, 1),
+    ((1, 7, 9, 10, 4), (6, 2, 2, 3, 2), (1, 2, 2), (1, 1, 2), (1, 2, 3), 2),
+    ((1, 900, 5), (33, 5, 3), 3, 4, 1, 1),
+    ((2, 4, 14, 14, 3), (70, 3, 3, 3, 3), 1, 1, 0, 1),
+]
+
+
+@pytest.mark.parametrize("cfg", range(8))
+def test_channels_last_every_tile_config_integer_exact(cfg, monkeypatch):
+    monkeypatch.setenv("CONVHIP_CONV_CFG", str(cfg))
+    r = np.random.default_rng(88 + cfg)
+    for xs, ws, s, d, p, g in CFG_CASES:
+        x, w, b = _int_inputs(r, xs, ws, bias=True)
+        say(f"cl cfg {cfg}: x={xs} w={ws}: " + ch.plan_describe(xs, ws, s, d, p, g, channels_last=True))
+        y = gpu_conv_cl(x, w, b, s, d, p, g)
+        np.testing.assert_array_equal(y.astype(np.float64), oracle.conv_channels_last(x, w, b, s, d, p, g))
+
+
+def _cl_workload_inputs(name, integer=False, n_samples=None):
+    """A workload's seeded inputs (NCDHW / NCL), moved to channels-last order."""
+    x, w, b = synth.make_inputs(name, integer=integer, n_samples=n_samples)
+    return np.ascontiguousarray(np.moveaxis(x, 1, -1)), w, b
+
+
+@pytest.mark.parametrize("name", ["tiny_conv3d", "general_conv3d"])
+def test_channels_last_workload_full(name):
+    cfg = synth.WORKLOADS[name]
+    args = (cfg["stride"], cfg["dilation"], cfg["padding"], cfg["groups"])
+    for integer in (True, False):
+        x, w, b = _cl_workload_inputs(name, integer=integer)
+        say(f"cl workload {name} integer={integer}: "
+            + ch.plan_describe(x.shape, w.shape, *args, channels_last=True))
+        y = gpu_conv_cl(x, w, b, *args)
+        ref = oracle.conv_channels_last(x, w, b, *args)
+        if integer:
+            np.testing.assert_array_equal(y.astype(np.float64), ref)
+        else:
+            assert_conv_close(y, ref, w.shape, f"cl {name}")
+
+
+def test_channels_last_matches_ncdhw_path_bit_for_bit_on_integers():
+    """The two layouts give the same exact results (integer inputs)."""
+    cfg = synth.WORKLOADS["general_conv3d"]
+    args = (cfg["stride"], cfg["dilation"], cfg["padding"], cfg["groups"])
+    x, w, b = synth.make_inputs("general_conv3d", integer=True, n_samples=2)
+    y_ncdhw = ch.conv_fwd(to_dev(x), to_dev(w), to_dev(b), *args)
+    x_cl = to_dev(np.ascontiguousarray(np.moveaxis(x, 1, -1)))
+    y_cl = ch.conv_fwd_channels_last(x_cl, to_dev(w), to_dev(b), *args)
+    torch.cuda.synchronize()
+    assert torch.equal(y_cl, y_ncdhw.movedim(1, -1))
+
+
+def test_channels_last_asym_workload_slices():
+    """Full-size asymmetric Conv3d in channels-last order, checked on two samples."""
+    name = "asym_conv3d"
+    cfg = synth.WORKLOADS[name]
+    args = (cfg["stride"], cfg["dilation"], cfg["padding"], cfg["groups"])
+    x, w, _ = _cl_workload_inputs(name)
+    say(f"cl workload {name}: " + ch.plan_describe(x.shape, w.shape, *args, channels_last=True))
+    y = ch.conv_fwd_channels_last(to_dev(x), to_dev(w), None, *args)
+    torch.cuda.synchronize()
+    for n in (0, x.shape[0] - 1):
+        ref = oracle.conv_channels_last(x[n:n + 1], w, None, *args)
+        assert_conv_close(y[n:n + 1].cpu().numpy(), ref, w.shape, f"cl {name} sample {n}")

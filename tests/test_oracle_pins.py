@@ -112,6 +112,32 @@ def test_oracle_matches_brute_force(nd):
 
 
 @pytest.mark.parametrize("nd", [1, 2, 3])
+def test_channels_last_oracle_matches_brute_force(nd):
+    """The channels-last oracle against a brute force that indexes x[n, pos..., c]
+    directly (a swapped axis or a wrong channel offset fails here)."""
+    r = _rng(300 + nd)
+    for _ in range(40 if nd == 1 else 20):
+        x, w, b, s, d, p, g = _random_case(r, nd)
+        x_cl = np.ascontiguousarray(np.moveaxis(x, 1, -1))
+        yo = oracle.conv_channels_last(x_cl, w, b, s, d, p, g)
+        yb = brute.conv_channels_last(x_cl, w, b, s, d, p, g)
+        assert yo.shape == yb.shape == (x.shape[0], *yo.shape[1:-1], w.shape[0])
+        np.testing.assert_allclose(yo, yb, rtol=1e-12, atol=1e-12)
+
+
+def test_channels_last_brute_force_against_torch_channels_last_3d():
+    """torch's Conv3d on a channels_last_3d tensor (memory order N, D, H, W, C)."""
+    r = _rng(310)
+    for _ in range(6):
+        x, w, b, s, d, p, g = _random_case(r, 3)
+        xt = torch.from_numpy(x).double().contiguous(memory_format=torch.channels_last_3d)
+        yt = F.conv3d(xt, torch.from_numpy(w).double(), None if b is None else torch.from_numpy(b).double(),
+                      stride=s, padding=p, dilation=d, groups=g)
+        yb = brute.conv_channels_last(np.moveaxis(x, 1, -1), w, b, s, d, p, g)
+        np.testing.assert_allclose(yb, yt.permute(0, 2, 3, 4, 1).numpy(), rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("nd", [1, 2, 3])
 def test_oracle_matches_torch_float64(nd):
     """The definition is what torch's float64 CPU convolution computes."""
     r = _rng(200 + nd)
