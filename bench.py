@@ -6,7 +6,9 @@ One "step" is one call of the library's entry point over one batch of the
 headline workload, the general-parameter Conv3d (x[4,16,32,32,32], w[32,8,3,5,7],
 groups 2, stride (1,2,2), padding (1,2,3), dilation (1,1,2)). The same run also
 times every other workload (tiny Conv3d, fused Conv3d+min+softmax, asymmetric
-Conv3d, long Conv1d) and reports them under "shapes". Inputs are seeded
+Conv3d, long Conv1d, and three of them again on channels-last tensors through
+conv_fwd_channels_last, "<workload>_channels_last") and reports them under
+"shapes". Inputs are seeded
 synthetic tensors already resident in device memory; each workload is first run
 back to back for at least 0.5 s (the GPU's clocks ramp up from idle over
 that time), then the timed region is K back-to-back calls between two device
@@ -34,7 +36,9 @@ PEAK_FP32_TFLOPS = 157.3
 WARM_S = 0.5  # default seconds of warm-up calls per workload (--warm-seconds)
 PEAK_HBM_GBS = 8000.0
 HEADLINE = "general_conv3d"
-ORDER = ["tiny_conv3d", "general_conv3d", "conv3d_min_softmax", "asym_conv3d", "long_conv1d"]
+CL_SUFFIX = "_channels_last"
+ORDER = ["tiny_conv3d", "general_conv3d", "conv3d_min_softmax", "asym_conv3d", "long_conv1d",
+         "general_conv3d" + CL_SUFFIX, "asym_conv3d" + CL_SUFFIX, "long_conv1d" + CL_SUFFIX]
 KERNEL_SOURCES = [os.path.join(ROOT, "implicit_gemm_convolution_direct_amd", "csrc", f)
                   for f in ("conv_kernels.hip", "convhip_plan.cpp", "convhip_plan.h")]
 
@@ -86,11 +90,22 @@ def read_traffic(name):
         return None
 
 
-def make_device_inputs(name, torch, ch, synth):
+def split_name(name):
+    """(workload, channels_last): a "<workload>_channels_last" entry times the same
+    workload with x [N, spatial..., C_in] and y [N, out..., C_out]."""
+    if name.endswith(CL_SUFFIX):
+        return name[:-len(CL_SUFFIX)], True
+    return name, False
+
+
+def make_device_inputs(name, torch, ch, synth, channels_last=False):
     cfg = synth.WORKLOADS[name]
     dev = torch.device("cuda:0")
     sx, sw, sb = cfg["seeds"]
-    x = torch.empty(cfg["x"], dtype=torch.float32, device=dev)
+    xs = cfg["x"]
+    if channels_last:
+        xs = (xs[0], *xs[2:], xs[1])
+    x = torch.empty(xs, dtype=torch.float32, device=dev)
     ch.synth_fill(x, sx, ch.KIND_UNIFORM01)
     fan = synth.fan_in(cfg["w"])
     w = torch.empty(cfg["w"], dtype=torch.float32, device=dev)
@@ -103,10 +118,14 @@ def make_device_inputs(name, torch, ch, synth):
 
 
 def time_workload(name, steps, warmup, torch, ch, synth, flush=None, warm_s=WARM_S):
-    cfg, x, w, b = make_device_inputs(name, torch, ch, synth)
+    base, cl = split_name(name)
+    cfg, x, w, b = make_device_inputs(base, torch, ch, synth, channels_last=cl)
     out, macs, nbytes, conv_elems, y_elems = geometry(cfg)
     args = (cfg["stride"], cfg["dilation"], cfg["padding"], cfg["groups"])
-    if cfg["fused"]:
+    if cl:
+        y = torch.empty((cfg["x"][0], *out, cfg["w"][0]), dtype=torch.float32, device=x.device)
+        call = lambda: ch.conv_fwd_channels_last(x, w, b, *args, out=y)
+    elif cfg["fused"]:
         y = torch.empty((cfg["x"][0], cfg["w"][0], *out[1:]), dtype=torch.float32, device=x.device)
         call = lambda: ch.conv3d_min_softmax(x, w, b, *args, min_dim=2, out=y)
     else:
@@ -157,7 +176,7 @@ def time_workload(name, steps, warmup, torch, ch, synth, flush=None, warm_s=WARM
     gbs = nbytes / (ms * 1e-3) / 1e9
     rec = {
         "workload": name,
-        "plan": ch.plan_describe(cfg["x"], cfg["w"], *args, fused=cfg["fused"]),
+        "plan": ch.plan_describe(tuple(x.shape), cfg["w"], *args, fused=cfg["fused"], channels_last=cl),
         "ms": round(ms, 5),
         "ms_single_min": round(min(singles), 5),
         "ms_single_max": round(max(singles), 5),
@@ -170,7 +189,7 @@ def time_workload(name, steps, warmup, torch, ch, synth, flush=None, warm_s=WARM
         "alg_bytes": nbytes,
         "wall_s": round(wall, 3),
     }
-    if cfg["fused"]:
+    if cfg["fused"] and not cl:
         # Unfused chain: conv writes the 5-D result, min reads it and writes its
         # result, softmax reads and writes that (algorithmic bytes).
         unfused = 4 * (int(np.prod(cfg["x"])) + int(np.prod(cfg["w"])) + cfg["w"][0]
@@ -274,7 +293,7 @@ def main():
         tol = 1e-4 * math.sqrt(int(np.prod(cfg["w"][1:]))) * float(np.abs(ref).max())
         parity = {"max_abs_err": err, "tol": tol, "pass": err <= tol}
 
-    cfgh = synth.WORKLOADS[head_name]
+    cfgh = synth.WORKLOADS[split_name(head_name)[0]]
     traffic = read_traffic(head_name)
     achieved = head["tflops"]
     line = {

@@ -71,6 +71,7 @@ struct ConvArgs {
   int nchunks;
   int items;  // persistent kernel: (tile, plane) work items
   int ccp;        // channels-last box: LDS floats per (plane, row, column) site
+  int cl_vec;     // channels-last box copied in 16-byte channel quads (ccp, Cc, C_in/groups multiples of 4)
   int vec_store;  // channels-last output: 4 consecutive channels stored as one 16-byte write
 };
 
@@ -241,11 +242,32 @@ template <int NWAVES = 4>
 __device__ __forceinline__ void stage_box_cl(const ConvArgs& a, const TileGeo& t, int c0, float* dst, int wave,
                                              int lane) {
   const int cc_count = min(a.Cc, a.Cg - c0);
-  const int total = a.kdspan * t.rows_ld * a.bw * a.ccp;
-  const float inv_ccp = 1.0f / float(a.ccp);
   const float inv_bw = 1.0f / float(a.bw);
   const float inv_rows = 1.0f / float(t.rows_ld);
   const float* xn = a.x + int64_t(t.n) * a.L0 * a.L1 * a.L2 * a.Cin + (int64_t(t.g) * a.Cg + c0);
+  if (a.cl_vec) {
+    // 16-byte units: a site holds ccp/4 channel quads, 64 quads per copy instruction.
+    const int q = a.ccp >> 2, q_valid = cc_count >> 2;
+    const float inv_q = 1.0f / float(q);
+    const int total4 = a.kdspan * t.rows_ld * a.bw * q;
+    for (int r = wave; r * 64 < total4; r += NWAVES) {
+      const int s = r * 64 + lane;
+      if (s < total4) {
+        int cq, col, zr;
+        const int site = divmod_small(s, q, inv_q, cq);
+        const int zz = divmod_small(site, a.bw, inv_bw, col);
+        const int zd = divmod_small(zz, t.rows_ld, inv_rows, zr);
+        const int id = t.id0 + zd, ih = t.ih0 + zr, iw = t.iw0 + col;
+        const bool ok = (cq < q_valid) && (unsigned(id) < unsigned(a.L0)) && (unsigned(ih) < unsigned(a.L1)) &&
+                        (unsigned(iw) < unsigned(a.L2));
+        const float* src = ok ? xn + ((int64_t(id) * a.L1 + ih) * a.L2 + iw) * a.Cin + 4 * cq : kZeroWord;
+        lds_dma_f32x4(src, dst + r * 256);
+      }
+    }
+    return;
+  }
+  const int total = a.kdspan * t.rows_ld * a.bw * a.ccp;
+  const float inv_ccp = 1.0f / float(a.ccp);
   for (int r = wave; r * 64 < total; r += NWAVES) {
     const int s = r * 64 + lane;
     if (s < total) {
@@ -1673,6 +1695,7 @@ static ConvArgs conv_args(const Geom& g, const ConvPlan& p, const float* x, cons
   a.rows = p.rows; a.bw = p.bw; a.boxc = p.boxc; a.row_tiles = p.row_tiles; a.ctiles = p.ctiles;
   a.plane_out = int(g.plane_out());
   a.ccp = p.ccp;
+  a.cl_vec = p.cl_vec ? 1 : 0;
   a.vec_store = 0;
   return a;
 }
@@ -1797,6 +1820,8 @@ int conv_fwd_channels_last(int nd, const float* x, const int64_t* x_shape, const
   int rc = make_geom_channels_last(nd, x_shape, w_shape, stride, dilation, padding, groups, &g);
   if (rc != CONV_OK) return rc;
   if (!x || !w || !y) return CONV_ERR_NULL;
+  // 16-byte copies of channel quads need a 16-byte aligned x.
+  g.x_aligned16 = (reinterpret_cast<uintptr_t>(x) & 15) == 0;
   ConvPlan p;
   rc = plan_conv(g, &p, forced_conv_cfg(), device_num_cu(), 0);
   if (rc != CONV_OK) return rc;

@@ -230,13 +230,22 @@ static bool plan_tap(const Geom& g, const TapSpecDesc& d, int num_cu, ConvPlan* 
   return true;
 }
 
-// Channels-last box pitch: Cc floats per site unless the 16 position lanes of a
-// matrix-core operand read (stride W * Cc floats apart) would share LDS banks;
-// then one float of padding per site.
-static int cl_pitch(int64_t cc, int64_t stride_w) {
-  int64_t v = cc * stride_w, gcd = 64;
-  while (v % gcd != 0) gcd /= 2;
-  return int(gcd <= 4 ? cc : cc + 1);
+// Channels-last box pitch (floats per site). The 16 position lanes of a
+// matrix-core operand read sit stride_w * pitch floats apart; they fall in
+// distinct banks (of 64) when gcd(stride_w * pitch, 64) <= 4. Scalar copies:
+// Cc, else Cc + 1. Quad copies (vec): the multiple of 4 in [Cc, Cc + 12] with
+// the smallest such gcd.
+static int64_t bank_gcd(int64_t v) {
+  int64_t g = 64;
+  while (v % g != 0) g /= 2;
+  return g;
+}
+static int cl_pitch(int64_t cc, int64_t stride_w, bool vec) {
+  if (!vec) return int(bank_gcd(cc * stride_w) <= 4 ? cc : cc + 1);
+  int64_t best = cc;
+  for (int64_t p = cc; p <= cc + 12; p += 4)
+    if (bank_gcd(p * stride_w) < bank_gcd(best * stride_w)) best = p;
+  return int(best);
 }
 
 int plan_conv(const Geom& g, ConvPlan* out, int force_cfg, int num_cu, int use_tap) {
@@ -290,9 +299,12 @@ int plan_conv(const Geom& g, ConvPlan* out, int force_cfg, int num_cu, int use_t
   // whole 256-float blocks (the DMA writes whole wave-wide rows of 64 slots); the
   // split-K partial sums reuse the two buffers after the reduction.
   auto r256 = [](int64_t v) { return (v + 255) / 256 * 256; };
+  // Channels-last inputs whose group channels come in aligned quads are copied
+  // 16 bytes per lane (chunks of a multiple of 4 channels).
+  bool clvec = g.cl && g.x_aligned16 && g.Cg % 4 == 0 && g.Cin % 4 == 0;
   auto layout = [&](int64_t cc, int64_t* xs, int64_t* ko, int64_t* ws) {
     const int64_t kcp = r4(cc * g.kvol());
-    *xs = r256((g.cl ? cl_pitch(cc, g.S[2]) : cc) * p.boxc);
+    *xs = r256((g.cl ? cl_pitch(cc, g.S[2], clvec) : cc) * p.boxc);
     *ko = r4(kcp + 8 * cs.KS);
     *ws = (kcp / 4 + cs.KS) * cs.WM * 64 * cs.MT;
     if (2 * (*xs + *ws) < red) *xs = r256(red / 2);
@@ -303,26 +315,37 @@ int plan_conv(const Geom& g, ConvPlan* out, int force_cfg, int num_cu, int use_t
   // taps per chunk), then the fewest chunks. Unsplit tiles keep room for two
   // workgroups per CU; split tiles are used where the grid is small.
   const int64_t budget = cs.KS > 1 ? kLdsLimit : 80 * 1024;  // double-buffered chunks
-  int best = 0;
-  int64_t best_work = 0, best_chunks = 0;
-  for (int64_t cc = 1; cc <= std::min<int64_t>(g.Cg, 1024); cc++) {
-    int64_t xs, ko, ws;
-    if (layout(cc, &xs, &ko, &ws) > budget) break;
-    const int64_t chunks = ceil_div(g.Cg, cc);
-    const int64_t work = chunks * r4(cc * g.kvol());
-    if (best == 0 || work < best_work || (work == best_work && chunks < best_chunks)) {
-      best = int(cc);
-      best_work = work;
-      best_chunks = chunks;
+  auto choose = [&]() {
+    const int64_t step = clvec ? 4 : 1;
+    int best = 0;
+    int64_t best_work = 0, best_chunks = 0;
+    for (int64_t cc = step; cc <= std::min<int64_t>(g.Cg, 1024); cc += step) {
+      int64_t xs, ko, ws;
+      if (layout(cc, &xs, &ko, &ws) > budget) break;
+      const int64_t chunks = ceil_div(g.Cg, cc);
+      const int64_t work = chunks * r4(cc * g.kvol());
+      if (best == 0 || work < best_work || (work == best_work && chunks < best_chunks)) {
+        best = int(cc);
+        best_work = work;
+        best_chunks = chunks;
+      }
     }
+    return best;
+  };
+  int best = choose();
+  if (best == 0 && clvec) {  // no quad chunk fits: scalar copies
+    clvec = false;
+    best = choose();
   }
   if (best == 0) {
+    // Nothing fits the budget: one channel per chunk if it fits at all.
     int64_t xs, ko, ws;
     if (layout(1, &xs, &ko, &ws) > kLdsLimit) return CONV_ERR_UNSUPPORTED;
     best = 1;
   }
   p.Cc = best;
-  p.ccp = g.cl ? cl_pitch(best, g.S[2]) : 0;
+  p.ccp = g.cl ? cl_pitch(best, g.S[2], clvec) : 0;
+  p.cl_vec = clvec;
   int64_t xs, ko, ws;
   p.lds_bytes = layout(p.Cc, &xs, &ko, &ws);
   p.xs_floats = int(xs);
@@ -441,7 +464,7 @@ std::string describe(const Geom& g, const ConvPlan& p) {
                 "kernel=%s%s cfg=%d MT=%d NT=%d WM=%d WN=%d KS=%d BM=%d BN=%d mode=%s Cc=%d kc_pad=%d "
                 "box=%dx%dx%d grid=%lldx%lldx%lld lds=%lld macs=%lld",
                 p.tap_spec >= 0 ? "conv_tap" : p.split_spec >= 0 ? "conv_tap_split" : "conv_mfma16",
-                g.cl ? " layout=channels_last" : "",
+                g.cl ? (p.cl_vec ? " layout=channels_last copy=quad" : " layout=channels_last copy=scalar") : "",
                 p.tap_spec >= 0 ? p.tap_spec : p.split_spec >= 0 ? p.split_spec : p.cfg, cs.MT, cs.NT,
                 cs.WM, cs.WN, cs.KS, p.BM, p.BN, p.mode == TILE_FLAT ? "flat" : "row", p.Cc,
                 p.kc_pad, p.kdspan, p.rows, p.bw, (long long)p.grid[0], (long long)p.grid[1],

@@ -13,6 +13,7 @@ namespace convhip {
 struct Geom {
   int nd = 3;
   bool cl = false;            // channels-last tensors: x [N, D, H, W, C_in], y [N, D_out, H_out, W_out, C_out]
+  bool x_aligned16 = true;    // channels-last: x starts on a 16-byte boundary
   int64_t N = 0, Cin = 0, Cout = 0, G = 1, Cg = 0, Coutg = 0;
   int64_t L[3] = {1, 1, 1};   // input D, H, W
   int64_t K[3] = {1, 1, 1};   // kernel kD, kH, kW
@@ -70,7 +71,8 @@ struct ConvPlan {
   int rows = 0;        // input rows in the box (maximum over tiles)
   int bw = 0;          // input columns in the box
   int boxc = 0;        // floats per channel in the box: kdspan * rows * bw (channels-last: sites)
-  int ccp = 0;         // channels-last: LDS floats per box site (Cc, or Cc + 1 against bank conflicts)
+  int ccp = 0;         // channels-last: LDS floats per box site (Cc padded against bank conflicts)
+  bool cl_vec = false; // channels-last: box copied in 16-byte channel quads
   int xs_floats = 0;   // LDS floats of the box region (box, or the split-K partial sums if larger)
   int koff_ints = 0;   // LDS ints of the tap-offset table (padded for prefetch)
   int ws_floats = 0;   // LDS floats of the weight fragments (padded for prefetch)

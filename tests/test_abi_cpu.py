@@ -98,6 +98,8 @@ def test_channels_last_plans_take_the_generic_kernel():
         fields = dict(t.split("=", 1) for t in desc.split() if "=" in t)
         assert fields["kernel"] == "conv_mfma16" and fields["layout"] == "channels_last", desc
         assert int(fields["lds"]) <= 160 * 1024, desc
+        # channel quads (C_in/groups a multiple of 4) are copied 16 bytes at a time
+        assert fields["copy"] == ("quad" if (xs[-1] // g) % 4 == 0 and int(fields["Cc"]) % 4 == 0 else "scalar"), desc
 
 
 def test_conv3d_min_softmax_validation_errors():
