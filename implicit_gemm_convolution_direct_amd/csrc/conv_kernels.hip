@@ -288,7 +288,9 @@ __device__ __forceinline__ void stage_box_cl(const ConvArgs& a, const TileGeo& t
 // chunk) into dst, in the order the matrix core consumes them: for k-step s and
 // wave row wm, lane l holds W[m = wm*16*MT + 16*mi + (l%16)][k = 4s + l/16] for
 // mi = 0..MT-1 contiguously, so one vector LDS read delivers a lane's A operands.
-template <int MT, int WM, int NWAVES = 4>
+// TAPMAJOR: the chunk's reduction index runs k = tap * Cc + c (channels-last
+// specialisations) instead of k = c * kvol + tap.
+template <int MT, int WM, int NWAVES = 4, bool TAPMAJOR = false>
 __device__ __forceinline__ void stage_wfrag(const ConvArgs& a, int g, int m0, int c0, int nsteps, float* dst,
                                             int wave, int lane) {
   const int cc_count = min(a.Cc, a.Cg - c0);
@@ -306,7 +308,8 @@ __device__ __forceinline__ void stage_wfrag(const ConvArgs& a, int g, int m0, in
     const int k = 4 * s + (fl >> 4);
     const int m = fwm * 16 * MT + 16 * mi + (fl & 15);
     const bool ok = (k < kvalid) && (m0 + m < a.Coutg);
-    const float* src = ok ? a.w + (w_g + int64_t(m) * a.kfull + k) : kZeroWord;
+    const int kw = TAPMAJOR ? (k % a.Cc) * a.kvol + k / a.Cc : k;
+    const float* src = ok ? a.w + (w_g + int64_t(m) * a.kfull + kw) : kZeroWord;
     lds_dma_f32(src, dst + wi * 64);
   }
 }
@@ -560,6 +563,8 @@ struct TapGeo {
   // Box rows a multiple of 4 floats long: copied in 16-byte chunks (the planner
   // checks the alignment of the rows' first input column).
   static constexpr bool ROWCOPY = BW % 4 == 0;
+  static constexpr bool CL = false;       // channel-major box (NCDHW input)
+  static constexpr bool TAPMAJOR = false; // reduction index k = c * KVOL + tap
   static constexpr int BW_ = BW, ROWS_ = ROWS, KDSPAN_ = KDSPAN;
   template <int NCH, int WM, int MT>
   static constexpr int lds_floats() { return 2 * XS + (NCH * NS + 1) * WM * 64 * MT; }
@@ -569,6 +574,34 @@ struct TapGeo {
     if (k >= K) return 0;
     const int c = k / KVOL, r = k % KVOL, td = r / (KH * KW), r2 = r % (KH * KW), th = r2 / KW, tw = r2 % KW;
     return c * BOXC + td * DD * PLANE + th * DH * BW + tw * DW;
+  }
+};
+
+// The same specialisation for channels-last input x [N, D, H, W, C_in]: the box
+// holds CCP floats per (plane, row, column) site, channels innermost, and the
+// reduction index runs tap-major, k = tap * CC + c, so each 4-deep k-step reads 4
+// consecutive channels of one tap (one lane pattern for every step).
+template <int KD, int KH, int KW, int DD, int DH, int DW, int CC, int KDSPAN, int ROWS, int BW, int CCP>
+struct TapGeoCL {
+  static_assert(CC % 4 == 0 && CCP % 4 == 0 && CCP >= CC, "channel quads");
+  static constexpr int CCH = CC;
+  static constexpr int KVOL = KD * KH * KW;
+  static constexpr int K = CC * KVOL;
+  static constexpr int NS = (K + 3) / 4;
+  static constexpr int PLANE = ROWS * BW;     // sites per box plane
+  static constexpr int BOXC = KDSPAN * PLANE; // sites in the box
+  static constexpr int XS = (CCP * BOXC + 255) / 256 * 256;
+  static constexpr bool ROWCOPY = false;
+  static constexpr bool CL = true;
+  static constexpr bool TAPMAJOR = true;
+  static constexpr int CCP_ = CCP;
+  static constexpr int BW_ = BW, ROWS_ = ROWS, KDSPAN_ = KDSPAN;
+  template <int NCH, int WM, int MT>
+  static constexpr int lds_floats() { return 2 * XS + (NCH * NS + 1) * WM * 64 * MT; }
+  static constexpr int koff(int k) {
+    if (k >= K) return 0;
+    const int c = k % CC, tap = k / CC, td = tap / (KH * KW), r2 = tap % (KH * KW), th = r2 / KW, tw = r2 % KW;
+    return c + (td * DD * PLANE + th * DH * BW + tw * DW) * CCP;
   }
 };
 
@@ -640,10 +673,39 @@ __device__ __forceinline__ void stage_rows16(const ConvArgs& a, const TileGeo& t
   }
 }
 
+// Channels-last box of one chunk (TapGeoCL) as 16-byte channel quads: box quad u
+// = (site, cq) <- channels c0 + 4cq .. c0 + 4cq + 3 of input site (id0 + zd,
+// ih0 + zr, iw0 + col); quads past the chunk's channels and sites outside the
+// input read the zero word. Copy i of wave w moves quads (i*NWAVES + w)*64 + lane.
+template <class G, int NWAVES>
+__device__ __forceinline__ void stage_cl_quads(const ConvArgs& a, const TileGeo& t, int c0, float* dst, int wave,
+                                               int lane) {
+  constexpr int Q = G::CCP_ / 4, QV = G::CCH / 4;
+  constexpr int NQ = G::BOXC * Q;
+  constexpr int NI = (NQ + 64 * NWAVES - 1) / (64 * NWAVES);
+  const float* xn = a.x + int64_t(t.n) * a.L0 * a.L1 * a.L2 * a.Cin + (int64_t(t.g) * a.Cg + c0);
+#pragma unroll
+  for (int i = 0; i < NI; i++) {
+    const int u0 = (i * NWAVES + wave) * 64;
+    const int u = u0 + lane;
+    if (u < NQ) {
+      const int site = u / Q, cq = u - site * Q;
+      const int zz = site / G::BW_, col = site - zz * G::BW_;
+      const int zd = zz / G::ROWS_, zr = zz - zd * G::ROWS_;
+      const int id = t.id0 + zd, ih = t.ih0 + zr, iw = t.iw0 + col;
+      const bool ok = cq < QV && unsigned(id) < unsigned(a.L0) && unsigned(ih) < unsigned(a.L1) &&
+                      unsigned(iw) < unsigned(a.L2);
+      const float* src = xn + ((int64_t(id) * a.L1 + ih) * a.L2 + iw) * a.Cin + 4 * cq;
+      lds_dma_f32x4(ok ? src : kZeroWord, dst + 4 * u0);
+    }
+  }
+}
+
 template <class G, int NWAVES>
 __device__ __forceinline__ void stage_tap_box(const ConvArgs& a, const TileGeo& t, int c0, float* dst, int wave,
                                               int lane) {
-  if constexpr (G::ROWCOPY) stage_rows16<G, NWAVES>(a, t, c0, dst, wave, lane);
+  if constexpr (G::CL) stage_cl_quads<G, NWAVES>(a, t, c0, dst, wave, lane);
+  else if constexpr (G::ROWCOPY) stage_rows16<G, NWAVES>(a, t, c0, dst, wave, lane);
   else stage_box<NWAVES>(a, t, c0, dst, wave, lane);
 }
 
@@ -723,7 +785,7 @@ __global__ __launch_bounds__(64 * WM * WN) void conv_tap_kernel(ConvArgs a) {
   if (item >= a.items) return;
 #pragma unroll
   for (int c = 0; c < NCH; c++)
-    stage_wfrag<MT, WM, NWAVES>(a, 0, 0, c * G::CCH, G::NS, Wres + c * G::NS * SSTRIDE, wave, lane);
+    stage_wfrag<MT, WM, NWAVES, G::TAPMAJOR>(a, 0, 0, c * G::CCH, G::NS, Wres + c * G::NS * SSTRIDE, wave, lane);
   TileGeo t = tile_geo(a, item % a.tiles_per_plane, item / a.tiles_per_plane, 0, BM, BN, true);
   stage_tap_box<G, NWAVES>(a, t, 0, box0, wave, lane);
   wait_vmem();
@@ -745,7 +807,7 @@ __global__ __launch_bounds__(64 * WM * WN) void conv_tap_kernel(ConvArgs a) {
   int parity = 0;  // buffer holding chunk 0 of the current item
   for (;;) {
     int noff[NT], pidx[NT];
-    tile_positions<NT>(a, t, wn, li, noff, pidx);
+    tile_positions<NT, G::CL>(a, t, wn, li, noff, pidx);
     int addr[NP][NT];
 #pragma unroll
     for (int q = 0; q < NP; q++)
@@ -769,7 +831,7 @@ __global__ __launch_bounds__(64 * WM * WN) void conv_tap_kernel(ConvArgs a) {
         tap_stage<MT, NT, WM, NWAVES, G, NP>(a, last ? tn : t, has_next, c0n, box0, box1, wchunk, addr, acc, wave,
                                              lane);
       if (last) {
-        store_tile<MT, NT>(a, t, wm, kg, pidx, acc, bias);
+        store_tile<MT, NT, G::CL>(a, t, wm, kg, pidx, acc, bias);
 #pragma unroll
         for (int mi = 0; mi < MT; mi++)
 #pragma unroll
@@ -1582,19 +1644,31 @@ static int launch_conv_cfg(const ConvArgs& args, const ConvPlan& p, hipStream_t 
   return hipGetLastError() == hipSuccess ? CONV_OK : CONV_ERR_HIP;
 }
 
-template <int MT, int NT, int WM, int WN, int NCH, int KD, int KH, int KW, int DD, int DH, int DW, int CC, int KDSPAN,
-          int ROWS, int BW>
-static int launch_tap(const ConvArgs& args, const ConvPlan& p, hipStream_t stream) {
-  using G = TapGeo<KD, KH, KW, DD, DH, DW, CC, KDSPAN, ROWS, BW>;
-  static std::once_flag once;
-  static hipError_t err = hipSuccess;
+template <int MT, int NT, int WM, int WN, int NCH, class G>
+static int launch_tap_geo(const ConvArgs& args, const ConvPlan& p, hipStream_t stream) {
   auto fn = conv_tap_kernel<MT, NT, WM, WN, NCH, G>;
   static_assert(4 * G::template lds_floats<NCH, WM, MT>() <= kLdsLimit, "tap specialisation exceeds LDS");
   if (4 * int64_t(G::template lds_floats<NCH, WM, MT>()) != p.lds_bytes) return CONV_ERR_UNSUPPORTED;
-  (void)once;
-  (void)err;
   hipLaunchKernelGGL(fn, dim3(unsigned(p.grid[0])), dim3(64 * WM * WN), 0, stream, args);
   return hipGetLastError() == hipSuccess ? CONV_OK : CONV_ERR_HIP;
+}
+
+template <int MT, int NT, int WM, int WN, int NCH, int KD, int KH, int KW, int DD, int DH, int DW, int CC, int KDSPAN,
+          int ROWS, int BW>
+static int launch_tap(const ConvArgs& args, const ConvPlan& p, hipStream_t stream) {
+  return launch_tap_geo<MT, NT, WM, WN, NCH, TapGeo<KD, KH, KW, DD, DH, DW, CC, KDSPAN, ROWS, BW>>(args, p, stream);
+}
+
+static int launch_tap_cl_spec(const ConvArgs& args, const ConvPlan& p, hipStream_t stream) {
+  switch (p.tap_spec) {
+#define CONVHIP_TAP_CL_CASE(id, MT, NT, WM, WN, NCH, KD, KH, KW, DD, DH, DW, CC, KDSPAN, ROWS, BW, CCP)            \
+  case id:                                                                                                       \
+    return launch_tap_geo<MT, NT, WM, WN, NCH, TapGeoCL<KD, KH, KW, DD, DH, DW, CC, KDSPAN, ROWS, BW, CCP>>(args, p, \
+                                                                                                           stream);
+    CONVHIP_TAP_CL_SPECS(CONVHIP_TAP_CL_CASE)
+#undef CONVHIP_TAP_CL_CASE
+    default: return CONV_ERR_UNSUPPORTED;
+  }
 }
 
 template <int NT, int NW, int KD, int KH, int KW, int DD, int DH, int DW, int F, int ROWS, int BW>
@@ -1713,7 +1787,7 @@ static int forced_conv_cfg() {
   return (v >= 0 && v < CFG_COUNT) ? v : -1;
 }
 
-// CONVHIP_TAP=0 keeps conv_fwd and conv3d_min_softmax off the build-time
+// CONVHIP_TAP=0 keeps conv_fwd, conv_fwd_channels_last and conv3d_min_softmax off the build-time
 // specialised kernels.
 static int use_tap() {
   const char* s = std::getenv("CONVHIP_TAP");
@@ -1784,7 +1858,7 @@ int conv_plan_describe(int nd, const int64_t* x_shape, const int64_t* w_shape, c
     s = describe(g, p);
   } else {
     ConvPlan p;
-    rc = plan_conv(g, &p, forced_conv_cfg(), 256, fused == 2 ? 0 : use_tap());
+    rc = plan_conv(g, &p, forced_conv_cfg(), 256, use_tap());
     if (rc != CONV_OK) return rc;
     s = describe(g, p);
   }
@@ -1823,11 +1897,13 @@ int conv_fwd_channels_last(int nd, const float* x, const int64_t* x_shape, const
   // 16-byte copies of channel quads need a 16-byte aligned x.
   g.x_aligned16 = (reinterpret_cast<uintptr_t>(x) & 15) == 0;
   ConvPlan p;
-  rc = plan_conv(g, &p, forced_conv_cfg(), device_num_cu(), 0);
+  rc = plan_conv(g, &p, forced_conv_cfg(), device_num_cu(), use_tap());
   if (rc != CONV_OK) return rc;
   ConvArgs a = conv_args(g, p, x, w, bias, y);
   a.vec_store = (g.Cout % 4 == 0 && g.Coutg % 4 == 0 && (reinterpret_cast<uintptr_t>(y) & 15) == 0) ? 1 : 0;
-  return launch_generic<true>(a, p, reinterpret_cast<hipStream_t>(stream));
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (p.tap_spec >= 0) return launch_tap_cl_spec(a, p, s);
+  return launch_generic<true>(a, p, s);
 }
 int conv3d_min_softmax(const float* x, const int64_t* x_shape, const float* w, const int64_t* w_shape,
                        const float* bias, const int* stride, const int* dilation, const int* padding, int groups,

@@ -116,6 +116,15 @@ const TapSpecDesc* tap_specs(int* count) {
   return specs;
 }
 
+const TapClSpecDesc* tap_cl_specs(int* count) {
+#define CONVHIP_TAP_CL_DESC(id, MT, NT, WM, WN, NCH, KD, KH, KW, DD, DH, DW, CC, KDSPAN, ROWS, BW, CCP) \
+  {id, MT, NT, WM, WN, NCH, KD, KH, KW, DD, DH, DW, CC, KDSPAN, ROWS, BW, CCP},
+  static const TapClSpecDesc specs[] = {CONVHIP_TAP_CL_SPECS(CONVHIP_TAP_CL_DESC)};
+#undef CONVHIP_TAP_CL_DESC
+  *count = int(sizeof(specs) / sizeof(specs[0]));
+  return specs;
+}
+
 const SplitSpecDesc* split_specs(int* count) {
 #define CONVHIP_SPLIT_DESC(id, NT, NW, KD, KH, KW, DD, DH, DW, F, ROWS, BW, TS) \
   {id, NT, NW, KD, KH, KW, DD, DH, DW, F, ROWS, BW, TS},
@@ -248,8 +257,77 @@ static int cl_pitch(int64_t cc, int64_t stride_w, bool vec) {
   return int(best);
 }
 
+// Plan of a channels-last tap specialisation if the geometry is the one it was
+// built for (16-byte aligned x with C_in a multiple of 4: the box is copied in
+// channel quads).
+static bool plan_tap_cl(const Geom& g, const TapClSpecDesc& d, int num_cu, ConvPlan* p) {
+  const int BM = 16 * d.MT * d.WM, BN = 16 * d.NT * d.WN;
+  if (!g.cl || !g.x_aligned16 || g.Cin % 4 != 0) return false;
+  if (g.G != 1 || g.Coutg > BM || g.Cg != int64_t(d.CC) * d.NCH) return false;
+  if (g.K[0] != d.KD || g.K[1] != d.KH || g.K[2] != d.KW) return false;
+  if (g.Dl[0] != d.DD || g.Dl[1] != d.DH || g.Dl[2] != d.DW) return false;
+  const int mode = (g.O[2] * 2 <= BN) ? TILE_FLAT : TILE_ROW;
+  int rows, bw, row_tiles;
+  int64_t tiles;
+  box_dims(g, mode, BN, &rows, &bw, &tiles, &row_tiles);
+  const int kdspan = int((g.K[0] - 1) * g.Dl[0] + 1);
+  if (rows != d.ROWS || kdspan != d.KDSPAN) return false;
+  // A single-row box (1-D) may be staged wider than the tile needs.
+  if (d.ROWS == 1 && d.KDSPAN == 1 && mode == TILE_ROW) {
+    if (bw > d.BW) return false;
+  } else if (bw != d.BW) {
+    return false;
+  }
+  const int64_t items = tiles * g.N * g.O[0];
+  if (items > std::numeric_limits<int32_t>::max()) return false;
+  const int64_t kvol = int64_t(d.KD) * d.KH * d.KW;
+  const int64_t ns = (d.CC * kvol + 3) / 4;
+  const int64_t xs = (int64_t(d.CCP) * d.KDSPAN * d.ROWS * d.BW + 255) / 256 * 256;
+  const int64_t wf = (d.NCH * ns + 1) * d.WM * 64 * d.MT;
+  const int64_t bytes = 4 * (2 * xs + wf);
+  if (bytes > kLdsLimit) return false;
+  ConvPlan q;
+  q.cfg = -1;
+  q.tap_spec = d.id;
+  q.threads = 64 * d.WM * d.WN;
+  q.BM = BM;
+  q.BN = BN;
+  q.mode = mode;
+  q.Cc = d.CC;
+  q.kc_pad = int(ns * 4);
+  q.kdspan = kdspan;
+  q.rows = rows;
+  q.bw = d.BW;
+  q.boxc = kdspan * rows * d.BW;
+  q.ccp = d.CCP;
+  q.cl_vec = true;
+  q.xs_floats = int(xs);
+  q.koff_ints = 0;
+  q.ws_floats = int(wf);
+  q.tiles_per_plane = tiles;
+  q.row_tiles = row_tiles;
+  q.ctiles = 1;
+  q.nchunks = d.NCH;
+  q.items = items;
+  q.lds_bytes = bytes;
+  const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(2, kLdsLimit / bytes));
+  q.grid[0] = std::min<int64_t>(items, per_cu * num_cu);
+  q.grid[1] = 1;
+  q.grid[2] = 1;
+  *p = q;
+  return true;
+}
+
 int plan_conv(const Geom& g, ConvPlan* out, int force_cfg, int num_cu, int use_tap) {
-  if (g.cl) use_tap = 0;
+  if (g.cl) {
+    if (use_tap != 0 && force_cfg < 0) {
+      int n = 0;
+      const TapClSpecDesc* specs = tap_cl_specs(&n);
+      for (int i = 0; i < n; i++)
+        if (plan_tap_cl(g, specs[i], num_cu, out)) return CONV_OK;
+    }
+    use_tap = 0;
+  }
   if (use_tap != 0 && force_cfg < 0) {
     int n = 0;
     const TapSpecDesc* specs = tap_specs(&n);
@@ -451,7 +529,11 @@ int plan_fused(const Geom& g, int min_dim, FusedPlan* out, bool allow_spec) {
 std::string describe(const Geom& g, const ConvPlan& p) {
   char buf[512];
   CfgShape cs = cfg_shape(p.cfg);
-  if (p.tap_spec >= 0) {
+  if (p.tap_spec >= 0 && g.cl) {
+    int n = 0;
+    const TapClSpecDesc& d = tap_cl_specs(&n)[p.tap_spec];
+    cs = CfgShape{d.MT, d.NT, d.WM, d.WN, 1};
+  } else if (p.tap_spec >= 0) {
     int n = 0;
     const TapSpecDesc& d = tap_specs(&n)[p.tap_spec];
     cs = CfgShape{d.MT, d.NT, d.WM, d.WN, 1};

@@ -121,9 +121,24 @@ struct TapSpecDesc {
 };
 const TapSpecDesc* tap_specs(int* count);
 
+// The persistent tap kernel on channels-last input (x [N, spatial..., C_in]):
+// the staged box holds CCP floats per input site (channels innermost, copied as
+// 16-byte quads). X(id, MT, NT, WM, WN, NCH, KD, KH, KW, DD, DH, DW, CC, KDSPAN,
+// ROWS, BW, CCP) with BW input sites per box row.
+#define CONVHIP_TAP_CL_SPECS(X)                                                       \
+  /* Conv1d 64->128, k=3, stride 3, dilation 4: 128 ch x 256 positions, 8 input  \
+     channels per chunk, 774 input sites per tile */                               \
+  X(0, 4, 4, 2, 4, 8, 1, 1, 3, 1, 1, 4, 8, 1, 1, 774, 8)
+
+struct TapClSpecDesc {
+  int id, MT, NT, WM, WN, NCH, KD, KH, KW, DD, DH, DW, CC, KDSPAN, ROWS, BW, CCP;
+};
+const TapClSpecDesc* tap_cl_specs(int* count);
+
 // num_cu: compute units of the device (sizes the persistent grid).
 // use_tap: -1 planner's choice, 0 never use a tap specialisation. Channels-last
-// geometries (g.cl) always take the generic kernel.
+// geometries (g.cl) take the channels-last tap specialisations (tap_spec then
+// indexes CONVHIP_TAP_CL_SPECS) or the generic kernel.
 int plan_conv(const Geom& g, ConvPlan* p, int force_cfg = -1, int num_cu = 256, int use_tap = -1);
 
 // Build-time specialisations of the depth-streamed fused kernel (stride 1,

@@ -191,3 +191,72 @@ def test_channels_last_asym_workload_slices():
     for n in (0, x.shape[0] - 1):
         ref = oracle.conv_channels_last(x[n:n + 1], w, None, *args)
         assert_conv_close(y[n:n + 1].cpu().numpy(), ref, w.shape, f"cl {name} sample {n}")
+
+
+# Shapes with the geometry of the channels-last tap specialisation (Conv1d
+# 64 -> <=128 channels, k = 3, dilation 4, stride 3, 8 channels per chunk) at
+# lengths the oracle checks in full.
+TAP_CL_CASES = [
+    ((2, 3000, 64), (128, 64, 3), 3, 4, 0, False),
+    ((1, 5000, 64), (100, 64, 3), 3, 4, 4, True),     # padding, fewer channels, ragged last tile
+    ((2, 3001, 64), (128, 64, 3), 3, 4, 2, True),
+    ((4, 200000, 64), (128, 64, 3), 3, 4, 0, False),  # several items per workgroup
+    ((2, 2000, 64), (128, 64, 3), 2, 4, 1, True),     # stride 2: a narrower box inside the staged one
+]
+
+
+@pytest.mark.parametrize("case", range(len(TAP_CL_CASES)))
+def test_channels_last_tap_kernel_integer_exact(case):
+    xs, ws, s, d, p, bias = TAP_CL_CASES[case]
+    desc = ch.plan_describe(xs, ws, s, d, p, 1, channels_last=True)
+    assert "kernel=conv_tap " in desc and "layout=channels_last" in desc, desc
+    r = np.random.default_rng(600 + case)
+    x, w, b = _int_inputs(r, xs, ws, bias)
+    say(f"cl tap case {case}: x={xs} w={ws}: {desc}")
+    y = gpu_conv_cl(x, w, b, s, d, p, 1)
+    np.testing.assert_array_equal(y.astype(np.float64), oracle.conv_channels_last(x, w, b, s, d, p, 1))
+
+
+def test_channels_last_tap_disabled_and_misaligned_take_generic(monkeypatch):
+    """CONVHIP_TAP=0, or an x that is not 16-byte aligned, keep the channels-last
+    call on the generic kernel; results unchanged."""
+    xs, ws, s, d, p, _ = TAP_CL_CASES[0]
+    r = np.random.default_rng(9)
+    x, w, b = _int_inputs(r, xs, ws, True)
+    ref = oracle.conv_channels_last(x, w, b, s, d, p, 1)
+    xd = torch.empty(x.size + 1, dtype=torch.float32, device=dev())[1:].view(xs)
+    xd.copy_(torch.from_numpy(x))
+    assert xd.data_ptr() % 16 != 0
+    y = ch.conv_fwd_channels_last(xd, to_dev(w), to_dev(b), s, d, p, 1)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(y.cpu().numpy().astype(np.float64), ref)
+    monkeypatch.setenv("CONVHIP_TAP", "0")
+    desc = ch.plan_describe(xs, ws, s, d, p, 1, channels_last=True)
+    assert "kernel=conv_mfma16 " in desc, desc
+    np.testing.assert_array_equal(gpu_conv_cl(x, w, b, s, d, p, 1).astype(np.float64), ref)
+
+
+def test_channels_last_long_conv1d_full_size_slices():
+    """The long Conv1d in channels-last order at full size (x [64, 524280, 64],
+    8.6 GB, generated on the device): two samples regenerated on the host are
+    checked bit for bit against the device copy and their outputs against the
+    oracle."""
+    cfg = synth.WORKLOADS["long_conv1d"]
+    N, C, L = cfg["x"]
+    xs = (N, L, C)
+    sx, _, _ = cfg["seeds"]
+    args = (cfg["stride"], cfg["dilation"], cfg["padding"], cfg["groups"])
+    _, w, _ = synth.make_inputs("long_conv1d", n_samples=1)
+    say("cl long conv1d: " + ch.plan_describe(xs, w.shape, *args, channels_last=True))
+    xd = torch.empty(xs, dtype=torch.float32, device=dev())
+    ch.synth_fill(xd, sx, ch.KIND_UNIFORM01)
+    y = ch.conv_fwd_channels_last(xd, to_dev(w), None, *args)
+    torch.cuda.synchronize()
+    per = L * C
+    for n in (0, N - 1):
+        xh = synth.uniform01(sx, (1, L, C), start=n * per)
+        np.testing.assert_array_equal(xd[n:n + 1].cpu().numpy(), xh)
+        ref = oracle.conv_channels_last(xh, w, None, *args)
+        assert_conv_close(y[n:n + 1].cpu().numpy(), ref, w.shape, f"cl long conv1d n={n}")
+    del xd, y
+    torch.cuda.empty_cache()
