@@ -907,7 +907,10 @@ struct SplitGeo {
   }
 };
 
-template <int NT, int NW, class G>
+// CL: channels-last x [N, D, H, W, C_in] and y [N, D_out, H_out, W_out, C_out];
+// the LDS box keeps the same per-channel layout, only the copies' sources (input
+// sites C_in floats apart) and the output addresses change.
+template <int NT, int NW, class G, bool CL = false>
 __global__ __launch_bounds__(64 * NW) void conv_tap_split_kernel(ConvArgs a) {
   constexpr TapPatterns<G> P{};
   constexpr int NP = P.np;
@@ -973,7 +976,10 @@ __global__ __launch_bounds__(64 * NW) void conv_tap_split_kernel(ConvArgs a) {
   // (od*S0 - P0 + td*DD, zr - P1, F*j - P2) of channel g*Cg + c. Copy i of a
   // plane moves elements 64i .. 64i + 63; the in-plane part of each lane's
   // source is the same for every plane.
-  const float* xc = a.x + (int64_t(n) * a.Cin + int64_t(g) * a.Cg + c) * (int64_t(a.L0) * a.L1 * a.L2);
+  const int64_t vol_in = int64_t(a.L0) * a.L1 * a.L2;
+  const float* xc = CL ? a.x + int64_t(n) * vol_in * a.Cin + (int64_t(g) * a.Cg + c)
+                       : a.x + (int64_t(n) * a.Cin + int64_t(g) * a.Cg + c) * vol_in;
+  const int site = CL ? a.Cin : 1;  // floats between neighbouring input sites
   int soff[G::PLANE_INSTR];
   uint32_t sok = 0;
 #pragma unroll
@@ -982,14 +988,14 @@ __global__ __launch_bounds__(64 * NW) void conv_tap_split_kernel(ConvArgs a) {
     const int zr = e / G::BWC, j = e - zr * G::BWC;
     const int ih = zr - a.P1, iw = G::FF * j - a.P2;
     const bool ok = e < G::PLANE && unsigned(ih) < unsigned(a.L1) && unsigned(iw) < unsigned(a.L2);
-    soff[i] = ok ? ih * a.L2 + iw : 0;
+    soff[i] = ok ? (ih * a.L2 + iw) * site : 0;
     sok |= uint32_t(ok) << i;
   }
   auto stage_copy = [&](int td, int i) {
     const int id = od * a.S0 - a.P0 + td * a.D0;
     const bool ok = unsigned(id) < unsigned(a.L0) && ((sok >> i) & 1);
     if (i * 64 + lane < G::PLANE)
-      lds_dma_f32(ok ? xc + (int64_t(id) * a.L1 * a.L2 + soff[i]) : kZeroWord, box + td * G::PLANE + i * 64);
+      lds_dma_f32(ok ? xc + (int64_t(id) * a.L1 * a.L2 * site + soff[i]) : kZeroWord, box + td * G::PLANE + i * 64);
   };
 #pragma unroll
   for (int i = 0; i < G::PLANE_INSTR; i++) stage_copy(0, i);
@@ -1086,7 +1092,12 @@ __global__ __launch_bounds__(64 * NW) void conv_tap_split_kernel(ConvArgs a) {
     for (int w2 = 0; w2 < NW; w2++)
       part[j][w2] = pr < NT * 4 ? smem[((w2 * NT + (pr >> 2)) * 4 + (pr & 3)) * 64 + lane] : 0.0f;
   }
-  float* yg = a.y + (int64_t(n) * a.Cout + int64_t(g) * a.Coutg) * a.O0 * out_plane + int64_t(od) * out_plane;
+  // Channel ch of position p: NCDHW y[n][g*Coutg + ch][od][p], channels-last
+  // y[n][od][p][g*Coutg + ch].
+  float* yg = CL ? a.y + (int64_t(n) * a.O0 + od) * out_plane * a.Cout + int64_t(g) * a.Coutg
+                 : a.y + (int64_t(n) * a.Cout + int64_t(g) * a.Coutg) * a.O0 * out_plane + int64_t(od) * out_plane;
+  const int64_t ch_stride = CL ? 1 : int64_t(a.O0) * out_plane;
+  const int64_t p_stride = CL ? a.Cout : 1;
 #pragma unroll
   for (int j = 0; j < NPR; j++) {
     const int pr = wave + NW * j;
@@ -1097,7 +1108,7 @@ __global__ __launch_bounds__(64 * NW) void conv_tap_split_kernel(ConvArgs a) {
     const int ch = 4 * kg + r;
     const int p = 16 * (int(blockIdx.z) * NT + ni) + li;
     const float b = r == 0 ? b4[0] : r == 1 ? b4[1] : r == 2 ? b4[2] : b4[3];
-    if (pr < NT * 4 && ch < a.Coutg && p < a.plane_out) yg[int64_t(ch) * a.O0 * out_plane + p] = v + b;
+    if (pr < NT * 4 && ch < a.Coutg && p < a.plane_out) yg[ch * ch_stride + p * p_stride] = v + b;
   }
 }
 
@@ -1671,20 +1682,21 @@ static int launch_tap_cl_spec(const ConvArgs& args, const ConvPlan& p, hipStream
   }
 }
 
-template <int NT, int NW, int KD, int KH, int KW, int DD, int DH, int DW, int F, int ROWS, int BW>
+template <int NT, int NW, int KD, int KH, int KW, int DD, int DH, int DW, int F, int ROWS, int BW, bool CL>
 static int launch_split(const ConvArgs& args, const ConvPlan& p, hipStream_t stream) {
   using G = SplitGeo<KD, KH, KW, DD, DH, DW, F, ROWS, BW, NW>;
-  hipLaunchKernelGGL((conv_tap_split_kernel<NT, NW, G>),
+  hipLaunchKernelGGL((conv_tap_split_kernel<NT, NW, G, CL>),
                      dim3(unsigned(p.grid[0]), unsigned(p.grid[1]), unsigned(p.grid[2])),
                      dim3(64 * NW), 0, stream, args);
   return hipGetLastError() == hipSuccess ? CONV_OK : CONV_ERR_HIP;
 }
 
+template <bool CL>
 static int launch_split_spec(const ConvArgs& args, const ConvPlan& p, hipStream_t stream) {
   switch (p.split_spec) {
 #define CONVHIP_SPLIT_CASE(id, NT, NW, KD, KH, KW, DD, DH, DW, F, ROWS, BW, TS) \
   case id:                                                                  \
-    return launch_split<NT, NW, KD, KH, KW, DD, DH, DW, F, ROWS, BW>(args, p, stream);
+    return launch_split<NT, NW, KD, KH, KW, DD, DH, DW, F, ROWS, BW, CL>(args, p, stream);
     CONVHIP_SPLIT_SPECS(CONVHIP_SPLIT_CASE)
 #undef CONVHIP_SPLIT_CASE
     default: return CONV_ERR_UNSUPPORTED;
@@ -1883,7 +1895,7 @@ int conv_fwd(int nd, const float* x, const int64_t* x_shape, const float* w, con
   ConvArgs a = conv_args(g, p, x, w, bias, y);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (p.tap_spec >= 0) return launch_tap_spec(a, p, s);
-  if (p.split_spec >= 0) return launch_split_spec(a, p, s);
+  if (p.split_spec >= 0) return launch_split_spec<false>(a, p, s);
   return launch_generic<false>(a, p, s);
 }
 
@@ -1894,8 +1906,10 @@ int conv_fwd_channels_last(int nd, const float* x, const int64_t* x_shape, const
   int rc = make_geom_channels_last(nd, x_shape, w_shape, stride, dilation, padding, groups, &g);
   if (rc != CONV_OK) return rc;
   if (!x || !w || !y) return CONV_ERR_NULL;
-  // 16-byte copies of channel quads need a 16-byte aligned x.
+  // 16-byte copies of channel quads need a 16-byte aligned x, 16-byte weight
+  // copies an aligned w.
   g.x_aligned16 = (reinterpret_cast<uintptr_t>(x) & 15) == 0;
+  g.w_aligned16 = (reinterpret_cast<uintptr_t>(w) & 15) == 0;
   ConvPlan p;
   rc = plan_conv(g, &p, forced_conv_cfg(), device_num_cu(), use_tap());
   if (rc != CONV_OK) return rc;
@@ -1903,6 +1917,7 @@ int conv_fwd_channels_last(int nd, const float* x, const int64_t* x_shape, const
   a.vec_store = (g.Cout % 4 == 0 && g.Coutg % 4 == 0 && (reinterpret_cast<uintptr_t>(y) & 15) == 0) ? 1 : 0;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (p.tap_spec >= 0) return launch_tap_cl_spec(a, p, s);
+  if (p.split_spec >= 0) return launch_split_spec<true>(a, p, s);
   return launch_generic<true>(a, p, s);
 }
 int conv3d_min_softmax(const float* x, const int64_t* x_shape, const float* w, const int64_t* w_shape,

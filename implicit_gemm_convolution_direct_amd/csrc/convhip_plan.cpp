@@ -146,6 +146,9 @@ static bool plan_split(const Geom& g, const SplitSpecDesc& d, ConvPlan* p) {
   const int64_t bw = ((g.O[2] - 1) * g.S[2] + (g.K[2] - 1) * g.Dl[2]) / d.F + 1;
   if (rows != d.ROWS || bw > d.BW) return false;  // rows may be staged wider (bank spread)
   if (g.N * g.O[0] > std::numeric_limits<int32_t>::max() || g.G > 65535) return false;
+  // Channels-last: in-plane source offsets (row * W + column) * C_in in 32 bits;
+  // 16-byte weight copies need an aligned w.
+  if (g.cl && (g.L[1] * g.L[2] * g.Cin > std::numeric_limits<int32_t>::max() || !g.w_aligned16)) return false;
   ConvPlan q;
   q.cfg = -1;
   q.split_spec = d.id;
@@ -325,6 +328,9 @@ int plan_conv(const Geom& g, ConvPlan* out, int force_cfg, int num_cu, int use_t
       const TapClSpecDesc* specs = tap_cl_specs(&n);
       for (int i = 0; i < n; i++)
         if (plan_tap_cl(g, specs[i], num_cu, out)) return CONV_OK;
+      const SplitSpecDesc* ss = split_specs(&n);
+      for (int i = 0; i < n; i++)
+        if (plan_split(g, ss[i], out)) return CONV_OK;
     }
     use_tap = 0;
   }

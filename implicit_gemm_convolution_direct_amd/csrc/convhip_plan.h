@@ -14,6 +14,7 @@ struct Geom {
   int nd = 3;
   bool cl = false;            // channels-last tensors: x [N, D, H, W, C_in], y [N, D_out, H_out, W_out, C_out]
   bool x_aligned16 = true;    // channels-last: x starts on a 16-byte boundary
+  bool w_aligned16 = true;    // channels-last: w starts on a 16-byte boundary
   int64_t N = 0, Cin = 0, Cout = 0, G = 1, Cg = 0, Coutg = 0;
   int64_t L[3] = {1, 1, 1};   // input D, H, W
   int64_t K[3] = {1, 1, 1};   // kernel kD, kH, kW
@@ -138,7 +139,8 @@ const TapClSpecDesc* tap_cl_specs(int* count);
 // num_cu: compute units of the device (sizes the persistent grid).
 // use_tap: -1 planner's choice, 0 never use a tap specialisation. Channels-last
 // geometries (g.cl) take the channels-last tap specialisations (tap_spec then
-// indexes CONVHIP_TAP_CL_SPECS) or the generic kernel.
+// indexes CONVHIP_TAP_CL_SPECS), the channel-split specialisations or the
+// generic kernel.
 int plan_conv(const Geom& g, ConvPlan* p, int force_cfg = -1, int num_cu = 256, int use_tap = -1);
 
 // Build-time specialisations of the depth-streamed fused kernel (stride 1,

@@ -260,3 +260,40 @@ def test_channels_last_long_conv1d_full_size_slices():
         assert_conv_close(y[n:n + 1].cpu().numpy(), ref, w.shape, f"cl long conv1d n={n}")
     del xd, y
     torch.cuda.empty_cache()
+
+
+# Geometries of the channel-split specialisations (general and tiny Conv3d) in
+# channels-last order, with fewer planes.
+SPLIT_CL_CASES = [
+    ((1, 6, 32, 32, 16), (32, 8, 3, 5, 7), (1, 2, 2), (1, 1, 2), (1, 2, 3), 2),
+    ((2, 3, 32, 32, 16), (20, 8, 3, 5, 7), (1, 2, 2), (1, 1, 2), (0, 2, 3), 2),
+    ((1, 4, 32, 32, 8), (16, 8, 3, 5, 7), (1, 2, 2), (1, 1, 2), (1, 2, 3), 1),
+    ((2, 4, 16, 16, 3), (8, 3, 3, 3, 3), 1, 1, 0, 1),
+    ((1, 5, 16, 16, 3), (5, 3, 3, 3, 3), 1, 1, 0, 1),
+]
+
+
+@pytest.mark.parametrize("case", range(len(SPLIT_CL_CASES)))
+def test_channels_last_split_kernel_integer_exact(case):
+    xs, ws, s, d, p, g = SPLIT_CL_CASES[case]
+    desc = ch.plan_describe(xs, ws, s, d, p, g, channels_last=True)
+    assert "kernel=conv_tap_split" in desc and "layout=channels_last" in desc, desc
+    r = np.random.default_rng(700 + case)
+    x, w, b = _int_inputs(r, xs, ws, bias=True)
+    say(f"cl split case {case}: x={xs} w={ws}: {desc}")
+    y = gpu_conv_cl(x, w, b, s, d, p, g)
+    np.testing.assert_array_equal(y.astype(np.float64), oracle.conv_channels_last(x, w, b, s, d, p, g))
+
+
+def test_channels_last_split_geometry_misaligned_weights_take_generic():
+    """A w view 4 bytes past its allocation keeps the channel-split kernel (16-byte
+    weight copies) out; results unchanged."""
+    xs, ws, s, d, p, g = SPLIT_CL_CASES[0]
+    r = np.random.default_rng(12)
+    x, w, b = _int_inputs(r, xs, ws, bias=True)
+    wd = torch.empty(w.size + 1, dtype=torch.float32, device=dev())[1:].view(ws)
+    wd.copy_(torch.from_numpy(w))
+    assert wd.data_ptr() % 16 != 0
+    y = ch.conv_fwd_channels_last(to_dev(x), wd, to_dev(b), s, d, p, g)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(y.cpu().numpy().astype(np.float64), oracle.conv_channels_last(x, w, b, s, d, p, g))
