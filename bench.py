@@ -6,7 +6,7 @@ One "step" is one call of the library's entry point over one batch of the
 headline workload, the general-parameter Conv3d (x[4,16,32,32,32], w[32,8,3,5,7],
 groups 2, stride (1,2,2), padding (1,2,3), dilation (1,1,2)). The same run also
 times every other workload (tiny Conv3d, fused Conv3d+min+softmax, asymmetric
-Conv3d, long Conv1d, and three of them again on channels-last tensors through
+Conv3d, long Conv1d, and the four plain convolutions again on channels-last tensors through
 conv_fwd_channels_last, "<workload>_channels_last") and reports them under
 "shapes". Inputs are seeded
 synthetic tensors already resident in device memory; each workload is first run
@@ -38,7 +38,8 @@ PEAK_HBM_GBS = 8000.0
 HEADLINE = "general_conv3d"
 CL_SUFFIX = "_channels_last"
 ORDER = ["tiny_conv3d", "general_conv3d", "conv3d_min_softmax", "asym_conv3d", "long_conv1d",
-         "general_conv3d" + CL_SUFFIX, "asym_conv3d" + CL_SUFFIX, "long_conv1d" + CL_SUFFIX]
+         "tiny_conv3d" + CL_SUFFIX, "general_conv3d" + CL_SUFFIX, "asym_conv3d" + CL_SUFFIX,
+         "long_conv1d" + CL_SUFFIX]
 KERNEL_SOURCES = [os.path.join(ROOT, "implicit_gemm_convolution_direct_amd", "csrc", f)
                   for f in ("conv_kernels.hip", "convhip_plan.cpp", "convhip_plan.h")]
 

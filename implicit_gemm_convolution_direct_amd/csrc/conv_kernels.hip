@@ -579,11 +579,13 @@ struct TapGeo {
 
 // The same specialisation for channels-last input x [N, D, H, W, C_in]: the box
 // holds CCP floats per (plane, row, column) site, channels innermost, and the
-// reduction index runs tap-major, k = tap * CC + c, so each 4-deep k-step reads 4
-// consecutive channels of one tap (one lane pattern for every step).
+// reduction index runs tap-major, k = tap * CC + c (with CC a multiple of 4 each
+// 4-deep k-step reads 4 consecutive channels of one tap). CC and CCP multiples
+// of 4: the box is copied in 16-byte channel quads, else float by float.
 template <int KD, int KH, int KW, int DD, int DH, int DW, int CC, int KDSPAN, int ROWS, int BW, int CCP>
 struct TapGeoCL {
-  static_assert(CC % 4 == 0 && CCP % 4 == 0 && CCP >= CC, "channel quads");
+  static_assert(CCP >= CC, "site pitch");
+  static constexpr bool QUADS = CC % 4 == 0 && CCP % 4 == 0;
   static constexpr int CCH = CC;
   static constexpr int KVOL = KD * KH * KW;
   static constexpr int K = CC * KVOL;
@@ -677,6 +679,30 @@ __device__ __forceinline__ void stage_rows16(const ConvArgs& a, const TileGeo& t
 // = (site, cq) <- channels c0 + 4cq .. c0 + 4cq + 3 of input site (id0 + zd,
 // ih0 + zr, iw0 + col); quads past the chunk's channels and sites outside the
 // input read the zero word. Copy i of wave w moves quads (i*NWAVES + w)*64 + lane.
+// Float-by-float form (TapGeoCL without quads): box slot u = (site, c).
+template <class G, int NWAVES>
+__device__ __forceinline__ void stage_cl_floats(const ConvArgs& a, const TileGeo& t, int c0, float* dst, int wave,
+                                                int lane) {
+  constexpr int NU = G::BOXC * G::CCP_;
+  constexpr int NI = (NU + 64 * NWAVES - 1) / (64 * NWAVES);
+  const float* xn = a.x + int64_t(t.n) * a.L0 * a.L1 * a.L2 * a.Cin + (int64_t(t.g) * a.Cg + c0);
+#pragma unroll
+  for (int i = 0; i < NI; i++) {
+    const int u0 = (i * NWAVES + wave) * 64;
+    const int u = u0 + lane;
+    if (u < NU) {
+      const int site = u / G::CCP_, c = u - site * G::CCP_;
+      const int zz = site / G::BW_, col = site - zz * G::BW_;
+      const int zd = zz / G::ROWS_, zr = zz - zd * G::ROWS_;
+      const int id = t.id0 + zd, ih = t.ih0 + zr, iw = t.iw0 + col;
+      const bool ok = c < G::CCH && unsigned(id) < unsigned(a.L0) && unsigned(ih) < unsigned(a.L1) &&
+                      unsigned(iw) < unsigned(a.L2);
+      const float* src = xn + ((int64_t(id) * a.L1 + ih) * a.L2 + iw) * a.Cin + c;
+      lds_dma_f32(ok ? src : kZeroWord, dst + u0);
+    }
+  }
+}
+
 template <class G, int NWAVES>
 __device__ __forceinline__ void stage_cl_quads(const ConvArgs& a, const TileGeo& t, int c0, float* dst, int wave,
                                                int lane) {
@@ -704,8 +730,10 @@ __device__ __forceinline__ void stage_cl_quads(const ConvArgs& a, const TileGeo&
 template <class G, int NWAVES>
 __device__ __forceinline__ void stage_tap_box(const ConvArgs& a, const TileGeo& t, int c0, float* dst, int wave,
                                               int lane) {
-  if constexpr (G::CL) stage_cl_quads<G, NWAVES>(a, t, c0, dst, wave, lane);
-  else if constexpr (G::ROWCOPY) stage_rows16<G, NWAVES>(a, t, c0, dst, wave, lane);
+  if constexpr (G::CL) {
+    if constexpr (G::QUADS) stage_cl_quads<G, NWAVES>(a, t, c0, dst, wave, lane);
+    else stage_cl_floats<G, NWAVES>(a, t, c0, dst, wave, lane);
+  } else if constexpr (G::ROWCOPY) stage_rows16<G, NWAVES>(a, t, c0, dst, wave, lane);
   else stage_box<NWAVES>(a, t, c0, dst, wave, lane);
 }
 

@@ -261,11 +261,12 @@ static int cl_pitch(int64_t cc, int64_t stride_w, bool vec) {
 }
 
 // Plan of a channels-last tap specialisation if the geometry is the one it was
-// built for (16-byte aligned x with C_in a multiple of 4: the box is copied in
-// channel quads).
+// built for (copies in channel quads need a 16-byte aligned x with C_in a
+// multiple of 4).
 static bool plan_tap_cl(const Geom& g, const TapClSpecDesc& d, int num_cu, ConvPlan* p) {
   const int BM = 16 * d.MT * d.WM, BN = 16 * d.NT * d.WN;
-  if (!g.cl || !g.x_aligned16 || g.Cin % 4 != 0) return false;
+  const bool quads = d.CC % 4 == 0 && d.CCP % 4 == 0;
+  if (!g.cl || (quads && (!g.x_aligned16 || g.Cin % 4 != 0))) return false;
   if (g.G != 1 || g.Coutg > BM || g.Cg != int64_t(d.CC) * d.NCH) return false;
   if (g.K[0] != d.KD || g.K[1] != d.KH || g.K[2] != d.KW) return false;
   if (g.Dl[0] != d.DD || g.Dl[1] != d.DH || g.Dl[2] != d.DW) return false;
@@ -303,7 +304,7 @@ static bool plan_tap_cl(const Geom& g, const TapClSpecDesc& d, int num_cu, ConvP
   q.bw = d.BW;
   q.boxc = kdspan * rows * d.BW;
   q.ccp = d.CCP;
-  q.cl_vec = true;
+  q.cl_vec = quads;
   q.xs_floats = int(xs);
   q.koff_ints = 0;
   q.ws_floats = int(wf);

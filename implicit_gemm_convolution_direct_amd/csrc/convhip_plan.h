@@ -123,13 +123,16 @@ struct TapSpecDesc {
 const TapSpecDesc* tap_specs(int* count);
 
 // The persistent tap kernel on channels-last input (x [N, spatial..., C_in]):
-// the staged box holds CCP floats per input site (channels innermost, copied as
-// 16-byte quads). X(id, MT, NT, WM, WN, NCH, KD, KH, KW, DD, DH, DW, CC, KDSPAN,
-// ROWS, BW, CCP) with BW input sites per box row.
+// the staged box holds CCP floats per input site (channels innermost; copied as
+// 16-byte quads when CC and CCP are multiples of 4, else float by float).
+// X(id, MT, NT, WM, WN, NCH, KD, KH, KW, DD, DH, DW, CC, KDSPAN, ROWS, BW, CCP)
+// with BW input sites per box row.
 #define CONVHIP_TAP_CL_SPECS(X)                                                       \
   /* Conv1d 64->128, k=3, stride 3, dilation 4: 128 ch x 256 positions, 8 input  \
      channels per chunk, 774 input sites per tile */                               \
-  X(0, 4, 4, 2, 4, 8, 1, 1, 3, 1, 1, 4, 8, 1, 1, 774, 8)
+  X(0, 4, 4, 2, 4, 8, 1, 1, 3, 1, 1, 4, 8, 1, 1, 774, 8)                            \
+  /* Conv3d 3->64, kernel 3x5x7, 64^3 input: 64 ch x 256 positions, 8 waves */   \
+  X(1, 4, 2, 1, 8, 1, 3, 5, 7, 1, 1, 1, 3, 3, 10, 64, 3)
 
 struct TapClSpecDesc {
   int id, MT, NT, WM, WN, NCH, KD, KH, KW, DD, DH, DW, CC, KDSPAN, ROWS, BW, CCP;

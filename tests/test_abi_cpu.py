@@ -96,6 +96,7 @@ def test_channels_last_plans():
             ((2, 16, 16, 16, 3), (8, 3, 3, 3, 3), 1, 1, 0, 1, "conv_tap_split"),
             ((2, 16, 16, 16, 4), (8, 4, 3, 3, 3), 1, 1, 0, 1, "conv_mfma16"),
             ((4, 4096, 64), (128, 64, 3), 3, 4, 0, 1, "conv_tap"),        # the long Conv1d geometry
+            ((16, 64, 64, 64, 3), (64, 3, 3, 5, 7), 1, 1, 0, 1, "conv_tap"),  # the asymmetric Conv3d
             ((4, 4096, 64), (128, 64, 3), 2, 4, 0, 1, "conv_tap"),        # stride 2: a narrower box fits
             ((4, 4096, 64), (128, 64, 3), 3, 2, 0, 1, "conv_mfma16"),     # another dilation: generic
             ((4, 4096, 32), (128, 32, 3), 3, 4, 0, 1, "conv_mfma16")]:

@@ -193,15 +193,19 @@ def test_channels_last_asym_workload_slices():
         assert_conv_close(y[n:n + 1].cpu().numpy(), ref, w.shape, f"cl {name} sample {n}")
 
 
-# Shapes with the geometry of the channels-last tap specialisation (Conv1d
-# 64 -> <=128 channels, k = 3, dilation 4, stride 3, 8 channels per chunk) at
-# lengths the oracle checks in full.
+# Shapes with the geometries of the channels-last tap specialisations (Conv1d
+# 64 -> <=128 channels, k = 3, dilation 4, 8 channels per chunk; Conv3d 3 -> <=64
+# channels, kernel 3x5x7 on 64x64 planes) at sizes the oracle checks in full.
 TAP_CL_CASES = [
     ((2, 3000, 64), (128, 64, 3), 3, 4, 0, False),
     ((1, 5000, 64), (100, 64, 3), 3, 4, 4, True),     # padding, fewer channels, ragged last tile
     ((2, 3001, 64), (128, 64, 3), 3, 4, 2, True),
     ((4, 200000, 64), (128, 64, 3), 3, 4, 0, False),  # several items per workgroup
     ((2, 2000, 64), (128, 64, 3), 2, 4, 1, True),     # stride 2: a narrower box inside the staged one
+    # asymmetric Conv3d geometry (C_in = 3: float-by-float box copies)
+    ((2, 8, 64, 64, 3), (64, 3, 3, 5, 7), 1, 1, 0, True),
+    ((2, 5, 64, 64, 3), (40, 3, 3, 5, 7), 1, 1, 0, False),  # fewer output channels
+    ((3, 9, 64, 64, 3), (64, 3, 3, 5, 7), 1, 1, 0, True),   # odd item count per workgroup
 ]
 
 
