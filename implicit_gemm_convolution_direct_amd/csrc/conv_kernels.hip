@@ -130,6 +130,26 @@ __device__ __forceinline__ void wait_vmem_le() {
   __builtin_amdgcn_s_waitcnt((V & 15) | ((V >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// Keeps a wave-uniform value in scalar registers from here on: the compiler may
+// not re-read it from the kernel-argument segment later (such a scalar load
+// inside a loop costs a wait that also drains the LDS reads in flight).
+__device__ __forceinline__ void pin_sgpr(int& v) {
+  v = __builtin_amdgcn_readfirstlane(v);
+  asm volatile("" : "+s"(v));
+}
+__device__ __forceinline__ void pin_sgpr(int64_t& v) {
+  int lo = int(uint64_t(v)), hi = int(uint64_t(v) >> 32);
+  pin_sgpr(lo);
+  pin_sgpr(hi);
+  v = int64_t((uint64_t(uint32_t(hi)) << 32) | uint32_t(lo));
+}
+template <class T>
+__device__ __forceinline__ void pin_sgpr(T*& p) {
+  int64_t v = int64_t(reinterpret_cast<uintptr_t>(p));
+  pin_sgpr(v);
+  p = reinterpret_cast<T*>(uintptr_t(v));
+}
+
 // Asynchronous 16-byte copy per lane: lane l writes dst[4l .. 4l+3].
 __device__ __forceinline__ void lds_dma_f32x4(const float* src, float* dst) {
   __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
@@ -1141,6 +1161,321 @@ __global__ __launch_bounds__(64 * NW) void conv_tap_split_kernel(ConvArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// conv_tap_split_pipe: the channel-split kernel with a short start and its
+// cross-wave sums overlapped with products. The plane's tiles run in two
+// batches (NT1, then NT2 tiles) over the same staged box.
+// - Start: each wave copies its own channel's weights, one kernel depth tap at a
+//   time, into its own LDS region, and its box one input plane at a time; it
+//   starts on the first tap's weights and plane, and no barrier precedes the
+//   products. The A operands are then held in VGPRs.
+// - Tap rotation: box slot j holds depth tap (j + t0) % KD, with t0 chosen per
+//   output depth so that three neighbouring depths (one XCD, one L2) start on
+//   the same input plane: the burst of first copies reads a third of x.
+// - Batch 1's partial tiles are parked in the (then free) weight region and a
+//   counter in LDS is incremented; late in batch 2, wave w waits for the
+//   counter, then sums batch-1 tile w over all waves and stores it. Batch 2's
+//   tiles are parked in the box regions and summed after one barrier.
+// ---------------------------------------------------------------------------
+template <int NT1, int NT2, class G>
+struct SplitPipeLds {
+  // Weights of one depth tap: KPP floats from an aligned start at most 3 floats
+  // below them, as WQT 16-byte slots per row (a multiple of 4: whole copies),
+  // stored slot-major, [slot][row m], so one A read hits 64 distinct banks.
+  static constexpr int WQT = ((G::KPP + 3 + 3) / 4 + 3) / 4 * 4;
+  static constexpr int TAPW = WQT * 16 * 4;  // floats per depth tap
+  static constexpr int WI_TAP = WQT / 4;     // copies per depth tap
+  static constexpr int WREG = (G::KDT * TAPW > NT1 * 256) ? G::KDT * TAPW : NT1 * 256;
+  static constexpr int XREG = (G::XSW > NT2 * 256) ? G::XSW : NT2 * 256;
+  static constexpr int CNT = 4;  // floats reserved for the batch-1 counter
+};
+
+template <int NT1, int NT2, int NW, class G, bool CL = false>
+__global__ __launch_bounds__(64 * NW) void conv_tap_split_pipe_kernel(ConvArgs a) {
+  constexpr int NT = NT1 + NT2;
+  using L = SplitPipeLds<NT1, NT2, G>;
+  constexpr TapPatterns<G> P{};
+  constexpr int NP = P.np;
+  constexpr int NS = G::NS;
+  constexpr int PI = G::PLANE_INSTR;
+  constexpr int KDT = G::KDT;
+  constexpr int STAGE = L::WI_TAP + PI;  // copies per depth tap (weights, then plane)
+  constexpr int TCOPY = (KDT - 1) * STAGE;  // copies of slots 1 .. KD-1, issued during batch 1
+  constexpr int DPS = G::FIRST_TD1 > 0 ? (TCOPY + G::FIRST_TD1 - 1) / G::FIRST_TD1 : TCOPY;
+  static_assert(KDT * STAGE < 64, "vmcnt range");
+  static_assert(NT1 <= NW && NT2 <= NW, "one parked tile per wave in each sum");
+  static_assert(G::W4, "16-byte weight copies need C_in/groups * kvol to be a multiple of 4");
+  __shared__ __align__(16) float smem[NW * (L::WREG + L::XREG) + L::CNT];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kg = lane >> 4;
+  const int li = lane & 15;
+  // Every kernel argument used is read here, in one batch of scalar loads:
+  // one memory round trip at the start instead of a chain of dependent ones.
+  const float* xg = a.x;
+  const float* wgl = a.w;
+  const float* bg = a.bias;
+  float* yglob = a.y;
+  int Cin = a.Cin, Cout = a.Cout, Cg = a.Cg, Coutg = a.Coutg;
+  int L0 = a.L0, L1 = a.L1, L2 = a.L2, S0 = a.S0, S1 = a.S1, S2 = a.S2, D0 = a.D0;
+  int P0 = a.P0, P1 = a.P1, P2 = a.P2, O0 = a.O0, O1 = a.O1, O2 = a.O2, plane_out = a.plane_out;
+  int gx = gridDim.x, gy = gridDim.y;
+  asm volatile("" : "+s"(xg), "+s"(wgl), "+s"(bg), "+s"(yglob), "+s"(Cin), "+s"(Cout), "+s"(Cg), "+s"(Coutg),
+               "+s"(L0), "+s"(L1), "+s"(L2), "+s"(S0), "+s"(S1), "+s"(S2), "+s"(D0), "+s"(P0), "+s"(P1), "+s"(P2),
+               "+s"(O0), "+s"(O1), "+s"(O2), "+s"(plane_out), "+s"(gx), "+s"(gy));
+  // XCD-aware item order, as in conv_tap_split.
+  int item = blockIdx.x + gx * blockIdx.y;
+  const int items = gx * gy;
+  if ((items & 7) == 0) item = (item & 7) * (items >> 3) + (item >> 3);
+  const int plane = item % gx;
+  const int g = item / gx;
+  const int n = plane / O0;
+  const int od = plane - n * O0;
+  const int c = wave;  // this wave's input channel within the group
+  const int t0 = (KDT - 1) - od % KDT;  // depth tap of box slot 0
+  float* wreg = smem + wave * L::WREG;
+  float* box = smem + NW * L::WREG + wave * L::XREG;
+  unsigned* counter = reinterpret_cast<unsigned*>(smem + NW * (L::WREG + L::XREG));
+
+  // Bias loads go out before the copies, whose waits count the loads issued
+  // after them.
+  float b4[4];
+#pragma unroll
+  for (int r = 0; r < 4; r++) {
+    const int ch = 4 * kg + r;
+    b4[r] = (bg && ch < Coutg) ? bg[g * Coutg + ch] : 0.0f;
+  }
+  // Copies, in the order they are waited for: for box slot j = 0 .. KD-1, the
+  // weights of depth tap t = (j + t0) % KD, then its input plane.
+  // Weights of tap t: row m, slot q <- floats ab_t + 4q .. of weight row
+  // g*Coutg + m, ab_t the aligned float at or below the tap's first weight
+  // (which sits at float o_t of the copy). Slots past the row, or rows past
+  // C_out/g, read zero.
+  const int cs = c * G::KVOL;
+  const int64_t vol_in = int64_t(L0) * L1 * L2;
+  const float* xc = CL ? xg + int64_t(n) * vol_in * Cin + (int64_t(g) * Cg + c)
+                       : xg + (int64_t(n) * Cin + int64_t(g) * Cg + c) * vol_in;
+  const int site = CL ? Cin : 1;
+  int soff[PI];
+  uint32_t sok = 0;
+#pragma unroll
+  for (int i = 0; i < PI; i++) {
+    const int e = i * 64 + lane;
+    const int zr = e / G::BWC, j = e - zr * G::BWC;
+    const int ih = zr - P1, iw = G::FF * j - P2;
+    const bool ok = e < G::PLANE && unsigned(ih) < unsigned(L1) && unsigned(iw) < unsigned(L2);
+    soff[i] = ok ? (ih * L2 + iw) * site : 0;
+    sok |= uint32_t(ok) << i;
+  }
+  // Per box slot: the weight block of its tap (wsrc, starting at float wab of
+  // the rows) and its input plane (xsrc; null where the plane is padding).
+  const float* wsrc[KDT];
+  const float* xsrc[KDT];
+  int wab[KDT];
+  int tap[KDT];
+#pragma unroll
+  for (int j = 0; j < KDT; j++) {
+    int t = j + t0;
+    t = t >= KDT ? t - KDT : t;
+    tap[j] = t;
+    wab[j] = (cs + t * G::KPP) & ~3;
+    wsrc[j] = wgl + int64_t(g) * Coutg * G::WROW + wab[j];
+    const int id = od * S0 - P0 + t * D0;
+    xsrc[j] = unsigned(id) < unsigned(L0) ? xc + int64_t(id) * L1 * L2 * site : nullptr;
+    pin_sgpr(tap[j]);
+    pin_sgpr(wab[j]);
+    pin_sgpr(wsrc[j]);
+    pin_sgpr(xsrc[j]);
+  }
+  const int wm = lane & 15, wq = lane >> 4;  // row and slot-in-copy of this lane's weight piece
+  // Copy u (0 <= u < STAGE) of box slot j: the tap's weight copies, then its plane.
+  auto copy = [&](int j, int u) {
+    if (u < L::WI_TAP) {
+      const int q = 4 * u + wq;
+      const bool ok = wm < Coutg && wab[j] + 4 * q < G::WROW;
+      lds_dma_f32x4(ok ? wsrc[j] + wm * G::WROW + 4 * q : kZeroWord, wreg + tap[j] * L::TAPW + 256 * u);
+    } else {
+      const int i = u - L::WI_TAP;
+      const bool ok = xsrc[j] != nullptr && ((sok >> i) & 1);
+      if (i * 64 + lane < G::PLANE) lds_dma_f32(ok ? xsrc[j] + soff[i] : kZeroWord, box + j * G::PLANE + i * 64);
+    }
+  };
+  // Slot 0 now; slots 1 .. KD-1 during batch 1's first steps.
+#pragma unroll
+  for (int u = 0; u < STAGE; u++) copy(0, u);
+  // The batch-1 counter starts at zero before any wave can increment it.
+  if (wave == 0 && lane == 0) *counter = 0u;
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+
+  int dpat[NP];
+  fill_pat_deltas<G>(dpat, kg, std::make_integer_sequence<int, NP>{});
+  const int base_b = int(reinterpret_cast<uintptr_t>(box) - reinterpret_cast<uintptr_t>(smem));
+  int nb[NT], dp[NP];
+#pragma unroll
+  for (int ni = 0; ni < NT; ni++) {
+    const int p = 16 * (int(blockIdx.z) * NT + ni) + li;
+    const int oh = p / O2, ow = p - (p / O2) * O2;
+    nb[ni] = base_b + 4 * (p < plane_out ? oh * S1 * G::BWC + ow * (S2 / G::FF) : 0);
+  }
+#pragma unroll
+  for (int q = 0; q < NP; q++) dp[q] = 4 * dpat[q];
+
+  // A[m = li][k = 4s + kg] for box slot j = k / KPP (depth tap (j + t0) % KD),
+  // in-tap index r = k % KPP; indices past the kernel volume take a zero weight.
+  float av[NS];
+  auto load_a = [&](auto sc) {
+    constexpr int s = decltype(sc)::value;
+    const int k = 4 * s + kg;
+    const int j = k / G::KPP;
+    const int r = k - j * G::KPP;
+    int t = j + t0;
+    t = t >= KDT ? t - KDT : t;
+    const int f = ((cs + t * G::KPP) & 3) + r;
+    const float v = wreg[t * L::TAPW + (f >> 2) * 64 + li * 4 + (f & 3)];
+    av[s] = (4 * s + 3 < G::KVOL || k < G::KVOL) ? v : 0.0f;
+  };
+  // Slot 0's weights and plane have landed (this wave's own copies).
+  wait_vmem_le<0>();
+  static_for<NS>([&](auto sc) {
+    if constexpr (G::td_of(decltype(sc)::value) == 0) load_a(sc);
+  });
+
+  const char* bb = reinterpret_cast<const char*>(smem);
+  // Products of tiles T0 .. T0+BT-1 over the channel's NS k-steps; operands of
+  // step s+1 are read while the matrix core works on step s. In batch 1 the
+  // copies of the next box slot are waited for (and its A operands read) before
+  // the first step that reads it. hook(s) runs after step s's products.
+  auto products = [&](auto t0c, auto btc, v4f* acc, auto&& hook) {
+    constexpr int T0 = decltype(t0c)::value, BT = decltype(btc)::value;
+    float bv[2][BT];
+#pragma unroll
+    for (int ni = 0; ni < BT; ni++)
+      bv[0][ni] = *reinterpret_cast<const float*>(bb + nb[T0 + ni] + dp[P.pid[0]] + 4 * G::koff(0));
+    static_for<NS>([&](auto sc) {
+      constexpr int s = decltype(sc)::value;
+      constexpr int cu = s & 1, nx = cu ^ 1;
+      if constexpr (T0 == 0) {
+#pragma unroll
+        for (int q = DPS * s; q < DPS * (s + 1) && q < TCOPY; q++) copy(1 + q / STAGE, q % STAGE);
+      }
+      if constexpr (s + 1 < NS) {
+        if constexpr (T0 == 0 && G::td_of(s + 1) != G::td_of(s)) {
+          // Copies issued so far that belong to slots after td_of(s + 1) may
+          // still be in flight.
+          constexpr int issued = DPS * (s + 1) < TCOPY ? DPS * (s + 1) : TCOPY;
+          constexpr int later = issued - G::td_of(s + 1) * STAGE;
+          static_assert(issued >= G::td_of(s + 1) * STAGE, "slot copies issued before their first step");
+          wait_vmem_le<(later > 0 ? later : 0)>();
+          static_for<NS>([&](auto s2) {
+            if constexpr (G::td_of(decltype(s2)::value) == G::td_of(s + 1)) load_a(s2);
+          });
+        }
+#pragma unroll
+        for (int ni = 0; ni < BT; ni++)
+          bv[nx][ni] = *reinterpret_cast<const float*>(bb + nb[T0 + ni] + dp[P.pid[s + 1]] + 4 * G::koff(4 * (s + 1)));
+      }
+#pragma unroll
+      for (int ni = 0; ni < BT; ni++) acc[ni] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[s], bv[cu][ni], acc[ni], 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < BT; i++) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
+      hook(sc);
+      // Step boundary for the scheduler: step s+1's operand reads stay here,
+      // behind step s's products, instead of sinking next to their use.
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+
+  // Output of tile T of this workgroup: channel 4 kg + r, position 16 T + li.
+  const int64_t out_plane = int64_t(O1) * O2;
+  float* yg = CL ? yglob + (int64_t(n) * O0 + od) * out_plane * Cout + int64_t(g) * Coutg
+                 : yglob + (int64_t(n) * Cout + int64_t(g) * Coutg) * O0 * out_plane + int64_t(od) * out_plane;
+  int64_t ch_stride = CL ? 1 : int64_t(O0) * out_plane;
+  int64_t p_stride = CL ? Cout : 1;
+  pin_sgpr(yg);
+  pin_sgpr(ch_stride);
+  pin_sgpr(p_stride);
+  auto store_tile = [&](int T, const v4f& v) {
+    const int p = 16 * (int(blockIdx.z) * NT + T) + li;
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      const int ch = 4 * kg + r;
+      if (ch < Coutg && p < plane_out) yg[ch * ch_stride + p * p_stride] = v[r] + b4[r];
+    }
+  };
+  // Parked tile `slot` of every wave's region (region0 + w * stride), and their
+  // sum in a fixed order.
+  auto read_parked = [&](const float* region0, int stride, int slot, v4f* part) {
+#pragma unroll
+    for (int w2 = 0; w2 < NW; w2++)
+      part[w2] = *reinterpret_cast<const v4f*>(region0 + w2 * stride + (slot * 64 + lane) * 4);
+  };
+  auto sum_parts = [&](const v4f* part) {
+    v4f v = part[0];
+#pragma unroll
+    for (int w2 = 1; w2 < NW; w2++) v += part[w2];
+    return v;
+  };
+
+  // Batch 1.
+  {
+    v4f acc[NT1];
+#pragma unroll
+    for (int ni = 0; ni < NT1; ni++) acc[ni] = v4f{0.f, 0.f, 0.f, 0.f};
+    products(std::integral_constant<int, 0>{}, std::integral_constant<int, NT1>{}, acc, [](auto) {});
+    // Every A operand was read from the weight region before the last steps'
+    // products: park batch 1 there, then count this wave in.
+#pragma unroll
+    for (int ni = 0; ni < NT1; ni++) *reinterpret_cast<v4f*>(wreg + (ni * 64 + lane) * 4) = acc[ni];
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the parked tiles are in LDS
+    asm volatile("" ::: "memory");
+    if (lane == 0) __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  }
+  // Batch 2. Late in it, wave w < NT1 waits until every wave has parked batch 1
+  // (each does so unconditionally after its own batch-1 products; the wait is
+  // also capped), then sums batch-1 tile w and stores it.
+  constexpr int S_WAIT = NS > 8 ? NS - 7 : NS - 1;
+  {
+    v4f acc[NT2];
+#pragma unroll
+    for (int ni = 0; ni < NT2; ni++) acc[ni] = v4f{0.f, 0.f, 0.f, 0.f};
+    v4f part[NW];
+    const bool sums1 = wave < NT1;
+    products(std::integral_constant<int, NT1>{}, std::integral_constant<int, NT2>{}, acc, [&](auto sc) {
+      constexpr int s = decltype(sc)::value;
+      if constexpr (s == S_WAIT) {
+        if (sums1) {
+          for (int spin = 0; spin < (1 << 22); spin++) {
+            if (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= unsigned(NW)) break;
+            __builtin_amdgcn_s_sleep(1);
+          }
+          asm volatile("" ::: "memory");
+          read_parked(smem, L::WREG, wave, part);
+        }
+      } else if constexpr (s == (S_WAIT + 3 < NS ? S_WAIT + 3 : NS - 1)) {
+        if (sums1) store_tile(wave, sum_parts(part));
+      }
+    });
+    // The box is no longer read by this wave: park batch 2 in it.
+#pragma unroll
+    for (int ni = 0; ni < NT2; ni++) *reinterpret_cast<v4f*>(box + (ni * 64 + lane) * 4) = acc[ni];
+  }
+  __syncthreads();
+  if (wave < NT2) {
+    v4f part[NW];
+    read_parked(smem + NW * L::WREG, L::XREG, wave, part);
+    store_tile(NT1 + wave, sum_parts(part));
+  }
+}
+
+// ---------------------------------------------------------------------------
 // fused_min_softmax_mfma4
 // ---------------------------------------------------------------------------
 struct FusedArgs {
@@ -1710,12 +2045,25 @@ static int launch_tap_cl_spec(const ConvArgs& args, const ConvPlan& p, hipStream
   }
 }
 
+// CONVHIP_SPLIT_PIPE=0 keeps the channel-split specialisations on the kernel
+// whose cross-wave sum follows all products (tests run both kernels).
+static bool split_pipe_enabled() {
+  const char* s = std::getenv("CONVHIP_SPLIT_PIPE");
+  return !(s && *s && std::atoi(s) == 0);
+}
+
 template <int NT, int NW, int KD, int KH, int KW, int DD, int DH, int DW, int F, int ROWS, int BW, bool CL>
 static int launch_split(const ConvArgs& args, const ConvPlan& p, hipStream_t stream) {
   using G = SplitGeo<KD, KH, KW, DD, DH, DW, F, ROWS, BW, NW>;
-  hipLaunchKernelGGL((conv_tap_split_kernel<NT, NW, G, CL>),
-                     dim3(unsigned(p.grid[0]), unsigned(p.grid[1]), unsigned(p.grid[2])),
-                     dim3(64 * NW), 0, stream, args);
+  const dim3 grid(unsigned(p.grid[0]), unsigned(p.grid[1]), unsigned(p.grid[2]));
+  if constexpr (split_pipe_fits(NT, NW, G::WROW)) {
+    if (p.split_pipe) {
+      hipLaunchKernelGGL((conv_tap_split_pipe_kernel<(NT + 1) / 2, NT / 2, NW, G, CL>), grid, dim3(64 * NW), 0,
+                         stream, args);
+      return hipGetLastError() == hipSuccess ? CONV_OK : CONV_ERR_HIP;
+    }
+  }
+  hipLaunchKernelGGL((conv_tap_split_kernel<NT, NW, G, CL>), grid, dim3(64 * NW), 0, stream, args);
   return hipGetLastError() == hipSuccess ? CONV_OK : CONV_ERR_HIP;
 }
 
@@ -1898,7 +2246,7 @@ int conv_plan_describe(int nd, const int64_t* x_shape, const int64_t* w_shape, c
     s = describe(g, p);
   } else {
     ConvPlan p;
-    rc = plan_conv(g, &p, forced_conv_cfg(), 256, use_tap());
+    rc = plan_conv(g, &p, forced_conv_cfg(), 256, use_tap(), split_pipe_enabled());
     if (rc != CONV_OK) return rc;
     s = describe(g, p);
   }
@@ -1918,7 +2266,7 @@ int conv_fwd(int nd, const float* x, const int64_t* x_shape, const float* w, con
   // they need 16-byte aligned pointers (any tensor allocation is; a sliced view
   // may not be).
   const bool aligned = ((reinterpret_cast<uintptr_t>(w) | reinterpret_cast<uintptr_t>(x)) & 15) == 0;
-  rc = plan_conv(g, &p, forced_conv_cfg(), device_num_cu(), aligned ? use_tap() : 0);
+  rc = plan_conv(g, &p, forced_conv_cfg(), device_num_cu(), aligned ? use_tap() : 0, split_pipe_enabled());
   if (rc != CONV_OK) return rc;
   ConvArgs a = conv_args(g, p, x, w, bias, y);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -1939,7 +2287,7 @@ int conv_fwd_channels_last(int nd, const float* x, const int64_t* x_shape, const
   g.x_aligned16 = (reinterpret_cast<uintptr_t>(x) & 15) == 0;
   g.w_aligned16 = (reinterpret_cast<uintptr_t>(w) & 15) == 0;
   ConvPlan p;
-  rc = plan_conv(g, &p, forced_conv_cfg(), device_num_cu(), use_tap());
+  rc = plan_conv(g, &p, forced_conv_cfg(), device_num_cu(), use_tap(), split_pipe_enabled());
   if (rc != CONV_OK) return rc;
   ConvArgs a = conv_args(g, p, x, w, bias, y);
   a.vec_store = (g.Cout % 4 == 0 && g.Coutg % 4 == 0 && (reinterpret_cast<uintptr_t>(y) & 15) == 0) ? 1 : 0;

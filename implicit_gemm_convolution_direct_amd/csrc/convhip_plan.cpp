@@ -134,7 +134,7 @@ const SplitSpecDesc* split_specs(int* count) {
   return specs;
 }
 
-static bool plan_split(const Geom& g, const SplitSpecDesc& d, ConvPlan* p) {
+static bool plan_split(const Geom& g, const SplitSpecDesc& d, bool pipe, ConvPlan* p) {
   if (g.Coutg > 16 || g.Cg != d.NW) return false;
   if (g.K[0] != d.KD || g.K[1] != d.KH || g.K[2] != d.KW) return false;
   if (g.Dl[0] != d.DD || g.Dl[1] != d.DH || g.Dl[2] != d.DW) return false;
@@ -170,6 +170,16 @@ static bool plan_split(const Geom& g, const SplitSpecDesc& d, ConvPlan* p) {
   const int64_t wld = (wrow % 4 == 0 && (wrow / 4) % 2 == 0) ? wrow + 4 : wrow;
   const int64_t wsh = (16 * wld + 4 + 3) / 4 * 4;
   q.lds_bytes = 4 * std::max<int64_t>(wsh + int64_t(d.NW) * xsw, int64_t(d.NW) * d.NT * 4 * 64);
+  if (pipe && split_pipe_fits(d.NT, d.NW, int(wrow))) {
+    // Per wave: the weights, one depth tap at a time (16 rows of a multiple of
+    // 4 16-byte slots covering kH*kW + 3 floats), later batch 1's parked tiles;
+    // the box, later batch 2's parked tiles; plus one counter.
+    const int64_t wqt = ((int64_t(d.KH) * d.KW + 6) / 4 + 3) / 4 * 4;
+    const int64_t wreg = std::max<int64_t>(int64_t(d.KD) * wqt * 64, int64_t((d.NT + 1) / 2) * 256);
+    const int64_t xreg = std::max<int64_t>(xsw, int64_t(d.NT / 2) * 256);
+    q.split_pipe = 1;
+    q.lds_bytes = 4 * (int64_t(d.NW) * (wreg + xreg) + 4);
+  }
   if (q.lds_bytes > kLdsLimit) return false;
   q.grid[0] = g.N * g.O[0];
   q.grid[1] = g.G;
@@ -322,7 +332,7 @@ static bool plan_tap_cl(const Geom& g, const TapClSpecDesc& d, int num_cu, ConvP
   return true;
 }
 
-int plan_conv(const Geom& g, ConvPlan* out, int force_cfg, int num_cu, int use_tap) {
+int plan_conv(const Geom& g, ConvPlan* out, int force_cfg, int num_cu, int use_tap, bool split_pipe) {
   if (g.cl) {
     if (use_tap != 0 && force_cfg < 0) {
       int n = 0;
@@ -331,7 +341,7 @@ int plan_conv(const Geom& g, ConvPlan* out, int force_cfg, int num_cu, int use_t
         if (plan_tap_cl(g, specs[i], num_cu, out)) return CONV_OK;
       const SplitSpecDesc* ss = split_specs(&n);
       for (int i = 0; i < n; i++)
-        if (plan_split(g, ss[i], out)) return CONV_OK;
+        if (plan_split(g, ss[i], split_pipe, out)) return CONV_OK;
     }
     use_tap = 0;
   }
@@ -342,7 +352,7 @@ int plan_conv(const Geom& g, ConvPlan* out, int force_cfg, int num_cu, int use_t
       if (plan_tap(g, specs[i], num_cu, out)) return CONV_OK;
     const SplitSpecDesc* ss = split_specs(&n);
     for (int i = 0; i < n; i++)
-      if (plan_split(g, ss[i], out)) return CONV_OK;
+      if (plan_split(g, ss[i], split_pipe, out)) return CONV_OK;
   }
   ConvPlan p;
   if (force_cfg >= 0 && force_cfg < CFG_COUNT) {
@@ -552,7 +562,7 @@ std::string describe(const Geom& g, const ConvPlan& p) {
   std::snprintf(buf, sizeof buf,
                 "kernel=%s%s cfg=%d MT=%d NT=%d WM=%d WN=%d KS=%d BM=%d BN=%d mode=%s Cc=%d kc_pad=%d "
                 "box=%dx%dx%d grid=%lldx%lldx%lld lds=%lld macs=%lld",
-                p.tap_spec >= 0 ? "conv_tap" : p.split_spec >= 0 ? "conv_tap_split" : "conv_mfma16",
+                p.tap_spec >= 0 ? "conv_tap" : p.split_spec >= 0 ? (p.split_pipe ? "conv_tap_split pipe=1" : "conv_tap_split") : "conv_mfma16",
                 g.cl ? (p.cl_vec ? " layout=channels_last copy=quad" : " layout=channels_last copy=scalar") : "",
                 p.tap_spec >= 0 ? p.tap_spec : p.split_spec >= 0 ? p.split_spec : p.cfg, cs.MT, cs.NT,
                 cs.WM, cs.WN, cs.KS, p.BM, p.BN, p.mode == TILE_FLAT ? "flat" : "row", p.Cc,

@@ -83,6 +83,7 @@ struct ConvPlan {
   int nchunks = 0;      // chunks of Cc input channels per tile
   int tap_spec = -1;    // >= 0: build-time specialised persistent kernel (grid[0] workgroups walk `items`)
   int split_spec = -1;  // >= 0: build-time specialised channel-split kernel
+  int split_pipe = 0;   // channel-split kernel summing the first tile batch during the second's products
   int threads = 256;    // workgroup size
   int64_t items = 0;    // tap kernel: work items (tile, plane)
   int64_t grid[3] = {0, 0, 0};
@@ -111,6 +112,15 @@ struct ConvPlan {
   X(0, 13, 8, 3, 5, 7, 1, 1, 2, 2, 35, 20, 1)                                     \
   /* Conv3d 3->8, kernel 3x3x3 on 16^3: 4 workgroups per plane */                \
   X(1, 4, 3, 3, 3, 3, 1, 1, 1, 1, 16, 16, 4)
+
+// The pipelined channel-split kernel runs a plane's NT tiles in two batches
+// (ceil(NT/2), then floor(NT/2)), sums each batch's tiles one per wave, and
+// copies each wave's weight slice in 16-byte pieces: it needs NT >= 8 (two
+// batches worth overlapping), ceil(NT/2) <= NW and a group reduction length
+// (C_in/groups * kvol) that is a multiple of 4.
+constexpr bool split_pipe_fits(int NT, int NW, int wrow) {
+  return NT >= 8 && (NT + 1) / 2 <= NW && wrow % 4 == 0;
+}
 
 struct SplitSpecDesc {
   int id, NT, NW, KD, KH, KW, DD, DH, DW, F, ROWS, BW, TS;
@@ -144,7 +154,8 @@ const TapClSpecDesc* tap_cl_specs(int* count);
 // geometries (g.cl) take the channels-last tap specialisations (tap_spec then
 // indexes CONVHIP_TAP_CL_SPECS), the channel-split specialisations or the
 // generic kernel.
-int plan_conv(const Geom& g, ConvPlan* p, int force_cfg = -1, int num_cu = 256, int use_tap = -1);
+int plan_conv(const Geom& g, ConvPlan* p, int force_cfg = -1, int num_cu = 256, int use_tap = -1,
+              bool split_pipe = true);
 
 // Build-time specialisations of the depth-streamed fused kernel (stride 1,
 // dilation 1, groups 1, kD = 3, min over depth): X(id, CIN, KH, KW, NG, O2, ROWS)

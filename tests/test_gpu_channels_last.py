@@ -277,11 +277,14 @@ SPLIT_CL_CASES = [
 ]
 
 
+@pytest.mark.parametrize("pipe", ["1", "0"])
 @pytest.mark.parametrize("case", range(len(SPLIT_CL_CASES)))
-def test_channels_last_split_kernel_integer_exact(case):
+def test_channels_last_split_kernel_integer_exact(case, pipe, monkeypatch):
+    monkeypatch.setenv("CONVHIP_SPLIT_PIPE", pipe)
     xs, ws, s, d, p, g = SPLIT_CL_CASES[case]
     desc = ch.plan_describe(xs, ws, s, d, p, g, channels_last=True)
     assert "kernel=conv_tap_split" in desc and "layout=channels_last" in desc, desc
+    assert ("pipe=1" in desc) == (pipe == "1" and tuple(ws[2:]) == (3, 5, 7)), desc
     r = np.random.default_rng(700 + case)
     x, w, b = _int_inputs(r, xs, ws, bias=True)
     say(f"cl split case {case}: x={xs} w={ws}: {desc}")

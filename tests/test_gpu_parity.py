@@ -152,6 +152,19 @@ def test_workload_full_float(name):
     assert_conv_close(y, oracle.conv(x, w, b, *_cfg_args(cfg)), cfg["w"], name)
 
 
+def test_general_conv3d_deterministic():
+    """The channel-split kernels sum the per-wave partial tiles in a fixed order:
+    repeated calls give identical bits."""
+    name = "general_conv3d"
+    cfg = synth.WORKLOADS[name]
+    x, w, b = synth.make_inputs(name)
+    xd, wd, bd = to_dev(x), to_dev(w), to_dev(b)
+    y1 = ch.conv_fwd(xd, wd, bd, *_cfg_args(cfg))
+    y2 = ch.conv_fwd(xd, wd, bd, *_cfg_args(cfg))
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+
+
 def test_workload_asym_conv3d_slices():
     name = "asym_conv3d"
     cfg = synth.WORKLOADS[name]
@@ -439,11 +452,16 @@ SPLIT_CASES = [
 ]
 
 
+@pytest.mark.parametrize("pipe", ["1", "0"])
 @pytest.mark.parametrize("case", range(len(SPLIT_CASES)))
-def test_split_specialised_kernel_integer_exact(case):
+def test_split_specialised_kernel_integer_exact(case, pipe, monkeypatch):
+    """Both channel-split kernels: the pipelined one (batch sums overlapped with
+    products; the general geometry's 13 tiles) and the one summing at the end."""
+    monkeypatch.setenv("CONVHIP_SPLIT_PIPE", pipe)
     xs, ws, s, d, p, g = SPLIT_CASES[case]
     desc = ch.plan_describe(xs, ws, s, d, p, g)
     assert "kernel=conv_tap_split" in desc, desc
+    assert ("pipe=1" in desc) == (pipe == "1" and tuple(ws[2:]) == (3, 5, 7)), desc
     r = np.random.default_rng(500 + case)
     x, w, b = _int_inputs(r, xs, ws, bias=True)
     say(f"split case {case}: x={xs} w={ws}: {desc}")
