@@ -16,6 +16,10 @@
 // conv_tap_split    build-time specialised, few output channels per group: one
 //                   wave per input channel of the group, partial tiles summed in
 //                   LDS; the whole (n, od) output plane per workgroup.
+// conv_tap_split_pipe  the same split for planes of 8+ tiles, with per-wave
+//                   weights staged one depth tap at a time and held in VGPRs,
+//                   and the first tile batch's sum overlapped with the second
+//                   batch's products.
 // fused_stream      Conv3d -> min over depth -> softmax over channels for a
 //                   build-time geometry: depth planes streamed through a 4-slot
 //                   LDS ring, 4x4x1 MFMA with the weight operand broadcast.
