@@ -1674,9 +1674,13 @@ __global__ __launch_bounds__(256) void fused_min_softmax_mfma4_kernel(FusedArgs 
 // fused_stream: Conv3d -> min over depth -> softmax over channels for a fixed
 // small geometry (stride 1, dilation 1, groups 1, kD = 3), streaming the input
 // depth planes through LDS.
-// - One wave owns 64 consecutive output positions (h, w) of one sample and a
+// - One wave owns a tile of output positions (h, w) of one sample and a
 //   contiguous range of output depths (the depth range is split over DSPLIT
-//   waves); the waves of a workgroup are independent (no barriers).
+//   waves); the waves of a workgroup are independent (no barriers). A tile is
+//   RT whole output rows (lanes past RT * W_out idle), so lane l reads staged
+//   row l / W_out at column l % W_out and the 64 operand reads of one wave fall
+//   on distinct LDS banks; or, with RT = 0, 64 consecutive positions of the
+//   flattened plane.
 // - Output depth od reads input planes od, od+1, od+2; planes sit in a ring of
 //   four LDS slots and the plane three ahead is copied while od is reduced.
 // - Matrix core: 4x4x1 MFMA with 16 blocks, the weight operand broadcast from
@@ -1689,9 +1693,11 @@ __global__ __launch_bounds__(256) void fused_min_softmax_mfma4_kernel(FusedArgs 
 //   partial minima of the depth ranges meet in LDS first.
 // ---------------------------------------------------------------------------
 
-template <int CIN, int KH, int KW_, int NG, int O2, int ROWS>
+template <int CIN, int KH, int KW_, int NG, int O2, int ROWS, int RT>
 struct StreamGeo {
   static constexpr int CIN_ = CIN, NG_ = NG, O2_ = O2, KW = KW_;
+  static constexpr int RT_ = RT;  // > 0: a wave tile is RT whole output rows; 0: 64 flattened positions
+  static_assert(RT * O2 <= 64, "a row tile fits the wave");
   static constexpr int KD = 3;
   static constexpr int BW = O2 + KW_ - 1;       // input columns per staged row
   static constexpr int CH = ROWS * BW;           // floats per channel of a plane
@@ -1715,7 +1721,13 @@ struct StreamGeo {
   static constexpr int NPAIR = NG4 * KRED;        // (channel group, reduction index) pairs
   static constexpr int NAREG = (NPAIR + 15) / 16;
   static constexpr int WAVES = 4;                // waves per workgroup
-  static constexpr int LDS_FLOATS = WAVES * NSLOT * SLOT;
+  // The rings; after the depth loop (depth range split over waves) the partial
+  // minima, 4*NG registers per wave, and past them one 1024-float channel
+  // transpose area per (sample, tile).
+  static constexpr int RING_FLOATS = WAVES * NSLOT * SLOT;
+  static constexpr int EPI_FLOATS = 4 * NG * 64 * WAVES + WAVES * 1024;
+  static constexpr int LDS_FLOATS = RING_FLOATS > EPI_FLOATS ? RING_FLOATS : EPI_FLOATS;
+  static_assert(NSLOT * SLOT >= 1024, "an undivided depth range transposes in its own ring");
   static_assert(PI < 64, "vmcnt range");
 };
 
@@ -1752,7 +1764,11 @@ __global__ __launch_bounds__(256, 4) void fused_stream_kernel(StreamArgs a) {
   const int tu = unit / a.dsplit;
   const int part = unit - tu * a.dsplit;
   const int n = tu / a.tiles_per_plane;
-  const int p0 = (tu - n * a.tiles_per_plane) * 64;
+  const int tile = tu - n * a.tiles_per_plane;
+  // First output row of the tile and this lane's output position.
+  const int oh_first = G::RT_ > 0 ? tile * G::RT_ : (tile * 64) / G::O2_;
+  const int oh = G::RT_ > 0 ? oh_first + lane / G::O2_ : (tile * 64 + lane) / G::O2_;
+  const int ow = G::RT_ > 0 ? lane - (lane / G::O2_) * G::O2_ : (tile * 64 + lane) - ((tile * 64 + lane) / G::O2_) * G::O2_;
   const int od0 = part * a.ods;
   const int od1 = live ? min(a.O0, od0 + a.ods) : od0;
   float* ring = smem + wave * (G::NSLOT * G::SLOT);
@@ -1780,7 +1796,6 @@ __global__ __launch_bounds__(256, 4) void fused_stream_kernel(StreamArgs a) {
   // Copy sources: copy i, lane l moves 16-byte chunk e = 64i + l = (c, row, q) of
   // the slot from input (c, ih0 + row, 4q .. 4q+3) of the plane being staged
   // (input rows are exactly BW wide: no padding along W).
-  const int oh_first = p0 / G::O2_;
   const int ih0 = oh_first - a.P1;
   const int64_t chan_stride = int64_t(a.L0) * a.L1 * a.L2;
   const float* xn = a.x + int64_t(n) * G::CIN_ * chan_stride;
@@ -1813,9 +1828,8 @@ __global__ __launch_bounds__(256, 4) void fused_stream_kernel(StreamArgs a) {
   };
 
   // This lane's output position and its byte offset inside a slot.
-  const int p = p0 + lane;
-  const bool valid = live && p < a.plane_out;
-  const int oh = p / G::O2_, ow = p - (p / G::O2_) * G::O2_;
+  const int p = oh * G::O2_ + ow;
+  const bool valid = live && (G::RT_ > 0 ? (lane < G::RT_ * G::O2_ && oh < a.O1) : p < a.plane_out);
   const int lbase = valid ? (oh - oh_first) * G::BW + ow : 0;
   const char* bbase = reinterpret_cast<const char*>(ring + lbase);
 
@@ -2109,9 +2123,9 @@ static int launch_fused_ng(const FusedArgs& args, const FusedPlan& p, hipStream_
   return hipGetLastError() == hipSuccess ? CONV_OK : CONV_ERR_HIP;
 }
 
-template <int CIN, int KH, int KW, int NG, int O2, int ROWS>
+template <int CIN, int KH, int KW, int NG, int O2, int ROWS, int RT>
 static int launch_stream(const StreamArgs& args, const FusedPlan& p, hipStream_t stream) {
-  using G = StreamGeo<CIN, KH, KW, NG, O2, ROWS>;
+  using G = StreamGeo<CIN, KH, KW, NG, O2, ROWS, RT>;
   if (int64_t(4) * G::LDS_FLOATS != p.lds_bytes || G::WAVES % p.dsplit != 0) return CONV_ERR_UNSUPPORTED;
   hipLaunchKernelGGL(fused_stream_kernel<G>, dim3(unsigned(p.grid[0])), dim3(64 * G::WAVES), 0, stream, args);
   return hipGetLastError() == hipSuccess ? CONV_OK : CONV_ERR_HIP;
@@ -2119,9 +2133,9 @@ static int launch_stream(const StreamArgs& args, const FusedPlan& p, hipStream_t
 
 static int launch_stream_spec(const StreamArgs& args, const FusedPlan& p, hipStream_t stream) {
   switch (p.spec) {
-#define CONVHIP_FUSED_CASE(id, CIN, KH, KW, NG, O2, ROWS) \
-  case id:                                              \
-    return launch_stream<CIN, KH, KW, NG, O2, ROWS>(args, p, stream);
+#define CONVHIP_FUSED_CASE(id, CIN, KH, KW, NG, O2, ROWS, RT) \
+  case id:                                                  \
+    return launch_stream<CIN, KH, KW, NG, O2, ROWS, RT>(args, p, stream);
     CONVHIP_FUSED_SPECS(CONVHIP_FUSED_CASE)
 #undef CONVHIP_FUSED_CASE
     default: return CONV_ERR_UNSUPPORTED;

@@ -459,7 +459,7 @@ int plan_conv(const Geom& g, ConvPlan* out, int force_cfg, int num_cu, int use_t
   return CONV_OK;
 }
 
-#define CONVHIP_FUSED_DESC(id, CIN, KH, KW, NG, O2, ROWS) {id, CIN, KH, KW, NG, O2, ROWS},
+#define CONVHIP_FUSED_DESC(id, CIN, KH, KW, NG, O2, ROWS, RT) {id, CIN, KH, KW, NG, O2, ROWS, RT},
 static const FusedSpecDesc kFusedSpecs[] = {CONVHIP_FUSED_SPECS(CONVHIP_FUSED_DESC)};
 #undef CONVHIP_FUSED_DESC
 
@@ -477,10 +477,17 @@ static bool plan_fused_stream(const Geom& g, const FusedSpecDesc& d, FusedPlan* 
   // Input rows are copied whole in 16-byte chunks: no padding along W.
   if (g.P[2] != 0 || g.L[2] != d.O2 + d.KW - 1 || g.L[2] % 4 != 0) return false;
   const int64_t plane_out = g.plane_out();
-  const int64_t tiles = (plane_out + 63) / 64;
-  for (int64_t t = 0; t < tiles; t++) {
-    const int64_t p0 = 64 * t, p1 = std::min(p0 + 63, plane_out - 1);
-    if (p1 / g.O[2] - p0 / g.O[2] + d.KH > d.ROWS) return false;
+  int64_t tiles;
+  if (d.RT > 0) {
+    // Tiles of RT whole output rows.
+    if (d.RT * d.O2 > 64 || d.ROWS != d.RT + d.KH - 1) return false;
+    tiles = (g.O[1] + d.RT - 1) / d.RT;
+  } else {
+    tiles = (plane_out + 63) / 64;
+    for (int64_t t = 0; t < tiles; t++) {
+      const int64_t p0 = 64 * t, p1 = std::min(p0 + 63, plane_out - 1);
+      if (p1 / g.O[2] - p0 / g.O[2] + d.KH > d.ROWS) return false;
+    }
   }
   if (g.Cin * g.L[0] * g.L[1] * g.L[2] > std::numeric_limits<int32_t>::max()) return false;
   // Two waves split the output depths of each tile: twice the waves in flight,
@@ -502,7 +509,9 @@ static bool plan_fused_stream(const Geom& g, const FusedSpecDesc& d, FusedPlan* 
   q.tiles_per_plane = tiles;
   const int64_t slot = int64_t(d.CIN) * d.ROWS * q.bw;
   q.boxc = int(slot);
-  q.lds_bytes = 4 * 4 * 4 * slot;  // 4 waves x 4 ring slots
+  // 4 waves x 4 ring slots, or the epilogue's partial minima and channel
+  // transpose areas if larger.
+  q.lds_bytes = 4 * std::max<int64_t>(4 * 4 * slot, 4 * int64_t(d.NG) * 64 * 4 + 4 * 1024);
   q.grid[0] = (units + 3) / 4;
   q.grid[1] = 1;
   q.grid[2] = 1;

@@ -158,15 +158,17 @@ int plan_conv(const Geom& g, ConvPlan* p, int force_cfg = -1, int num_cu = 256, 
               bool split_pipe = true);
 
 // Build-time specialisations of the depth-streamed fused kernel (stride 1,
-// dilation 1, groups 1, kD = 3, min over depth): X(id, CIN, KH, KW, NG, O2, ROWS)
+// dilation 1, groups 1, kD = 3, min over depth): X(id, CIN, KH, KW, NG, O2, ROWS, RT)
 // with NG groups of 4 output channels, W_out = O2 and at most ROWS staged input
-// rows per 64-position tile.
-#define CONVHIP_FUSED_SPECS(X)                                 \
-  /* Conv3d 3->24, kernel 3x3x3, 32x32 planes (W_out 30) */ \
-  X(0, 3, 3, 3, 6, 30, 6)
+// rows per wave tile. RT > 0: a wave tile is RT whole output rows (RT * O2 <= 64
+// positions, lanes past them idle; ROWS = RT + KH - 1); RT = 0: 64 consecutive
+// positions of the flattened plane.
+#define CONVHIP_FUSED_SPECS(X)                                                    \
+  /* Conv3d 3->24, kernel 3x3x3, 32x32 planes (W_out 30): tiles of 2 rows */ \
+  X(0, 3, 3, 3, 6, 30, 4, 2)
 
 struct FusedSpecDesc {
-  int id, CIN, KH, KW, NG, O2, ROWS;
+  int id, CIN, KH, KW, NG, O2, ROWS, RT;
 };
 const FusedSpecDesc* fused_specs(int* count);
 
