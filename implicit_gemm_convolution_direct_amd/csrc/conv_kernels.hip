@@ -882,15 +882,25 @@ __global__ __launch_bounds__(64 * WM * WN) void conv_tap_kernel(ConvArgs a) {
       else
         tap_stage<MT, NT, WM, NWAVES, G, NP>(a, last ? tn : t, has_next, c0n, box0, box1, wchunk, addr, acc, wave,
                                              lane);
-      if (last) {
+      auto store_and_clear = [&] {
         store_tile<MT, NT, G::CL>(a, t, wm, kg, pidx, acc, bias);
 #pragma unroll
         for (int mi = 0; mi < MT; mi++)
 #pragma unroll
           for (int ni = 0; ni < NT; ni++) acc[mi][ni] = v4f{0.f, 0.f, 0.f, 0.f};
-      }
+      };
+      // With several chunks per item, the item's stores go out after the
+      // barrier below: they complete while the next item's first chunk is
+      // reduced, instead of inside the wait. With one chunk per item they would
+      // sit in front of the next item's copies, so they go out before the wait.
+      if constexpr (NCH == 1) store_and_clear();
+      // The next chunk's copies have landed in every wave and no wave still
+      // reads this chunk's buffer.
       wait_vmem();
       __syncthreads();
+      if constexpr (NCH > 1) {
+        if (last) store_and_clear();
+      }
     }
     if (!more) break;
     if (NCH & 1) parity ^= 1;
