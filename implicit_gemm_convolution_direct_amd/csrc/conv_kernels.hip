@@ -986,16 +986,45 @@ __global__ __launch_bounds__(64 * NW) void conv_tap_split_kernel(ConvArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kg = lane >> 4;
   const int li = lane & 15;
+  // Every kernel argument used is read here, in one batch of scalar loads (one
+  // memory round trip), and pinned in scalar registers.
+  const float* k_x = a.x;
+  const float* k_w = a.w;
+  const float* k_bias = a.bias;
+  float* k_y = a.y;
+  int k_Cin = a.Cin;
+  int k_Cout = a.Cout;
+  int k_Cg = a.Cg;
+  int k_Coutg = a.Coutg;
+  int k_L0 = a.L0;
+  int k_L1 = a.L1;
+  int k_L2 = a.L2;
+  int k_S0 = a.S0;
+  int k_S1 = a.S1;
+  int k_S2 = a.S2;
+  int k_D0 = a.D0;
+  int k_P0 = a.P0;
+  int k_P1 = a.P1;
+  int k_P2 = a.P2;
+  int k_O0 = a.O0;
+  int k_O1 = a.O1;
+  int k_O2 = a.O2;
+  int k_plane_out = a.plane_out;
+  int gx = gridDim.x, gy = gridDim.y;
+  asm volatile(""
+               : "+s"(k_x), "+s"(k_w), "+s"(k_bias), "+s"(k_y), "+s"(k_Cin), "+s"(k_Cout), "+s"(k_Cg), "+s"(k_Coutg),
+                 "+s"(k_L0), "+s"(k_L1), "+s"(k_L2), "+s"(k_S0), "+s"(k_S1), "+s"(k_S2), "+s"(k_D0), "+s"(k_P0),
+                 "+s"(k_P1), "+s"(k_P2), "+s"(k_O0), "+s"(k_O1), "+s"(k_O2), "+s"(k_plane_out), "+s"(gx), "+s"(gy));
   // Workgroups are dispatched round-robin over the 8 XCDs; give each XCD a
   // contiguous run of (plane, group) items so the input planes that
   // neighbouring output depths share stay in that XCD's L2.
-  int item = blockIdx.x + gridDim.x * blockIdx.y;
-  const int items = gridDim.x * gridDim.y;
+  int item = blockIdx.x + gx * blockIdx.y;
+  const int items = gx * gy;
   if ((items & 7) == 0) item = (item & 7) * (items >> 3) + (item >> 3);
-  const int plane = item % gridDim.x;
-  const int g = item / gridDim.x;
-  const int n = plane / a.O0;
-  const int od = plane - n * a.O0;
+  const int plane = item % gx;
+  const int g = item / gx;
+  const int n = plane / k_O0;
+  const int od = plane - n * k_O0;
   const int c = wave;  // this wave's input channel within the group
   float* wsh = smem;
   float* box = smem + G::WSH + wave * G::XSW;
@@ -1004,11 +1033,11 @@ __global__ __launch_bounds__(64 * NW) void conv_tap_split_kernel(ConvArgs a) {
 #pragma unroll
   for (int r = 0; r < 4; r++) {
     const int ch = 4 * kg + r;
-    b4[r] = (a.bias && ch < a.Coutg) ? a.bias[g * a.Coutg + ch] : 0.0f;
+    b4[r] = (k_bias && ch < k_Coutg) ? k_bias[g * k_Coutg + ch] : 0.0f;
   }
   {
     // The group's weights, 16 rows (rows past C_out/g read as zero).
-    const float* wg = a.w + int64_t(g) * a.Coutg * G::WROW;
+    const float* wg = k_w + int64_t(g) * k_Coutg * G::WROW;
     if constexpr (G::W4) {
       // Copy (m, i) moves chunks 64i .. 64i+63 of row m into row m of stride WLD.
 #pragma unroll
@@ -1017,7 +1046,7 @@ __global__ __launch_bounds__(64 * NW) void conv_tap_split_kernel(ConvArgs a) {
         if (ci < 16 * G::WRI) {
           const int m = ci / G::WRI, i = ci - m * G::WRI;
           const int q = 64 * i + lane;
-          const bool ok = m < a.Coutg;
+          const bool ok = m < k_Coutg;
           if (q < G::WQ) lds_dma_f32x4(ok ? wg + m * G::WROW + 4 * q : kZeroWord, wsh + m * G::WLD + 256 * i);
         }
       }
@@ -1028,7 +1057,7 @@ __global__ __launch_bounds__(64 * NW) void conv_tap_split_kernel(ConvArgs a) {
         const int j0 = (i * NW + wave) * 64;
         const int j = j0 + lane;
         if (j < G::WCH) {
-          const bool ok = j / G::WROW < a.Coutg;
+          const bool ok = j / G::WROW < k_Coutg;
           lds_dma_f32(ok ? wg + j : kZeroWord, wsh + j0);
         }
       }
@@ -1038,26 +1067,26 @@ __global__ __launch_bounds__(64 * NW) void conv_tap_split_kernel(ConvArgs a) {
   // (od*S0 - P0 + td*DD, zr - P1, F*j - P2) of channel g*Cg + c. Copy i of a
   // plane moves elements 64i .. 64i + 63; the in-plane part of each lane's
   // source is the same for every plane.
-  const int64_t vol_in = int64_t(a.L0) * a.L1 * a.L2;
-  const float* xc = CL ? a.x + int64_t(n) * vol_in * a.Cin + (int64_t(g) * a.Cg + c)
-                       : a.x + (int64_t(n) * a.Cin + int64_t(g) * a.Cg + c) * vol_in;
-  const int site = CL ? a.Cin : 1;  // floats between neighbouring input sites
+  const int64_t vol_in = int64_t(k_L0) * k_L1 * k_L2;
+  const float* xc = CL ? k_x + int64_t(n) * vol_in * k_Cin + (int64_t(g) * k_Cg + c)
+                       : k_x + (int64_t(n) * k_Cin + int64_t(g) * k_Cg + c) * vol_in;
+  const int site = CL ? k_Cin : 1;  // floats between neighbouring input sites
   int soff[G::PLANE_INSTR];
   uint32_t sok = 0;
 #pragma unroll
   for (int i = 0; i < G::PLANE_INSTR; i++) {
     const int e = i * 64 + lane;
     const int zr = e / G::BWC, j = e - zr * G::BWC;
-    const int ih = zr - a.P1, iw = G::FF * j - a.P2;
-    const bool ok = e < G::PLANE && unsigned(ih) < unsigned(a.L1) && unsigned(iw) < unsigned(a.L2);
-    soff[i] = ok ? (ih * a.L2 + iw) * site : 0;
+    const int ih = zr - k_P1, iw = G::FF * j - k_P2;
+    const bool ok = e < G::PLANE && unsigned(ih) < unsigned(k_L1) && unsigned(iw) < unsigned(k_L2);
+    soff[i] = ok ? (ih * k_L2 + iw) * site : 0;
     sok |= uint32_t(ok) << i;
   }
   auto stage_copy = [&](int td, int i) {
-    const int id = od * a.S0 - a.P0 + td * a.D0;
-    const bool ok = unsigned(id) < unsigned(a.L0) && ((sok >> i) & 1);
+    const int id = od * k_S0 - k_P0 + td * k_D0;
+    const bool ok = unsigned(id) < unsigned(k_L0) && ((sok >> i) & 1);
     if (i * 64 + lane < G::PLANE)
-      lds_dma_f32(ok ? xc + (int64_t(id) * a.L1 * a.L2 * site + soff[i]) : kZeroWord, box + td * G::PLANE + i * 64);
+      lds_dma_f32(ok ? xc + (int64_t(id) * k_L1 * k_L2 * site + soff[i]) : kZeroWord, box + td * G::PLANE + i * 64);
   };
 #pragma unroll
   for (int i = 0; i < G::PLANE_INSTR; i++) stage_copy(0, i);
@@ -1066,8 +1095,8 @@ __global__ __launch_bounds__(64 * NW) void conv_tap_split_kernel(ConvArgs a) {
 #pragma unroll
   for (int ni = 0; ni < NT; ni++) {
     const int p = 16 * (int(blockIdx.z) * NT + ni) + li;
-    const int oh = p / a.O2, ow = p - (p / a.O2) * a.O2;
-    noff[ni] = p < a.plane_out ? oh * a.S1 * G::BWC + ow * (a.S2 / G::FF) : 0;
+    const int oh = p / k_O2, ow = p - (p / k_O2) * k_O2;
+    noff[ni] = p < k_plane_out ? oh * k_S1 * G::BWC + ow * (k_S2 / G::FF) : 0;
   }
   int dpat[NP];
   fill_pat_deltas<G>(dpat, kg, std::make_integer_sequence<int, NP>{});
@@ -1144,7 +1173,7 @@ __global__ __launch_bounds__(64 * NW) void conv_tap_split_kernel(ConvArgs a) {
     for (int r = 0; r < 4; r++) smem[((wave * NT + ni) * 4 + r) * 64 + lane] = acc[ni][r];
   __syncthreads();
   // All of this wave's partial reads are issued before the sums and stores.
-  const int64_t out_plane = int64_t(a.O1) * a.O2;
+  const int64_t out_plane = int64_t(k_O1) * k_O2;
   constexpr int NPR = (NT * 4 + NW - 1) / NW;  // (tile, register) pairs per wave
   float part[NPR][NW];
 #pragma unroll
@@ -1156,10 +1185,10 @@ __global__ __launch_bounds__(64 * NW) void conv_tap_split_kernel(ConvArgs a) {
   }
   // Channel ch of position p: NCDHW y[n][g*Coutg + ch][od][p], channels-last
   // y[n][od][p][g*Coutg + ch].
-  float* yg = CL ? a.y + (int64_t(n) * a.O0 + od) * out_plane * a.Cout + int64_t(g) * a.Coutg
-                 : a.y + (int64_t(n) * a.Cout + int64_t(g) * a.Coutg) * a.O0 * out_plane + int64_t(od) * out_plane;
-  const int64_t ch_stride = CL ? 1 : int64_t(a.O0) * out_plane;
-  const int64_t p_stride = CL ? a.Cout : 1;
+  float* yg = CL ? k_y + (int64_t(n) * k_O0 + od) * out_plane * k_Cout + int64_t(g) * k_Coutg
+                 : k_y + (int64_t(n) * k_Cout + int64_t(g) * k_Coutg) * k_O0 * out_plane + int64_t(od) * out_plane;
+  const int64_t ch_stride = CL ? 1 : int64_t(k_O0) * out_plane;
+  const int64_t p_stride = CL ? k_Cout : 1;
 #pragma unroll
   for (int j = 0; j < NPR; j++) {
     const int pr = wave + NW * j;
@@ -1170,7 +1199,7 @@ __global__ __launch_bounds__(64 * NW) void conv_tap_split_kernel(ConvArgs a) {
     const int ch = 4 * kg + r;
     const int p = 16 * (int(blockIdx.z) * NT + ni) + li;
     const float b = r == 0 ? b4[0] : r == 1 ? b4[1] : r == 2 ? b4[2] : b4[3];
-    if (pr < NT * 4 && ch < a.Coutg && p < a.plane_out) yg[ch * ch_stride + p * p_stride] = v + b;
+    if (pr < NT * 4 && ch < k_Coutg && p < k_plane_out) yg[ch * ch_stride + p * p_stride] = v + b;
   }
 }
 

@@ -446,6 +446,10 @@ SPLIT_CASES = [
     ((1, 16, 6, 32, 32), (32, 8, 3, 5, 7), (1, 2, 2), (1, 1, 2), (1, 2, 3), 2),
     ((2, 16, 3, 32, 32), (20, 8, 3, 5, 7), (1, 2, 2), (1, 1, 2), (0, 2, 3), 2),
     ((1, 8, 4, 32, 32), (16, 8, 3, 5, 7), (1, 2, 2), (1, 1, 2), (1, 2, 3), 1),
+    # depth stride 2 (the depth-tap rotation no longer lines up with the planes neighbours share)
+    ((1, 16, 7, 32, 32), (32, 8, 3, 5, 7), (2, 2, 2), (1, 1, 2), (1, 2, 3), 2),
+    # depth padding 2: whole padding planes in the box
+    ((2, 16, 3, 32, 32), (32, 8, 3, 5, 7), (1, 2, 2), (1, 1, 2), (2, 2, 3), 2),
     # tiny Conv3d geometry
     ((2, 3, 4, 16, 16), (8, 3, 3, 3, 3), 1, 1, 0, 1),
     ((1, 3, 5, 16, 16), (5, 3, 3, 3, 3), 1, 1, 0, 1),
@@ -463,7 +467,7 @@ def test_split_specialised_kernel_integer_exact(case, pipe, monkeypatch):
     assert "kernel=conv_tap_split" in desc, desc
     assert ("pipe=1" in desc) == (pipe == "1" and tuple(ws[2:]) == (3, 5, 7)), desc
     r = np.random.default_rng(500 + case)
-    x, w, b = _int_inputs(r, xs, ws, bias=True)
+    x, w, b = _int_inputs(r, xs, ws, bias=case % 2 == 0)
     say(f"split case {case}: x={xs} w={ws}: {desc}")
     y = gpu_conv(x, w, b, s, d, p, g)
     np.testing.assert_array_equal(y.astype(np.float64), oracle.conv(x, w, b, s, d, p, g))
