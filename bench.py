@@ -202,6 +202,46 @@ def time_workload(name, steps, warmup, torch, ch, synth, flush=None, warm_s=WARM
     return rec, macs
 
 
+def calibrate(torch, ch, seconds=0.05):
+    """Rates this chip reaches in practice: fp32 matrix-core and vector-FMA
+    throughput from the library's probes (each launch sized to about `seconds`),
+    and HBM bandwidth from a plain 1 GiB device-to-device copy (2 bytes moved per
+    byte copied). Each is the best of 5 timed repetitions after 0.3 s of warm-up."""
+    sink = torch.zeros(1, dtype=torch.float32, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    out = {}
+
+    def best_rate(run, work):
+        t_w = time.perf_counter()
+        while time.perf_counter() - t_w < 0.3:
+            run()
+            torch.cuda.synchronize()
+        rates = []
+        for _ in range(5):
+            a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            run()
+            z.record(stream)
+            torch.cuda.synchronize()
+            rates.append(work / (a.elapsed_time(z) * 1e-3))
+        return max(rates)
+
+    for key, kind, guess in (("mfma_f32_tflops", ch.PROBE_MFMA_F32, PEAK_FP32_TFLOPS),
+                             ("fma_f32_tflops", ch.PROBE_FMA_F32, PEAK_FP32_TFLOPS / 2)):
+        # Size the launch from the published rate: about `seconds` of work.
+        flop1 = ch.peak_probe(kind, 1, sink)
+        iters = max(1, int(seconds * guess * 1e12 / flop1))
+        flop = flop1 * iters
+        out[key] = round(best_rate(lambda: ch.peak_probe(kind, iters, sink), flop) / 1e12, 2)
+    n = (1 << 30) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    out["hbm_copy_gbs"] = round(best_rate(lambda: dst.copy_(src), 2.0 * 4 * n) / 1e9, 1)
+    del src, dst
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(name):
     """The fp64 oracle on the full headline workload, timed on the host cores."""
     import oracle
@@ -294,6 +334,16 @@ def main():
         tol = 1e-4 * math.sqrt(int(np.prod(cfg["w"][1:]))) * float(np.abs(ref).max())
         parity = {"max_abs_err": err, "tol": tol, "pass": err <= tol}
 
+    # Achievable rates on this GPU, and each workload against them (the matrix
+    # rate binds every workload here).
+    achievable = None
+    if not args.only:
+        print("[bench] calibration probes", file=sys.stderr, flush=True)
+        achievable = calibrate(torch, ch)
+        for rec in shapes.values():
+            rec["frac_achievable_mfma"] = round(rec["tflops"] / achievable["mfma_f32_tflops"], 4)
+            rec["frac_achievable_hbm"] = round(rec["gbs"] / achievable["hbm_copy_gbs"], 4)
+
     cfgh = synth.WORKLOADS[split_name(head_name)[0]]
     traffic = read_traffic(head_name)
     achieved = head["tflops"]
@@ -316,6 +366,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_FP32_TFLOPS, 4), "traffic": traffic},
         "cpu_baseline": cpu,
+        "achievable": achievable,
         "parity": parity,
         "shapes": shapes,
         "kernel_src": kernel_source_hash(),

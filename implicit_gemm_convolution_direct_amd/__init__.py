@@ -28,7 +28,7 @@ STATUS_NAMES = {
     -9: "CONV_ERR_HIP",
 }
 EXPORTED = ["conv_out_shape", "conv_fwd", "conv_fwd_channels_last", "conv3d_min_softmax", "conv_status_string",
-            "conv_plan_describe", "convhip_synth_fill"]
+            "conv_plan_describe", "convhip_synth_fill", "convhip_peak_probe"]
 
 
 class ConvError(RuntimeError):
@@ -68,6 +68,8 @@ def lib():
         L.convhip_synth_fill.restype = ctypes.c_int
         L.convhip_synth_fill.argtypes = [vp, ctypes.c_int64, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int,
                                          ctypes.c_float, ctypes.c_int, ctypes.c_int, vp]
+        L.convhip_peak_probe.restype = ctypes.c_int
+        L.convhip_peak_probe.argtypes = [ctypes.c_int, ctypes.c_int64, vp, ctypes.POINTER(ctypes.c_int64), vp]
         _lib = L
     return _lib
 
@@ -251,3 +253,19 @@ def synth_fill(t, seed, kind=KIND_UNIFORM01, start=0, bound=1.0, lo=0, span=1):
     if rc != CONV_OK:
         raise ConvError(rc, "convhip_synth_fill")
     return t
+
+
+PROBE_MFMA_F32, PROBE_FMA_F32 = 0, 1
+
+
+def peak_probe(kind, iters, sink):
+    """Enqueue one calibration launch (kind PROBE_MFMA_F32 or PROBE_FMA_F32) on the
+    current stream of sink's device; returns the floating-point operations it
+    performs. sink: a GPU fp32 tensor of at least one element."""
+    _check_tensor(sink, "sink")
+    flop = ctypes.c_int64(0)
+    rc = lib().convhip_peak_probe(int(kind), int(iters), sink.data_ptr(), ctypes.byref(flop),
+                                  _stream_handle(sink.device))
+    if rc != CONV_OK:
+        raise ConvError(rc, "convhip_peak_probe")
+    return flop.value

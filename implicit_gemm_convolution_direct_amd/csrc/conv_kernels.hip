@@ -2025,6 +2025,46 @@ __global__ __launch_bounds__(256, 4) void fused_stream_kernel(StreamArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Calibration probes: the fp32 rates this chip reaches in practice, against
+// which measured kernels are also reported (not part of the operation).
+// - peak_mfma_kernel: each wave keeps 8 independent 16x16x4 fp32 MFMA
+//   accumulation chains busy (each accumulator is reused 8 instructions later,
+//   far past the instruction's latency).
+// - peak_fma_kernel: each lane keeps 8 independent fp32 FMA chains (plain
+//   v_fma_f32; packed fp32 is not generated by this build).
+// The results stay in registers; a store that no input can trigger keeps them.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void peak_mfma_kernel(int64_t iters, float* __restrict__ sink) {
+  const float av = 1.0f + 1e-7f * float(threadIdx.x), bv = 1.0f - 1e-7f * float(threadIdx.x);
+  v4f acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; j++) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int64_t i = 0; i < iters; i++) {
+#pragma unroll
+    for (int j = 0; j < 8; j++) acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc[j], 0, 0, 0);
+  }
+  float t = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; j++) t += acc[j][0] + acc[j][1] + acc[j][2] + acc[j][3];
+  if (t < 0.0f) sink[0] = t;  // every product is positive
+}
+
+__global__ __launch_bounds__(256) void peak_fma_kernel(int64_t iters, float* __restrict__ sink) {
+  const float m = 0.999999f, c = 1e-6f * float(threadIdx.x & 7);
+  float v[8];
+#pragma unroll
+  for (int j = 0; j < 8; j++) v[j] = 1.0f + 0.125f * float(j);
+  for (int64_t i = 0; i < iters; i++) {
+#pragma unroll
+    for (int j = 0; j < 8; j++) v[j] = __builtin_fmaf(v[j], m, c);
+  }
+  float t = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; j++) t += v[j];
+  if (t < 0.0f) sink[0] = t;  // every chain stays positive
+}
+
+// ---------------------------------------------------------------------------
 // Device-side synthetic input generator (SplitMix64, one output per element).
 // ---------------------------------------------------------------------------
 __global__ void synth_fill_kernel(float* __restrict__ dst, int64_t count, uint64_t seed, uint64_t start,
@@ -2439,6 +2479,23 @@ int conv3d_min_softmax(const float* x, const int64_t* x_shape, const float* w, c
     case 15: return launch_fused_ng<15>(a, p, s);
     default: return launch_fused_ng<16>(a, p, s);
   }
+}
+
+int convhip_peak_probe(int kind, int64_t iters, float* sink, int64_t* flop, convhip_stream_t stream) {
+  if (!sink || !flop) return CONV_ERR_NULL;
+  if ((kind != 0 && kind != 1) || iters < 1 || iters > (int64_t(1) << 32)) return CONV_ERR_PARAM;
+  // 4 workgroups of 4 waves per compute unit: 4 waves per SIMD.
+  const int64_t blocks = 4 * int64_t(device_num_cu());
+  const int64_t threads = blocks * 256;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (kind == 0) {
+    *flop = (threads / 64) * iters * 8 * (2 * 16 * 16 * 4);
+    hipLaunchKernelGGL(peak_mfma_kernel, dim3(unsigned(blocks)), dim3(256), 0, s, iters, sink);
+  } else {
+    *flop = threads * iters * 8 * 2;
+    hipLaunchKernelGGL(peak_fma_kernel, dim3(unsigned(blocks)), dim3(256), 0, s, iters, sink);
+  }
+  return hipGetLastError() == hipSuccess ? CONV_OK : CONV_ERR_HIP;
 }
 
 int convhip_synth_fill(float* dst, int64_t count, uint64_t seed, uint64_t start, int kind, float bound, int lo,

@@ -150,6 +150,20 @@ int conv_plan_describe(int nd, const int64_t *x_shape, const int64_t *w_shape,
 int convhip_synth_fill(float *dst, int64_t count, uint64_t seed, uint64_t start, int kind,
                        float bound, int lo, int span, convhip_stream_t stream);
 
+/*
+ * Calibration probe (not part of the operation): one launch that keeps every
+ * SIMD of the device busy with independent fp32 arithmetic for `iters` rounds,
+ * to measure the rate the chip reaches in practice. kind 0: 16x16x4 fp32
+ * matrix-core instructions (8 independent accumulators per wave); kind 1:
+ * plain fp32 FMA on the vector ALU (8 independent chains per lane). Enqueues on
+ * `stream` and stores in *flop (host memory) the floating-point operations the
+ * launch performs; the caller times it. sink is a device pointer to at least
+ * one float, written by no input (it keeps the results live). Returns CONV_OK,
+ * CONV_ERR_NULL, CONV_ERR_PARAM (kind not 0 or 1, iters outside [1, 2^32]) or
+ * CONV_ERR_HIP.
+ */
+int convhip_peak_probe(int kind, int64_t iters, float *sink, int64_t *flop, convhip_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -144,3 +144,12 @@ def test_plans_fit_lds_and_cover_workloads():
         assert int(fields["lds"]) <= 160 * 1024, d
         gx, gy, gz = (int(v) for v in fields["grid"].split("x"))
         assert gx >= 1 and gy >= 1 and gz >= 1
+
+
+def test_peak_probe_validates_before_launch():
+    flop = ctypes.c_int64(0)
+    L = ch.lib()
+    assert L.convhip_peak_probe(2, 10, FAKE, ctypes.byref(flop), None) == -5   # unknown kind
+    assert L.convhip_peak_probe(0, 0, FAKE, ctypes.byref(flop), None) == -5    # iters < 1
+    assert L.convhip_peak_probe(0, 10, None, ctypes.byref(flop), None) == -1   # no sink
+    assert L.convhip_peak_probe(1, 10, FAKE, None, None) == -1                 # no flop output

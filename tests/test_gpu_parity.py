@@ -493,3 +493,15 @@ def test_workloads_use_expected_kernels():
         cfg = synth.WORKLOADS[name]
         d = ch.plan_describe(cfg["x"], cfg["w"], *_cfg_args(cfg)) + " "
         assert f"kernel={kernel}" in d, d
+
+
+def test_peak_probes_run_and_count_their_work():
+    """The calibration probes launch on the caller's stream and report the work
+    of one launch: 4 workgroups of 4 waves per compute unit."""
+    sink = torch.zeros(1, dtype=torch.float32, device=dev())
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    waves = 4 * cus * 4
+    assert ch.peak_probe(ch.PROBE_MFMA_F32, 3, sink) == waves * 3 * 8 * 2 * 16 * 16 * 4
+    assert ch.peak_probe(ch.PROBE_FMA_F32, 3, sink) == waves * 64 * 3 * 8 * 2
+    torch.cuda.synchronize()
+    assert float(sink.cpu()[0]) == 0.0  # the guard store never fires
