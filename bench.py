@@ -273,6 +273,10 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--warm-seconds", type=float, default=WARM_S,
                     help="minimum seconds of back-to-back warm-up calls per workload")
+    ap.add_argument("--unfused-chain", action="store_true",
+                    help="only run the fused workload as three separate steps (conv_fwd writing the 5-D result, "
+                         "torch.amin over depth, torch.softmax over channels) and time it; for measuring the "
+                         "HBM traffic the fused kernel avoids")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device-to-device copy of this many bytes per step "
                          "(calibrates rocprofv3's FETCH_SIZE / WRITE_SIZE against a known traffic)")
@@ -300,6 +304,31 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": 4 * n, "steps": args.warmup + args.steps}), flush=True)
+        return
+
+    if args.unfused_chain:
+        name = "conv3d_min_softmax"
+        cfg, x, w, b = make_device_inputs(name, torch, ch, synth)
+        args4 = (cfg["stride"], cfg["dilation"], cfg["padding"], cfg["groups"])
+
+        def chain():
+            y5 = ch.conv_fwd(x, w, b, *args4)
+            return torch.softmax(torch.amin(y5, dim=2), dim=1)
+
+        fused = ch.conv3d_min_softmax(x, w, b, *args4)
+        err = float((chain() - fused).abs().max())
+        for _ in range(args.warmup):
+            chain()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(torch.cuda.current_stream())
+        for _ in range(args.steps):
+            chain()
+        e1.record(torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        print(json.dumps({"unfused_chain": name, "steps": args.steps, "warmup": args.warmup,
+                          "ms_per_chain": round(e0.elapsed_time(e1) / args.steps, 5),
+                          "max_abs_diff_vs_fused": err}), flush=True)
         return
 
     names = [args.only] if args.only else ORDER
