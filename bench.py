@@ -230,7 +230,7 @@ def calibrate(torch, ch, seconds=0.05):
                              ("fma_f32_tflops", ch.PROBE_FMA_F32, PEAK_FP32_TFLOPS / 2)):
         # Size the launch from the published rate: about `seconds` of work.
         flop1 = ch.peak_probe(kind, 1, sink)
-        iters = max(1, int(seconds * guess * 1e12 / flop1))
+        iters = min(1 << 22, max(1, int(seconds * guess * 1e12 / flop1)))
         flop = flop1 * iters
         out[key] = round(best_rate(lambda: ch.peak_probe(kind, iters, sink), flop) / 1e12, 2)
     n = (1 << 30) // 4

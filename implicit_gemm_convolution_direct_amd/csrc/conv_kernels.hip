@@ -2483,7 +2483,8 @@ int conv3d_min_softmax(const float* x, const int64_t* x_shape, const float* w, c
 
 int convhip_peak_probe(int kind, int64_t iters, float* sink, int64_t* flop, convhip_stream_t stream) {
   if (!sink || !flop) return CONV_ERR_NULL;
-  if ((kind != 0 && kind != 1) || iters < 1 || iters > (int64_t(1) << 32)) return CONV_ERR_PARAM;
+  // At most 2^22 rounds: about 2 s of matrix-core work per launch.
+  if ((kind != 0 && kind != 1) || iters < 1 || iters > (int64_t(1) << 22)) return CONV_ERR_PARAM;
   // 4 workgroups of 4 waves per compute unit: 4 waves per SIMD.
   const int64_t blocks = 4 * int64_t(device_num_cu());
   const int64_t threads = blocks * 256;

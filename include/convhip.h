@@ -159,7 +159,8 @@ int convhip_synth_fill(float *dst, int64_t count, uint64_t seed, uint64_t start,
  * `stream` and stores in *flop (host memory) the floating-point operations the
  * launch performs; the caller times it. sink is a device pointer to at least
  * one float, written by no input (it keeps the results live). Returns CONV_OK,
- * CONV_ERR_NULL, CONV_ERR_PARAM (kind not 0 or 1, iters outside [1, 2^32]) or
+ * CONV_ERR_NULL, CONV_ERR_PARAM (kind not 0 or 1, iters outside [1, 2^22]: a
+ * launch stays within about 2 s) or
  * CONV_ERR_HIP.
  */
 int convhip_peak_probe(int kind, int64_t iters, float *sink, int64_t *flop, convhip_stream_t stream);

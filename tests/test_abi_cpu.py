@@ -151,5 +151,6 @@ def test_peak_probe_validates_before_launch():
     L = ch.lib()
     assert L.convhip_peak_probe(2, 10, FAKE, ctypes.byref(flop), None) == -5   # unknown kind
     assert L.convhip_peak_probe(0, 0, FAKE, ctypes.byref(flop), None) == -5    # iters < 1
+    assert L.convhip_peak_probe(0, (1 << 22) + 1, FAKE, ctypes.byref(flop), None) == -5  # too long a launch
     assert L.convhip_peak_probe(0, 10, None, ctypes.byref(flop), None) == -1   # no sink
     assert L.convhip_peak_probe(1, 10, FAKE, None, None) == -1                 # no flop output
