@@ -264,6 +264,37 @@ def cpu_baseline(name):
                       f"{t:.3f} s per pass"}, ref
 
 
+def cpu_baselines_per_workload(shapes, seconds=1.0):
+    """The fp64 oracle on one sample of each workload (channels-first), timed on
+    the host cores for about `seconds` each: its FLOP rate, the full workload's
+    time extrapolated from it, and the GPU's speed-up over it."""
+    import oracle
+    import synth
+    out = {}
+    for name in ("tiny_conv3d", "general_conv3d", "conv3d_min_softmax", "asym_conv3d", "long_conv1d"):
+        cfg = synth.WORKLOADS[name]
+        x, w, b = synth.make_inputs(name, n_samples=1)
+        _, macs_full, _, _, _ = geometry(cfg)
+        macs = macs_full // cfg["x"][0]
+        args = (cfg["stride"], cfg["dilation"], cfg["padding"], cfg["groups"])
+        run = (lambda: oracle.conv3d_min_softmax(x, w, b, *args)) if cfg["fused"] else \
+              (lambda: oracle.conv(x, w, b, *args))
+        reps = 0
+        t0 = time.perf_counter()
+        while reps < 1 or time.perf_counter() - t0 < seconds:
+            run()
+            reps += 1
+        t = (time.perf_counter() - t0) / reps
+        rec = {"tflops": round(2.0 * macs / t / 1e12, 6), "cores": oracle.num_threads(),
+               "sample": f"sample 0 of {cfg['x'][0]}, {reps} pass(es), {t:.3f} s per pass",
+               "full_s_extrapolated": round(t * cfg["x"][0], 3)}
+        if name in shapes:
+            rec["gpu_over_cpu"] = round(rec["full_s_extrapolated"] / (shapes[name]["ms"] * 1e-3), 1)
+        out[name] = rec
+        del x, w, b
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -351,6 +382,7 @@ def main():
         head_name = HEADLINE
 
     cpu = None
+    cpu_all = None
     parity = None
     if not args.no_cpu and not args.only:
         print("[bench] oracle CPU baseline", file=sys.stderr, flush=True)
@@ -362,6 +394,8 @@ def main():
         err = float(np.abs(y.cpu().numpy().astype(np.float64) - ref).max())
         tol = 1e-4 * math.sqrt(int(np.prod(cfg["w"][1:]))) * float(np.abs(ref).max())
         parity = {"max_abs_err": err, "tol": tol, "pass": err <= tol}
+        print("[bench] oracle CPU rate per workload (one sample each)", file=sys.stderr, flush=True)
+        cpu_all = cpu_baselines_per_workload(shapes)
 
     # Achievable rates on this GPU, and each workload against them (the matrix
     # rate binds every workload here).
@@ -395,6 +429,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_FP32_TFLOPS, 4), "traffic": traffic},
         "cpu_baseline": cpu,
+        "cpu_baseline_per_workload": cpu_all,
         "achievable": achievable,
         "parity": parity,
         "shapes": shapes,
