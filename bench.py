@@ -285,11 +285,12 @@ def cpu_baselines_per_workload(shapes, seconds=1.0):
             run()
             reps += 1
         t = (time.perf_counter() - t0) / reps
+        full_s = t * cfg["x"][0]
         rec = {"tflops": round(2.0 * macs / t / 1e12, 6), "cores": oracle.num_threads(),
-               "sample": f"sample 0 of {cfg['x'][0]}, {reps} pass(es), {t:.3f} s per pass",
-               "full_s_extrapolated": round(t * cfg["x"][0], 3)}
+               "sample": f"sample 0 of {cfg['x'][0]}, {reps} pass(es), {1e3 * t:.4g} ms per pass",
+               "full_s_extrapolated": float(f"{full_s:.4g}")}
         if name in shapes:
-            rec["gpu_over_cpu"] = round(rec["full_s_extrapolated"] / (shapes[name]["ms"] * 1e-3), 1)
+            rec["gpu_over_cpu"] = round(full_s / (shapes[name]["ms"] * 1e-3), 1)
         out[name] = rec
         del x, w, b
     return out
