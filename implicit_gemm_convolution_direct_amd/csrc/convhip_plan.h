@@ -110,8 +110,8 @@ struct ConvPlan {
 #define CONVHIP_SPLIT_SPECS(X)                                                     \
   /* Conv3d 16->32, groups 2, kernel 3x5x7, stride (1,2,2), dilation (1,1,2) */  \
   X(0, 13, 8, 3, 5, 7, 1, 1, 2, 2, 35, 20, 1)                                     \
-  /* Conv3d 3->8, kernel 3x3x3 on 16^3: 4 workgroups per plane */                \
-  X(1, 4, 3, 3, 3, 3, 1, 1, 1, 1, 16, 16, 4)
+  /* Conv3d 3->8, kernel 3x3x3 on 16^3: 7 workgroups of 2 tiles per plane */   \
+  X(1, 2, 3, 3, 3, 3, 1, 1, 1, 1, 16, 16, 7)
 
 // The pipelined channel-split kernel runs a plane's NT tiles in two batches
 // (ceil(NT/2), then floor(NT/2)), sums each batch's tiles one per wave, and
