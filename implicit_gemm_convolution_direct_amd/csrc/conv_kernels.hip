@@ -338,20 +338,42 @@ __device__ __forceinline__ void stage_wfrag(const ConvArgs& a, int g, int m0, in
   }
 }
 
+// Row and column of flattened plane positions p, p + 16, p + 32, ... in a plane
+// `width` wide: one division for the first, then steps of 16 = q16 rows plus
+// r16 columns (r16 < width, so a step wraps at most once). This replaces a
+// division per tile, which sat on the path to the first product.
+struct PosStep {
+  int oh, ow, q16, r16, width;
+  __device__ __forceinline__ PosStep(int p, int w) : width(w) {
+    oh = p / w;
+    ow = p - oh * w;
+    q16 = 16 / w;
+    r16 = 16 - q16 * w;
+  }
+  __device__ __forceinline__ void next() {
+    ow += r16;
+    oh += q16;
+    const bool wrap = ow >= width;
+    ow -= wrap ? width : 0;
+    oh += wrap ? 1 : 0;
+  }
+};
+
 // Per-lane output positions of a wave's NT sub-tiles: LDS offset inside the box
 // (row stride bw) and flattened index in the (n, co, od) output plane (-1: none).
 template <int NT, bool CL = false>
 __device__ __forceinline__ void tile_positions(const ConvArgs& a, const TileGeo& t, int wn, int li, int noff[NT],
                                                int pidx[NT]) {
+  PosStep ps(t.p0 + wn * (16 * NT) + li, a.O2);
 #pragma unroll
   for (int ni = 0; ni < NT; ni++) {
     const int q = wn * (16 * NT) + 16 * ni + li;
     int oh, ow, valid;
     if (a.mode == TILE_FLAT) {
-      const int p = t.p0 + q;
-      valid = p < a.plane_out;
-      oh = p / a.O2;
-      ow = p - oh * a.O2;
+      valid = t.p0 + q < a.plane_out;
+      oh = ps.oh;
+      ow = ps.ow;
+      ps.next();
     } else {
       oh = t.oh_first;
       ow = t.ow0 + q;
@@ -656,13 +678,15 @@ struct TapPatterns {
   }
 };
 
-// Lane kg's share of distinct step pattern Q, selected among compile-time
-// constants (no table in memory).
+// Lane kg's share of distinct step pattern Q, from compile-time constants (no
+// table in memory), computed from the two bits of kg (a chain of selects was
+// compiled to exec-mask branches).
 template <class G, int Q>
 __device__ __forceinline__ int pat_delta(int kg) {
   constexpr TapPatterns<G> P{};
   constexpr int d0 = P.pat[Q][0], d1 = P.pat[Q][1], d2 = P.pat[Q][2], d3 = P.pat[Q][3];
-  return kg == 0 ? d0 : kg == 1 ? d1 : kg == 2 ? d2 : d3;
+  const int b0 = kg & 1, b1 = (kg >> 1) & 1;
+  return d0 + b0 * (d1 - d0) + b1 * (d2 - d0) + (b0 & b1) * (d3 - d2 - d1 + d0);
 }
 template <class G, int... Q>
 __device__ __forceinline__ void fill_pat_deltas(int* dp, int kg, std::integer_sequence<int, Q...>) {
@@ -1092,11 +1116,14 @@ __global__ __launch_bounds__(64 * NW) void conv_tap_split_kernel(ConvArgs a) {
   for (int i = 0; i < G::PLANE_INSTR; i++) stage_copy(0, i);
   // Output positions: tiles blockIdx.z*NT .. of the plane (flattened (oh, ow)).
   int noff[NT];
+  {
+    const int p0 = 16 * int(blockIdx.z) * NT + li;
+    PosStep ps(p0, k_O2);
 #pragma unroll
-  for (int ni = 0; ni < NT; ni++) {
-    const int p = 16 * (int(blockIdx.z) * NT + ni) + li;
-    const int oh = p / k_O2, ow = p - (p / k_O2) * k_O2;
-    noff[ni] = p < k_plane_out ? oh * k_S1 * G::BWC + ow * (k_S2 / G::FF) : 0;
+    for (int ni = 0; ni < NT; ni++) {
+      noff[ni] = p0 + 16 * ni < k_plane_out ? ps.oh * k_S1 * G::BWC + ps.ow * (k_S2 / G::FF) : 0;
+      ps.next();
+    }
   }
   int dpat[NP];
   fill_pat_deltas<G>(dpat, kg, std::make_integer_sequence<int, NP>{});
@@ -1358,11 +1385,14 @@ __global__ __launch_bounds__(64 * NW) void conv_tap_split_pipe_kernel(ConvArgs a
   fill_pat_deltas<G>(dpat, kg, std::make_integer_sequence<int, NP>{});
   const int base_b = int(reinterpret_cast<uintptr_t>(box) - reinterpret_cast<uintptr_t>(smem));
   int nb[NT], dp[NP];
+  {
+    const int p0 = 16 * int(blockIdx.z) * NT + li;
+    PosStep ps(p0, O2);
 #pragma unroll
-  for (int ni = 0; ni < NT; ni++) {
-    const int p = 16 * (int(blockIdx.z) * NT + ni) + li;
-    const int oh = p / O2, ow = p - (p / O2) * O2;
-    nb[ni] = base_b + 4 * (p < plane_out ? oh * S1 * G::BWC + ow * (S2 / G::FF) : 0);
+    for (int ni = 0; ni < NT; ni++) {
+      nb[ni] = base_b + 4 * (p0 + 16 * ni < plane_out ? ps.oh * S1 * G::BWC + ps.ow * (S2 / G::FF) : 0);
+      ps.next();
+    }
   }
 #pragma unroll
   for (int q = 0; q < NP; q++) dp[q] = 4 * dpat[q];
