@@ -359,6 +359,28 @@ struct PosStep {
   }
 };
 
+// Box offsets base + (p / width) * row + (p % width) * col of positions p,
+// p + 16, p + 32, ..., stepped by additions only.
+struct OffStep {
+  int ow, off, r16, width, d16, dwrap;
+  __device__ __forceinline__ OffStep(int p, int w, int base, int row, int col) : width(w) {
+    const int oh = p / w;
+    ow = p - oh * w;
+    off = base + oh * row + ow * col;
+    const int q16 = 16 / w;
+    r16 = 16 - q16 * w;
+    d16 = q16 * row + r16 * col;
+    dwrap = row - w * col;
+  }
+  __device__ __forceinline__ void next() {
+    ow += r16;
+    off += d16;
+    const bool wrap = ow >= width;
+    ow -= wrap ? width : 0;
+    off += wrap ? dwrap : 0;
+  }
+};
+
 // Per-lane output positions of a wave's NT sub-tiles: LDS offset inside the box
 // (row stride bw) and flattened index in the (n, co, od) output plane (-1: none).
 template <int NT, bool CL = false>
@@ -1118,11 +1140,12 @@ __global__ __launch_bounds__(64 * NW) void conv_tap_split_kernel(ConvArgs a) {
   int noff[NT];
   {
     const int p0 = 16 * int(blockIdx.z) * NT + li;
-    PosStep ps(p0, k_O2);
+    const int nlive = k_plane_out - p0;  // tile ni holds a position if 16 ni < nlive
+    OffStep os(p0, k_O2, 0, k_S1 * G::BWC, k_S2 / G::FF);
 #pragma unroll
     for (int ni = 0; ni < NT; ni++) {
-      noff[ni] = p0 + 16 * ni < k_plane_out ? ps.oh * k_S1 * G::BWC + ps.ow * (k_S2 / G::FF) : 0;
-      ps.next();
+      noff[ni] = 16 * ni < nlive ? os.off : 0;
+      os.next();
     }
   }
   int dpat[NP];
@@ -1387,11 +1410,12 @@ __global__ __launch_bounds__(64 * NW) void conv_tap_split_pipe_kernel(ConvArgs a
   int nb[NT], dp[NP];
   {
     const int p0 = 16 * int(blockIdx.z) * NT + li;
-    PosStep ps(p0, O2);
+    const int nlive = plane_out - p0;  // tile ni holds a position if 16 ni < nlive
+    OffStep os(p0, O2, base_b, 4 * S1 * G::BWC, 4 * (S2 / G::FF));
 #pragma unroll
     for (int ni = 0; ni < NT; ni++) {
-      nb[ni] = base_b + 4 * (p0 + 16 * ni < plane_out ? ps.oh * S1 * G::BWC + ps.ow * (S2 / G::FF) : 0);
-      ps.next();
+      nb[ni] = 16 * ni < nlive ? os.off : base_b;
+      os.next();
     }
   }
 #pragma unroll
