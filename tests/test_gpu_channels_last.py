@@ -59,6 +59,20 @@ def _random_geometry(r, nd):
 RANDOM_CASES = [(nd, seed) for nd in (1, 2, 3) for seed in range(8)]
 
 
+def test_flat_tile_positions_every_width_channels_last():
+    """Tiles of 16 flattened (row, column) positions over planes of every width
+    class (a step wraps no row, one row, or several), channels-last."""
+    r = np.random.default_rng(950)
+    for wo in (1, 2, 3, 5, 8, 15, 16, 17, 31, 33):
+        for sw in (1, 2):
+            xs, ws = (1, 11, (wo - 1) * sw + 3, 4), (8, 4, 3, 3)
+            s, d, p, g = (1, sw), 1, 0, 1
+            x, w, b = _int_inputs(r, xs, ws, bias=True)
+            say(f"cl flat width {wo} stride {sw}: " + ch.plan_describe(xs, ws, s, d, p, g, channels_last=True))
+            y = gpu_conv_cl(x, w, b, s, d, p, g)
+            np.testing.assert_array_equal(y.astype(np.float64), oracle.conv_channels_last(x, w, b, s, d, p, g))
+
+
 @pytest.mark.parametrize("nd,seed", RANDOM_CASES)
 def test_channels_last_random_integer_exact(nd, seed):
     r = np.random.default_rng(7000 + 100 * nd + seed)

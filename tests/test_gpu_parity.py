@@ -416,6 +416,28 @@ def test_every_tile_config_integer_exact(cfg, monkeypatch):
         np.testing.assert_array_equal(y.astype(np.float64), oracle.conv(x, w, b, s, d, p, g))
 
 
+# Output widths around the 16-position tile step: one step wraps no row (width
+# >= 16), exactly one (16 > width > 8) or several rows (width 1, 2, 3, 5, 8).
+FLAT_WIDTHS = [1, 2, 3, 5, 8, 15, 16, 17, 31, 33]
+
+
+@pytest.mark.parametrize("cfg", [None] + list(range(8)))
+def test_flat_tile_positions_every_width(cfg, monkeypatch):
+    """Tiles of 16 flattened (row, column) positions, stepped through planes of
+    every width class, under the default plan and each forced tile configuration."""
+    if cfg is not None:
+        monkeypatch.setenv("CONVHIP_CONV_CFG", str(cfg))
+    r = np.random.default_rng(900 + (cfg if cfg is not None else 9))
+    for wo in FLAT_WIDTHS:
+        for sw in (1, 2):
+            xs, ws = (1, 3, 11, (wo - 1) * sw + 3), (8, 3, 3, 3)
+            s, d, p, g = (1, sw), 1, 0, 1
+            x, w, b = _int_inputs(r, xs, ws, bias=True)
+            say(f"flat width {wo} stride {sw} cfg {cfg}: " + ch.plan_describe(xs, ws, s, d, p, g))
+            y = gpu_conv(x, w, b, s, d, p, g)
+            np.testing.assert_array_equal(y.astype(np.float64), oracle.conv(x, w, b, s, d, p, g))
+
+
 # Shapes that keep the geometry of a build-time specialisation (channel chunk,
 # taps, dilations, staged box) with fewer samples / shorter extents, so the
 # specialised persistent kernel runs on sizes the oracle checks in full.
