@@ -314,9 +314,9 @@ def main():
                          "(calibrates rocprofv3's FETCH_SIZE / WRITE_SIZE against a known traffic)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the convolution shards over the batch with no exchange; see DESIGN.md). Use --gpus 1.",
-              file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path (the convolution "
+              "would shard over the batch, each GPU computing its own samples with no exchange). "
+              "Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -2085,7 +2085,7 @@ __global__ __launch_bounds__(256, 4) void fused_stream_kernel(StreamArgs a) {
 //   accumulation chains busy (each accumulator is reused 8 instructions later,
 //   far past the instruction's latency).
 // - peak_fma_kernel: each lane keeps 8 independent fp32 FMA chains (plain
-//   v_fma_f32; packed fp32 is not generated by this build).
+//   v_fma_f32; the library is compiled without packed fp32).
 // The results stay in registers; a store that no input can trigger keeps them.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void peak_mfma_kernel(int64_t iters, float* __restrict__ sink) {
@@ -2373,7 +2373,7 @@ const char* conv_status_string(int status) {
     case CONV_ERR_GROUPS: return "CONV_ERR_GROUPS: groups < 1 or channels not divisible by groups";
     case CONV_ERR_PARAM: return "CONV_ERR_PARAM: stride/dilation < 1 or padding < 0";
     case CONV_ERR_EMPTY_OUTPUT: return "CONV_ERR_EMPTY_OUTPUT: an output length is <= 0";
-    case CONV_ERR_UNSUPPORTED: return "CONV_ERR_UNSUPPORTED: valid arguments this build does not handle";
+    case CONV_ERR_UNSUPPORTED: return "CONV_ERR_UNSUPPORTED: valid arguments the library does not handle";
     case CONV_ERR_OVERFLOW: return "CONV_ERR_OVERFLOW: a size exceeds the index arithmetic";
     case CONV_ERR_HIP: return "CONV_ERR_HIP: the HIP runtime reported an error";
     default: return "unknown conv_status";

@@ -41,7 +41,7 @@ typedef enum {
   CONV_ERR_GROUPS = -4,       /* groups < 1, or C_in or C_out not divisible by groups */
   CONV_ERR_PARAM = -5,        /* stride < 1, dilation < 1 or padding < 0 */
   CONV_ERR_EMPTY_OUTPUT = -6, /* some output length <= 0 */
-  CONV_ERR_UNSUPPORTED = -7,  /* valid, but not handled by this build (stated per entry point) */
+  CONV_ERR_UNSUPPORTED = -7,  /* valid, but not handled by the library (stated per entry point) */
   CONV_ERR_OVERFLOW = -8,     /* a size does not fit the index arithmetic */
   CONV_ERR_HIP = -9           /* the HIP runtime reported an error at launch */
 } conv_status;
@@ -110,7 +110,7 @@ int conv_fwd_channels_last(int nd,
  *   min_dim 2: y [N, C_out, H_out, W_out],
  *              y[n,:,h,w] = softmax_c( min_{od} conv3d(x,w,bias)[n,c,od,h,w] );
  *   min_dim 3: y [N, C_out, D_out, W_out];  min_dim 4: y [N, C_out, D_out, H_out].
- * Supported in this build: C_out <= 64, and the input box of one output tile
+ * Supported: C_out <= 64, and the input box of one output tile
  * over the whole min axis must fit in LDS (groups > 1 run as a block-diagonal
  * dense conv); other valid arguments return CONV_ERR_UNSUPPORTED. Non-finite
  * inputs: unspecified.
