@@ -120,15 +120,40 @@ def plan_describe(x_shape, w_shape, stride=1, dilation=1, padding=0, groups=1, f
     return buf.value.decode()
 
 
-def _check_tensor(t, name):
+def _check_meta(t, name):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be on the GPU (got {t.device}); there is no CPU path")
     if t.dtype != torch.float32:
         raise TypeError(f"{name} must be float32 (got {t.dtype})")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+
+
+def _check_tensor(t, name):
+    _check_meta(t, name)
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU (got {t.device}); there is no CPU path")
+
+
+def _check_operands(x, w, bias, out):
+    """Types, shapes and devices of a call's tensors, checked before anything is
+    launched. The kernels read bias[co] for every output channel co, and the C ABI
+    carries no bias length, so a bias of the wrong size is caught here; every
+    tensor must sit on x's device, where the library launches."""
+    _check_meta(x, "x")
+    _check_meta(w, "w")
+    if bias is not None:
+        _check_meta(bias, "bias")
+        if bias.dim() != 1 or bias.numel() != w.shape[0]:
+            raise ValueError(f"bias must be 1-D with C_out = {w.shape[0]} entries (got shape {tuple(bias.shape)})")
+    if out is not None:
+        _check_meta(out, "out")
+    for t, name in ((x, "x"), (w, "w"), (bias, "bias"), (out, "out")):
+        if t is not None and not t.is_cuda:
+            raise ValueError(f"{name} must be on the GPU (got {t.device}); there is no CPU path")
+    for t, name in ((w, "w"), (bias, "bias"), (out, "out")):
+        if t is not None and t.device != x.device:
+            raise ValueError(f"{name} is on {t.device} but x is on {x.device}: all operands must share one device")
 
 
 _raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
@@ -168,10 +193,7 @@ def _conv_args(x_shape, w_shape, stride, dilation, padding, drop_axis=None):
 
 def conv_fwd(x, w, bias=None, stride=1, dilation=1, padding=0, groups=1, out=None):
     """y = Conv{1,2,3}d(x, w, bias) with zero padding; x [N,C,L], [N,C,H,W] or [N,C,D,H,W] fp32 on the GPU."""
-    _check_tensor(x, "x")
-    _check_tensor(w, "w")
-    if bias is not None:
-        _check_tensor(bias, "bias")
+    _check_operands(x, w, bias, out)
     nd = x.dim() - 2
     if nd not in (1, 2, 3) or w.dim() != x.dim():
         raise ValueError("x and w must both be 3-D (Conv1d), 4-D (Conv2d) or 5-D (Conv3d)")
@@ -179,7 +201,6 @@ def conv_fwd(x, w, bias=None, stride=1, dilation=1, padding=0, groups=1, out=Non
     if out is None:
         out = torch.empty(shape, dtype=torch.float32, device=x.device)
     else:
-        _check_tensor(out, "out")
         if tuple(out.shape) != shape:
             raise ValueError(f"out has shape {tuple(out.shape)}, expected {shape}")
     rc = lib().conv_fwd(nd, x.data_ptr(), xs, w.data_ptr(), ws, bias.data_ptr() if bias is not None else None,
@@ -192,10 +213,7 @@ def conv_fwd(x, w, bias=None, stride=1, dilation=1, padding=0, groups=1, out=Non
 def conv_fwd_channels_last(x, w, bias=None, stride=1, dilation=1, padding=0, groups=1, out=None):
     """Channels-last convolution: x [N, L, C], [N, H, W, C] or [N, D, H, W, C] fp32 on the GPU
     (contiguous in that order), w [C_out, C_in/groups, k...]; returns y [N, out..., C_out]."""
-    _check_tensor(x, "x")
-    _check_tensor(w, "w")
-    if bias is not None:
-        _check_tensor(bias, "bias")
+    _check_operands(x, w, bias, out)
     nd = x.dim() - 2
     if nd not in (1, 2, 3) or w.dim() != x.dim():
         raise ValueError("x and w must both be 3-D, 4-D or 5-D")
@@ -206,7 +224,6 @@ def conv_fwd_channels_last(x, w, bias=None, stride=1, dilation=1, padding=0, gro
     if out is None:
         out = torch.empty(shape, dtype=torch.float32, device=x.device)
     else:
-        _check_tensor(out, "out")
         if tuple(out.shape) != shape:
             raise ValueError(f"out has shape {tuple(out.shape)}, expected {shape}")
     rc = lib().conv_fwd_channels_last(nd, x.data_ptr(), _i64(xs_cl), w.data_ptr(), ws,
@@ -219,10 +236,7 @@ def conv_fwd_channels_last(x, w, bias=None, stride=1, dilation=1, padding=0, gro
 
 def conv3d_min_softmax(x, w, bias=None, stride=1, dilation=1, padding=0, groups=1, min_dim=2, out=None):
     """softmax(min(Conv3d(x, w, bias), dim=min_dim), dim=1) without storing the conv result."""
-    _check_tensor(x, "x")
-    _check_tensor(w, "w")
-    if bias is not None:
-        _check_tensor(bias, "bias")
+    _check_operands(x, w, bias, out)
     if x.dim() != 5 or w.dim() != 5:
         raise ValueError("x and w must be 5-D")
     if min_dim not in (2, 3, 4):
@@ -232,7 +246,6 @@ def conv3d_min_softmax(x, w, bias=None, stride=1, dilation=1, padding=0, groups=
     if out is None:
         out = torch.empty(shape, dtype=torch.float32, device=x.device)
     else:
-        _check_tensor(out, "out")
         if tuple(out.shape) != shape:
             raise ValueError(f"out has shape {tuple(out.shape)}, expected {shape}")
     rc = lib().conv3d_min_softmax(x.data_ptr(), xs, w.data_ptr(), ws, bias.data_ptr() if bias is not None else None,

@@ -47,7 +47,12 @@ typedef enum {
 } conv_status;
 
 /*
- * Output length per spatial axis (the pages' formula, with floor division):
+ * Output length per spatial axis. The formula is the one page l1_p76 states in
+ * its turns 1 and 2 when sizing the Conv1d output (174758 for L = 524280, k = 3,
+ * stride 3, dilation 4); page l2_p24 turn 1 and page l1_p60's monologue apply it
+ * per axis to their Conv3d outputs. Division is floor division here (the
+ * pages' C code truncates toward zero, which gives one output, not zero, for a
+ * numerator of -1):
  *   out[i] = floor((in[i] + 2*padding[i] - dilation[i]*(k[i]-1) - 1) / stride[i]) + 1
  * nd in {1, 2, 3}. Writes out_spatial[0..nd-1] (which may be <= 0) and returns
  * CONV_OK, or CONV_ERR_EMPTY_OUTPUT if any entry is <= 0 (the entries are still
@@ -120,12 +125,22 @@ int conv3d_min_softmax(const float *x, const int64_t *x_shape,
                        const int *stride, const int *dilation, const int *padding, int groups,
                        int min_dim, float *y, convhip_stream_t stream);
 
-/* Static text for a status code (never NULL). */
+/*
+ * Static text for a status code (never NULL). The codes name the failure
+ * modes the pages run into (page l1_p76 turns 2-4: a launch the runtime
+ * rejected, output lengths off by one, indices near INT_MAX; page
+ * l2_p24 turn 3: a missing host binding) plus the argument checks of
+ * PyTorch's Conv modules that the pages' problem statements inherit.
+ */
 const char *conv_status_string(int status);
 
 /*
  * Describe the launch plan the library would use for these arguments (kernel
- * variant, tile, grid, LDS bytes) as one line of text into buf (NUL-terminated,
+ * variant, tile, grid, LDS bytes): the host-side choices that page l1_p60's
+ * monologue makes by hand (tile shape against shared-memory size and occupancy,
+ * compile-time specialisation of the kernel size with a generic fallback) and
+ * page l1_p76 turn 2 makes for the Conv1d (block of positions x channels, the
+ * input slice per block). One line of text into buf (NUL-terminated,
  * truncated to buflen). fused = 0 for conv_fwd, 1 for conv3d_min_softmax (then
  * nd must be 3), 2 for conv_fwd_channels_last (x_shape in its channels-last
  * order); other values give CONV_ERR_PARAM. Host only; launches nothing.

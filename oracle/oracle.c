@@ -25,6 +25,9 @@
  * Fused op (page l2_p24, opening turns): m = min over the chosen spatial axis of
  * the conv output (bias included before the min), then softmax over the channel
  * axis with the row maximum subtracted before exp (the page's softmax epilogue).
+ * Non-finite values follow the PyTorch modules the pages replace: a NaN in the
+ * conv output makes its minimum NaN (torch.min propagates it), and a NaN
+ * minimum makes its whole softmax row NaN.
  *
  * Parallelism: OpenMP over (n, co) output planes only; the arithmetic order
  * inside one output is the plain nested loop above.
@@ -167,10 +170,13 @@ int oracle_conv3d_min_softmax(const float *x, const int64_t *xs, const float *w,
                     else if (r == 1) { s0 = st[0]; s1 = st[2]; }
                     else { s0 = st[0]; s1 = st[1]; }
                     base = i0 * s0 + i1 * s1;
+                    /* A NaN anywhere along the axis makes the minimum NaN, as
+                       torch.min does (the module the page replaces). */
                     double v = cp[base];
                     for (int64_t j = 1; j < R; j++) {
                         double u = cp[base + j * st[r]];
-                        if (u < v) v = u;
+                        if (u < v || isnan(u)) v = u;
+                        if (isnan(v)) break;
                     }
                     m[(n * C + c) * rest + i0 * keep[1] + i1] = v;
                 }

@@ -154,3 +154,34 @@ def test_peak_probe_validates_before_launch():
     assert L.convhip_peak_probe(0, (1 << 22) + 1, FAKE, ctypes.byref(flop), None) == -5  # too long a launch
     assert L.convhip_peak_probe(0, 10, None, ctypes.byref(flop), None) == -1   # no sink
     assert L.convhip_peak_probe(1, 10, FAKE, None, None) == -1                 # no flop output
+
+
+def _cpu(*shape):
+    import torch
+    return torch.zeros(shape, dtype=torch.float32)
+
+
+@pytest.mark.parametrize("fn", ["conv_fwd", "conv_fwd_channels_last", "conv3d_min_softmax"])
+@pytest.mark.parametrize("bias_shape", [(7,), (9,), (8, 1), ()])
+def test_binding_rejects_bias_of_wrong_size_before_launch(fn, bias_shape):
+    """The kernels read one bias value per output channel; the C ABI carries no
+    bias length, so the binding rejects any bias that is not [C_out]."""
+    x, w = _cpu(2, 3, 6, 6, 6), _cpu(8, 3, 3, 3, 3)
+    with pytest.raises(ValueError, match="bias must be 1-D with C_out = 8"):
+        getattr(ch, fn)(x, w, _cpu(*bias_shape))
+
+
+@pytest.mark.parametrize("fn", ["conv_fwd", "conv_fwd_channels_last", "conv3d_min_softmax"])
+def test_binding_rejects_host_tensors_before_launch(fn):
+    x, w, b = _cpu(2, 3, 6, 6, 6), _cpu(8, 3, 3, 3, 3), _cpu(8)
+    with pytest.raises(ValueError, match="must be on the GPU"):
+        getattr(ch, fn)(x, w, b)
+
+
+def test_binding_rejects_wrong_dtype_and_layout():
+    import torch
+    x, w = _cpu(2, 3, 6, 6, 6), _cpu(8, 3, 3, 3, 3)
+    with pytest.raises(TypeError, match="bias must be float32"):
+        ch.conv_fwd(x, w, torch.zeros(8, dtype=torch.float64))
+    with pytest.raises(ValueError, match="w must be contiguous"):
+        ch.conv_fwd(x, _cpu(8, 3, 3, 3, 6)[..., ::2])

@@ -341,3 +341,21 @@ def test_integer_inputs_give_exact_integer_outputs():
     y = oracle.conv(x, w, b)
     assert np.all(y == np.round(y))
     assert np.abs(y).max() < 2 ** 24
+
+
+def test_fused_nan_propagates_like_torch_min():
+    """A NaN in the input reaches every conv output whose window covers it; the
+    minimum along the axis is then NaN (torch.min propagates NaN) and so is the
+    whole softmax row. The oracle must agree with torch's composition on where
+    the NaNs are and match it elsewhere."""
+    r = _rng(34)
+    x, w, b = _fused_case(r, N=2, C_in=2, C_out=5, D=6, H=7, W=8, k=(3, 3, 3))
+    x[1, 0, 4, 2, 3] = np.nan
+    for min_dim in (2, 3, 4):
+        yo = oracle.conv3d_min_softmax(x, w, b, 1, 1, 0, 1, min_dim)
+        t = F.conv3d(torch.from_numpy(x).double(), torch.from_numpy(w).double(), torch.from_numpy(b).double())
+        t = torch.softmax(torch.min(t, dim=min_dim)[0], dim=1).numpy()
+        assert np.isnan(t).any() and not np.isnan(t).all()
+        np.testing.assert_array_equal(np.isnan(yo), np.isnan(t))
+        ok = ~np.isnan(t)
+        np.testing.assert_allclose(yo[ok], t[ok], rtol=1e-12, atol=1e-15)
