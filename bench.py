@@ -3,21 +3,32 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAME] [--no-cpu]
 
 One "step" is one call of the library's entry point over one batch of the
-headline workload, the general-parameter Conv3d (x[4,16,32,32,32], w[32,8,3,5,7],
-groups 2, stride (1,2,2), padding (1,2,3), dilation (1,1,2)). The same run also
-times every other workload (tiny Conv3d, fused Conv3d+min+softmax, asymmetric
-Conv3d, long Conv1d, and the four plain convolutions again on channels-last tensors through
-conv_fwd_channels_last, "<workload>_channels_last") and reports them under
-"shapes". Inputs are seeded
-synthetic tensors already resident in device memory; each workload is first run
-back to back for at least 0.5 s (the GPU's clocks ramp up from idle over
-that time), then the timed region is K back-to-back calls between two device
-synchronisations, timed with events on the stream the kernels are launched on.
+headline workload, the long strided and dilated Conv1d (x[64,64,524280],
+w[128,64,3], stride 3, dilation 4), the largest configuration. The same run
+also times every other workload and reports it under "shapes":
 
-Prints one JSON line. Throughput = 2 * MACs / time (MACs count every kernel
-tap, padded ones included). Each workload also reports the median of single
-launches after a 512 MiB write that evicts L2 and the MALL (ms_cold_median). Roofline fractions use MI355X's published peaks:
-fp32 matrix 157.3 TFLOP/s, HBM 8.0 TB/s.
+* the tiny, general and asymmetric Conv3d and the fused Conv3d+min+softmax;
+* the four plain convolutions again on channels-last tensors through
+  conv_fwd_channels_last ("<workload>_channels_last");
+* the five workloads on the generic kernels, with the build-time
+  specialisations switched off ("<workload>_generic", CONVHIP_TAP=0);
+* neighbouring shapes that no specialisation was built for, and the fused op
+  with the minimum over H or W and with groups (synth.VARIANTS).
+
+Inputs are seeded synthetic tensors already resident in device memory; each
+entry is first run back to back for at least 0.5 s (the GPU's clocks ramp up
+from idle over that time), then the timed region is K back-to-back calls
+between two device synchronisations, timed with events on the stream the
+kernels are launched on. Each entry also reports the median of single launches
+after a 512 MiB write that evicts L2 and the MALL (ms_cold_median).
+
+Prints one JSON line. Throughput = 2 * MACs / time, with MACs = outputs x
+(C_in/groups) x kernel volume (every tap, padded ones included). Each entry
+carries a roofline object against MI355X's published fp32 matrix peak
+(157.3 TFLOP/s) and, where a counter summary of the current sources exists,
+the HBM bytes one launch moves. The CPU baseline is the fp64 oracle on the
+headline's batch slice n in {0, 63}, timed on the host cores; the headline's
+parity is checked on the same slice.
 """
 import argparse
 import hashlib
@@ -35,11 +46,16 @@ sys.path.insert(0, ROOT)
 PEAK_FP32_TFLOPS = 157.3
 WARM_S = 0.5  # default seconds of warm-up calls per workload (--warm-seconds)
 PEAK_HBM_GBS = 8000.0
-HEADLINE = "general_conv3d"
+HEADLINE = "long_conv1d"
+HEADLINE_SLICE = (0, 63)  # batch samples the oracle computes for the CPU baseline and parity
 CL_SUFFIX = "_channels_last"
-ORDER = ["tiny_conv3d", "general_conv3d", "conv3d_min_softmax", "asym_conv3d", "long_conv1d",
-         "tiny_conv3d" + CL_SUFFIX, "general_conv3d" + CL_SUFFIX, "asym_conv3d" + CL_SUFFIX,
-         "long_conv1d" + CL_SUFFIX]
+GEN_SUFFIX = "_generic"
+WORKLOAD_NAMES = ["tiny_conv3d", "general_conv3d", "conv3d_min_softmax", "asym_conv3d", "long_conv1d"]
+ORDER = (WORKLOAD_NAMES
+         + [n + CL_SUFFIX for n in ("tiny_conv3d", "general_conv3d", "asym_conv3d", "long_conv1d")]
+         + [n + GEN_SUFFIX for n in WORKLOAD_NAMES]
+         + ["asym_conv3d_48", "general_conv3d_24", "long_conv1d_c96_d2", "conv3d_min_softmax_min_h",
+            "conv3d_min_softmax_min_w", "conv3d_min_softmax_groups3"])
 KERNEL_SOURCES = [os.path.join(ROOT, "implicit_gemm_convolution_direct_amd", "csrc", f)
                   for f in ("conv_kernels.hip", "convhip_plan.cpp", "convhip_plan.h")]
 
@@ -53,7 +69,9 @@ def kernel_source_hash():
 
 
 def geometry(cfg):
-    """Output shape, MACs and algorithmic bytes (x, w, bias read once, y written once)."""
+    """Output shape, MACs and algorithmic bytes (x, w, bias read once, y written once).
+    MACs count (C_in/groups) x kernel volume per conv output: a grouped conv does
+    no products across groups."""
     xs, ws = cfg["x"], cfg["w"]
     nd = cfg["nd"]
     out = []
@@ -64,7 +82,8 @@ def geometry(cfg):
     conv_elems = xs[0] * ws[0] * int(np.prod(out))
     macs = conv_elems * kred
     if cfg["fused"]:
-        y_elems = xs[0] * ws[0] * int(np.prod(out[1:]))
+        md = cfg.get("min_dim", 2)
+        y_elems = xs[0] * ws[0] * int(np.prod([o for a, o in enumerate(out) if a != md - 2]))
     else:
         y_elems = conv_elems
     nbytes = 4 * (int(np.prod(xs)) + int(np.prod(ws)) + (ws[0] if cfg["bias"] else 0) + y_elems)
@@ -92,15 +111,28 @@ def read_traffic(name):
 
 
 def split_name(name):
-    """(workload, channels_last): a "<workload>_channels_last" entry times the same
-    workload with x [N, spatial..., C_in] and y [N, out..., C_out]."""
+    """(workload, channels_last, generic): a "<workload>_channels_last" entry times
+    the same workload with x [N, spatial..., C_in] and y [N, out..., C_out]; a
+    "<workload>_generic" entry times it with the build-time specialisations off."""
     if name.endswith(CL_SUFFIX):
-        return name[:-len(CL_SUFFIX)], True
-    return name, False
+        return name[:-len(CL_SUFFIX)], True, False
+    if name.endswith(GEN_SUFFIX):
+        return name[:-len(GEN_SUFFIX)], False, True
+    return name, False, False
+
+
+def roofline(tflops, name, latency_bound=False):
+    """The roofline object of one entry: every workload here contracts on the
+    fp32 matrix cores (tiny Conv3d: launch latency binds before either peak)."""
+    rec = {"bound": "mfma", "achieved": tflops, "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
+           "frac": round(tflops / PEAK_FP32_TFLOPS, 4), "traffic": read_traffic(name)}
+    if latency_bound:
+        rec["limited_by"] = "launch latency"
+    return rec
 
 
 def make_device_inputs(name, torch, ch, synth, channels_last=False):
-    cfg = synth.WORKLOADS[name]
+    cfg = synth.config(name)
     dev = torch.device("cuda:0")
     sx, sw, sb = cfg["seeds"]
     xs = cfg["x"]
@@ -119,16 +151,32 @@ def make_device_inputs(name, torch, ch, synth, channels_last=False):
 
 
 def time_workload(name, steps, warmup, torch, ch, synth, flush=None, warm_s=WARM_S):
-    base, cl = split_name(name)
+    base, cl, generic = split_name(name)
+    saved_tap = os.environ.get("CONVHIP_TAP")
+    if generic:
+        os.environ["CONVHIP_TAP"] = "0"  # read by the library at every call
+    try:
+        return _time_workload(name, base, cl, steps, warmup, torch, ch, synth, flush, warm_s)
+    finally:
+        if generic:
+            if saved_tap is None:
+                del os.environ["CONVHIP_TAP"]
+            else:
+                os.environ["CONVHIP_TAP"] = saved_tap
+
+
+def _time_workload(name, base, cl, steps, warmup, torch, ch, synth, flush, warm_s):
     cfg, x, w, b = make_device_inputs(base, torch, ch, synth, channels_last=cl)
     out, macs, nbytes, conv_elems, y_elems = geometry(cfg)
     args = (cfg["stride"], cfg["dilation"], cfg["padding"], cfg["groups"])
+    md = cfg.get("min_dim", 2)
     if cl:
         y = torch.empty((cfg["x"][0], *out, cfg["w"][0]), dtype=torch.float32, device=x.device)
         call = lambda: ch.conv_fwd_channels_last(x, w, b, *args, out=y)
     elif cfg["fused"]:
-        y = torch.empty((cfg["x"][0], cfg["w"][0], *out[1:]), dtype=torch.float32, device=x.device)
-        call = lambda: ch.conv3d_min_softmax(x, w, b, *args, min_dim=2, out=y)
+        keep = [o for a, o in enumerate(out) if a != md - 2]
+        y = torch.empty((cfg["x"][0], cfg["w"][0], *keep), dtype=torch.float32, device=x.device)
+        call = lambda: ch.conv3d_min_softmax(x, w, b, *args, min_dim=md, out=y)
     else:
         y = torch.empty((cfg["x"][0], cfg["w"][0], *out), dtype=torch.float32, device=x.device)
         call = lambda: ch.conv_fwd(x, w, b, *args, out=y)
@@ -175,9 +223,10 @@ def time_workload(name, steps, warmup, torch, ch, synth, flush=None, warm_s=WARM
             colds.append(a.elapsed_time(z))
     tflops = 2.0 * macs / (ms * 1e-3) / 1e12
     gbs = nbytes / (ms * 1e-3) / 1e9
+    plan = ch.plan_describe(tuple(x.shape), cfg["w"], *args, fused=cfg["fused"], channels_last=cl, min_dim=md)
     rec = {
         "workload": name,
-        "plan": ch.plan_describe(tuple(x.shape), cfg["w"], *args, fused=cfg["fused"], channels_last=cl),
+        "plan": plan,
         "ms": round(ms, 5),
         "ms_single_min": round(min(singles), 5),
         "ms_single_max": round(max(singles), 5),
@@ -189,6 +238,7 @@ def time_workload(name, steps, warmup, torch, ch, synth, flush=None, warm_s=WARM
         "macs": macs,
         "alg_bytes": nbytes,
         "wall_s": round(wall, 3),
+        "roofline": roofline(round(tflops, 3), name, latency_bound=base == "tiny_conv3d"),
     }
     if cfg["fused"] and not cl:
         # Unfused chain: conv writes the 5-D result, min reads it and writes its
@@ -242,26 +292,53 @@ def calibrate(torch, ch, seconds=0.05):
     return out
 
 
-def cpu_baseline(name):
-    """The fp64 oracle on the full headline workload, timed on the host cores."""
-    import oracle
+def headline_slice_inputs(name, samples):
+    """Host copies of the given batch samples of a workload's input (the same
+    seeded stream the device generator fills), and its weights and bias."""
     import synth
     cfg = synth.WORKLOADS[name]
-    x, w, b = synth.make_inputs(name)
-    _, macs, _, _, _ = geometry(cfg)
+    sx = cfg["seeds"][0]
+    per = int(np.prod(cfg["x"][1:]))
+    x = np.concatenate([synth.uniform01(sx, (1, *cfg["x"][1:]), start=n * per) for n in samples])
+    _, w, b = synth.make_inputs(name, n_samples=1)
+    return cfg, x, w, b
+
+
+def cpu_baseline(name, samples, seconds=10.0):
+    """The fp64 oracle on a batch slice of the headline workload, timed on the
+    host cores for about `seconds`; returns the record and the slice's result."""
+    import oracle
+    cfg, x, w, b = headline_slice_inputs(name, samples)
+    _, macs_full, _, _, _ = geometry(cfg)
+    macs = macs_full // cfg["x"][0] * len(samples)
     args = (cfg["stride"], cfg["dilation"], cfg["padding"], cfg["groups"])
-    oracle.conv(x[:1], w, b, *args)  # load the library, warm the threads
-    # Repeat the whole-workload pass for about 10 s of CPU work.
-    reps, t = 0, 0.0
+    oracle.conv(x[:1, :, :64], w, b, *args)  # load the library, start the threads
+    reps = 0
     t0 = time.perf_counter()
-    while reps < 1 or time.perf_counter() - t0 < 10.0:
+    while reps < 1 or time.perf_counter() - t0 < seconds:
         ref = oracle.conv(x, w, b, *args)
         reps += 1
     t = (time.perf_counter() - t0) / reps
     return {"value": round(2.0 * macs / t / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
             "kind": "oracle",
-            "sample": f"full {name} workload (batch {cfg['x'][0]}), fp64 nested loops, {reps} pass(es), "
-                      f"{t:.3f} s per pass"}, ref
+            "sample": f"{name} batch samples n in {list(samples)} of {cfg['x'][0]} (full length), "
+                      f"{macs} MAC per pass, fp64 nested loops, {reps} pass(es), {t:.3f} s per pass; "
+                      f"full workload extrapolated: {t * cfg['x'][0] / len(samples):.1f} s"}, x, ref
+
+
+def headline_parity(name, samples, ref, torch, ch, synth):
+    """The headline call at full size (input generated on the device) against
+    the oracle's result on the batch slice."""
+    cfg, x, w, b = make_device_inputs(name, torch, ch, synth)
+    y = ch.conv_fwd(x, w, b, cfg["stride"], cfg["dilation"], cfg["padding"], cfg["groups"])
+    torch.cuda.synchronize()
+    err = 0.0
+    for i, n in enumerate(samples):
+        err = max(err, float(np.abs(y[n].cpu().numpy().astype(np.float64) - ref[i]).max()))
+    tol = 1e-4 * math.sqrt(int(np.prod(cfg["w"][1:]))) * float(np.abs(ref).max())
+    del x, w, b, y
+    torch.cuda.empty_cache()
+    return {"max_abs_err": err, "tol": tol, "pass": err <= tol, "compared": f"batch samples {list(samples)}"}
 
 
 def cpu_baselines_per_workload(shapes, seconds=1.0):
@@ -387,14 +464,11 @@ def main():
     parity = None
     if not args.no_cpu and not args.only:
         print("[bench] oracle CPU baseline", file=sys.stderr, flush=True)
-        cpu, ref = cpu_baseline(HEADLINE)
+        cpu, _, ref = cpu_baseline(HEADLINE, HEADLINE_SLICE)
         # Parity of the headline launch against the oracle on the same seeded inputs.
-        cfg, x, w, b = make_device_inputs(HEADLINE, torch, ch, synth)
-        y = ch.conv_fwd(x, w, b, cfg["stride"], cfg["dilation"], cfg["padding"], cfg["groups"])
-        torch.cuda.synchronize()
-        err = float(np.abs(y.cpu().numpy().astype(np.float64) - ref).max())
-        tol = 1e-4 * math.sqrt(int(np.prod(cfg["w"][1:]))) * float(np.abs(ref).max())
-        parity = {"max_abs_err": err, "tol": tol, "pass": err <= tol}
+        print("[bench] headline parity", file=sys.stderr, flush=True)
+        parity = headline_parity(HEADLINE, HEADLINE_SLICE, ref, torch, ch, synth)
+        del ref
         print("[bench] oracle CPU rate per workload (one sample each)", file=sys.stderr, flush=True)
         cpu_all = cpu_baselines_per_workload(shapes)
 
@@ -408,8 +482,7 @@ def main():
             rec["frac_achievable_mfma"] = round(rec["tflops"] / achievable["mfma_f32_tflops"], 4)
             rec["frac_achievable_hbm"] = round(rec["gbs"] / achievable["hbm_copy_gbs"], 4)
 
-    cfgh = synth.WORKLOADS[split_name(head_name)[0]]
-    traffic = read_traffic(head_name)
+    cfgh = synth.config(split_name(head_name)[0])
     achieved = head["tflops"]
     line = {
         "metric": "conv fwd TFLOP/s (fp32) and % of MI355X FP32/HBM roofline per shape",
@@ -419,6 +492,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": head["ms"],
+        "ms_per_step_cold": head["ms_cold_median"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -427,8 +501,7 @@ def main():
         "config": {"workload": head_name, "x": list(cfgh["x"]), "w": list(cfgh["w"]),
                    "stride": list(cfgh["stride"]), "padding": list(cfgh["padding"]),
                    "dilation": list(cfgh["dilation"]), "groups": cfgh["groups"], "bias": cfgh["bias"]},
-        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_FP32_TFLOPS, 4), "traffic": traffic},
+        "roofline": head["roofline"],
         "cpu_baseline": cpu,
         "cpu_baseline_per_workload": cpu_all,
         "achievable": achievable,

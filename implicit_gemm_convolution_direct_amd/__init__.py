@@ -107,11 +107,13 @@ def out_shape(in_spatial, k_spatial, stride, dilation, padding):
     return rc, [int(v) for v in out]
 
 
-def plan_describe(x_shape, w_shape, stride=1, dilation=1, padding=0, groups=1, fused=False, channels_last=False):
-    """The library's launch plan; channels_last=True takes x_shape as [N, spatial..., C_in]."""
+def plan_describe(x_shape, w_shape, stride=1, dilation=1, padding=0, groups=1, fused=False, channels_last=False,
+                  min_dim=2):
+    """The library's launch plan; channels_last=True takes x_shape as [N, spatial..., C_in];
+    fused=True describes conv3d_min_softmax with that min_dim."""
     nd = len(x_shape) - 2
     buf = ctypes.create_string_buffer(1024)
-    mode = 2 if channels_last else (1 if fused else 0)
+    mode = 2 if channels_last else ((1 if min_dim == 2 else int(min_dim)) if fused else 0)
     rc = lib().conv_plan_describe(nd, _i64(x_shape), _i64(w_shape), _i32(_vec(stride, nd, "stride")),
                                   _i32(_vec(dilation, nd, "dilation")), _i32(_vec(padding, nd, "padding")),
                                   int(groups), mode, buf, 1024)

@@ -77,6 +77,7 @@ struct ConvArgs {
   int ccp;        // channels-last box: LDS floats per (plane, row, column) site
   int cl_vec;     // channels-last box copied in 16-byte channel quads (ccp, Cc, C_in/groups multiples of 4)
   int vec_store;  // channels-last output: 4 consecutive channels stored as one 16-byte write
+  int spin_cap;   // conv_tap_split_pipe: polls of the batch-1 counter before a wave gives up
 };
 
 // q = n / d and r = n % d for 0 <= n < 2^24, d >= 1, from a float reciprocal
@@ -1313,10 +1314,11 @@ __global__ __launch_bounds__(64 * NW) void conv_tap_split_pipe_kernel(ConvArgs a
   int Cin = a.Cin, Cout = a.Cout, Cg = a.Cg, Coutg = a.Coutg;
   int L0 = a.L0, L1 = a.L1, L2 = a.L2, S0 = a.S0, S1 = a.S1, S2 = a.S2, D0 = a.D0;
   int P0 = a.P0, P1 = a.P1, P2 = a.P2, O0 = a.O0, O1 = a.O1, O2 = a.O2, plane_out = a.plane_out;
+  int spin_cap = a.spin_cap;
   int gx = gridDim.x, gy = gridDim.y;
   asm volatile("" : "+s"(xg), "+s"(wgl), "+s"(bg), "+s"(yglob), "+s"(Cin), "+s"(Cout), "+s"(Cg), "+s"(Coutg),
                "+s"(L0), "+s"(L1), "+s"(L2), "+s"(S0), "+s"(S1), "+s"(S2), "+s"(D0), "+s"(P0), "+s"(P1), "+s"(P2),
-               "+s"(O0), "+s"(O1), "+s"(O2), "+s"(plane_out), "+s"(gx), "+s"(gy));
+               "+s"(O0), "+s"(O1), "+s"(O2), "+s"(plane_out), "+s"(spin_cap), "+s"(gx), "+s"(gy));
   // XCD-aware item order, as in conv_tap_split.
   int item = blockIdx.x + gx * blockIdx.y;
   const int items = gx * gy;
@@ -1536,8 +1538,10 @@ __global__ __launch_bounds__(64 * NW) void conv_tap_split_pipe_kernel(ConvArgs a
     if (lane == 0) __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   }
   // Batch 2. Late in it, wave w < NT1 waits until every wave has parked batch 1
-  // (each does so unconditionally after its own batch-1 products; the wait is
-  // also capped), then sums batch-1 tile w and stores it.
+  // (each does so unconditionally after its own batch-1 products), then sums
+  // batch-1 tile w and stores it. The wait is capped at spin_cap polls; a wave
+  // that gives up stores NaN for its whole tile instead of a sum over tiles that
+  // may not have been parked, so the event cannot pass unnoticed.
   constexpr int S_WAIT = NS > 8 ? NS - 7 : NS - 1;
   {
     v4f acc[NT2];
@@ -1545,19 +1549,26 @@ __global__ __launch_bounds__(64 * NW) void conv_tap_split_pipe_kernel(ConvArgs a
     for (int ni = 0; ni < NT2; ni++) acc[ni] = v4f{0.f, 0.f, 0.f, 0.f};
     v4f part[NW];
     const bool sums1 = wave < NT1;
+    bool parked = false;
     products(std::integral_constant<int, NT1>{}, std::integral_constant<int, NT2>{}, acc, [&](auto sc) {
       constexpr int s = decltype(sc)::value;
       if constexpr (s == S_WAIT) {
         if (sums1) {
-          for (int spin = 0; spin < (1 << 22); spin++) {
-            if (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= unsigned(NW)) break;
+          for (int spin = 0; spin < spin_cap; spin++) {
+            if (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= unsigned(NW)) {
+              parked = true;
+              break;
+            }
             __builtin_amdgcn_s_sleep(1);
           }
           asm volatile("" ::: "memory");
           read_parked(smem, L::WREG, wave, part);
         }
       } else if constexpr (s == (S_WAIT + 3 < NS ? S_WAIT + 3 : NS - 1)) {
-        if (sums1) store_tile(wave, sum_parts(part));
+        if (sums1) {
+          const float nan = __builtin_nanf("");
+          store_tile(wave, parked ? sum_parts(part) : v4f{nan, nan, nan, nan});
+        }
       }
     });
     // The box is no longer read by this wave: park batch 2 in it.
@@ -2196,6 +2207,17 @@ static int launch_tap_cl_spec(const ConvArgs& args, const ConvPlan& p, hipStream
   }
 }
 
+// Polls of the batch-1 counter before a wave of conv_tap_split_pipe gives up
+// (and stores NaN for its tile): 2^22 (seconds; the waves of a workgroup are
+// co-resident, so it is never reached), or CONVHIP_SPIN_CAP for tests that
+// force the give-up path from the host.
+static int split_spin_cap() {
+  const char* s = std::getenv("CONVHIP_SPIN_CAP");
+  if (!s || !*s) return 1 << 22;
+  const long v = std::atol(s);
+  return v < 0 ? 0 : (v > (1 << 22) ? (1 << 22) : int(v));
+}
+
 // CONVHIP_SPLIT_PIPE=0 keeps the channel-split specialisations on the kernel
 // whose cross-wave sum follows all products (tests run both kernels).
 static bool split_pipe_enabled() {
@@ -2310,6 +2332,7 @@ static ConvArgs conv_args(const Geom& g, const ConvPlan& p, const float* x, cons
   a.ccp = p.ccp;
   a.cl_vec = p.cl_vec ? 1 : 0;
   a.vec_store = 0;
+  a.spin_cap = split_spin_cap();
   return a;
 }
 
@@ -2345,6 +2368,26 @@ static int device_num_cu() {
     cache[dev] = n;
   }
   return cache[dev];
+}
+
+// The fused kernels take the minimum over their axis 0. For a minimum over H or
+// W the spatial axes are permuted (conv commutes with a permutation of the
+// spatial axes applied to x, w, stride, dilation and padding alike); the two
+// remaining axes keep their order, so the output [N, C_out, rest...] is
+// contiguous in the permuted order too. perm[i] = original axis of kernel axis i.
+static const int kFusedPerm[3][3] = {{0, 1, 2}, {1, 0, 2}, {2, 0, 1}};
+static Geom fused_geom(const Geom& g0, int min_dim) {
+  const int* perm = kFusedPerm[min_dim - 2];
+  Geom g = g0;
+  for (int i = 0; i < 3; i++) {
+    g.L[i] = g0.L[perm[i]];
+    g.K[i] = g0.K[perm[i]];
+    g.S[i] = g0.S[perm[i]];
+    g.Dl[i] = g0.Dl[perm[i]];
+    g.P[i] = g0.P[perm[i]];
+    g.O[i] = g0.O[perm[i]];
+  }
+  return g;
 }
 
 extern "C" {
@@ -2384,17 +2427,19 @@ int conv_plan_describe(int nd, const int64_t* x_shape, const int64_t* w_shape, c
                        const int* dilation, const int* padding, int groups, int fused, char* buf, int buflen) {
   if (!buf || buflen < 1) return CONV_ERR_NULL;
   buf[0] = 0;
-  if (fused < 0 || fused > 2) return CONV_ERR_PARAM;
+  if (fused < 0 || fused > 4) return CONV_ERR_PARAM;
   Geom g;
   int rc = fused == 2 ? make_geom_channels_last(nd, x_shape, w_shape, stride, dilation, padding, groups, &g)
                       : make_geom(nd, x_shape, w_shape, stride, dilation, padding, groups, &g);
   if (rc != CONV_OK) return rc;
   std::string s;
-  if (fused == 1) {
+  if (fused == 1 || fused >= 3) {
+    if (nd != 3) return CONV_ERR_RANK;
+    const int min_dim = fused == 1 ? 2 : fused;
     FusedPlan p;
-    rc = plan_fused(g, 2, &p, use_tap() != 0);
+    rc = plan_fused(fused_geom(g, min_dim), min_dim, &p, use_tap() != 0 && min_dim == 2);
     if (rc != CONV_OK) return rc;
-    s = describe(g, p);
+    s = describe(fused_geom(g, min_dim), p);
   } else {
     ConvPlan p;
     rc = plan_conv(g, &p, forced_conv_cfg(), 256, use_tap(), split_pipe_enabled());
@@ -2455,22 +2500,9 @@ int conv3d_min_softmax(const float* x, const int64_t* x_shape, const float* w, c
   if (rc != CONV_OK) return rc;
   if (!x || !w || !y) return CONV_ERR_NULL;
   if (min_dim < 2 || min_dim > 4) return CONV_ERR_PARAM;
-  // The kernels take the minimum over their axis 0. For a minimum over H or W the
-  // spatial axes are permuted (conv commutes with a permutation of the spatial
-  // axes applied to x, w, stride, dilation and padding alike); the remaining two
-  // axes keep their order, so the output [N, C_out, rest...] is contiguous in the
-  // permuted order too.
-  static const int kPerm[3][3] = {{0, 1, 2}, {1, 0, 2}, {2, 0, 1}};
-  const int* perm = kPerm[min_dim - 2];
+  const int* perm = kFusedPerm[min_dim - 2];
   const Geom g0 = g;
-  for (int i = 0; i < 3; i++) {
-    g.L[i] = g0.L[perm[i]];
-    g.K[i] = g0.K[perm[i]];
-    g.S[i] = g0.S[perm[i]];
-    g.Dl[i] = g0.Dl[perm[i]];
-    g.P[i] = g0.P[perm[i]];
-    g.O[i] = g0.O[perm[i]];
-  }
+  g = fused_geom(g0, min_dim);
   const int64_t xst[3] = {g0.L[1] * g0.L[2], g0.L[2], 1};
   const int64_t wst[3] = {g0.K[1] * g0.K[2], g0.K[2], 1};
   FusedPlan p;

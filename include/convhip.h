@@ -141,9 +141,11 @@ const char *conv_status_string(int status);
  * compile-time specialisation of the kernel size with a generic fallback) and
  * page l1_p76 turn 2 makes for the Conv1d (block of positions x channels, the
  * input slice per block). One line of text into buf (NUL-terminated,
- * truncated to buflen). fused = 0 for conv_fwd, 1 for conv3d_min_softmax (then
- * nd must be 3), 2 for conv_fwd_channels_last (x_shape in its channels-last
- * order); other values give CONV_ERR_PARAM. Host only; launches nothing.
+ * truncated to buflen). fused = 0 for conv_fwd, 1 for conv3d_min_softmax with
+ * min_dim 2, 3 or 4 for conv3d_min_softmax with that min_dim (then nd must be
+ * 3, else CONV_ERR_RANK), 2 for conv_fwd_channels_last (x_shape in its
+ * channels-last order); other values give CONV_ERR_PARAM. Host only; launches
+ * nothing.
  * Returns a conv_status.
  */
 int conv_plan_describe(int nd, const int64_t *x_shape, const int64_t *w_shape,

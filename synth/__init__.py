@@ -121,6 +121,26 @@ WORKLOADS = {
 }
 
 
+# Shapes measured beside the five workloads: neighbours of three of them that
+# are not among the build-time specialised geometries (a smaller asymmetric
+# Conv3d input, a smaller general Conv3d input, the long Conv1d with 96 output
+# channels and dilation 2), and the fused op with the minimum over H or W and
+# with groups. Same distributions; each reuses its base workload's seeds.
+VARIANTS = {
+    "asym_conv3d_48": dict(WORKLOADS["asym_conv3d"], x=(16, 3, 48, 48, 48)),
+    "general_conv3d_24": dict(WORKLOADS["general_conv3d"], x=(4, 16, 24, 24, 24)),
+    "long_conv1d_c96_d2": dict(WORKLOADS["long_conv1d"], w=(96, 64, 3), dilation=(2,)),
+    "conv3d_min_softmax_min_h": dict(WORKLOADS["conv3d_min_softmax"], min_dim=3),
+    "conv3d_min_softmax_min_w": dict(WORKLOADS["conv3d_min_softmax"], min_dim=4),
+    "conv3d_min_softmax_groups3": dict(WORKLOADS["conv3d_min_softmax"], w=(24, 1, 3, 3, 3), groups=3),
+}
+
+
+def config(name):
+    """A workload or a variant by name."""
+    return WORKLOADS[name] if name in WORKLOADS else VARIANTS[name]
+
+
 def fan_in(w_shape):
     return int(np.prod(w_shape[1:]))
 
@@ -131,7 +151,7 @@ def make_inputs(name, n_samples=None, sample_start=0, integer=False):
     ``integer`` switches to the exact-arithmetic distribution: x in {0..3},
     w in {-2..2}, bias in {-4..4}.
     """
-    cfg = WORKLOADS[name]
+    cfg = config(name)
     xs = list(cfg["x"])
     per_sample = int(np.prod(xs[1:]))
     if n_samples is None:

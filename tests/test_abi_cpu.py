@@ -87,7 +87,22 @@ def test_conv_fwd_channels_last_validation_errors():
     assert f(s=I32(1, 0, 1)) == -5
     assert f(nd=1, xs=(1, 8, 4), ws=(4, 4, 9)) == -6
     buf = ctypes.create_string_buffer(256)
-    assert lib.conv_plan_describe(3, I64(1, 8, 8, 8, 4), I64(4, 4, 3, 3, 3), one, one, zero, 1, 3, buf, 256) == -5
+    assert lib.conv_plan_describe(3, I64(1, 8, 8, 8, 4), I64(4, 4, 3, 3, 3), one, one, zero, 1, 5, buf, 256) == -5
+    assert lib.conv_plan_describe(3, I64(1, 8, 8, 8, 4), I64(4, 4, 3, 3, 3), one, one, zero, 1, -1, buf, 256) == -5
+
+
+def test_fused_plan_per_min_axis():
+    """conv_plan_describe's fused modes: min over depth takes the depth-streamed
+    specialisation at the fused workload's geometry; min over H or W the generic
+    fused kernel on the permuted axes (whose box then spans the min axis)."""
+    xs, ws = (128, 3, 24, 32, 32), (24, 3, 3, 3, 3)
+    assert "kernel=fused_stream" in ch.plan_describe(xs, ws, fused=True, min_dim=2)
+    for md in (3, 4):
+        d = ch.plan_describe(xs, ws, fused=True, min_dim=md)
+        assert "kernel=fused_min_softmax_mfma4" in d, d
+    one, zero = I32(1, 1, 1), I32(0, 0, 0)
+    buf = ctypes.create_string_buffer(256)
+    assert ch.lib().conv_plan_describe(1, I64(1, 8, 40), I64(4, 8, 3), one, one, zero, 1, 3, buf, 256) == -2
 
 
 def test_channels_last_plans():

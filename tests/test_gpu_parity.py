@@ -529,3 +529,27 @@ def test_peak_probes_run_and_count_their_work():
     assert ch.peak_probe(ch.PROBE_FMA_F32, 3, sink) == waves * 64 * 3 * 8 * 2
     torch.cuda.synchronize()
     assert float(sink.cpu()[0]) == 0.0  # the guard store never fires
+
+
+def test_split_pipe_wait_give_up_stores_nan(monkeypatch):
+    """The pipelined channel-split kernel caps its wait for the other waves'
+    batch-1 tiles. A wave that gives up stores NaN for its whole tile, never a
+    sum over tiles that may not be parked yet. The cap is forced to zero from
+    the host (every kernel still exits normally): each plane's batch-1 tiles
+    (positions 0..111 of 208) are NaN, the rest exact; with the default cap the
+    output is exact everywhere."""
+    name = "general_conv3d"
+    cfg = synth.WORKLOADS[name]
+    monkeypatch.setenv("CONVHIP_SPLIT_KERNEL", "pipe")
+    desc = ch.plan_describe(cfg["x"], cfg["w"], *_cfg_args(cfg))
+    assert "pipe=1" in desc, desc
+    x, w, b = synth.make_inputs(name, integer=True, n_samples=1)
+    ref = oracle.conv(x, w, b, *_cfg_args(cfg))
+    monkeypatch.setenv("CONVHIP_SPIN_CAP", "0")
+    y = gpu_conv(x, w, b, *_cfg_args(cfg)).reshape(ref.shape[0], ref.shape[1], ref.shape[2], -1)
+    r = ref.reshape(y.shape)
+    assert np.isnan(y[..., :112]).all()
+    np.testing.assert_array_equal(y[..., 112:].astype(np.float64), r[..., 112:])
+    monkeypatch.delenv("CONVHIP_SPIN_CAP")
+    y = gpu_conv(x, w, b, *_cfg_args(cfg))
+    np.testing.assert_array_equal(y.astype(np.float64), ref)
