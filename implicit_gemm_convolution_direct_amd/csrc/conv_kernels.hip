@@ -42,6 +42,7 @@
 namespace convhip {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) const float GlobalF;  // a float in global memory
 typedef float v16f __attribute__((ext_vector_type(16)));
 
 // f(integral_constant<int, 0>) ... f(integral_constant<int, N-1>): loops whose
@@ -1584,6 +1585,460 @@ __global__ __launch_bounds__(64 * NW) void conv_tap_split_pipe_kernel(ConvArgs a
 }
 
 // ---------------------------------------------------------------------------
+// conv_tap_kstream: one workgroup per (n, od) output plane and group, for few
+// output channels per group (<= 16) and planes of at most 16 tiles of 16
+// positions. Four compute waves, one per SIMD, split the plane's work (tiles x
+// reduction) evenly and without a cross-wave reduction for all but T % 4 tiles:
+// - compute wave w owns T/4 whole tiles and reduces them over the group's
+//   entire reduction (C_in/groups x kernel taps, no per-channel padding);
+// - each of the T % 4 remaining tiles is split by 16-deep blocks of the
+//   reduction: wave w takes the blocks q with q % 4 == w (stream-K within the
+//   workgroup), and the four partial tiles are summed in a fixed order at the end.
+// Four copy waves issue every LDS DMA copy and do nothing else, so the compute
+// waves' instruction streams hold only operand reads and products: with one
+// compute wave per SIMD, address arithmetic or copy issue in its stream would
+// stall the matrix core, and with copies in flight the compiler's wait-count
+// tracking could only wait for an LDS read by draining all of them.
+// Reduction order: block q holds reduction indices 16q .. 16q+15 as two pairs of
+// k-steps; at k-step 2p + i, matrix row kg of the 4-deep step takes index
+// 8p + 2kg + i. With that order the A operands of a k-step pair are, per lane,
+// 2 consecutive weights of one output channel, and those of a block are 16-byte
+// runs of w: one 16-byte LDS DMA copy per block stages them for all 64 lanes
+// straight from w (layout [p][row][kg][2]), one 8-byte LDS read per k-step pair
+// fetches them, and the 4 matrix rows of a k-step read taps at most 6 apart,
+// so the B operand reads of a step mostly share LDS banks' addresses.
+// The input box keeps every F-th input column (stride and dilation along W
+// multiples of F) of every input row the plane reads, per (channel, depth tap)
+// plane; planes are copied by 4-byte LDS DMA in the order the reduction
+// consumes them, several blocks ahead. Each copy wave waits for its own copies
+// and meets the compute waves at a barrier before the blocks that read them.
+// ---------------------------------------------------------------------------
+template <int CG, int KD, int KH, int KW, int DH, int DW, int F, int ROWS, int BW, int T>
+struct KsGeo {
+  static constexpr int KVOL = KD * KH * KW;
+  static constexpr int KPP = KH * KW;           // reduction indices per box plane
+  static constexpr int K = CG * KVOL;           // group reduction length
+  static_assert(K % 4 == 0, "16-byte weight copies");
+  static constexpr int NQ = (K + 15) / 16;      // 16-deep reduction blocks
+  static constexpr int NS = 4 * NQ;             // 4-deep k-steps
+  static constexpr int FF = F, BWC = BW, ROWSC = ROWS, KDC = KD, KHC = KH, KWC = KW, DHC = DH, DWC = DW, CGC = CG;
+  static constexpr int PLANE = ROWS * BW;       // box floats per (channel, depth tap)
+  static constexpr int PI = (PLANE + 63) / 64;  // copy instructions per plane
+  static constexpr int PIW = (PI + 3) / 4;      // ... per wave (the rest pad to a multiple of 4)
+  static constexpr int PSLOT = PI * 64;         // floats per plane slot (whole copies)
+  static constexpr int NPL = CG * KD;           // planes in the box
+  static constexpr int FT = T / 4, R = T % 4;   // whole tiles per wave, split tiles
+  static constexpr int NTW = FT + R;            // tiles a wave accumulates
+  static constexpr int WQ = 4;                  // reduction blocks per weight stage (1 per copy wave)
+  static constexpr int NWS = (NQ + WQ - 1) / WQ;
+  // LDS (floats): box planes | weight operands [q][lane][4] | padding-copy target | split-tile partials
+  static constexpr int WOFF = NPL * PSLOT;
+  static constexpr int DUMMY = WOFF + NQ * 256;
+  static constexpr int RED = DUMMY + 256;
+  static constexpr int LDS = RED + 4 * (R > 0 ? R : 1) * 256;
+  // Reduction index of matrix row kg at k-step s: k-steps 2p and 2p+1 take
+  // indices 8p .. 8p+7, row kg the pair 8p + 2kg, 8p + 2kg + 1.
+  static constexpr int kidx(int s, int kg) { return 8 * (s >> 1) + 2 * kg + (s & 1); }
+  // LDS offset (floats) of reduction index k = (c, td, th, tw); indices past K
+  // (zero weights) point at the box start.
+  static constexpr int koff(int k) {
+    if (k >= K) return 0;
+    const int c = k / KVOL, r = k % KVOL, td = r / KPP, r2 = r % KPP, th = r2 / KW, tw = r2 % KW;
+    return (c * KD + td) * PSLOT + th * DH * BW + tw * (DW / F);
+  }
+};
+
+// Distinct per-step lane patterns koff(kidx(s, kg)) - koff(kidx(s, 0)).
+template <class G>
+struct KsPatterns {
+  int np = 0;
+  int pid[G::NS] = {};
+  int pat[G::NS][4] = {};
+  constexpr KsPatterns() {
+    for (int s = 0; s < G::NS; s++) {
+      int d[4] = {};
+      for (int j = 0; j < 4; j++) d[j] = G::koff(G::kidx(s, j)) - G::koff(G::kidx(s, 0));
+      int found = -1;
+      for (int q = 0; q < np && found < 0; q++) {
+        bool eq = true;
+        for (int j = 0; j < 4; j++) eq = eq && pat[q][j] == d[j];
+        if (eq) found = q;
+      }
+      if (found < 0) {
+        for (int j = 0; j < 4; j++) pat[np][j] = d[j];
+        found = np++;
+      }
+      pid[s] = found;
+    }
+  }
+};
+
+// Lane kg's share of distinct step pattern Q (from the two bits of kg).
+template <class G, int Q>
+__device__ __forceinline__ int ks_delta(int kg) {
+  constexpr KsPatterns<G> P{};
+  constexpr int d0 = P.pat[Q][0], d1 = P.pat[Q][1], d2 = P.pat[Q][2], d3 = P.pat[Q][3];
+  const int b0 = kg & 1, b1 = (kg >> 1) & 1;
+  return d0 + b0 * (d1 - d0) + b1 * (d2 - d0) + (b0 & b1) * (d3 - d2 - d1 + d0);
+}
+template <class G, int... Q>
+__device__ __forceinline__ void fill_ks_deltas(int* dp, int kg, std::integer_sequence<int, Q...>) {
+  ((dp[Q] = ks_delta<G, Q>(kg)), ...);
+}
+
+// Copy stages in the order they are needed: plane p = c * KD + td (first read by
+// block p * KPP / 16) and weight stage r (blocks 16r .. 16r+15). Each stage is
+// the same number of copy instructions in every wave, so a wave's own copy
+// count (vmcnt) tells which stages it has landed.
+template <class G>
+struct KsSchedule {
+  static constexpr int NST = G::NPL + G::NWS;
+  static constexpr int EARLY = 2;  // a stage is waited for at least this many blocks before its first use
+  static constexpr int LOOK = 14;  // and issued this many blocks before its first use
+  // Waits (and barriers) at blocks 0, 2 and then every 4 blocks: between two
+  // barriers after the start every wave takes the same number of split-tile
+  // turns, and the first barrier waits only for what blocks 0 and 1 read.
+  static constexpr bool wait_point(int q) { return q == 0 || q == 2 || q % 4 == 0; }
+  static constexpr int next_wait_point(int q) {
+    int r = q + 1;
+    while (r < G::NQ && !wait_point(r)) r++;
+    return r;
+  }
+  int type[NST] = {};  // 0: plane, 1: weights
+  int idx[NST] = {};
+  int need[NST] = {};
+  int cnt[NST] = {};   // copy instructions per wave
+  int wait_pre[G::NQ] = {};   // stages complete before block q's operands are read: prefix length
+  int issue_pre[G::NQ] = {};  // stages issued by the end of block q's issue point
+  int vm_allow[G::NQ] = {};   // vmcnt allowed at block q's wait (-1: no wait)
+  int max_out = 0;
+  constexpr KsSchedule() {
+    int n = 0;
+    for (int r = 0; r < G::NWS; r++) { type[n] = 1; idx[n] = r; need[n] = r * G::WQ; cnt[n] = G::WQ / 4; n++; }
+    for (int p = 0; p < G::NPL; p++) { type[n] = 0; idx[n] = p; need[n] = (p * G::KPP) / 16; cnt[n] = G::PIW; n++; }
+    // Stable insertion sort by first use (weights before planes on a tie).
+    for (int i = 1; i < NST; i++)
+      for (int j = i; j > 0 && need[j - 1] > need[j]; j--) {
+        int t;
+        t = type[j]; type[j] = type[j - 1]; type[j - 1] = t;
+        t = idx[j]; idx[j] = idx[j - 1]; idx[j - 1] = t;
+        t = need[j]; need[j] = need[j - 1]; need[j - 1] = t;
+        t = cnt[j]; cnt[j] = cnt[j - 1]; cnt[j - 1] = t;
+      }
+    int waited = 0;
+    for (int q = 0; q < G::NQ; q++) {
+      int ip = 0, wp = 0;
+      while (ip < NST && need[ip] <= q + LOOK) ip++;
+      // at a wait point, every stage read before the next wait point (+ EARLY)
+      if (wait_point(q))
+        while (wp < NST && need[wp] <= next_wait_point(q) - 1 + EARLY) wp++;
+      issue_pre[q] = ip;
+      wait_pre[q] = wp;
+      // The wait at block q comes before block q's issue: copies issued by
+      // the end of block q-1 (or at the start, for q = 0) are in flight.
+      const int issued = q == 0 ? issue_pre[0] : issue_pre[q - 1];
+      if (wait_point(q) && wp > waited) {
+        int later = 0;
+        for (int s = wp; s < issued; s++) later += cnt[s];
+        vm_allow[q] = later;
+        waited = wp;
+      } else {
+        vm_allow[q] = -1;
+      }
+      int out = 0;
+      for (int s = 0; s < ip; s++) out += cnt[s];
+      if (out > max_out) max_out = out;
+    }
+  }
+};
+
+template <class G>
+__global__ __launch_bounds__(512) void conv_tap_kstream_kernel(ConvArgs a) {
+  constexpr KsPatterns<G> P{};
+  constexpr KsSchedule<G> SC{};
+  constexpr int NP = P.np;
+  constexpr int NTW = G::NTW;
+  static_assert(G::NTW >= 1 && G::FT * 4 + G::R <= 16, "at most 16 tiles per plane");
+  __shared__ __align__(16) float smem[G::LDS];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool copier = wid >= 4;
+  const int wave = copier ? wid - 4 : wid;  // compute wave, or copy wave index
+  const int kg = lane >> 4;
+  const int li = lane & 15;
+  // Every kernel argument used is read here, in one batch of scalar loads, and
+  // pinned in scalar registers.
+  const float* xg = a.x;
+  const float* wgl = a.w;
+  const float* bg = a.bias;
+  float* yglob = a.y;
+  int Cin = a.Cin, Cout = a.Cout, Cg = a.Cg, Coutg = a.Coutg;
+  int L0 = a.L0, L1 = a.L1, L2 = a.L2, S0 = a.S0, S1 = a.S1, S2 = a.S2, D0 = a.D0;
+  int P0 = a.P0, P1 = a.P1, P2 = a.P2, O0 = a.O0, O1 = a.O1, O2 = a.O2, plane_out = a.plane_out;
+  int nitems = gridDim.x;
+  asm volatile("" : "+s"(xg), "+s"(wgl), "+s"(bg), "+s"(yglob), "+s"(Cin), "+s"(Cout), "+s"(Cg), "+s"(Coutg),
+               "+s"(L0), "+s"(L1), "+s"(L2), "+s"(S0), "+s"(S1), "+s"(S2), "+s"(D0), "+s"(P0), "+s"(P1), "+s"(P2),
+               "+s"(O0), "+s"(O1), "+s"(O2), "+s"(plane_out), "+s"(nitems));
+  // Workgroups are dispatched round-robin over the 8 XCDs: give each XCD a
+  // contiguous run of (plane, group) items, so the input planes that
+  // neighbouring output depths share stay in that XCD's L2.
+  int item = blockIdx.x;
+  if ((nitems & 7) == 0) item = (item & 7) * (nitems >> 3) + (item >> 3);
+  const int nplanes = nitems / (Cout / Coutg);
+  const int plane = item % nplanes;
+  const int g = item / nplanes;
+  const int n = plane / O0;
+  const int od = plane - n * O0;
+  float* box = smem;
+  float* wts = smem + G::WOFF;
+
+  if (copier) {
+    // Copy sources. Plane element e = zr * BW + j <- input row zr - P1, column
+    // F*j - P2 of the plane's channel and depth; copy wave w's copy i of a plane
+    // moves elements (4i + w) * 64 + lane, the same in-plane offsets for every plane.
+    float* dummy = smem + G::DUMMY;
+    const int64_t plane_in = int64_t(L1) * L2;
+    const int64_t vol_in = int64_t(L0) * plane_in;
+    const float* xg0 = xg + (int64_t(n) * Cin + int64_t(g) * Cg) * vol_in;
+    const int id0 = od * S0 - P0;
+    int soff[G::PIW];
+    uint32_t sok = 0;
+#pragma unroll
+    for (int i = 0; i < G::PIW; i++) {
+      const int e = (4 * i + wave) * 64 + lane;
+      const int zr = e / G::BWC, j = e - zr * G::BWC;
+      const int ih = zr - P1, iw = G::FF * j - P2;
+      const bool ok = e < G::PLANE && unsigned(ih) < unsigned(L1) && unsigned(iw) < unsigned(L2);
+      soff[i] = ok ? ih * L2 + iw : 0;
+      sok |= uint32_t(ok) << i;
+    }
+    const float* wg = wgl + int64_t(g) * Coutg * G::K;
+    auto issue_stage = [&](auto stc) {
+      constexpr int st = decltype(stc)::value;
+      if constexpr (SC.type[st] == 0) {
+        constexpr int p = SC.idx[st];
+        constexpr int c = p / G::KDC, td = p % G::KDC;
+        const int id = id0 + td * D0;
+        const bool dok = unsigned(id) < unsigned(L0);
+        const float* pl = xg0 + int64_t(c) * vol_in + int64_t(id) * plane_in;
+#pragma unroll
+        for (int i = 0; i < G::PIW; i++) {
+          const int ii = 4 * i + wave;  // copy instruction of the plane (wave-uniform)
+          const bool real = ii < G::PI;
+          const bool ok = real && dok && ((sok >> i) & 1);
+          lds_dma_f32(ok ? pl + soff[i] : kZeroWord, real ? box + p * G::PSLOT + ii * 64 : dummy);
+        }
+      } else {
+        constexpr int r = SC.idx[st];
+        // Lane l of block q's copy: k-step pair p = 2q + l/32, row m = (l%32)/2,
+        // weights 8p + 4(l%2) .. +3 of channel m -> floats 128p + 8m + 4(l%2).
+        const int wl = lane & 31, wm = wl >> 1;
+#pragma unroll
+        for (int i = 0; i < G::WQ / 4; i++) {
+          const int q = r * G::WQ + 4 * i + wave;  // reduction block (wave-uniform)
+          const bool real = q < G::NQ;
+          const int k = 16 * q + 8 * (lane >> 5) + 4 * (wl & 1);
+          const bool ok = real && wm < Coutg && k < G::K;
+          lds_dma_f32x4(ok ? wg + wm * G::K + k : kZeroWord, real ? wts + q * 256 : dummy);
+        }
+      }
+    };
+    // The stages first read within the look-ahead of block 0; then, at each of
+    // the compute waves' barriers, this wave's copies of the stages that barrier
+    // releases have landed, and the stages that enter the look-ahead are issued.
+    static_for<SC.issue_pre[0]>([&](auto st) { issue_stage(st); });
+    static_for<G::NQ>([&](auto qc) {
+      constexpr int q = decltype(qc)::value;
+      if constexpr (SC.vm_allow[q] >= 0) {
+        static_assert(SC.vm_allow[q] < 64, "vmcnt range");
+        wait_vmem_le<SC.vm_allow[q]>();
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+      }
+      if constexpr (q > 0) {
+        static_for<SC.issue_pre[q] - SC.issue_pre[q - 1]>([&](auto sc) {
+          issue_stage(std::integral_constant<int, SC.issue_pre[q - 1] + decltype(sc)::value>{});
+        });
+      }
+    });
+    if constexpr (G::R > 0) __syncthreads();  // the split tiles' partial sums are parked
+    return;
+  }
+
+  // Compute waves. Bias of the 4 channels this lane's accumulator registers
+  // hold, read through a global-address-space pointer (a flat load would count
+  // against the LDS counter too, and the compiler would then drain every LDS
+  // read at each operand wait of the product loop), and waited for here.
+  float b4[4];
+  const GlobalF* bgg = (const GlobalF*)(bg);
+#pragma unroll
+  for (int r = 0; r < 4; r++) {
+    const int ch = 4 * kg + r;
+    b4[r] = (bg && ch < Coutg) ? bgg[g * Coutg + ch] : 0.0f;
+  }
+  // Tiles of this wave: whole tiles wave*FT .. wave*FT + FT-1, then the split
+  // tiles 4FT .. T-1. Lane li's position in tile t is 16t + li.
+  int nb[NTW];
+  {
+    OffStep os(16 * wave * G::FT + li, O2, 0, S1 * G::BWC, S2 / G::FF);
+#pragma unroll
+    for (int i = 0; i < G::FT; i++) {
+      nb[i] = 16 * (wave * G::FT + i) + li < plane_out ? os.off : 0;
+      os.next();
+    }
+    if constexpr (G::R > 0) {
+      OffStep os2(16 * 4 * G::FT + li, O2, 0, S1 * G::BWC, S2 / G::FF);
+#pragma unroll
+      for (int i = 0; i < G::R; i++) {
+        nb[G::FT + i] = 16 * (4 * G::FT + i) + li < plane_out ? os2.off : 0;
+        os2.next();
+      }
+    }
+  }
+  int dpat[NP];
+  fill_ks_deltas<G>(dpat, kg, std::make_integer_sequence<int, NP>{});
+  int addr[NP][NTW];
+#pragma unroll
+  for (int q = 0; q < NP; q++)
+#pragma unroll
+    for (int t = 0; t < NTW; t++) addr[q][t] = 4 * (nb[t] + dpat[q]);
+
+  v4f acc[NTW];
+#pragma unroll
+  for (int t = 0; t < NTW; t++) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
+  v4f acc2[G::R > 0 ? G::R : 1];  // the split tiles' odd k-steps (a second chain)
+#pragma unroll
+  for (int r = 0; r < G::R; r++) acc2[r] = v4f{0.f, 0.f, 0.f, 0.f};
+  wait_vmem_le<0>();  // no memory access of this path is left in flight in the product loop
+  const char* bb = reinterpret_cast<const char*>(smem);
+  // B operand of tile t at k-step S: one LDS read at (lane register + immediate).
+  auto bread = [&](auto sc, int t) {
+    constexpr int S = decltype(sc)::value;
+    return *reinterpret_cast<const float*>(bb + addr[P.pid[S]][t] + 4 * G::koff(G::kidx(S, 0)));
+  };
+  // Operands are read two k-steps ahead of the products that use them, one or
+  // two reads after each product in issue order (a burst of reads between two
+  // products would hold back the second while they issue). A: a float2 per
+  // k-step pair (two pairs buffered); B: per k-step and whole tile, three
+  // k-steps buffered; the split tiles' B of a block, read only before this
+  // wave's turns, two blocks buffered.
+  float2 ap[2];
+  float bs[3][G::FT > 0 ? G::FT : 1];
+  float br[2][4][G::R > 0 ? G::R : 1];
+  auto read_a = [&](auto pc) {
+    constexpr int pp = decltype(pc)::value;
+    ap[pp & 1] = *reinterpret_cast<const float2*>(wts + pp * 128 + li * 8 + kg * 2);
+  };
+  auto read_b = [&](auto sc, int t) {
+    constexpr int S = decltype(sc)::value;
+    bs[S % 3][t] = bread(std::integral_constant<int, S>{}, t);
+  };
+  auto read_r = [&](auto qc) {
+    constexpr int q = decltype(qc)::value;
+    static_for<4>([&](auto jc) {
+      constexpr int S = 4 * q + decltype(jc)::value;
+#pragma unroll
+      for (int r = 0; r < G::R; r++) br[q & 1][decltype(jc)::value][r] = bread(std::integral_constant<int, S>{}, G::FT + r);
+    });
+  };
+
+  static_for<G::NQ>([&](auto qc) {
+    constexpr int q = decltype(qc)::value;
+    // The stages this block and the next ones read have landed in every wave.
+    if constexpr (SC.vm_allow[q] >= 0) {
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    }
+    if constexpr (q == 0) {
+      read_a(std::integral_constant<int, 0>{});
+#pragma unroll
+      for (int t = 0; t < G::FT; t++) read_b(std::integral_constant<int, 0>{}, t);
+#pragma unroll
+      for (int t = 0; t < G::FT; t++) read_b(std::integral_constant<int, 1>{}, t);
+      if constexpr (G::R > 0) {
+        if (wave == 0) read_r(std::integral_constant<int, 0>{});
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    float aa[4];  // the block's A operands, kept for the split tiles' turn
+    static_for<4>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      constexpr int s = 4 * q + j;
+      const float av = (s & 1) ? ap[(s >> 1) & 1].y : ap[(s >> 1) & 1].x;
+      aa[j] = av;
+      static_for<G::FT>([&](auto tc) {
+        constexpr int t = decltype(tc)::value;
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bs[s % 3][t], acc[t], 0, 0, 0);
+        // Reads after this product: B of step s+2 for tile t; after the first
+        // product of an odd step, A of pair s/2 + 1.
+        constexpr bool rb = s + 2 < G::NS;
+        constexpr bool ra = t == 0 && (s & 1) && (s >> 1) + 1 < G::NS / 2;
+        if constexpr (rb) read_b(std::integral_constant<int, s + 2>{}, t);
+        if constexpr (ra) read_a(std::integral_constant<int, (s >> 1) + 1>{});
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        constexpr int nr = (rb ? 1 : 0) + (ra ? 1 : 0);
+        if constexpr (nr > 0) __builtin_amdgcn_sched_group_barrier(0x100, nr, 0);
+      });
+    });
+    if constexpr (G::R > 0) {
+      // The split tiles: this block's 4 k-steps if it is this wave's turn (two
+      // chains, even and odd k-steps, added at the end); then the split tiles'
+      // B operands of the next block if that is this wave's turn.
+      if ((q & 3) == wave) {
+#pragma unroll
+        for (int jj = 0; jj < 4; jj++)
+#pragma unroll
+          for (int r = 0; r < G::R; r++) {
+            if (jj & 1) acc2[r] = __builtin_amdgcn_mfma_f32_16x16x4f32(aa[jj], br[q & 1][jj][r], acc2[r], 0, 0, 0);
+            else acc[G::FT + r] = __builtin_amdgcn_mfma_f32_16x16x4f32(aa[jj], br[q & 1][jj][r], acc[G::FT + r], 0, 0, 0);
+          }
+      }
+      if constexpr (q + 1 < G::NQ) {
+        if (((q + 1) & 3) == wave) read_r(std::integral_constant<int, q + 1>{});
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  });
+
+  // Output: channel 4kg + r, position 16t + li of the (n, g*Coutg + ch, od) plane.
+  const int64_t out_plane = int64_t(O1) * O2;
+  float* yg = yglob + (int64_t(n) * Cout + int64_t(g) * Coutg) * O0 * out_plane + int64_t(od) * out_plane;
+  const int64_t ch_stride = int64_t(O0) * out_plane;
+#pragma unroll
+  for (int i = 0; i < G::FT; i++) {
+    const int p = 16 * (wave * G::FT + i) + li;
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      const int ch = 4 * kg + r;
+      if (ch < Coutg && p < plane_out) yg[ch * ch_stride + p] = acc[i][r] + b4[r];
+    }
+  }
+  if constexpr (G::R > 0) {
+    // Split tiles: park the partials, then wave w sums register w of every
+    // split tile over the 4 compute waves (fixed order) and stores channel 4kg + w.
+    float* red = smem + G::RED;
+#pragma unroll
+    for (int r = 0; r < G::R; r++)
+      *reinterpret_cast<v4f*>(red + ((wave * G::R + r) * 64 + lane) * 4) = acc[G::FT + r] + acc2[r];
+    __syncthreads();
+    const int ch = 4 * kg + wave;
+    const float bw_ = (bg && ch < Coutg) ? bgg[g * Coutg + ch] : 0.0f;
+#pragma unroll
+    for (int r = 0; r < G::R; r++) {
+      float v = 0.0f;
+#pragma unroll
+      for (int w2 = 0; w2 < 4; w2++) v += red[((w2 * G::R + r) * 64 + lane) * 4 + wave];
+      const int p = 16 * (4 * G::FT + r) + li;
+      if (ch < Coutg && p < plane_out) yg[ch * ch_stride + p] = v + bw_;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // fused_min_softmax_mfma4
 // ---------------------------------------------------------------------------
 struct FusedArgs {
@@ -2218,11 +2673,15 @@ static int split_spin_cap() {
   return v < 0 ? 0 : (v > (1 << 22) ? (1 << 22) : int(v));
 }
 
-// CONVHIP_SPLIT_PIPE=0 keeps the channel-split specialisations on the kernel
-// whose cross-wave sum follows all products (tests run both kernels).
-static bool split_pipe_enabled() {
+// Kernel family for the geometries the channel-split specialisations serve:
+// unset = the planner's choice (the stream-K kernel where a specialisation
+// fits, else the pipelined channel-split kernel); CONVHIP_SPLIT_PIPE=1 forces
+// the pipelined channel-split kernel, =0 the one whose cross-wave sum follows
+// all products (tests and A/B timings run each).
+static int split_kernel_choice() {
   const char* s = std::getenv("CONVHIP_SPLIT_PIPE");
-  return !(s && *s && std::atoi(s) == 0);
+  if (!s || !*s) return 0;
+  return std::atoi(s) ? 1 : 2;
 }
 
 template <int NT, int NW, int KD, int KH, int KW, int DD, int DH, int DW, int F, int ROWS, int BW, bool CL>
@@ -2248,6 +2707,26 @@ static int launch_split_spec(const ConvArgs& args, const ConvPlan& p, hipStream_
     return launch_split<NT, NW, KD, KH, KW, DD, DH, DW, F, ROWS, BW, CL>(args, p, stream);
     CONVHIP_SPLIT_SPECS(CONVHIP_SPLIT_CASE)
 #undef CONVHIP_SPLIT_CASE
+    default: return CONV_ERR_UNSUPPORTED;
+  }
+}
+
+template <int CG, int KD, int KH, int KW, int DH, int DW, int F, int ROWS, int BW, int T>
+static int launch_kstream(const ConvArgs& args, const ConvPlan& p, hipStream_t stream) {
+  using G = KsGeo<CG, KD, KH, KW, DH, DW, F, ROWS, BW, T>;
+  static_assert(4 * G::LDS <= kLdsLimit, "stream-K specialisation exceeds LDS");
+  if (int64_t(4) * G::LDS != p.lds_bytes) return CONV_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL(conv_tap_kstream_kernel<G>, dim3(unsigned(p.grid[0])), dim3(512), 0, stream, args);
+  return hipGetLastError() == hipSuccess ? CONV_OK : CONV_ERR_HIP;
+}
+
+static int launch_ks_spec(const ConvArgs& args, const ConvPlan& p, hipStream_t stream) {
+  switch (p.ks_spec) {
+#define CONVHIP_KS_CASE(id, CG, KD, KH, KW, DH, DW, F, ROWS, BW, T) \
+  case id:                                                        \
+    return launch_kstream<CG, KD, KH, KW, DH, DW, F, ROWS, BW, T>(args, p, stream);
+    CONVHIP_KSTREAM_SPECS(CONVHIP_KS_CASE)
+#undef CONVHIP_KS_CASE
     default: return CONV_ERR_UNSUPPORTED;
   }
 }
@@ -2442,7 +2921,7 @@ int conv_plan_describe(int nd, const int64_t* x_shape, const int64_t* w_shape, c
     s = describe(fused_geom(g, min_dim), p);
   } else {
     ConvPlan p;
-    rc = plan_conv(g, &p, forced_conv_cfg(), 256, use_tap(), split_pipe_enabled());
+    rc = plan_conv(g, &p, forced_conv_cfg(), 256, use_tap(), split_kernel_choice());
     if (rc != CONV_OK) return rc;
     s = describe(g, p);
   }
@@ -2462,11 +2941,12 @@ int conv_fwd(int nd, const float* x, const int64_t* x_shape, const float* w, con
   // they need 16-byte aligned pointers (any tensor allocation is; a sliced view
   // may not be).
   const bool aligned = ((reinterpret_cast<uintptr_t>(w) | reinterpret_cast<uintptr_t>(x)) & 15) == 0;
-  rc = plan_conv(g, &p, forced_conv_cfg(), device_num_cu(), aligned ? use_tap() : 0, split_pipe_enabled());
+  rc = plan_conv(g, &p, forced_conv_cfg(), device_num_cu(), aligned ? use_tap() : 0, split_kernel_choice());
   if (rc != CONV_OK) return rc;
   ConvArgs a = conv_args(g, p, x, w, bias, y);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (p.tap_spec >= 0) return launch_tap_spec(a, p, s);
+  if (p.ks_spec >= 0) return launch_ks_spec(a, p, s);
   if (p.split_spec >= 0) return launch_split_spec<false>(a, p, s);
   return launch_generic<false>(a, p, s);
 }
@@ -2483,7 +2963,7 @@ int conv_fwd_channels_last(int nd, const float* x, const int64_t* x_shape, const
   g.x_aligned16 = (reinterpret_cast<uintptr_t>(x) & 15) == 0;
   g.w_aligned16 = (reinterpret_cast<uintptr_t>(w) & 15) == 0;
   ConvPlan p;
-  rc = plan_conv(g, &p, forced_conv_cfg(), device_num_cu(), use_tap(), split_pipe_enabled());
+  rc = plan_conv(g, &p, forced_conv_cfg(), device_num_cu(), use_tap(), split_kernel_choice());
   if (rc != CONV_OK) return rc;
   ConvArgs a = conv_args(g, p, x, w, bias, y);
   a.vec_store = (g.Cout % 4 == 0 && g.Coutg % 4 == 0 && (reinterpret_cast<uintptr_t>(y) & 15) == 0) ? 1 : 0;

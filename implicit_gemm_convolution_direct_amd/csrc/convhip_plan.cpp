@@ -134,6 +134,68 @@ const SplitSpecDesc* split_specs(int* count) {
   return specs;
 }
 
+const KsSpecDesc* ks_specs(int* count) {
+#define CONVHIP_KS_DESC(id, CG, KD, KH, KW, DH, DW, F, ROWS, BW, T) {id, CG, KD, KH, KW, DH, DW, F, ROWS, BW, T},
+  static const KsSpecDesc specs[] = {CONVHIP_KSTREAM_SPECS(CONVHIP_KS_DESC)};
+#undef CONVHIP_KS_DESC
+  *count = int(sizeof(specs) / sizeof(specs[0]));
+  return specs;
+}
+
+// LDS floats of a stream-K specialisation (the kernel's layout: box planes of
+// whole 64-float copies, the weight operands of every 16-deep reduction block,
+// a 256-float target for padding copies, the split tiles' partial sums).
+static int64_t ks_lds_floats(const KsSpecDesc& d) {
+  const int64_t kred = int64_t(d.CG) * d.KD * d.KH * d.KW;
+  const int64_t pslot = (int64_t(d.ROWS) * d.BW + 63) / 64 * 64;
+  const int64_t nq = (kred + 15) / 16;
+  const int64_t r = d.T % 4;
+  return int64_t(d.CG) * d.KD * pslot + nq * 256 + 256 + 4 * (r > 0 ? r : 1) * 256;
+}
+
+// Plan of a stream-K specialisation if the geometry fits it: NCDHW tensors, the
+// spec's channels, kernel and W/H dilations, W stride and dilation multiples of
+// F, exactly T tiles per output plane, and a box within the staged extents.
+static bool plan_kstream(const Geom& g, const KsSpecDesc& d, ConvPlan* p) {
+  if (g.cl || g.Coutg > 16 || g.Cg != d.CG) return false;
+  if (g.K[0] != d.KD || g.K[1] != d.KH || g.K[2] != d.KW) return false;
+  if (g.Dl[1] != d.DH || g.Dl[2] != d.DW) return false;
+  if (g.S[2] % d.F != 0 || d.DW % d.F != 0) return false;
+  if ((int64_t(d.CG) * d.KD * d.KH * d.KW) % 4 != 0) return false;
+  if ((g.plane_out() + 15) / 16 != d.T) return false;
+  const int64_t rows = (g.O[1] - 1) * g.S[1] + (g.K[1] - 1) * g.Dl[1] + 1;
+  const int64_t bw = ((g.O[2] - 1) * g.S[2] + (g.K[2] - 1) * g.Dl[2]) / d.F + 1;
+  if (rows > d.ROWS || bw > d.BW) return false;
+  const int64_t items = g.N * g.O[0] * g.G;
+  if (items > std::numeric_limits<int32_t>::max()) return false;
+  if (g.L[1] * g.L[2] > std::numeric_limits<int32_t>::max() / 2) return false;
+  const int64_t lds = 4 * ks_lds_floats(d);
+  if (lds > kLdsLimit) return false;
+  ConvPlan q;
+  q.cfg = -1;
+  q.ks_spec = d.id;
+  q.threads = 256;
+  q.BM = 16;
+  q.BN = 16 * d.T;
+  q.mode = TILE_FLAT;
+  q.Cc = d.CG;
+  q.kc_pad = int((int64_t(d.CG) * d.KD * d.KH * d.KW + 15) / 16 * 16);
+  q.kdspan = d.KD;
+  q.rows = int(rows);
+  q.bw = int(bw);
+  q.boxc = d.KD * d.ROWS * d.BW;
+  q.tiles_per_plane = 1;
+  q.ctiles = 1;
+  q.nchunks = 1;
+  q.items = items;
+  q.lds_bytes = lds;
+  q.grid[0] = items;
+  q.grid[1] = 1;
+  q.grid[2] = 1;
+  *p = q;
+  return true;
+}
+
 static bool plan_split(const Geom& g, const SplitSpecDesc& d, bool pipe, ConvPlan* p) {
   if (g.Coutg > 16 || g.Cg != d.NW) return false;
   if (g.K[0] != d.KD || g.K[1] != d.KH || g.K[2] != d.KW) return false;
@@ -332,7 +394,8 @@ static bool plan_tap_cl(const Geom& g, const TapClSpecDesc& d, int num_cu, ConvP
   return true;
 }
 
-int plan_conv(const Geom& g, ConvPlan* out, int force_cfg, int num_cu, int use_tap, bool split_pipe) {
+int plan_conv(const Geom& g, ConvPlan* out, int force_cfg, int num_cu, int use_tap, int split_kernel) {
+  const bool split_pipe = split_kernel != 2;
   if (g.cl) {
     if (use_tap != 0 && force_cfg < 0) {
       int n = 0;
@@ -350,6 +413,11 @@ int plan_conv(const Geom& g, ConvPlan* out, int force_cfg, int num_cu, int use_t
     const TapSpecDesc* specs = tap_specs(&n);
     for (int i = 0; i < n; i++)
       if (plan_tap(g, specs[i], num_cu, out)) return CONV_OK;
+    if (split_kernel == 0) {
+      const KsSpecDesc* ks = ks_specs(&n);
+      for (int i = 0; i < n; i++)
+        if (plan_kstream(g, ks[i], out)) return CONV_OK;
+    }
     const SplitSpecDesc* ss = split_specs(&n);
     for (int i = 0; i < n; i++)
       if (plan_split(g, ss[i], split_pipe, out)) return CONV_OK;
@@ -567,13 +635,21 @@ std::string describe(const Geom& g, const ConvPlan& p) {
     int n = 0;
     const SplitSpecDesc& d = split_specs(&n)[p.split_spec];
     cs = CfgShape{1, d.NT, 1, 1, d.NW};
+  } else if (p.ks_spec >= 0) {
+    int n = 0;
+    const KsSpecDesc& d = ks_specs(&n)[p.ks_spec];
+    cs = CfgShape{1, d.T, 1, 1, 4};
   }
   std::snprintf(buf, sizeof buf,
                 "kernel=%s%s cfg=%d MT=%d NT=%d WM=%d WN=%d KS=%d BM=%d BN=%d mode=%s Cc=%d kc_pad=%d "
                 "box=%dx%dx%d grid=%lldx%lldx%lld lds=%lld macs=%lld",
-                p.tap_spec >= 0 ? "conv_tap" : p.split_spec >= 0 ? (p.split_pipe ? "conv_tap_split pipe=1" : "conv_tap_split") : "conv_mfma16",
+                p.tap_spec >= 0    ? "conv_tap"
+                : p.ks_spec >= 0   ? "conv_tap_kstream"
+                : p.split_spec >= 0 ? (p.split_pipe ? "conv_tap_split pipe=1" : "conv_tap_split")
+                                    : "conv_mfma16",
                 g.cl ? (p.cl_vec ? " layout=channels_last copy=quad" : " layout=channels_last copy=scalar") : "",
-                p.tap_spec >= 0 ? p.tap_spec : p.split_spec >= 0 ? p.split_spec : p.cfg, cs.MT, cs.NT,
+                p.tap_spec >= 0 ? p.tap_spec : p.ks_spec >= 0 ? p.ks_spec : p.split_spec >= 0 ? p.split_spec : p.cfg,
+                cs.MT, cs.NT,
                 cs.WM, cs.WN, cs.KS, p.BM, p.BN, p.mode == TILE_FLAT ? "flat" : "row", p.Cc,
                 p.kc_pad, p.kdspan, p.rows, p.bw, (long long)p.grid[0], (long long)p.grid[1],
                 (long long)p.grid[2], (long long)p.lds_bytes, (long long)g.macs());

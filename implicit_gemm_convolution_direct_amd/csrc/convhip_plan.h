@@ -84,6 +84,7 @@ struct ConvPlan {
   int tap_spec = -1;    // >= 0: build-time specialised persistent kernel (grid[0] workgroups walk `items`)
   int split_spec = -1;  // >= 0: build-time specialised channel-split kernel
   int split_pipe = 0;   // channel-split kernel summing the first tile batch during the second's products
+  int ks_spec = -1;     // >= 0: build-time specialised workgroup-stream-K kernel (one plane per workgroup)
   int threads = 256;    // workgroup size
   int64_t items = 0;    // tap kernel: work items (tile, plane)
   int64_t grid[3] = {0, 0, 0};
@@ -122,6 +123,24 @@ constexpr bool split_pipe_fits(int NT, int NW, int wrow) {
   return NT >= 8 && (NT + 1) / 2 <= NW && wrow % 4 == 0;
 }
 
+// Build-time specialisations of the workgroup-stream-K kernel (conv_tap_kstream):
+// one workgroup of 4 waves per (n, od) output plane and group, <= 16 output
+// channels per group, the plane's T tiles of 16 positions split over the
+// waves (T/4 whole tiles each, the T % 4 others split by reduction blocks).
+// X(id, CG, KD, KH, KW, DH, DW, F, ROWS, BW, T): C_in/groups = CG, kernel
+// KD x KH x KW, dilations DH, DW along H and W (any along D), and a staged box
+// of at most ROWS input rows by BW kept columns (every F-th input column) per
+// (channel, depth tap) plane; the rows and columns a geometry needs may be fewer.
+#define CONVHIP_KSTREAM_SPECS(X)                                                   \
+  /* Conv3d 16->32, groups 2, kernel 3x5x7, stride (1,2,2), dilation (1,1,2):  \
+     32x32 inputs (16x13 outputs, 13 tiles) */                                   \
+  X(0, 8, 3, 5, 7, 1, 2, 2, 35, 20, 13)
+
+struct KsSpecDesc {
+  int id, CG, KD, KH, KW, DH, DW, F, ROWS, BW, T;
+};
+const KsSpecDesc* ks_specs(int* count);
+
 struct SplitSpecDesc {
   int id, NT, NW, KD, KH, KW, DD, DH, DW, F, ROWS, BW, TS;
 };
@@ -154,8 +173,12 @@ const TapClSpecDesc* tap_cl_specs(int* count);
 // geometries (g.cl) take the channels-last tap specialisations (tap_spec then
 // indexes CONVHIP_TAP_CL_SPECS), the channel-split specialisations or the
 // generic kernel.
+// split_kernel: for geometries the channel-split family serves, 0 = the
+// planner's choice (stream-K kernel, else the pipelined channel-split kernel),
+// 1 = the pipelined channel-split kernel, 2 = the channel-split kernel that sums
+// after all products.
 int plan_conv(const Geom& g, ConvPlan* p, int force_cfg = -1, int num_cu = 256, int use_tap = -1,
-              bool split_pipe = true);
+              int split_kernel = 0);
 
 // Build-time specialisations of the depth-streamed fused kernel (stride 1,
 // dilation 1, groups 1, kD = 3, min over depth): X(id, CIN, KH, KW, NG, O2, ROWS, RT)

@@ -200,3 +200,24 @@ def test_binding_rejects_wrong_dtype_and_layout():
         ch.conv_fwd(x, w, torch.zeros(8, dtype=torch.float64))
     with pytest.raises(ValueError, match="w must be contiguous"):
         ch.conv_fwd(x, _cpu(8, 3, 3, 3, 6)[..., ::2])
+
+
+def test_general_conv3d_kernel_choice(monkeypatch):
+    """The general Conv3d geometry takes the workgroup-stream-K kernel; the
+    channel-split kernels stay reachable for tests and A/B timings."""
+    import synth
+    cfg = synth.WORKLOADS["general_conv3d"]
+    args = (cfg["x"], cfg["w"], cfg["stride"], cfg["dilation"], cfg["padding"], cfg["groups"])
+    d = ch.plan_describe(*args)
+    fields = dict(t.split("=", 1) for t in d.split() if "=" in t)
+    assert fields["kernel"] == "conv_tap_kstream", d
+    assert fields["grid"] == "256x1x1" and int(fields["lds"]) <= 160 * 1024, d
+    monkeypatch.setenv("CONVHIP_SPLIT_PIPE", "1")
+    assert "kernel=conv_tap_split pipe=1" in ch.plan_describe(*args)
+    monkeypatch.setenv("CONVHIP_SPLIT_PIPE", "0")
+    d = ch.plan_describe(*args)
+    assert "kernel=conv_tap_split " in d and "pipe=1" not in d, d
+    monkeypatch.delenv("CONVHIP_SPLIT_PIPE")
+    # a plane of 12 tiles (16 x 12 outputs) is not the specialisation's 13
+    d = ch.plan_describe((2, 16, 8, 32, 24), cfg["w"], *args[2:])
+    assert "kernel=conv_tap_kstream" not in d, d

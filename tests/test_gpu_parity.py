@@ -497,6 +497,25 @@ def test_split_specialised_kernel_integer_exact(case, pipe, monkeypatch):
     np.testing.assert_array_equal(y.astype(np.float64), oracle.conv(x, w, b, s, d, p, g))
 
 
+# The general Conv3d's channel/kernel/dilation geometry on smaller batches and
+# depths, with padding planes, depth stride 2 and fewer output channels: the
+# workgroup-stream-K kernel (13 tiles per plane: 3 whole tiles per wave plus one
+# tile split over the waves by reduction blocks).
+KSTREAM_CASES = SPLIT_CASES[:5]
+
+
+@pytest.mark.parametrize("case", range(len(KSTREAM_CASES)))
+def test_kstream_specialised_kernel_integer_exact(case):
+    xs, ws, s, d, p, g = KSTREAM_CASES[case]
+    desc = ch.plan_describe(xs, ws, s, d, p, g)
+    assert "kernel=conv_tap_kstream" in desc, desc
+    r = np.random.default_rng(600 + case)
+    x, w, b = _int_inputs(r, xs, ws, bias=case % 2 == 0)
+    say(f"kstream case {case}: x={xs} w={ws}: {desc}")
+    y = gpu_conv(x, w, b, s, d, p, g)
+    np.testing.assert_array_equal(y.astype(np.float64), oracle.conv(x, w, b, s, d, p, g))
+
+
 def test_tap_disabled_falls_back_to_streamed(monkeypatch):
     monkeypatch.setenv("CONVHIP_TAP", "0")
     xs, ws, s, d, p, _ = TAP_CASES[0]
@@ -513,7 +532,7 @@ def test_workloads_use_expected_kernels():
     d = ch.plan_describe(cfg["x"], cfg["w"], fused=True)
     assert "kernel=fused_stream" in d, d
     for name, kernel in [("asym_conv3d", "conv_tap"), ("long_conv1d", "conv_tap"),
-                         ("general_conv3d", "conv_tap_split"), ("tiny_conv3d", "conv_tap_split")]:
+                         ("general_conv3d", "conv_tap_kstream"), ("tiny_conv3d", "conv_tap_split")]:
         cfg = synth.WORKLOADS[name]
         d = ch.plan_describe(cfg["x"], cfg["w"], *_cfg_args(cfg)) + " "
         assert f"kernel={kernel}" in d, d
@@ -540,7 +559,7 @@ def test_split_pipe_wait_give_up_stores_nan(monkeypatch):
     output is exact everywhere."""
     name = "general_conv3d"
     cfg = synth.WORKLOADS[name]
-    monkeypatch.setenv("CONVHIP_SPLIT_KERNEL", "pipe")
+    monkeypatch.setenv("CONVHIP_SPLIT_PIPE", "1")
     desc = ch.plan_describe(cfg["x"], cfg["w"], *_cfg_args(cfg))
     assert "pipe=1" in desc, desc
     x, w, b = synth.make_inputs(name, integer=True, n_samples=1)
