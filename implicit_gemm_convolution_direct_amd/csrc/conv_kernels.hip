@@ -107,6 +107,11 @@ struct AFrag<2> {
   }
 };
 template <>
+struct AFrag<3> {
+  float v[3];
+  __device__ __forceinline__ void load(const float* __restrict__ p) { v[0] = p[0]; v[1] = p[1]; v[2] = p[2]; }
+};
+template <>
 struct AFrag<4> {
   float v[4];
   __device__ __forceinline__ void load(const float* __restrict__ p) {

@@ -261,21 +261,18 @@ static bool plan_tap(const Geom& g, const TapSpecDesc& d, int num_cu, ConvPlan* 
   int64_t tiles;
   box_dims(g, mode, BN, &rows, &bw, &tiles, &row_tiles);
   const int kdspan = int((g.K[0] - 1) * g.Dl[0] + 1);
-  if (rows != d.ROWS || kdspan != d.KDSPAN) return false;
+  // The box is staged at the spec's extents: a geometry whose tiles need fewer
+  // rows or columns leaves the rest unread (copied from the input or zero).
+  if (rows > d.ROWS || kdspan != d.KDSPAN || bw > d.BW) return false;
   // Specialisations with rows of a multiple of 4 floats copy the box in 16-byte
   // chunks starting at input column ow0*S - P: the input rows, that column and
-  // the row length must be multiples of 4. A single-row box (1-D) may be staged
-  // wider than needed.
+  // the row length must be multiples of 4.
   if (d.BW % 4 == 0) {
     if (g.L[2] % 4 != 0 || g.P[2] % 4 != 0) return false;
     if (mode == TILE_ROW && (g.S[2] * BN) % 4 != 0) return false;
   }
-  if (d.ROWS == 1 && d.KDSPAN == 1 && d.BW % 4 == 0 && mode == TILE_ROW) {
-    if (bw > d.BW) return false;
-    bw = d.BW;
-  } else if (bw != d.BW) {
-    return false;
-  }
+  rows = d.ROWS;
+  bw = d.BW;
   const int64_t items = tiles * g.N * g.O[0];
   if (items > std::numeric_limits<int32_t>::max()) return false;
   const int64_t kvol = int64_t(d.KD) * d.KH * d.KW;
@@ -347,13 +344,9 @@ static bool plan_tap_cl(const Geom& g, const TapClSpecDesc& d, int num_cu, ConvP
   int64_t tiles;
   box_dims(g, mode, BN, &rows, &bw, &tiles, &row_tiles);
   const int kdspan = int((g.K[0] - 1) * g.Dl[0] + 1);
-  if (rows != d.ROWS || kdspan != d.KDSPAN) return false;
-  // A single-row box (1-D) may be staged wider than the tile needs.
-  if (d.ROWS == 1 && d.KDSPAN == 1 && mode == TILE_ROW) {
-    if (bw > d.BW) return false;
-  } else if (bw != d.BW) {
-    return false;
-  }
+  // The box is staged at the spec's extents (fewer needed rows or sites are
+  // left unread).
+  if (rows > d.ROWS || kdspan != d.KDSPAN || bw > d.BW) return false;
   const int64_t items = tiles * g.N * g.O[0];
   if (items > std::numeric_limits<int32_t>::max()) return false;
   const int64_t kvol = int64_t(d.KD) * d.KH * d.KW;
@@ -372,9 +365,9 @@ static bool plan_tap_cl(const Geom& g, const TapClSpecDesc& d, int num_cu, ConvP
   q.Cc = d.CC;
   q.kc_pad = int(ns * 4);
   q.kdspan = kdspan;
-  q.rows = rows;
+  q.rows = d.ROWS;
   q.bw = d.BW;
-  q.boxc = kdspan * rows * d.BW;
+  q.boxc = kdspan * d.ROWS * d.BW;
   q.ccp = d.CCP;
   q.cl_vec = quads;
   q.xs_floats = int(xs);

@@ -95,13 +95,21 @@ struct ConvPlan {
 // force_cfg >= 0 selects a tile configuration (tests cover every configuration).
 // Build-time specialisations of the persistent tap-unrolled kernel: each fixes
 // the tiling, the channel chunk, the kernel taps and dilations, and the staged
-// box shape. X(id, MT, NT, WM, WN, NCH, KD, KH, KW, DD, DH, DW, CC, KDSPAN, ROWS, BW)
+// box's extents: at most ROWS input rows per plane at a row pitch of BW floats
+// (a geometry whose tiles need fewer rows or columns stages the box at the same
+// pitch). X(id, MT, NT, WM, WN, NCH, KD, KH, KW, DD, DH, DW, CC, KDSPAN, ROWS, BW)
 #define CONVHIP_TAP_SPECS(X)                                                      \
-  /* Conv3d 3->64, kernel 3x5x7, 64^3 input: 64 ch x 256 positions, 8 waves */ \
+  /* Conv3d 3->64, kernel 3x5x7, inputs up to 64 wide whose 256-position tiles \
+     span <= 10 input rows (64^3): 64 ch x 256 positions, 8 waves */            \
   X(0, 4, 2, 1, 8, 1, 3, 5, 7, 1, 1, 1, 3, 3, 10, 64)                            \
   /* Conv1d 64->128, k=3, stride 3, dilation 4: 128 ch x 256 positions; the   \
      774-float input segment is copied as 776 (16-byte chunks) */               \
-  X(1, 4, 4, 2, 4, 8, 1, 1, 3, 1, 1, 4, 8, 1, 1, 776)
+  X(1, 4, 4, 2, 4, 8, 1, 1, 3, 1, 1, 4, 8, 1, 1, 776)                            \
+  /* the Conv3d 3->64 kernel 3x5x7 on narrower inputs (tiles span <= 12 rows, \
+     e.g. 48^3) */                                                               \
+  X(2, 4, 2, 1, 8, 1, 3, 5, 7, 1, 1, 1, 3, 3, 12, 64)                            \
+  /* Conv1d 64->96, k=3, dilation 2: 96 ch x 256 positions */                   \
+  X(3, 3, 4, 2, 4, 8, 1, 1, 3, 1, 1, 2, 8, 1, 1, 776)
 
 // Build-time specialisations of the channel-split kernel (one input channel per
 // wave, <= 16 output channels per group).
@@ -134,7 +142,9 @@ constexpr bool split_pipe_fits(int NT, int NW, int wrow) {
 #define CONVHIP_KSTREAM_SPECS(X)                                                   \
   /* Conv3d 16->32, groups 2, kernel 3x5x7, stride (1,2,2), dilation (1,1,2):  \
      32x32 inputs (16x13 outputs, 13 tiles) */                                   \
-  X(0, 8, 3, 5, 7, 1, 2, 2, 35, 20, 13)
+  X(0, 8, 3, 5, 7, 1, 2, 2, 35, 20, 13)                                          \
+  /* the same on 24x24 inputs (12x9 outputs, 7 tiles) */                        \
+  X(1, 8, 3, 5, 7, 1, 2, 2, 35, 20, 7)
 
 struct KsSpecDesc {
   int id, CG, KD, KH, KW, DH, DW, F, ROWS, BW, T;

@@ -572,3 +572,52 @@ def test_split_pipe_wait_give_up_stores_nan(monkeypatch):
     monkeypatch.delenv("CONVHIP_SPIN_CAP")
     y = gpu_conv(x, w, b, *_cfg_args(cfg))
     np.testing.assert_array_equal(y.astype(np.float64), ref)
+
+
+# Neighbours of the workloads that no specialisation was built for exactly:
+# smaller inputs (the staged box at the specialisation's extents, fewer rows
+# or columns read) and another dilation / channel count.
+NEIGHBOUR_CASES = [
+    # name, workload variant, batch samples checked (None: all), kernel
+    ("asym_conv3d_48", 2, "kernel=conv_tap cfg=2"),
+    ("general_conv3d_24", None, "kernel=conv_tap_kstream cfg=1"),
+]
+
+
+@pytest.mark.parametrize("case", NEIGHBOUR_CASES, ids=[c[0] for c in NEIGHBOUR_CASES])
+def test_neighbour_shapes_integer_exact(case):
+    name, nsamp, kernel = case
+    cfg = synth.config(name)
+    x, w, b = synth.make_inputs(name, integer=True, n_samples=nsamp)
+    desc = ch.plan_describe(x.shape, cfg["w"], *_cfg_args(cfg))
+    assert kernel in desc, desc
+    say(f"neighbour {name} x={x.shape}: {desc}")
+    y = gpu_conv(x, w, b, *_cfg_args(cfg))
+    np.testing.assert_array_equal(y.astype(np.float64), oracle.conv(x, w, b, *_cfg_args(cfg)))
+
+
+@pytest.mark.parametrize("L,p,bias", [(20000, 0, False), (3000, 4, True)])
+def test_neighbour_conv1d_96_channels_dilation_2_integer_exact(L, p, bias):
+    """The long Conv1d with 96 output channels and dilation 2 (its own
+    specialisation, 96 channels x 256 positions), on shorter rows."""
+    xs, ws = (2, 64, L), (96, 64, 3)
+    desc = ch.plan_describe(xs, ws, 3, 2, p, 1)
+    assert "kernel=conv_tap cfg=3" in desc, desc
+    r = np.random.default_rng(700 + L)
+    x, w, b = _int_inputs(r, xs, ws, bias=bias)
+    y = gpu_conv(x, w, b, 3, 2, p, 1)
+    np.testing.assert_array_equal(y.astype(np.float64), oracle.conv(x, w, b, 3, 2, p, 1))
+
+
+def test_tap_box_narrower_than_pitch_integer_exact():
+    """The 12-row asymmetric-Conv3d specialisation on inputs of several widths
+    (box columns fewer than its 64-float pitch, rows fewer than 12)."""
+    r = np.random.default_rng(720)
+    for W in (44, 48, 52, 56):
+        xs, ws = (1, 3, 5, W, W), (64, 3, 3, 5, 7)
+        desc = ch.plan_describe(xs, ws, 1, 1, 0, 1)
+        assert "kernel=conv_tap" in desc, desc
+        x, w, b = _int_inputs(r, xs, ws, bias=True)
+        say(f"tap narrow W={W}: {desc}")
+        y = gpu_conv(x, w, b, 1, 1, 0, 1)
+        np.testing.assert_array_equal(y.astype(np.float64), oracle.conv(x, w, b, 1, 1, 0, 1))
