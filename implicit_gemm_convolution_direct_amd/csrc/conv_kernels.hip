@@ -1590,6 +1590,173 @@ __global__ __launch_bounds__(64 * NW) void conv_tap_split_pipe_kernel(ConvArgs a
 }
 
 // ---------------------------------------------------------------------------
+// conv_direct16: small convolutions, latency first. One single-wave workgroup
+// per 16 output positions (flattened over n, od, oh, ow) and all output
+// channels of a group (<= 16). The wave reads its A operands (weights) and B
+// operands (input values at each position's taps) straight from global memory
+// into registers: no LDS staging, no barrier, no cross-wave sum, so a launch
+// costs one round of global loads, the products and the stores. Single-wave
+// workgroups spread the waves over all compute units, so that no unit's load
+// pipeline holds more than two of them. The reduction (C_in/groups x kernel
+// taps, k-steps of 4) runs in two accumulator chains (even and odd k-steps).
+// Build-time: C_in/groups, kernel, dilations; zero padding only.
+// Channels-last (CL): x [N, D, H, W, C_in], y [N, D_out, H_out, W_out, C_out].
+// ---------------------------------------------------------------------------
+template <int CIN, int KD, int KH, int KW, int DD, int DH, int DW>
+struct DirectGeo {
+  static constexpr int CG = CIN;
+  static constexpr int KVOL = KD * KH * KW;
+  static constexpr int K = CIN * KVOL;
+  static constexpr int NS = (K + 3) / 4;
+  // (channel, depth, row, column) coefficients of reduction index k; indices
+  // past K take tap 0 (their weights are zero).
+  static constexpr int kc(int k) { return k < K ? k / KVOL : 0; }
+  static constexpr int ktd(int k) { return k < K ? (k % KVOL) / (KH * KW) * DD : 0; }
+  static constexpr int kth(int k) { return k < K ? (k % (KH * KW)) / KW * DH : 0; }
+  static constexpr int ktw(int k) { return k < K ? (k % KW) * DW : 0; }
+};
+
+// Distinct per-step lane patterns of (channel, depth, row, column) deltas.
+template <class G>
+struct DirectPatterns {
+  int np = 0;
+  int pid[G::NS] = {};
+  int pat[G::NS][4][4] = {};  // [pattern][kg][c, td, th, tw]
+  constexpr DirectPatterns() {
+    for (int s = 0; s < G::NS; s++) {
+      int d[4][4] = {};
+      for (int j = 0; j < 4; j++) {
+        const int k = 4 * s + j, k0 = 4 * s;
+        d[j][0] = G::kc(k) - G::kc(k0);
+        d[j][1] = G::ktd(k) - G::ktd(k0);
+        d[j][2] = G::kth(k) - G::kth(k0);
+        d[j][3] = G::ktw(k) - G::ktw(k0);
+      }
+      int found = -1;
+      for (int q = 0; q < np && found < 0; q++) {
+        bool eq = true;
+        for (int j = 0; j < 4; j++)
+          for (int e = 0; e < 4; e++) eq = eq && pat[q][j][e] == d[j][e];
+        if (eq) found = q;
+      }
+      if (found < 0) {
+        for (int j = 0; j < 4; j++)
+          for (int e = 0; e < 4; e++) pat[np][j][e] = d[j][e];
+        found = np++;
+      }
+      pid[s] = found;
+    }
+  }
+};
+
+// Arguments of conv_direct16, precomputed on the host: element strides of the
+// input, reciprocals of the output extents, so that the first instructions
+// need no divide and every argument arrives in one round of scalar loads.
+struct DirectArgs {
+  const float* x;
+  const float* w;
+  const float* bias;
+  float* y;
+  int sc, sd, sh, sw, sn;  // input element strides: channel, depth, row, column, sample
+  int ssd, ssh, ssw;       // input offset of one output step in depth, row, column
+  int sg;                  // input offset of one group's first channel
+  int O0, O1, O2, npos;    // output extents; npos = N * O0 * O1 * O2 (< 2^24)
+  float r0, r1, r2;        // 1 / O0, 1 / O1, 1 / O2 (fp32)
+  int Cout, Coutg;
+};
+
+template <class G, bool CL>
+__global__ __launch_bounds__(64) void conv_direct16_kernel(DirectArgs a) {
+  // Every argument in registers before any use: the scalar loads leave together
+  // and meet one wait (otherwise they are spread over dependent rounds).
+  asm volatile("" ::"s"(a.x), "s"(a.w), "s"(a.bias), "s"(a.y), "s"(a.sc), "s"(a.sd), "s"(a.sh), "s"(a.sw),
+               "s"(a.sn), "s"(a.ssd), "s"(a.ssh), "s"(a.ssw), "s"(a.sg), "s"(a.O0), "s"(a.O1), "s"(a.O2),
+               "s"(a.npos), "s"(a.r0), "s"(a.r1), "s"(a.r2), "s"(a.Cout), "s"(a.Coutg));
+  __builtin_amdgcn_sched_barrier(0);
+  constexpr DirectPatterns<G> P{};
+  constexpr int NP = P.np;
+  const int lane = threadIdx.x;
+  const int kg = lane >> 4;
+  const int li = lane & 15;
+  const GlobalF* xg = (const GlobalF*)(a.x);
+  const GlobalF* wg = (const GlobalF*)(a.w);
+  const GlobalF* bg = (const GlobalF*)(a.bias);
+  float* yg = a.y;
+  const int Cout = a.Cout, Coutg = a.Coutg;
+  const int O0 = a.O0, O1 = a.O1, O2 = a.O2;
+  const int sc = a.sc, sd = a.sd, sh = a.sh, sw = a.sw;
+  const int g = blockIdx.y;
+  const int npos = a.npos;
+  // This lane's position (clamped into range for the loads; stores skip it).
+  const int p = int(blockIdx.x) * 16 + li;
+  const bool valid = p < npos;
+  const int pc = valid ? p : npos - 1;
+  int ow, oh, od;
+  int r = divmod_small(pc, O2, a.r2, ow);
+  r = divmod_small(r, O1, a.r1, oh);
+  const int n = divmod_small(r, O0, a.r0, od);
+  const int base = n * a.sn + g * a.sg + od * a.ssd + oh * a.ssh + ow * a.ssw;
+  // Lane part of each distinct step pattern.
+  int dp[NP];
+  static_for<NP>([&](auto qc) {
+    constexpr int q = decltype(qc)::value;
+    const int b0 = kg & 1, b1 = (kg >> 1) & 1;
+    auto sel = [&](int e) {
+      const int d0 = P.pat[q][0][e], d1 = P.pat[q][1][e], d2 = P.pat[q][2][e], d3 = P.pat[q][3][e];
+      return d0 + b0 * (d1 - d0) + b1 * (d2 - d0) + (b0 & b1) * (d3 - d2 - d1 + d0);
+    };
+    dp[q] = base + sel(0) * sc + sel(1) * sd + sel(2) * sh + sel(3) * sw;
+  });
+  // Operands of every k-step, all loads issued before the first product.
+  const bool arow = li < Coutg;
+  const int wrow = (g * Coutg + (arow ? li : 0)) * G::K;
+  float av[G::NS], bv[G::NS];
+  static_for<G::NS>([&](auto sc_) {
+    constexpr int s = decltype(sc_)::value;
+    constexpr int k0 = 4 * s;
+    const int tap0 = G::kc(k0) * sc + G::ktd(k0) * sd + G::kth(k0) * sh + G::ktw(k0) * sw;
+    bv[s] = xg[dp[P.pid[s]] + tap0];
+    const int k = k0 + kg;
+    const bool ok = arow && k < G::K;
+    const float wv = wg[wrow + (k < G::K ? k : 0)];
+    av[s] = ok ? wv : 0.0f;
+  });
+  // Bias of this lane's four channels (register r: channel 4kg + r).
+  float bias4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (bg) {
+#pragma unroll
+    for (int rr = 0; rr < 4; rr++) bias4[rr] = bg[g * Coutg + min(4 * kg + rr, Coutg - 1)];
+  }
+  // Keep every load ahead of the products: one round of memory latency.
+  __builtin_amdgcn_sched_barrier(0);
+  v4f acc0 = v4f{0.f, 0.f, 0.f, 0.f}, acc1 = v4f{0.f, 0.f, 0.f, 0.f};
+  static_for<G::NS>([&](auto sc_) {
+    constexpr int s = decltype(sc_)::value;
+    if constexpr (s & 1) acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(av[s], bv[s], acc1, 0, 0, 0);
+    else acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(av[s], bv[s], acc0, 0, 0, 0);
+  });
+  const v4f acc = acc0 + acc1;
+  if (!valid) return;
+  if constexpr (CL) {
+    const int64_t opos = ((int64_t(n) * O0 + od) * O1 + oh) * O2 + ow;
+    float* yp = yg + opos * Cout + g * Coutg;
+#pragma unroll
+    for (int rr = 0; rr < 4; rr++) {
+      const int ch = 4 * kg + rr;
+      if (ch < Coutg) yp[ch] = acc[rr] + bias4[rr];
+    }
+  } else {
+    const int64_t plane = int64_t(O0) * O1 * O2;
+    const int64_t sp = (int64_t(od) * O1 + oh) * O2 + ow;
+#pragma unroll
+    for (int rr = 0; rr < 4; rr++) {
+      const int ch = 4 * kg + rr;
+      if (ch < Coutg) yg[(int64_t(n) * Cout + g * Coutg + ch) * plane + sp] = acc[rr] + bias4[rr];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // conv_tap_kstream: one workgroup per (n, od) output plane and group, for few
 // output channels per group (<= 16) and planes of at most 16 tiles of 16
 // positions. Four compute waves, one per SIMD, split the plane's work (tiles x
@@ -2736,6 +2903,38 @@ static int launch_ks_spec(const ConvArgs& args, const ConvPlan& p, hipStream_t s
   }
 }
 
+template <int CIN, int KD, int KH, int KW, int DD, int DH, int DW, bool CL>
+static int launch_direct(const ConvArgs& c, const ConvPlan& p, hipStream_t stream) {
+  DirectArgs a;
+  a.x = c.x; a.w = c.w; a.bias = c.bias; a.y = c.y;
+  a.sw = CL ? c.Cin : 1;
+  a.sh = c.L2 * a.sw;
+  a.sd = c.L1 * a.sh;
+  a.sc = CL ? 1 : c.L0 * a.sd;
+  a.sn = c.L0 * c.L1 * c.L2 * c.Cin;
+  a.ssd = c.S0 * a.sd; a.ssh = c.S1 * a.sh; a.ssw = c.S2 * a.sw;
+  a.sg = CIN * a.sc;
+  a.O0 = c.O0; a.O1 = c.O1; a.O2 = c.O2;
+  a.npos = int(p.items);
+  a.r0 = 1.0f / float(c.O0); a.r1 = 1.0f / float(c.O1); a.r2 = 1.0f / float(c.O2);
+  a.Cout = c.Cout; a.Coutg = c.Coutg;
+  hipLaunchKernelGGL((conv_direct16_kernel<DirectGeo<CIN, KD, KH, KW, DD, DH, DW>, CL>),
+                     dim3(unsigned(p.grid[0]), unsigned(p.grid[1])), dim3(64), 0, stream, a);
+  return hipGetLastError() == hipSuccess ? CONV_OK : CONV_ERR_HIP;
+}
+
+template <bool CL>
+static int launch_direct_spec(const ConvArgs& args, const ConvPlan& p, hipStream_t stream) {
+  switch (p.direct_spec) {
+#define CONVHIP_DIRECT_CASE(id, CIN, KD, KH, KW, DD, DH, DW) \
+  case id:                                                 \
+    return launch_direct<CIN, KD, KH, KW, DD, DH, DW, CL>(args, p, stream);
+    CONVHIP_DIRECT_SPECS(CONVHIP_DIRECT_CASE)
+#undef CONVHIP_DIRECT_CASE
+    default: return CONV_ERR_UNSUPPORTED;
+  }
+}
+
 static int launch_tap_spec(const ConvArgs& args, const ConvPlan& p, hipStream_t stream) {
   switch (p.tap_spec) {
 #define CONVHIP_TAP_CASE(id, MT, NT, WM, WN, NCH, KD, KH, KW, DD, DH, DW, CC, KDSPAN, ROWS, BW) \
@@ -2951,6 +3150,7 @@ int conv_fwd(int nd, const float* x, const int64_t* x_shape, const float* w, con
   ConvArgs a = conv_args(g, p, x, w, bias, y);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (p.tap_spec >= 0) return launch_tap_spec(a, p, s);
+  if (p.direct_spec >= 0) return launch_direct_spec<false>(a, p, s);
   if (p.ks_spec >= 0) return launch_ks_spec(a, p, s);
   if (p.split_spec >= 0) return launch_split_spec<false>(a, p, s);
   return launch_generic<false>(a, p, s);
@@ -2974,6 +3174,7 @@ int conv_fwd_channels_last(int nd, const float* x, const int64_t* x_shape, const
   a.vec_store = (g.Cout % 4 == 0 && g.Coutg % 4 == 0 && (reinterpret_cast<uintptr_t>(y) & 15) == 0) ? 1 : 0;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (p.tap_spec >= 0) return launch_tap_cl_spec(a, p, s);
+  if (p.direct_spec >= 0) return launch_direct_spec<true>(a, p, s);
   if (p.split_spec >= 0) return launch_split_spec<true>(a, p, s);
   return launch_generic<true>(a, p, s);
 }

@@ -134,6 +134,45 @@ const SplitSpecDesc* split_specs(int* count) {
   return specs;
 }
 
+const DirectSpecDesc* direct_specs(int* count) {
+#define CONVHIP_DIRECT_DESC(id, CIN, KD, KH, KW, DD, DH, DW) {id, CIN, KD, KH, KW, DD, DH, DW},
+  static const DirectSpecDesc specs[] = {CONVHIP_DIRECT_SPECS(CONVHIP_DIRECT_DESC)};
+#undef CONVHIP_DIRECT_DESC
+  *count = int(sizeof(specs) / sizeof(specs[0]));
+  return specs;
+}
+
+// Plan of a direct-kernel specialisation: the spec's channels, kernel and
+// dilations, no padding, <= 16 output channels per group, a small problem, and
+// every element offset (positions < 2^24, tensors < 2^31 elements) in 32 bits.
+static bool plan_direct(const Geom& g, const DirectSpecDesc& d, ConvPlan* p) {
+  if (g.Coutg > 16 || g.Cg != d.CIN) return false;
+  if (g.K[0] != d.KD || g.K[1] != d.KH || g.K[2] != d.KW) return false;
+  if (g.Dl[0] != d.DD || g.Dl[1] != d.DH || g.Dl[2] != d.DW) return false;
+  if (g.P[0] != 0 || g.P[1] != 0 || g.P[2] != 0) return false;
+  if (g.macs() > kDirectMaxMacs) return false;
+  const int64_t npos = g.N * g.O[0] * g.O[1] * g.O[2];
+  if (npos >= (int64_t(1) << 24)) return false;
+  const int64_t xe = g.N * g.Cin * g.L[0] * g.L[1] * g.L[2];
+  const int64_t ye = npos * g.Cout;
+  if (xe >= (int64_t(1) << 31) || ye >= (int64_t(1) << 31) || g.G > 65535) return false;
+  ConvPlan q;
+  q.cfg = -1;
+  q.direct_spec = d.id;
+  q.threads = 64;
+  q.BM = 16;
+  q.BN = 16;
+  q.Cc = d.CIN;
+  q.kc_pad = int((int64_t(d.CIN) * d.KD * d.KH * d.KW + 3) / 4 * 4);
+  q.items = npos;
+  q.grid[0] = (npos + 15) / 16;
+  q.grid[1] = g.G;
+  q.grid[2] = 1;
+  q.lds_bytes = 0;
+  *p = q;
+  return true;
+}
+
 const KsSpecDesc* ks_specs(int* count) {
 #define CONVHIP_KS_DESC(id, CG, KD, KH, KW, DH, DW, F, ROWS, BW, T) {id, CG, KD, KH, KW, DH, DW, F, ROWS, BW, T},
   static const KsSpecDesc specs[] = {CONVHIP_KSTREAM_SPECS(CONVHIP_KS_DESC)};
@@ -395,6 +434,11 @@ int plan_conv(const Geom& g, ConvPlan* out, int force_cfg, int num_cu, int use_t
       const TapClSpecDesc* specs = tap_cl_specs(&n);
       for (int i = 0; i < n; i++)
         if (plan_tap_cl(g, specs[i], num_cu, out)) return CONV_OK;
+      if (split_kernel == 0) {
+        const DirectSpecDesc* ds = direct_specs(&n);
+        for (int i = 0; i < n; i++)
+          if (plan_direct(g, ds[i], out)) return CONV_OK;
+      }
       const SplitSpecDesc* ss = split_specs(&n);
       for (int i = 0; i < n; i++)
         if (plan_split(g, ss[i], split_pipe, out)) return CONV_OK;
@@ -407,6 +451,9 @@ int plan_conv(const Geom& g, ConvPlan* out, int force_cfg, int num_cu, int use_t
     for (int i = 0; i < n; i++)
       if (plan_tap(g, specs[i], num_cu, out)) return CONV_OK;
     if (split_kernel == 0) {
+      const DirectSpecDesc* ds = direct_specs(&n);
+      for (int i = 0; i < n; i++)
+        if (plan_direct(g, ds[i], out)) return CONV_OK;
       const KsSpecDesc* ks = ks_specs(&n);
       for (int i = 0; i < n; i++)
         if (plan_kstream(g, ks[i], out)) return CONV_OK;
@@ -632,16 +679,23 @@ std::string describe(const Geom& g, const ConvPlan& p) {
     int n = 0;
     const KsSpecDesc& d = ks_specs(&n)[p.ks_spec];
     cs = CfgShape{1, d.T, 1, 1, 4};
+  } else if (p.direct_spec >= 0) {
+    cs = CfgShape{1, 1, 1, 1, 1};
   }
   std::snprintf(buf, sizeof buf,
                 "kernel=%s%s cfg=%d MT=%d NT=%d WM=%d WN=%d KS=%d BM=%d BN=%d mode=%s Cc=%d kc_pad=%d "
                 "box=%dx%dx%d grid=%lldx%lldx%lld lds=%lld macs=%lld",
                 p.tap_spec >= 0    ? "conv_tap"
+                : p.direct_spec >= 0 ? "conv_direct16"
                 : p.ks_spec >= 0   ? "conv_tap_kstream"
                 : p.split_spec >= 0 ? (p.split_pipe ? "conv_tap_split pipe=1" : "conv_tap_split")
                                     : "conv_mfma16",
                 g.cl ? (p.cl_vec ? " layout=channels_last copy=quad" : " layout=channels_last copy=scalar") : "",
-                p.tap_spec >= 0 ? p.tap_spec : p.ks_spec >= 0 ? p.ks_spec : p.split_spec >= 0 ? p.split_spec : p.cfg,
+                p.tap_spec >= 0      ? p.tap_spec
+                : p.direct_spec >= 0 ? p.direct_spec
+                : p.ks_spec >= 0     ? p.ks_spec
+                : p.split_spec >= 0  ? p.split_spec
+                                     : p.cfg,
                 cs.MT, cs.NT,
                 cs.WM, cs.WN, cs.KS, p.BM, p.BN, p.mode == TILE_FLAT ? "flat" : "row", p.Cc,
                 p.kc_pad, p.kdspan, p.rows, p.bw, (long long)p.grid[0], (long long)p.grid[1],

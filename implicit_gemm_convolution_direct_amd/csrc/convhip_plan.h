@@ -85,6 +85,7 @@ struct ConvPlan {
   int split_spec = -1;  // >= 0: build-time specialised channel-split kernel
   int split_pipe = 0;   // channel-split kernel summing the first tile batch during the second's products
   int ks_spec = -1;     // >= 0: build-time specialised workgroup-stream-K kernel (one plane per workgroup)
+  int direct_spec = -1; // >= 0: build-time specialised direct kernel (small convolutions, no LDS)
   int threads = 256;    // workgroup size
   int64_t items = 0;    // tap kernel: work items (tile, plane)
   int64_t grid[3] = {0, 0, 0};
@@ -145,6 +146,23 @@ constexpr bool split_pipe_fits(int NT, int NW, int wrow) {
   X(0, 8, 3, 5, 7, 1, 2, 2, 35, 20, 13)                                          \
   /* the same on 24x24 inputs (12x9 outputs, 7 tiles) */                        \
   X(1, 8, 3, 5, 7, 1, 2, 2, 35, 20, 7)
+
+// Build-time specialisations of the direct kernel (conv_direct16) for small
+// convolutions: one wave per 16 output positions and all <= 16 output channels
+// of a group, operands read from global memory into registers. Zero padding 0.
+// X(id, CIN, KD, KH, KW, DD, DH, DW): C_in/groups, kernel and dilations.
+#define CONVHIP_DIRECT_SPECS(X)                     \
+  /* Conv3d 3->8, kernel 3x3x3 (16^3 inputs) */   \
+  X(0, 3, 3, 3, 3, 1, 1, 1)
+
+struct DirectSpecDesc {
+  int id, CIN, KD, KH, KW, DD, DH, DW;
+};
+const DirectSpecDesc* direct_specs(int* count);
+
+// Largest convolution the direct kernel takes: its waves read every operand
+// from global memory, which suits launches dominated by latency, not larger ones.
+constexpr int64_t kDirectMaxMacs = 16ll << 20;
 
 struct KsSpecDesc {
   int id, CG, KD, KH, KW, DH, DW, F, ROWS, BW, T;

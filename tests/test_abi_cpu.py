@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import implicit_gemm_convolution_direct_amd as ch
@@ -108,7 +109,7 @@ def test_fused_plan_per_min_axis():
 def test_channels_last_plans():
     for xs, ws, s, d, p, g, kernel in [
             ((4, 32, 32, 32, 16), (32, 8, 3, 5, 7), (1, 2, 2), (1, 1, 2), (1, 2, 3), 2, "conv_tap_split"),
-            ((2, 16, 16, 16, 3), (8, 3, 3, 3, 3), 1, 1, 0, 1, "conv_tap_split"),
+            ((2, 16, 16, 16, 3), (8, 3, 3, 3, 3), 1, 1, 0, 1, "conv_direct16"),
             ((2, 16, 16, 16, 4), (8, 4, 3, 3, 3), 1, 1, 0, 1, "conv_mfma16"),
             ((4, 4096, 64), (128, 64, 3), 3, 4, 0, 1, "conv_tap"),        # the long Conv1d geometry
             ((16, 64, 64, 64, 3), (64, 3, 3, 5, 7), 1, 1, 0, 1, "conv_tap"),  # the asymmetric Conv3d
@@ -122,6 +123,28 @@ def test_channels_last_plans():
         # generic kernel: channel quads (C_in/groups a multiple of 4) are copied 16 bytes at a time
         if kernel == "conv_mfma16":
             assert fields["copy"] == ("quad" if (xs[-1] // g) % 4 == 0 else "scalar"), desc
+
+
+def test_direct_kernel_plans():
+    """Small problems of the direct kernel's geometry take it in both layouts;
+    padding, a larger problem, more than 16 output channels per group or a
+    forced channel-split kernel do not."""
+    k3 = (8, 3, 3, 3, 3)
+    for xs, ws, s, p, g, cl, kernel in [
+            ((2, 3, 16, 16, 16), k3, 1, 0, 1, False, "conv_direct16"),
+            ((2, 16, 16, 16, 3), k3, 1, 0, 1, True, "conv_direct16"),
+            ((1, 3, 9, 11, 13), (5, 3, 3, 3, 3), (2, 1, 3), 0, 1, False, "conv_direct16"),
+            ((2, 3, 16, 16, 16), k3, 1, 1, 1, False, "conv_mfma16"),        # padding
+            ((2, 3, 40, 40, 40), k3, 1, 0, 1, False, "conv_mfma16"),        # 71M MACs
+            ((1, 3, 16, 16, 16), (17, 3, 3, 3, 3), 1, 0, 1, False, "conv_mfma16"),
+            ((1, 6, 16, 16, 16), (8, 6, 3, 3, 3), 1, 0, 1, False, "conv_mfma16")]:
+        desc = ch.plan_describe(xs, ws, s, 1, p, g, channels_last=cl)
+        fields = dict(t.split("=", 1) for t in desc.split() if "=" in t)
+        assert fields["kernel"] == kernel, desc
+        if kernel == "conv_direct16":
+            n_pos = xs[0] * np.prod([(l - 3) // st + 1 for l, st in
+                                     zip(xs[2:] if not cl else xs[1:4], np.broadcast_to(s, 3))])
+            assert fields["grid"] == f"{(n_pos + 15) // 16}x{g}x1" and fields["lds"] == "0", desc
 
 
 def test_conv3d_min_softmax_validation_errors():

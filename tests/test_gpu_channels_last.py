@@ -308,6 +308,28 @@ def test_channels_last_split_kernel_integer_exact(case, pipe, monkeypatch):
     np.testing.assert_array_equal(y.astype(np.float64), oracle.conv_channels_last(x, w, b, s, d, p, g))
 
 
+# The direct kernel's cases in channels-last order.
+DIRECT_CL_CASES = [
+    ((2, 16, 16, 16, 3), (8, 3, 3, 3, 3), 1, 1, 0, 1),
+    ((1, 9, 11, 13, 3), (5, 3, 3, 3, 3), (2, 1, 3), 1, 0, 1),
+    ((3, 7, 8, 5, 6), (10, 3, 3, 3, 3), (1, 2, 1), 1, 0, 2),
+    ((1, 3, 3, 3, 3), (16, 3, 3, 3, 3), 1, 1, 0, 1),
+    ((17, 3, 3, 3, 3), (7, 3, 3, 3, 3), 1, 1, 0, 1),
+]
+
+
+@pytest.mark.parametrize("case", range(len(DIRECT_CL_CASES)))
+def test_channels_last_direct_kernel_integer_exact(case):
+    xs, ws, s, d, p, g = DIRECT_CL_CASES[case]
+    desc = ch.plan_describe(xs, ws, s, d, p, g, channels_last=True)
+    assert "kernel=conv_direct16" in desc and "layout=channels_last" in desc, desc
+    r = np.random.default_rng(900 + case)
+    x, w, b = _int_inputs(r, xs, ws, bias=case % 2 == 1)
+    say(f"cl direct case {case}: x={xs} w={ws}: {desc}")
+    y = gpu_conv_cl(x, w, b, s, d, p, g)
+    np.testing.assert_array_equal(y.astype(np.float64), oracle.conv_channels_last(x, w, b, s, d, p, g))
+
+
 def test_channels_last_split_geometry_misaligned_weights_take_generic():
     """A w view 4 bytes past its allocation keeps the channel-split kernel (16-byte
     weight copies) out; results unchanged."""

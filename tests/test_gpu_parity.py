@@ -516,6 +516,32 @@ def test_kstream_specialised_kernel_integer_exact(case):
     np.testing.assert_array_equal(y.astype(np.float64), oracle.conv(x, w, b, s, d, p, g))
 
 
+# The tiny Conv3d's channel/kernel geometry (3 input channels, 3x3x3, no
+# padding) on ragged inputs: strides, 2 groups, a single output position, 16
+# output channels and a last wave with one valid position. The direct kernel
+# reads its operands from global memory, one wave per 16 positions.
+DIRECT_CASES = [
+    ((2, 3, 16, 16, 16), (8, 3, 3, 3, 3), 1, 1, 0, 1),
+    ((1, 3, 9, 11, 13), (5, 3, 3, 3, 3), (2, 1, 3), 1, 0, 1),
+    ((3, 6, 7, 8, 5), (10, 3, 3, 3, 3), (1, 2, 1), 1, 0, 2),
+    ((1, 3, 3, 3, 3), (16, 3, 3, 3, 3), 1, 1, 0, 1),
+    ((1, 3, 20, 20, 20), (16, 3, 3, 3, 3), 1, 1, 0, 1),
+    ((17, 3, 3, 3, 3), (7, 3, 3, 3, 3), 1, 1, 0, 1),
+]
+
+
+@pytest.mark.parametrize("case", range(len(DIRECT_CASES)))
+def test_direct_kernel_integer_exact(case):
+    xs, ws, s, d, p, g = DIRECT_CASES[case]
+    desc = ch.plan_describe(xs, ws, s, d, p, g)
+    assert "kernel=conv_direct16" in desc, desc
+    r = np.random.default_rng(800 + case)
+    x, w, b = _int_inputs(r, xs, ws, bias=case % 2 == 0)
+    say(f"direct case {case}: x={xs} w={ws}: {desc}")
+    y = gpu_conv(x, w, b, s, d, p, g)
+    np.testing.assert_array_equal(y.astype(np.float64), oracle.conv(x, w, b, s, d, p, g))
+
+
 def test_tap_disabled_falls_back_to_streamed(monkeypatch):
     monkeypatch.setenv("CONVHIP_TAP", "0")
     xs, ws, s, d, p, _ = TAP_CASES[0]
@@ -532,7 +558,7 @@ def test_workloads_use_expected_kernels():
     d = ch.plan_describe(cfg["x"], cfg["w"], fused=True)
     assert "kernel=fused_stream" in d, d
     for name, kernel in [("asym_conv3d", "conv_tap"), ("long_conv1d", "conv_tap"),
-                         ("general_conv3d", "conv_tap_kstream"), ("tiny_conv3d", "conv_tap_split")]:
+                         ("general_conv3d", "conv_tap_kstream"), ("tiny_conv3d", "conv_direct16")]:
         cfg = synth.WORKLOADS[name]
         d = ch.plan_describe(cfg["x"], cfg["w"], *_cfg_args(cfg)) + " "
         assert f"kernel={kernel}" in d, d
