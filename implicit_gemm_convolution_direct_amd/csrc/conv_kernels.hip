@@ -2211,7 +2211,17 @@ __global__ __launch_bounds__(512) void conv_tap_kstream_kernel(ConvArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// fused_min_softmax_mfma4
+// fused_min_softmax_mfma4: Conv3d -> min over axis 0 -> softmax over channels
+// for any geometry (the host permutes the axes for a minimum over H or W).
+// One workgroup per (64-position tile of the (axis 1, axis 2) output plane,
+// sample). The input box (every input plane the output depths read, the tile's
+// rows) and the weights arrive by LDS DMA in one round of memory latency; the
+// 4 waves share the output depths, each keeping running minima in registers.
+// Groups are native: group g's outputs reduce over its own C_in/groups input
+// channels only (no zero blocks), one group after the other. Matrix cores:
+// 4x4x1 products with the weight operand broadcast from one 4-lane block, so a
+// lane holds 4 channels of one position per product: 64 positions x 4
+// channels per instruction.
 // ---------------------------------------------------------------------------
 struct FusedArgs {
   const float* __restrict__ x;
@@ -2225,15 +2235,23 @@ struct FusedArgs {
   int D0, D1, D2;
   int P0, P1, P2;
   int O0, O1, O2;
-  int kvol, kfull, cpad;
+  int kvol;
   int mode, dspan, rows, bw, boxc, row_tiles;
+  int tile_pos;  // TILE_FLAT: consecutive output positions per tile (<= 64)
   int plane_out;
   // Element strides of x (per sample, per input channel, per spatial axis) and of
-  // w (per kernel axis), in the kernel's axis order: the minimum is always taken
-  // over axis 0, and the host permutes the axes for a minimum over H or W.
+  // w (per kernel axis), in the kernel's axis order.
   int64_t xs_n, xs_c, xs0, xs1, xs2;
   int ws0, ws1, ws2;
-  int Cg, Coutg;  // groups: input / output channels per group
+  int Cg, Coutg, groups;  // input / output channels per group, groups
+  int kg;                 // reduction length of one group: Cg * kvol
+  int kgp;                // kg rounded up to 4 (zero weights past kg)
+  int kgs;                // floats per weight row in LDS (kgp, or kgp + 4 against bank conflicts)
+  int cpadg;              // Coutg rounded up to 4: 4 * NG
+  int nrows;              // input rows of the box: Cin * dspan * rows
+  // LDS float offsets: koff (int per k), weights [group][channel][k], per-wave
+  // minima of one group (0: in the box space), merged minima (groups > 1).
+  int ko_off, wt_off, red_off, fin_off;
 };
 
 template <int A>
@@ -2248,24 +2266,21 @@ __device__ __forceinline__ void mfma4_all(float av, float bv, v4f* acc, std::int
 
 template <int NG>
 __global__ __launch_bounds__(256) void fused_min_softmax_mfma4_kernel(FusedArgs a) {
-  extern __shared__ float smem[];
+  extern __shared__ __align__(16) float smem[];
   float* Xs = smem;
-  const int box = a.Cin * a.boxc;
-  const int red_floats = 4 * a.cpad * 64;
-  const int region = max(box + 4, red_floats);
-  int* koff = reinterpret_cast<int*>(smem + region);
-  float* Wt = smem + region + a.kfull;
+  int* koff = reinterpret_cast<int*>(smem + a.ko_off);
+  float* Wt = smem + a.wt_off;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int tile = blockIdx.x;
   const int n = blockIdx.y;
 
   int oh_first, oh_last, ow0 = 0, p0 = 0;
   if (a.mode == TILE_FLAT) {
-    p0 = tile * 64;
-    const int p_last = min(p0 + 64, a.plane_out) - 1;
+    p0 = tile * a.tile_pos;
+    const int p_last = min(p0 + a.tile_pos, a.plane_out) - 1;
     oh_first = p0 / a.O2;
     oh_last = p_last / a.O2;
   } else {
@@ -2273,63 +2288,77 @@ __global__ __launch_bounds__(256) void fused_min_softmax_mfma4_kernel(FusedArgs 
     ow0 = (tile - oh_first * a.row_tiles) * 64;
   }
   const int iwb = ow0 * a.S2;
-  const int rows_needed = (oh_last - oh_first) * a.S1 + (a.K1 - 1) * a.D1 + 1;
   const int ih0 = oh_first * a.S1 - a.P1;
   const int iw0 = iwb - a.P2;
   const int plane_stride = a.rows * a.bw;
+  (void)oh_last;
 
-  for (int k = tid; k < a.kfull; k += 256) {
-    const int c = k / a.kvol;
-    const int r = k - c * a.kvol;
-    const int td = r / (a.K1 * a.K2);
-    const int r2 = r - td * a.K1 * a.K2;
-    const int th = r2 / a.K2;
-    const int tw = r2 - th * a.K2;
-    koff[k] = c * a.boxc + td * a.D0 * plane_stride + th * a.D1 * a.bw + tw * a.D2;
+  // Reduction offsets of one group's k (the group's first input channel at 0).
+  for (int k = tid; k < a.kgp; k += 256) {
+    int off = 0;
+    if (k < a.kg) {
+      const int c = k / a.kvol;
+      const int r = k - c * a.kvol;
+      const int td = r / (a.K1 * a.K2);
+      const int r2 = r - td * a.K1 * a.K2;
+      const int th = r2 / a.K2;
+      const int tw = r2 - th * a.K2;
+      off = c * a.boxc + td * a.D0 * plane_stride + th * a.D1 * a.bw + tw * a.D2;
+    }
+    koff[k] = off;
   }
-  // Weights transposed to [k][c_out] so lane c reads channel c of tap k
-  // (k = (input channel, td, th, tw) in the kernel's axis order, over all C_in
-  // input channels: with groups the matrix is block-diagonal, zero where the
-  // input channel lies outside output channel c's group).
-  for (int idx = tid; idx < a.kfull * a.cpad; idx += 256) {
-    const int c = idx / a.kfull;
-    const int k = idx - c * a.kfull;
-    const int ci = k / a.kvol, r = k - ci * a.kvol;
-    const int td = r / (a.K1 * a.K2), r2 = r - td * a.K1 * a.K2;
-    const int th = r2 / a.K2, tw = r2 - th * a.K2;
-    const int cl = ci - (c / a.Coutg) * a.Cg;  // input channel within c's group
-    const bool in_group = c < a.Cout && cl >= 0 && cl < a.Cg;
-    Wt[k * a.cpad + c] =
-        in_group ? a.w[int64_t(c) * a.Cg * a.kvol + cl * a.kvol + td * a.ws0 + th * a.ws1 + tw * a.ws2] : 0.0f;
-  }
-  // Input box: all input planes the output depths read, rows of this tile.
-  const int rows_per_c = a.dspan * rows_needed;
-  const int nrows = a.Cin * rows_per_c;
+
+  // Box rows [channel][plane][row], one DMA per row and 64 columns; wave w
+  // takes rows w, w+4, ... (row coordinates kept in scalar counters). No LDS
+  // read while the copies are in flight.
   const float* x_n = a.x + int64_t(n) * a.xs_n;
-  for (int r = wave; r < nrows; r += 4) {
-    const int c = r / rows_per_c;
-    const int rem = r - c * rows_per_c;
-    const int zd = rem / rows_needed;
-    const int zr = rem - zd * rows_needed;
-    const int id = zd - a.P0;
-    const int ih = ih0 + zr;
-    const bool rv = (id >= 0) && (id < a.L0) && (ih >= 0) && (ih < a.L1);
-    const float* src = x_n + c * a.xs_c + (rv ? id : 0) * a.xs0 + (rv ? ih : 0) * a.xs1;
-    float* dst = Xs + c * a.boxc + zd * plane_stride + zr * a.bw;
-    for (int col = lane; col < a.bw; col += 64) {
-      const int iw = iw0 + col;
-      float v = 0.0f;
-      if (rv && iw >= 0 && iw < a.L2) v = src[iw * a.xs2];
-      dst[col] = v;
+  {
+    int c = 0, zd = 0, zr = wave;
+    while (zr >= a.rows) { zr -= a.rows; zd++; }
+    for (int r = wave; r < a.nrows; r += 4) {
+      while (zd >= a.dspan) { zd -= a.dspan; c++; }
+      const int id = zd - a.P0;
+      const int ih = ih0 + zr;
+      const bool rv = (id >= 0) && (id < a.L0) && (ih >= 0) && (ih < a.L1);
+      const float* src_row = x_n + c * a.xs_c + int64_t(rv ? id : 0) * a.xs0 + int64_t(rv ? ih : 0) * a.xs1;
+      for (int col0 = 0; col0 < a.bw; col0 += 64) {
+        const int col = col0 + lane;
+        const int iw = iw0 + col;
+        if (col < a.bw) {
+          const bool ok = rv && iw >= 0 && iw < a.L2;
+          lds_dma_f32(ok ? src_row + iw * a.xs2 : kZeroWord, Xs + r * a.bw + col0);
+        }
+      }
+      zr += 4;
+      while (zr >= a.rows) { zr -= a.rows; zd++; }
     }
   }
+  // Weights [group][channel][k], rows of kgs floats; zero past kg and Coutg.
+  const int w_total = a.groups * a.cpadg * a.kgs;
+  const float inv_kgs = 1.0f / float(a.kgs), inv_cpadg = 1.0f / float(a.cpadg), inv_kvol = 1.0f / float(a.kvol);
+  const float inv_k12 = 1.0f / float(a.K1 * a.K2), inv_k2 = 1.0f / float(a.K2);
+  for (int i = wave; i * 64 < w_total; i += 4) {
+    const int e = i * 64 + lane;
+    if (e < w_total) {
+      int k, c, cl, r, r2, th, tw;
+      const int gc = divmod_small(e, a.kgs, inv_kgs, k);
+      const int g = divmod_small(gc, a.cpadg, inv_cpadg, c);
+      const bool ok = c < a.Coutg && k < a.kg;
+      cl = divmod_small(ok ? k : 0, a.kvol, inv_kvol, r);
+      const int td = divmod_small(r, a.K1 * a.K2, inv_k12, r2);
+      th = divmod_small(r2, a.K2, inv_k2, tw);
+      const float* src = a.w + (int64_t(g * a.Coutg + c) * a.Cg + cl) * a.kvol + td * a.ws0 + th * a.ws1 + tw * a.ws2;
+      lds_dma_f32(ok ? src : kZeroWord, Wt + i * 64);
+    }
+  }
+  wait_vmem_le<0>();
   __syncthreads();
 
-  // This lane's output column.
+  // This lane's output position.
   int oh, ow, valid;
   if (a.mode == TILE_FLAT) {
     const int p = p0 + lane;
-    valid = p < a.plane_out;
+    valid = lane < a.tile_pos && p < a.plane_out;
     oh = p / a.O2;
     ow = p - oh * a.O2;
   } else {
@@ -2338,66 +2367,126 @@ __global__ __launch_bounds__(256) void fused_min_softmax_mfma4_kernel(FusedArgs 
     valid = ow < a.O2;
   }
   const int noff = valid ? (oh - oh_first) * a.S1 * a.bw + ow * a.S2 - iwb : 0;
-  const int wlane = min(lane, a.cpad - 1);
+  const int wlane = min(lane, a.cpadg - 1);
+  const int nq = a.kgp >> 2;
+  const int4* koff4 = reinterpret_cast<const int4*>(koff);
+  const bool red_overlaps_box = a.red_off == 0;
+  float* red = smem + a.red_off;
+  float* fin = smem + a.fin_off;
+  const int64_t out_plane = int64_t(a.O1) * a.O2;
+  float* yp = a.y + int64_t(n) * a.Cout * out_plane + int64_t(oh) * a.O2 + ow;
 
-  v4f mn[NG];
+  for (int g = 0; g < a.groups; g++) {
+    const float4* wrow = reinterpret_cast<const float4*>(Wt + (g * a.cpadg + wlane) * a.kgs);
+    const float* xg = Xs + g * a.Cg * a.boxc + noff;
+    v4f mn[NG];
 #pragma unroll
-  for (int i = 0; i < NG; i++) mn[i] = v4f{INFINITY, INFINITY, INFINITY, INFINITY};
-
-  for (int od = wave; od < a.O0; od += 4) {
-    const int base = od * a.S0 * plane_stride + noff;
-    v4f acc[NG];
+    for (int i = 0; i < NG; i++) mn[i] = v4f{INFINITY, INFINITY, INFINITY, INFINITY};
+    for (int od = wave; od < a.O0; od += 4) {
+      const float* xb = xg + od * a.S0 * plane_stride;
+      v4f acc[NG];
 #pragma unroll
-    for (int i = 0; i < NG; i++) acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
-    for (int k = 0; k < a.kfull; k++) {
-      const float bv = Xs[koff[k] + base];
-      const float av = Wt[k * a.cpad + wlane];
-      mfma4_all<NG>(av, bv, acc, std::make_integer_sequence<int, NG>{});
+      for (int i = 0; i < NG; i++) acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
+      // Software pipeline over k-quads, unrolled by two with operand sets A
+      // (even quads) and B (odd quads): a set's LDS reads are issued while the
+      // other set feeds the products, offsets one quad further ahead. Indices
+      // past the last quad are clamped (in-bounds reads, never used).
+      const int last = nq - 1;
+      int4 koA = koff4[0];
+      int4 koB = koff4[min(1, last)];
+      float4 wA = wrow[0];
+      float a0 = xb[koA.x], a1 = xb[koA.y], a2 = xb[koA.z], a3 = xb[koA.w];
+      koA = koff4[min(2, last)];
+      asm volatile("" ::: "memory");
+      for (int q = 0; q < nq; q += 2) {
+        const float4 wB = wrow[min(q + 1, last)];
+        const float c0 = xb[koB.x], c1 = xb[koB.y], c2 = xb[koB.z], c3 = xb[koB.w];
+        koB = koff4[min(q + 3, last)];
+        mfma4_all<NG>(wA.x, a0, acc, std::make_integer_sequence<int, NG>{});
+        mfma4_all<NG>(wA.y, a1, acc, std::make_integer_sequence<int, NG>{});
+        mfma4_all<NG>(wA.z, a2, acc, std::make_integer_sequence<int, NG>{});
+        mfma4_all<NG>(wA.w, a3, acc, std::make_integer_sequence<int, NG>{});
+        __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 4 * NG, 0);
+        asm volatile("" ::: "memory");
+        if (q + 1 < nq) {
+          wA = wrow[min(q + 2, last)];
+          a0 = xb[koA.x]; a1 = xb[koA.y]; a2 = xb[koA.z]; a3 = xb[koA.w];
+          koA = koff4[min(q + 4, last)];
+          mfma4_all<NG>(wB.x, c0, acc, std::make_integer_sequence<int, NG>{});
+          mfma4_all<NG>(wB.y, c1, acc, std::make_integer_sequence<int, NG>{});
+          mfma4_all<NG>(wB.z, c2, acc, std::make_integer_sequence<int, NG>{});
+          mfma4_all<NG>(wB.w, c3, acc, std::make_integer_sequence<int, NG>{});
+          __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 4 * NG, 0);
+        }
+        asm volatile("" ::: "memory");
+      }
+#pragma unroll
+      for (int i = 0; i < NG; i++) {
+        mn[i][0] = fminf(mn[i][0], acc[i][0]);
+        mn[i][1] = fminf(mn[i][1], acc[i][1]);
+        mn[i][2] = fminf(mn[i][2], acc[i][2]);
+        mn[i][3] = fminf(mn[i][3], acc[i][3]);
+      }
     }
+    // Merge the four waves' minima of this group through LDS.
+    if (red_overlaps_box) __syncthreads();  // the box is read for the last time above
 #pragma unroll
-    for (int i = 0; i < NG; i++) {
-      mn[i][0] = fminf(mn[i][0], acc[i][0]);
-      mn[i][1] = fminf(mn[i][1], acc[i][1]);
-      mn[i][2] = fminf(mn[i][2], acc[i][2]);
-      mn[i][3] = fminf(mn[i][3], acc[i][3]);
+    for (int i = 0; i < NG; i++)
+#pragma unroll
+      for (int r = 0; r < 4; r++) red[(wave * a.cpadg + 4 * i + r) * 64 + lane] = mn[i][r];
+    __syncthreads();
+    if (a.groups == 1) {
+      // One group: wave 0 merges and normalises in registers.
+      if (wave == 0 && valid) {
+        float m[4 * NG];
+#pragma unroll
+        for (int c = 0; c < 4 * NG; c++) {
+          float v = red[c * 64 + lane];
+          v = fminf(v, red[(a.cpadg + c) * 64 + lane]);
+          v = fminf(v, red[(2 * a.cpadg + c) * 64 + lane]);
+          v = fminf(v, red[(3 * a.cpadg + c) * 64 + lane]);
+          // fp32 addition is monotone, so min(v_i) + b == min(v_i + b) exactly.
+          m[c] = (c < a.Cout) ? v + (a.bias ? a.bias[c] : 0.0f) : -INFINITY;
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int c = 0; c < 4 * NG; c++) mx = fmaxf(mx, m[c]);
+        float sum = 0.0f;
+#pragma unroll
+        for (int c = 0; c < 4 * NG; c++) {
+          const float e = (c < a.Cout) ? expf(m[c] - mx) : 0.0f;
+          m[c] = e;
+          sum += e;
+        }
+        const float inv_den = 1.0f / sum;
+#pragma unroll
+        for (int c = 0; c < 4 * NG; c++)
+          if (c < a.Cout) yp[int64_t(c) * out_plane] = m[c] * inv_den;
+      }
+      return;
     }
-  }
-
-  // Merge the four waves' minima through LDS (the box is no longer needed).
-  __syncthreads();
-  float* red = smem;
-#pragma unroll
-  for (int i = 0; i < NG; i++)
-#pragma unroll
-    for (int r = 0; r < 4; r++) red[(wave * a.cpad + 4 * i + r) * 64 + lane] = mn[i][r];
-  __syncthreads();
-  if (wave == 0 && valid) {
-    float m[4 * NG];
-#pragma unroll
-    for (int c = 0; c < 4 * NG; c++) {
+    // Several groups: the waves merge a quarter of the group's channels each
+    // into fin[channel][position], then free red for the next group.
+    for (int c = wave; c < a.Coutg; c += 4) {
       float v = red[c * 64 + lane];
-      v = fminf(v, red[(a.cpad + c) * 64 + lane]);
-      v = fminf(v, red[(2 * a.cpad + c) * 64 + lane]);
-      v = fminf(v, red[(3 * a.cpad + c) * 64 + lane]);
-      // fp32 addition is monotone, so min(v_i) + b == min(v_i + b) exactly.
-      m[c] = (c < a.Cout) ? v + (a.bias ? a.bias[c] : 0.0f) : -INFINITY;
+      v = fminf(v, red[(a.cpadg + c) * 64 + lane]);
+      v = fminf(v, red[(2 * a.cpadg + c) * 64 + lane]);
+      v = fminf(v, red[(3 * a.cpadg + c) * 64 + lane]);
+      const int co = g * a.Coutg + c;
+      fin[co * 64 + lane] = v + (a.bias ? a.bias[co] : 0.0f);
     }
+    __syncthreads();
+  }
+  // Softmax over all channels, in channel order (wave 0, one lane per position).
+  if (wave == 0 && valid) {
     float mx = -INFINITY;
-#pragma unroll
-    for (int c = 0; c < 4 * NG; c++) mx = fmaxf(mx, m[c]);
+    for (int c = 0; c < a.Cout; c++) mx = fmaxf(mx, fin[c * 64 + lane]);
     float sum = 0.0f;
-#pragma unroll
-    for (int c = 0; c < 4 * NG; c++) {
-      const float e = (c < a.Cout) ? expf(m[c] - mx) : 0.0f;
-      m[c] = e;
-      sum += e;
-    }
+    for (int c = 0; c < a.Cout; c++) sum += expf(fin[c * 64 + lane] - mx);
     const float inv_den = 1.0f / sum;
-    const int64_t out_plane = int64_t(a.O1) * a.O2;
-    float* yp = a.y + int64_t(n) * a.Cout * out_plane + int64_t(oh) * a.O2 + ow;
-#pragma unroll
-    for (int c = 0; c < 4 * NG; c++)
-      if (c < a.Cout) yp[int64_t(c) * out_plane] = m[c] * inv_den;
+    for (int c = 0; c < a.Cout; c++) yp[int64_t(c) * out_plane] = expf(fin[c * 64 + lane] - mx) * inv_den;
   }
 }
 
@@ -3220,7 +3309,7 @@ int conv3d_min_softmax(const float* x, const int64_t* x_shape, const float* w, c
   a.D0 = int(g.Dl[0]); a.D1 = int(g.Dl[1]); a.D2 = int(g.Dl[2]);
   a.P0 = int(g.P[0]); a.P1 = int(g.P[1]); a.P2 = int(g.P[2]);
   a.O0 = int(g.O[0]); a.O1 = int(g.O[1]); a.O2 = int(g.O[2]);
-  a.kvol = int(g.kvol()); a.kfull = p.kfull; a.cpad = p.cpad;
+  a.kvol = int(g.kvol());
   a.mode = p.mode; a.dspan = p.dspan; a.rows = p.rows; a.bw = p.bw; a.boxc = p.boxc; a.row_tiles = p.row_tiles;
   a.plane_out = int(g.plane_out());
   a.xs_c = g0.L[0] * g0.L[1] * g0.L[2];
@@ -3233,6 +3322,11 @@ int conv3d_min_softmax(const float* x, const int64_t* x_shape, const float* w, c
   a.ws2 = int(wst[perm[2]]);
   a.Cg = int(g.Cg);
   a.Coutg = int(g.Coutg);
+  a.groups = int(g.G);
+  a.kg = p.kg; a.kgp = p.kgp; a.kgs = p.kgs; a.cpadg = p.cpad;
+  a.tile_pos = p.tile_pos;
+  a.nrows = p.nrows;
+  a.ko_off = p.ko_off; a.wt_off = p.wt_off; a.red_off = p.red_off; a.fin_off = p.fin_off;
   switch (p.ng) {
     case 1: return launch_fused_ng<1>(a, p, s);
     case 2: return launch_fused_ng<2>(a, p, s);

@@ -638,19 +638,54 @@ int plan_fused(const Geom& g, int min_dim, FusedPlan* out, bool allow_spec) {
       if (plan_fused_stream(g, specs[i], out)) return CONV_OK;
   }
   FusedPlan p;
-  p.cpad = int((g.Cout + 3) / 4 * 4);
+  p.cpad = int((g.Coutg + 3) / 4 * 4);
   p.ng = p.cpad / 4;
   const int BN = 64;
   p.mode = (g.O[2] * 2 <= BN) ? TILE_FLAT : TILE_ROW;
   box_dims(g, p.mode, BN, &p.rows, &p.bw, &p.tiles_per_plane, &p.row_tiles);
+  if (p.mode == TILE_FLAT && (BN / g.O[2]) * g.O[2] * 8 >= BN * 7) {
+    // Tiles of whole output rows when they fill at least 7/8 of the lanes: the
+    // box then holds exactly the rows those outputs read (64 consecutive
+    // positions can straddle one more row), so more workgroups fit a unit.
+    const int64_t r = BN / g.O[2];
+    p.tile_pos = int(r * g.O[2]);
+    p.rows = int((r - 1) * g.S[1] + (g.K[1] - 1) * g.Dl[1] + 1);
+    p.tiles_per_plane = ceil_div(g.O[1], r);
+  }
   p.dspan = int((g.O[0] - 1) * g.S[0] + (g.K[0] - 1) * g.Dl[0] + 1);
   const int64_t boxc = int64_t(p.dspan) * p.rows * p.bw;
   p.kfull = int(g.Cin * g.kvol());
+  p.kg = int(g.Cg * g.kvol());
+  p.kgp = (p.kg + 3) / 4 * 4;
+  // Weight rows of an odd number of 16-byte quads: the lanes' 16-byte reads of
+  // one k-quad fall in distinct banks.
+  p.kgs = ((p.kgp / 4) % 2 == 1) ? p.kgp : p.kgp + 4;
+  const int64_t nrows = g.Cin * int64_t(p.dspan) * p.rows;
   const int64_t box = g.Cin * boxc;
-  const int64_t red = 4 * int64_t(p.cpad) * 64;  // per-wave minima, reuses the box space
-  const int64_t region = std::max(box + 4, red);
-  p.lds_bytes = 4 * (region + p.kfull + int64_t(p.kfull) * p.cpad);
-  if (p.lds_bytes > kLdsLimit || boxc > (int64_t(1) << 28)) return CONV_ERR_UNSUPPORTED;
+  const int64_t red = 4 * int64_t(p.cpad) * 64;  // per-wave minima of one group
+  // One group: the minima reuse the box space once it is read for the last time.
+  const int64_t region = g.G == 1 ? std::max(box, red) : box;
+  int64_t off = (region + 3) / 4 * 4;
+  const int64_t ko_off = off;
+  off += p.kgp;
+  off = (off + 3) / 4 * 4;
+  const int64_t wt_off = off;
+  off += g.G * int64_t(p.cpad) * p.kgs;
+  int64_t red_off = 0, fin_off = 0;
+  if (g.G > 1) {
+    red_off = off;
+    off += red;
+    fin_off = off;
+    off += g.Cout * 64;
+  }
+  p.lds_bytes = 4 * off;
+  if (p.lds_bytes > kLdsLimit || boxc > (int64_t(1) << 28))
+    return CONV_ERR_UNSUPPORTED;
+  p.nrows = int(nrows);
+  p.ko_off = int(ko_off);
+  p.wt_off = int(wt_off);
+  p.red_off = int(red_off);
+  p.fin_off = int(fin_off);
   p.boxc = int(boxc);
   p.grid[0] = p.tiles_per_plane;
   p.grid[1] = g.N;
@@ -714,12 +749,17 @@ std::string describe(const Geom& g, const FusedPlan& p) {
                   (long long)g.macs());
     return buf;
   }
+  // Multiply-adds the matrix cores perform: every tile's 64 positions, every
+  // output depth, each group's channels rounded up to 4, over the group's
+  // reduction rounded up to 4 (no products across groups).
+  const int64_t issued = int64_t(p.grid[0]) * p.grid[1] * 64 * g.O[0] * g.G * p.cpad * p.kgp;
   std::snprintf(buf, sizeof buf,
-                "kernel=fused_min_softmax_mfma4 ng=%d cpad=%d mode=%s box=%dx%dx%dx%d grid=%lldx%lldx%lld "
-                "lds=%lld macs=%lld",
-                p.ng, p.cpad, p.mode == TILE_FLAT ? "flat" : "row", int(g.Cin), p.dspan, p.rows, p.bw,
-                (long long)p.grid[0], (long long)p.grid[1], (long long)p.grid[2], (long long)p.lds_bytes,
-                (long long)g.macs());
+                "kernel=fused_min_softmax_mfma4 ng=%d cpad=%d groups=%lld kred=%d mode=%s tile=%d box=%dx%dx%dx%d "
+                "grid=%lldx%lldx%lld lds=%lld macs=%lld issued=%lld",
+                p.ng, p.cpad, (long long)g.G, p.kg, p.mode == TILE_FLAT ? "flat" : "row",
+                p.mode == TILE_FLAT ? p.tile_pos : 64, int(g.Cin), p.dspan, p.rows,
+                p.bw, (long long)p.grid[0], (long long)p.grid[1], (long long)p.grid[2], (long long)p.lds_bytes,
+                (long long)g.macs(), (long long)issued);
   return buf;
 }
 

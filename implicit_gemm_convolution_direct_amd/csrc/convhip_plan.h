@@ -228,12 +228,17 @@ struct FusedPlan {
   int spec = -1;       // >= 0: depth-streamed specialisation (one wave per 64 positions)
   int dsplit = 1;      // streamed: waves sharing the output depths of one 64-position tile
   int64_t units = 0;   // streamed: N * tiles_per_plane * dsplit waves
-  int ng = 0;          // channel groups of 4 handled by one lane
-  int cpad = 0;        // C_out rounded up to 4
+  int ng = 0;          // blocks of 4 output channels handled by one lane (per group)
+  int cpad = 0;        // output channels per group rounded up to 4
   int mode = TILE_FLAT;
   int dspan = 0;       // input planes staged: (D_out-1)*sD + (kD-1)*dD + 1
   int rows = 0, bw = 0, boxc = 0;
   int kfull = 0;       // C_in * kvol
+  // Generic kernel: reduction of one group (C_in/groups * kvol), rounded up to 4,
+  // LDS weight row pitch; box rows; LDS float offsets of its regions.
+  int kg = 0, kgp = 0, kgs = 0, nrows = 0;
+  int tile_pos = 64;   // generic kernel, TILE_FLAT: output positions per tile
+  int ko_off = 0, wt_off = 0, red_off = 0, fin_off = 0;
   int64_t tiles_per_plane = 0;
   int row_tiles = 0;
   int64_t grid[3] = {0, 0, 0};

@@ -147,6 +147,23 @@ def test_direct_kernel_plans():
             assert fields["grid"] == f"{(n_pos + 15) // 16}x{g}x1" and fields["lds"] == "0", desc
 
 
+def test_fused_generic_groups_are_native():
+    """Grouped fused calls reduce over C_in/groups input channels per output
+    channel: the multiply-adds issued exceed the algorithmic count only by the
+    padding of positions to 64, of each group's channels to 4 and of its
+    reduction to 4, never by the number of groups."""
+    xs = (128, 3, 24, 32, 32)
+    for ws, g, kred in [((24, 3, 3, 3, 3), 1, 81), ((24, 1, 3, 3, 3), 3, 27), ((12, 1, 3, 3, 3), 3, 27),
+                        ((6, 2, 3, 3, 3), 3, 54)]:
+        xg = (xs[0], ws[1] * g) + xs[2:]
+        desc = ch.plan_describe(xg, ws, 1, 1, 0, g, fused=True, min_dim=3)
+        f = dict(t.split("=", 1) for t in desc.split() if "=" in t)
+        assert f["kernel"] == "fused_min_softmax_mfma4" and int(f["groups"]) == g and int(f["kred"]) == kred, desc
+        coutg = ws[0] // g
+        pad = (960 / 900) * (((kred + 3) // 4 * 4) / kred) * (((coutg + 3) // 4 * 4) / coutg)
+        assert int(f["issued"]) == pytest.approx(int(f["macs"]) * pad, rel=1e-9), desc
+
+
 def test_conv3d_min_softmax_validation_errors():
     lib = ch.lib()
     xs, ws = I64(2, 3, 6, 6, 6), I64(5, 3, 3, 3, 3)

@@ -303,7 +303,8 @@ GROUPED_FUSED_CASES = [
 
 @pytest.mark.parametrize("case", GROUPED_FUSED_CASES, ids=[c[0] for c in GROUPED_FUSED_CASES])
 def test_fused_grouped(case):
-    """Grouped convolutions in the fused op (block-diagonal weights)."""
+    """Grouped convolutions in the fused op: each group reduces over its own
+    input channels only."""
     name, xs, ws, s, d, p, g, md = case
     r = np.random.default_rng(1700 + len(name))
     x, w, b = _float_inputs(r, xs, ws, True)
@@ -311,6 +312,21 @@ def test_fused_grouped(case):
     ref = oracle.conv3d_min_softmax(x, w, b, s, d, p, g, md)
     err = float(np.abs(y - ref).max())
     say(f"  {name}: max|err| = {err:.3e}")
+    assert err <= FUSED_ATOL
+
+
+def test_fused_grouped_workload_slice():
+    """The fused workload's shape with groups 3 (w [24, 1, 3, 3, 3]) on a
+    two-sample slice, against the oracle."""
+    cfg = synth.VARIANTS["conv3d_min_softmax_groups3"]
+    x, w, b = synth.make_inputs("conv3d_min_softmax_groups3", n_samples=2, sample_start=5)
+    desc = ch.plan_describe(x.shape, w.shape, 1, 1, 0, cfg["groups"], fused=True)
+    assert "groups=3 kred=27" in desc, desc
+    say(f"fused groups3 slice: {desc}")
+    y = gpu_fused(x, w, b, 1, 1, 0, cfg["groups"], 2)
+    ref = oracle.conv3d_min_softmax(x, w, b, 1, 1, 0, cfg["groups"], 2)
+    err = float(np.abs(y - ref).max())
+    say(f"  max|err| = {err:.3e}")
     assert err <= FUSED_ATOL
 
 
