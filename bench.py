@@ -389,6 +389,9 @@ def main():
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device-to-device copy of this many bytes per step "
                          "(calibrates rocprofv3's FETCH_SIZE / WRITE_SIZE against a known traffic)")
+    ap.add_argument("--calibrate-only", action="store_true",
+                    help="only run the calibration probes (matrix-core and vector-FMA throughput, copy bandwidth) "
+                         "and print their rates; for collecting counters on the probes")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path (the convolution "
@@ -405,6 +408,9 @@ def main():
         sys.exit(1)
     ch.lib()
 
+    if args.calibrate_only:
+        print(json.dumps({"calibration": calibrate(torch, ch)}), flush=True)
+        return
     if args.copy_bytes:
         n = args.copy_bytes // 4
         src = torch.ones(n, dtype=torch.float32, device="cuda:0")

@@ -465,6 +465,16 @@ __device__ __forceinline__ void load_bias(const ConvArgs& a, const TileGeo& t, i
     }
 }
 
+// Channels-last output stores carry the non-temporal hint. A channels-last
+// kernel reads each input site's channels in several chunks, one after the
+// other; the output it writes meanwhile (as large as the input for the long
+// Conv1d) would otherwise push those sites' lines out of L2 before the later
+// chunks read them. Channels-first outputs keep plain stores: their tiles
+// reuse input through L2 within a shorter window, and non-temporal stores
+// there add write traffic.
+__device__ __forceinline__ void store_nt(float* p, float v) { __builtin_nontemporal_store(v, p); }
+__device__ __forceinline__ void store_nt4(float* p, v4f v) { __builtin_nontemporal_store(v, reinterpret_cast<v4f*>(p)); }
+
 // Store a wave tile (+ bias). D[m][n] of the matrix core sits in lane
 // n + 16*(m/4), register m%4: a lane holds 4 consecutive channels of one
 // position, which channels-last output y [N, D_out, H_out, W_out, C_out] takes
@@ -484,12 +494,12 @@ __device__ __forceinline__ void store_tile(const ConvArgs& a, const TileGeo& t, 
         if (pidx[ni] < 0 || ch0 >= a.Coutg) continue;
         float* yp = yplane + int64_t(pidx[ni]) * a.Cout + ch0;
         if (a.vec_store) {
-          *reinterpret_cast<float4*>(yp) = make_float4(acc[mi][ni][0] + bias[mi][0], acc[mi][ni][1] + bias[mi][1],
-                                                       acc[mi][ni][2] + bias[mi][2], acc[mi][ni][3] + bias[mi][3]);
+          store_nt4(yp, v4f{acc[mi][ni][0] + bias[mi][0], acc[mi][ni][1] + bias[mi][1], acc[mi][ni][2] + bias[mi][2],
+                            acc[mi][ni][3] + bias[mi][3]});
         } else {
 #pragma unroll
           for (int r = 0; r < 4; r++)
-            if (ch0 + r < a.Coutg) yp[r] = acc[mi][ni][r] + bias[mi][r];
+            if (ch0 + r < a.Coutg) store_nt(yp + r, acc[mi][ni][r] + bias[mi][r]);
         }
       }
     }
@@ -886,8 +896,18 @@ __global__ __launch_bounds__(64 * WM * WN) void conv_tap_kernel(ConvArgs a) {
   const int kg = lane >> 4;
   const int li = lane & 15;
 
-  int item = blockIdx.x;
-  if (item >= a.items) return;
+  // Workgroups are dispatched round-robin over the 8 XCDs. Each XCD takes a
+  // contiguous eighth of the items and its workgroups stride through it, so
+  // the items in flight on one XCD are neighbours (the same tile of adjacent
+  // output depths, adjacent tiles) whose input rows its L2 serves once.
+  int item = blockIdx.x, item_step = gridDim.x, item_end = a.items;
+  if ((gridDim.x & 7) == 0) {
+    const int xcd = blockIdx.x & 7;
+    item_step = gridDim.x >> 3;
+    item = int(int64_t(a.items) * xcd / 8) + (blockIdx.x >> 3);
+    item_end = int(int64_t(a.items) * (xcd + 1) / 8);
+  }
+  if (item >= item_end) return;
 #pragma unroll
   for (int c = 0; c < NCH; c++)
     stage_wfrag<MT, WM, NWAVES, G::TAPMAJOR>(a, 0, 0, c * G::CCH, G::NS, Wres + c * G::NS * SSTRIDE, wave, lane);
@@ -918,8 +938,8 @@ __global__ __launch_bounds__(64 * WM * WN) void conv_tap_kernel(ConvArgs a) {
     for (int q = 0; q < NP; q++)
 #pragma unroll
       for (int ni = 0; ni < NT; ni++) addr[q][ni] = 4 * (noff[ni] + dpat[q]);
-    const int next_item = item + gridDim.x;
-    const bool more = next_item < a.items;
+    const int next_item = item + item_step;
+    const bool more = next_item < item_end;
     TileGeo tn = t;
     if (more) tn = tile_geo(a, next_item % a.tiles_per_plane, next_item / a.tiles_per_plane, 0, BM, BN, true);
 #pragma unroll
