@@ -1944,7 +1944,7 @@ struct KsSchedule {
   }
 };
 
-template <class G>
+template <class G, bool CL>
 __global__ __launch_bounds__(512) void conv_tap_kstream_kernel(ConvArgs a) {
   constexpr KsPatterns<G> P{};
   constexpr KsSchedule<G> SC{};
@@ -1970,9 +1970,10 @@ __global__ __launch_bounds__(512) void conv_tap_kstream_kernel(ConvArgs a) {
   int L0 = a.L0, L1 = a.L1, L2 = a.L2, S0 = a.S0, S1 = a.S1, S2 = a.S2, D0 = a.D0;
   int P0 = a.P0, P1 = a.P1, P2 = a.P2, O0 = a.O0, O1 = a.O1, O2 = a.O2, plane_out = a.plane_out;
   int nitems = gridDim.x;
+  int vec_store = a.vec_store;
   asm volatile("" : "+s"(xg), "+s"(wgl), "+s"(bg), "+s"(yglob), "+s"(Cin), "+s"(Cout), "+s"(Cg), "+s"(Coutg),
                "+s"(L0), "+s"(L1), "+s"(L2), "+s"(S0), "+s"(S1), "+s"(S2), "+s"(D0), "+s"(P0), "+s"(P1), "+s"(P2),
-               "+s"(O0), "+s"(O1), "+s"(O2), "+s"(plane_out), "+s"(nitems));
+               "+s"(O0), "+s"(O1), "+s"(O2), "+s"(plane_out), "+s"(nitems), "+s"(vec_store));
   // Workgroups are dispatched round-robin over the 8 XCDs: give each XCD a
   // contiguous run of (plane, group) items, so the input planes that
   // neighbouring output depths share stay in that XCD's L2.
@@ -1990,10 +1991,15 @@ __global__ __launch_bounds__(512) void conv_tap_kstream_kernel(ConvArgs a) {
     // Copy sources. Plane element e = zr * BW + j <- input row zr - P1, column
     // F*j - P2 of the plane's channel and depth; copy wave w's copy i of a plane
     // moves elements (4i + w) * 64 + lane, the same in-plane offsets for every plane.
+    // Channels-last input: sites C_in floats apart, a channel at its offset in the site.
     float* dummy = smem + G::DUMMY;
     const int64_t plane_in = int64_t(L1) * L2;
     const int64_t vol_in = int64_t(L0) * plane_in;
-    const float* xg0 = xg + (int64_t(n) * Cin + int64_t(g) * Cg) * vol_in;
+    const float* xg0 = CL ? xg + int64_t(n) * vol_in * Cin + int64_t(g) * Cg
+                          : xg + (int64_t(n) * Cin + int64_t(g) * Cg) * vol_in;
+    const int64_t c_step = CL ? 1 : vol_in;                      // next channel
+    const int64_t d_step = CL ? plane_in * Cin : plane_in;       // next input depth
+    const int site = CL ? Cin : 1;
     const int id0 = od * S0 - P0;
     int soff[G::PIW];
     uint32_t sok = 0;
@@ -2003,7 +2009,7 @@ __global__ __launch_bounds__(512) void conv_tap_kstream_kernel(ConvArgs a) {
       const int zr = e / G::BWC, j = e - zr * G::BWC;
       const int ih = zr - P1, iw = G::FF * j - P2;
       const bool ok = e < G::PLANE && unsigned(ih) < unsigned(L1) && unsigned(iw) < unsigned(L2);
-      soff[i] = ok ? ih * L2 + iw : 0;
+      soff[i] = ok ? (ih * L2 + iw) * site : 0;
       sok |= uint32_t(ok) << i;
     }
     const float* wg = wgl + int64_t(g) * Coutg * G::K;
@@ -2014,7 +2020,7 @@ __global__ __launch_bounds__(512) void conv_tap_kstream_kernel(ConvArgs a) {
         constexpr int c = p / G::KDC, td = p % G::KDC;
         const int id = id0 + td * D0;
         const bool dok = unsigned(id) < unsigned(L0);
-        const float* pl = xg0 + int64_t(c) * vol_in + int64_t(id) * plane_in;
+        const float* pl = xg0 + c * c_step + int64_t(id) * d_step;
 #pragma unroll
         for (int i = 0; i < G::PIW; i++) {
           const int ii = 4 * i + wave;  // copy instruction of the plane (wave-uniform)
@@ -2196,17 +2202,33 @@ __global__ __launch_bounds__(512) void conv_tap_kstream_kernel(ConvArgs a) {
     __builtin_amdgcn_sched_barrier(0);
   });
 
-  // Output: channel 4kg + r, position 16t + li of the (n, g*Coutg + ch, od) plane.
+  // Output: channel 4kg + r, position 16t + li of the (n, g*Coutg + ch, od)
+  // plane; channels-last: of site (n, od, position), 4 consecutive channels.
   const int64_t out_plane = int64_t(O1) * O2;
-  float* yg = yglob + (int64_t(n) * Cout + int64_t(g) * Coutg) * O0 * out_plane + int64_t(od) * out_plane;
-  const int64_t ch_stride = int64_t(O0) * out_plane;
+  float* yg = CL ? yglob + (int64_t(n) * O0 + od) * out_plane * Cout + int64_t(g) * Coutg
+                 : yglob + (int64_t(n) * Cout + int64_t(g) * Coutg) * O0 * out_plane + int64_t(od) * out_plane;
+  const int64_t ch_stride = CL ? 1 : int64_t(O0) * out_plane;
+  const int64_t p_stride = CL ? Cout : 1;
 #pragma unroll
   for (int i = 0; i < G::FT; i++) {
     const int p = 16 * (wave * G::FT + i) + li;
+    if constexpr (CL) {
+      if (p < plane_out) {
+        float* yp = yg + p * p_stride + 4 * kg;
+        if (vec_store && 4 * kg + 4 <= Coutg) {
+          store_nt4(yp, v4f{acc[i][0] + b4[0], acc[i][1] + b4[1], acc[i][2] + b4[2], acc[i][3] + b4[3]});
+        } else {
 #pragma unroll
-    for (int r = 0; r < 4; r++) {
-      const int ch = 4 * kg + r;
-      if (ch < Coutg && p < plane_out) yg[ch * ch_stride + p] = acc[i][r] + b4[r];
+          for (int r = 0; r < 4; r++)
+            if (4 * kg + r < Coutg) store_nt(yp + r, acc[i][r] + b4[r]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+        const int ch = 4 * kg + r;
+        if (ch < Coutg && p < plane_out) yg[ch * ch_stride + p] = acc[i][r] + b4[r];
+      }
     }
   }
   if constexpr (G::R > 0) {
@@ -2225,7 +2247,10 @@ __global__ __launch_bounds__(512) void conv_tap_kstream_kernel(ConvArgs a) {
 #pragma unroll
       for (int w2 = 0; w2 < 4; w2++) v += red[((w2 * G::R + r) * 64 + lane) * 4 + wave];
       const int p = 16 * (4 * G::FT + r) + li;
-      if (ch < Coutg && p < plane_out) yg[ch * ch_stride + p] = v + bw_;
+      if (ch < Coutg && p < plane_out) {
+        if constexpr (CL) store_nt(yg + p * p_stride + ch, v + bw_);
+        else yg[ch * ch_stride + p] = v + bw_;
+      }
     }
   }
 }
@@ -2992,20 +3017,21 @@ static int launch_split_spec(const ConvArgs& args, const ConvPlan& p, hipStream_
   }
 }
 
-template <int CG, int KD, int KH, int KW, int DH, int DW, int F, int ROWS, int BW, int T>
+template <int CG, int KD, int KH, int KW, int DH, int DW, int F, int ROWS, int BW, int T, bool CL>
 static int launch_kstream(const ConvArgs& args, const ConvPlan& p, hipStream_t stream) {
   using G = KsGeo<CG, KD, KH, KW, DH, DW, F, ROWS, BW, T>;
   static_assert(4 * G::LDS <= kLdsLimit, "stream-K specialisation exceeds LDS");
   if (int64_t(4) * G::LDS != p.lds_bytes) return CONV_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL(conv_tap_kstream_kernel<G>, dim3(unsigned(p.grid[0])), dim3(512), 0, stream, args);
+  hipLaunchKernelGGL((conv_tap_kstream_kernel<G, CL>), dim3(unsigned(p.grid[0])), dim3(512), 0, stream, args);
   return hipGetLastError() == hipSuccess ? CONV_OK : CONV_ERR_HIP;
 }
 
+template <bool CL>
 static int launch_ks_spec(const ConvArgs& args, const ConvPlan& p, hipStream_t stream) {
   switch (p.ks_spec) {
 #define CONVHIP_KS_CASE(id, CG, KD, KH, KW, DH, DW, F, ROWS, BW, T) \
   case id:                                                        \
-    return launch_kstream<CG, KD, KH, KW, DH, DW, F, ROWS, BW, T>(args, p, stream);
+    return launch_kstream<CG, KD, KH, KW, DH, DW, F, ROWS, BW, T, CL>(args, p, stream);
     CONVHIP_KSTREAM_SPECS(CONVHIP_KS_CASE)
 #undef CONVHIP_KS_CASE
     default: return CONV_ERR_UNSUPPORTED;
@@ -3260,7 +3286,7 @@ int conv_fwd(int nd, const float* x, const int64_t* x_shape, const float* w, con
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (p.tap_spec >= 0) return launch_tap_spec(a, p, s);
   if (p.direct_spec >= 0) return launch_direct_spec<false>(a, p, s);
-  if (p.ks_spec >= 0) return launch_ks_spec(a, p, s);
+  if (p.ks_spec >= 0) return launch_ks_spec<false>(a, p, s);
   if (p.split_spec >= 0) return launch_split_spec<false>(a, p, s);
   return launch_generic<false>(a, p, s);
 }
@@ -3284,6 +3310,7 @@ int conv_fwd_channels_last(int nd, const float* x, const int64_t* x_shape, const
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (p.tap_spec >= 0) return launch_tap_cl_spec(a, p, s);
   if (p.direct_spec >= 0) return launch_direct_spec<true>(a, p, s);
+  if (p.ks_spec >= 0) return launch_ks_spec<true>(a, p, s);
   if (p.split_spec >= 0) return launch_split_spec<true>(a, p, s);
   return launch_generic<true>(a, p, s);
 }

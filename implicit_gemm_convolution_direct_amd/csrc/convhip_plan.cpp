@@ -196,7 +196,7 @@ static int64_t ks_lds_floats(const KsSpecDesc& d) {
 // spec's channels, kernel and W/H dilations, W stride and dilation multiples of
 // F, exactly T tiles per output plane, and a box within the staged extents.
 static bool plan_kstream(const Geom& g, const KsSpecDesc& d, ConvPlan* p) {
-  if (g.cl || g.Coutg > 16 || g.Cg != d.CG) return false;
+  if (g.Coutg > 16 || g.Cg != d.CG) return false;
   if (g.K[0] != d.KD || g.K[1] != d.KH || g.K[2] != d.KW) return false;
   if (g.Dl[1] != d.DH || g.Dl[2] != d.DW) return false;
   if (g.S[2] % d.F != 0 || d.DW % d.F != 0) return false;
@@ -207,7 +207,8 @@ static bool plan_kstream(const Geom& g, const KsSpecDesc& d, ConvPlan* p) {
   if (rows > d.ROWS || bw > d.BW) return false;
   const int64_t items = g.N * g.O[0] * g.G;
   if (items > std::numeric_limits<int32_t>::max()) return false;
-  if (g.L[1] * g.L[2] > std::numeric_limits<int32_t>::max() / 2) return false;
+  // In-plane source offsets (times C_in for channels-last sites) in 32 bits.
+  if (g.L[1] * g.L[2] * (g.cl ? g.Cin : 1) > std::numeric_limits<int32_t>::max() / 2) return false;
   const int64_t lds = 4 * ks_lds_floats(d);
   if (lds > kLdsLimit) return false;
   ConvPlan q;
@@ -438,6 +439,9 @@ int plan_conv(const Geom& g, ConvPlan* out, int force_cfg, int num_cu, int use_t
         const DirectSpecDesc* ds = direct_specs(&n);
         for (int i = 0; i < n; i++)
           if (plan_direct(g, ds[i], out)) return CONV_OK;
+        const KsSpecDesc* ks = ks_specs(&n);
+        for (int i = 0; i < n; i++)
+          if (plan_kstream(g, ks[i], out)) return CONV_OK;
       }
       const SplitSpecDesc* ss = split_specs(&n);
       for (int i = 0; i < n; i++)

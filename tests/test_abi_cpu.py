@@ -108,7 +108,7 @@ def test_fused_plan_per_min_axis():
 
 def test_channels_last_plans():
     for xs, ws, s, d, p, g, kernel in [
-            ((4, 32, 32, 32, 16), (32, 8, 3, 5, 7), (1, 2, 2), (1, 1, 2), (1, 2, 3), 2, "conv_tap_split"),
+            ((4, 32, 32, 32, 16), (32, 8, 3, 5, 7), (1, 2, 2), (1, 1, 2), (1, 2, 3), 2, "conv_tap_kstream"),
             ((2, 16, 16, 16, 3), (8, 3, 3, 3, 3), 1, 1, 0, 1, "conv_direct16"),
             ((2, 16, 16, 16, 4), (8, 4, 3, 3, 3), 1, 1, 0, 1, "conv_mfma16"),
             ((4, 4096, 64), (128, 64, 3), 3, 4, 0, 1, "conv_tap"),        # the long Conv1d geometry

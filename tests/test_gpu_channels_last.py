@@ -308,6 +308,23 @@ def test_channels_last_split_kernel_integer_exact(case, pipe, monkeypatch):
     np.testing.assert_array_equal(y.astype(np.float64), oracle.conv_channels_last(x, w, b, s, d, p, g))
 
 
+# The general Conv3d geometry's channels-last cases on the stream-K kernel (the
+# planner's default for them).
+KSTREAM_CL_CASES = SPLIT_CL_CASES[:5]
+
+
+@pytest.mark.parametrize("case", range(len(KSTREAM_CL_CASES)))
+def test_channels_last_kstream_kernel_integer_exact(case):
+    xs, ws, s, d, p, g = KSTREAM_CL_CASES[case]
+    desc = ch.plan_describe(xs, ws, s, d, p, g, channels_last=True)
+    assert "kernel=conv_tap_kstream" in desc and "layout=channels_last" in desc, desc
+    r = np.random.default_rng(1000 + case)
+    x, w, b = _int_inputs(r, xs, ws, bias=case % 2 == 0)
+    say(f"cl kstream case {case}: x={xs} w={ws}: {desc}")
+    y = gpu_conv_cl(x, w, b, s, d, p, g)
+    np.testing.assert_array_equal(y.astype(np.float64), oracle.conv_channels_last(x, w, b, s, d, p, g))
+
+
 # The direct kernel's cases in channels-last order.
 DIRECT_CL_CASES = [
     ((2, 16, 16, 16, 3), (8, 3, 3, 3, 3), 1, 1, 0, 1),
