@@ -465,13 +465,13 @@ __device__ __forceinline__ void load_bias(const ConvArgs& a, const TileGeo& t, i
     }
 }
 
-// Channels-last output stores carry the non-temporal hint. A channels-last
-// kernel reads each input site's channels in several chunks, one after the
-// other; the output it writes meanwhile (as large as the input for the long
-// Conv1d) would otherwise push those sites' lines out of L2 before the later
-// chunks read them. Channels-first outputs keep plain stores: their tiles
-// reuse input through L2 within a shorter window, and non-temporal stores
-// there add write traffic.
+// Non-temporal output stores, for the channels-last tap kernel when it reads
+// each input site's channels in several chunks, one after the other: the
+// output it writes meanwhile (as large as the input for the long Conv1d) would
+// otherwise push those sites' lines out of L2 before the later chunks read
+// them. Elsewhere outputs keep plain stores: non-temporal ones add write
+// traffic (partly written lines reach HBM separately), measured at 1.26x to
+// 1.42x of the output size.
 __device__ __forceinline__ void store_nt(float* p, float v) { __builtin_nontemporal_store(v, p); }
 __device__ __forceinline__ void store_nt4(float* p, v4f v) { __builtin_nontemporal_store(v, reinterpret_cast<v4f*>(p)); }
 
@@ -479,7 +479,7 @@ __device__ __forceinline__ void store_nt4(float* p, v4f v) { __builtin_nontempor
 // n + 16*(m/4), register m%4: a lane holds 4 consecutive channels of one
 // position, which channels-last output y [N, D_out, H_out, W_out, C_out] takes
 // as one 16-byte store.
-template <int MT, int NT, bool CL = false>
+template <int MT, int NT, bool CL = false, bool NTSTORE = false>
 __device__ __forceinline__ void store_tile(const ConvArgs& a, const TileGeo& t, int wm, int kg,
                                            const int (&pidx)[NT], const v4f (&acc)[MT][NT],
                                            const float (&bias)[MT][4]) {
@@ -494,12 +494,17 @@ __device__ __forceinline__ void store_tile(const ConvArgs& a, const TileGeo& t, 
         if (pidx[ni] < 0 || ch0 >= a.Coutg) continue;
         float* yp = yplane + int64_t(pidx[ni]) * a.Cout + ch0;
         if (a.vec_store) {
-          store_nt4(yp, v4f{acc[mi][ni][0] + bias[mi][0], acc[mi][ni][1] + bias[mi][1], acc[mi][ni][2] + bias[mi][2],
-                            acc[mi][ni][3] + bias[mi][3]});
+          const v4f v = v4f{acc[mi][ni][0] + bias[mi][0], acc[mi][ni][1] + bias[mi][1], acc[mi][ni][2] + bias[mi][2],
+                            acc[mi][ni][3] + bias[mi][3]};
+          if constexpr (NTSTORE) store_nt4(yp, v);
+          else *reinterpret_cast<v4f*>(yp) = v;
         } else {
 #pragma unroll
-          for (int r = 0; r < 4; r++)
-            if (ch0 + r < a.Coutg) store_nt(yp + r, acc[mi][ni][r] + bias[mi][r]);
+          for (int r = 0; r < 4; r++) {
+            if (ch0 + r >= a.Coutg) continue;
+            if constexpr (NTSTORE) store_nt(yp + r, acc[mi][ni][r] + bias[mi][r]);
+            else yp[r] = acc[mi][ni][r] + bias[mi][r];
+          }
         }
       }
     }
@@ -956,7 +961,7 @@ __global__ __launch_bounds__(64 * WM * WN) void conv_tap_kernel(ConvArgs a) {
         tap_stage<MT, NT, WM, NWAVES, G, NP>(a, last ? tn : t, has_next, c0n, box0, box1, wchunk, addr, acc, wave,
                                              lane);
       auto store_and_clear = [&] {
-        store_tile<MT, NT, G::CL>(a, t, wm, kg, pidx, acc, bias);
+        store_tile<MT, NT, G::CL, G::CL && (NCH > 1)>(a, t, wm, kg, pidx, acc, bias);
 #pragma unroll
         for (int mi = 0; mi < MT; mi++)
 #pragma unroll
@@ -1976,12 +1981,17 @@ __global__ __launch_bounds__(512) void conv_tap_kstream_kernel(ConvArgs a) {
                "+s"(O0), "+s"(O1), "+s"(O2), "+s"(plane_out), "+s"(nitems), "+s"(vec_store));
   // Workgroups are dispatched round-robin over the 8 XCDs: give each XCD a
   // contiguous run of (plane, group) items, so the input planes that
-  // neighbouring output depths share stay in that XCD's L2.
+  // neighbouring output depths share stay in that XCD's L2. Channels-last:
+  // group fastest, so the groups of one plane, which split the channels of the
+  // same input sites (and cache lines), share that L2 too; channels-first:
+  // plane fastest, so an XCD's run covers twice the depths and re-reads fewer
+  // planes at its ends.
   int item = blockIdx.x;
   if ((nitems & 7) == 0) item = (item & 7) * (nitems >> 3) + (item >> 3);
-  const int nplanes = nitems / (Cout / Coutg);
-  const int plane = item % nplanes;
-  const int g = item / nplanes;
+  const int ngroups = Cout / Coutg;
+  const int nplanes = nitems / ngroups;
+  const int plane = CL ? item / ngroups : item % nplanes;
+  const int g = CL ? item - plane * ngroups : item / nplanes;
   const int n = plane / O0;
   const int od = plane - n * O0;
   float* box = smem;
@@ -2110,6 +2120,12 @@ __global__ __launch_bounds__(512) void conv_tap_kstream_kernel(ConvArgs a) {
   v4f acc2[G::R > 0 ? G::R : 1];  // the split tiles' odd k-steps (a second chain)
 #pragma unroll
   for (int r = 0; r < G::R; r++) acc2[r] = v4f{0.f, 0.f, 0.f, 0.f};
+  // With fewer than 3 whole tiles per wave, their odd k-steps accumulate in a
+  // second chain too: consecutive products then do not wait for each other.
+  constexpr bool WCH2 = G::FT > 0 && G::FT < 3;
+  v4f accw[WCH2 ? G::FT : 1];
+#pragma unroll
+  for (int t = 0; t < (WCH2 ? G::FT : 1); t++) accw[t] = v4f{0.f, 0.f, 0.f, 0.f};
   wait_vmem_le<0>();  // no memory access of this path is left in flight in the product loop
   const char* bb = reinterpret_cast<const char*>(smem);
   // B operand of tile t at k-step S: one LDS read at (lane register + immediate).
@@ -2170,7 +2186,8 @@ __global__ __launch_bounds__(512) void conv_tap_kstream_kernel(ConvArgs a) {
       aa[j] = av;
       static_for<G::FT>([&](auto tc) {
         constexpr int t = decltype(tc)::value;
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bs[s % 3][t], acc[t], 0, 0, 0);
+        if constexpr (WCH2 && (s & 1)) accw[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bs[s % 3][t], accw[t], 0, 0, 0);
+        else acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bs[s % 3][t], acc[t], 0, 0, 0);
         // Reads after this product: B of step s+2 for tile t; after the first
         // product of an odd step, A of pair s/2 + 1.
         constexpr bool rb = s + 2 < G::NS;
@@ -2209,6 +2226,10 @@ __global__ __launch_bounds__(512) void conv_tap_kstream_kernel(ConvArgs a) {
                  : yglob + (int64_t(n) * Cout + int64_t(g) * Coutg) * O0 * out_plane + int64_t(od) * out_plane;
   const int64_t ch_stride = CL ? 1 : int64_t(O0) * out_plane;
   const int64_t p_stride = CL ? Cout : 1;
+  if constexpr (WCH2) {
+#pragma unroll
+    for (int i = 0; i < G::FT; i++) acc[i] += accw[i];
+  }
 #pragma unroll
   for (int i = 0; i < G::FT; i++) {
     const int p = 16 * (wave * G::FT + i) + li;
@@ -2216,11 +2237,11 @@ __global__ __launch_bounds__(512) void conv_tap_kstream_kernel(ConvArgs a) {
       if (p < plane_out) {
         float* yp = yg + p * p_stride + 4 * kg;
         if (vec_store && 4 * kg + 4 <= Coutg) {
-          store_nt4(yp, v4f{acc[i][0] + b4[0], acc[i][1] + b4[1], acc[i][2] + b4[2], acc[i][3] + b4[3]});
+          *reinterpret_cast<v4f*>(yp) = v4f{acc[i][0] + b4[0], acc[i][1] + b4[1], acc[i][2] + b4[2], acc[i][3] + b4[3]};
         } else {
 #pragma unroll
           for (int r = 0; r < 4; r++)
-            if (4 * kg + r < Coutg) store_nt(yp + r, acc[i][r] + b4[r]);
+            if (4 * kg + r < Coutg) yp[r] = acc[i][r] + b4[r];
         }
       }
     } else {
@@ -2248,8 +2269,7 @@ __global__ __launch_bounds__(512) void conv_tap_kstream_kernel(ConvArgs a) {
       for (int w2 = 0; w2 < 4; w2++) v += red[((w2 * G::R + r) * 64 + lane) * 4 + wave];
       const int p = 16 * (4 * G::FT + r) + li;
       if (ch < Coutg && p < plane_out) {
-        if constexpr (CL) store_nt(yg + p * p_stride + ch, v + bw_);
-        else yg[ch * ch_stride + p] = v + bw_;
+        yg[ch * ch_stride + p * p_stride] = v + bw_;
       }
     }
   }
