@@ -115,10 +115,11 @@ int conv_fwd_channels_last(int nd,
  *   min_dim 2: y [N, C_out, H_out, W_out],
  *              y[n,:,h,w] = softmax_c( min_{od} conv3d(x,w,bias)[n,c,od,h,w] );
  *   min_dim 3: y [N, C_out, D_out, W_out];  min_dim 4: y [N, C_out, D_out, H_out].
- * Supported: C_out <= 64, and the input box of one output tile
- * over the whole min axis must fit in LDS (groups > 1 run as a block-diagonal
- * dense conv); other valid arguments return CONV_ERR_UNSUPPORTED. Non-finite
- * inputs: unspecified.
+ * Supported: C_out <= 64, and the input box of one output tile over the whole
+ * min axis must fit in LDS; other valid arguments return CONV_ERR_UNSUPPORTED.
+ * With groups > 1 each output channel reduces over its own group's C_in/groups
+ * input channels only. Non-finite inputs: unspecified (the kernels' minimum
+ * drops a NaN that torch.min would propagate).
  */
 int conv3d_min_softmax(const float *x, const int64_t *x_shape,
                        const float *w, const int64_t *w_shape, const float *bias,
