@@ -91,6 +91,11 @@ __device__ __forceinline__ int divmod_small(int n, int d, float inv, int& r) {
   return q;
 }
 
+// Minimum that propagates NaN, as torch.min does (IEEE 754-2019 minimum: one
+// v_minimum / v_minimum3 instruction on gfx950; the C library's fmin would
+// drop the NaN).
+__device__ __forceinline__ float min_nan(float a, float b) { return __builtin_elementwise_minimum(a, b); }
+
 template <int MT>
 struct AFrag;
 template <>
@@ -2489,10 +2494,10 @@ __global__ __launch_bounds__(256) void fused_min_softmax_mfma4_kernel(FusedArgs 
       }
 #pragma unroll
       for (int i = 0; i < NG; i++) {
-        mn[i][0] = fminf(mn[i][0], acc[i][0]);
-        mn[i][1] = fminf(mn[i][1], acc[i][1]);
-        mn[i][2] = fminf(mn[i][2], acc[i][2]);
-        mn[i][3] = fminf(mn[i][3], acc[i][3]);
+        mn[i][0] = min_nan(mn[i][0], acc[i][0]);
+        mn[i][1] = min_nan(mn[i][1], acc[i][1]);
+        mn[i][2] = min_nan(mn[i][2], acc[i][2]);
+        mn[i][3] = min_nan(mn[i][3], acc[i][3]);
       }
     }
     // Merge the four waves' minima of this group through LDS.
@@ -2509,9 +2514,9 @@ __global__ __launch_bounds__(256) void fused_min_softmax_mfma4_kernel(FusedArgs 
 #pragma unroll
         for (int c = 0; c < 4 * NG; c++) {
           float v = red[c * 64 + lane];
-          v = fminf(v, red[(a.cpadg + c) * 64 + lane]);
-          v = fminf(v, red[(2 * a.cpadg + c) * 64 + lane]);
-          v = fminf(v, red[(3 * a.cpadg + c) * 64 + lane]);
+          v = min_nan(v, red[(a.cpadg + c) * 64 + lane]);
+          v = min_nan(v, red[(2 * a.cpadg + c) * 64 + lane]);
+          v = min_nan(v, red[(3 * a.cpadg + c) * 64 + lane]);
           // fp32 addition is monotone, so min(v_i) + b == min(v_i + b) exactly.
           m[c] = (c < a.Cout) ? v + (a.bias ? a.bias[c] : 0.0f) : -INFINITY;
         }
@@ -2536,9 +2541,9 @@ __global__ __launch_bounds__(256) void fused_min_softmax_mfma4_kernel(FusedArgs 
     // into fin[channel][position], then free red for the next group.
     for (int c = wave; c < a.Coutg; c += 4) {
       float v = red[c * 64 + lane];
-      v = fminf(v, red[(a.cpadg + c) * 64 + lane]);
-      v = fminf(v, red[(2 * a.cpadg + c) * 64 + lane]);
-      v = fminf(v, red[(3 * a.cpadg + c) * 64 + lane]);
+      v = min_nan(v, red[(a.cpadg + c) * 64 + lane]);
+      v = min_nan(v, red[(2 * a.cpadg + c) * 64 + lane]);
+      v = min_nan(v, red[(3 * a.cpadg + c) * 64 + lane]);
       const int co = g * a.Coutg + c;
       fin[co * 64 + lane] = v + (a.bias ? a.bias[co] : 0.0f);
     }
@@ -2782,8 +2787,7 @@ __global__ __launch_bounds__(256, 4) void fused_stream_kernel(StreamArgs a) {
       });
       __builtin_amdgcn_sched_barrier(0);
     });
-    // Running minimum as compare-and-select: a NaN product is dropped, as fminf
-    // drops it, without fminf's operand canonicalisation.
+    // Running minimum, NaN-propagating like torch.min.
     // mn[q], q < 4 (16x16x1 form): registers 4q .. 4q+3 of its output, lane l
     // holding channel 4(l/16) + i of position 16q + l%16; mn[q] otherwise: the
     // 4x4x1 form, lane l holding channel 4q + i of position l.
@@ -2794,7 +2798,7 @@ __global__ __launch_bounds__(256, 4) void fused_stream_kernel(StreamArgs a) {
         float v;
         if constexpr (G::MIX) v = q < 4 ? acc16[4 * q + i] : acc[q < 4 ? 0 : q - 4][i];
         else v = acc[q][i];
-        mn[q][i] = v < mn[q][i] ? v : mn[q][i];
+        mn[q][i] = min_nan(mn[q][i], v);
       }
   }
 
@@ -2818,7 +2822,7 @@ __global__ __launch_bounds__(256, 4) void fused_stream_kernel(StreamArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; i++) {
           const float v = red[(((wave + o) * NG + q) * 4 + i) * 64 + lane];
-          mn[q][i] = v < mn[q][i] ? v : mn[q][i];
+          mn[q][i] = min_nan(mn[q][i], v);
         }
   }
 

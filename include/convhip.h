@@ -75,6 +75,9 @@ int conv_out_shape(int nd, const int64_t *in_spatial, const int64_t *k_spatial,
  * x_shape / w_shape: nd+2 host entries. stride, dilation, padding: nd host
  * entries each. bias: device pointer to C_out floats, or NULL for none.
  * y: device buffer of N*C_out*prod(out) floats, preallocated by the caller.
+ * fp32 products and fp32 accumulation in an unspecified order. A NaN input
+ * makes NaN every output whose receptive field holds it; infinite inputs give
+ * unspecified results (a padded zero-weight term may turn them into NaN).
  */
 int conv_fwd(int nd,
              const float *x, const int64_t *x_shape,
@@ -118,8 +121,8 @@ int conv_fwd_channels_last(int nd,
  * Supported: C_out <= 64, and the input box of one output tile over the whole
  * min axis must fit in LDS; other valid arguments return CONV_ERR_UNSUPPORTED.
  * With groups > 1 each output channel reduces over its own group's C_in/groups
- * input channels only. Non-finite inputs: unspecified (the kernels' minimum
- * drops a NaN that torch.min would propagate).
+ * input channels only. A NaN input propagates as it does through the module's
+ * torch.min (the minimum is NaN-propagating); infinite inputs: unspecified.
  */
 int conv3d_min_softmax(const float *x, const int64_t *x_shape,
                        const float *w, const int64_t *w_shape, const float *bias,

@@ -663,3 +663,55 @@ def test_tap_box_narrower_than_pitch_integer_exact():
         say(f"tap narrow W={W}: {desc}")
         y = gpu_conv(x, w, b, 1, 1, 0, 1)
         np.testing.assert_array_equal(y.astype(np.float64), oracle.conv(x, w, b, 1, 1, 0, 1))
+
+
+# NaN inputs. A NaN reaches every output whose receptive field holds it, in the
+# oracle and on the GPU alike: the kernels' padded reduction indices carry zero
+# weights and read the position's own first tap, which lies in that field, and
+# the fused op's minimum propagates NaN as torch.min does. (Infinities are not
+# covered: a zero-weight padded index times an infinity is NaN where the
+# definition gives an infinity.)
+NAN_CASES = [
+    ("direct", (2, 3, 16, 16, 16), (8, 3, 3, 3, 3), 1, 1, 0, 1, "conv_direct16"),
+    ("kstream", (1, 16, 6, 32, 32), (32, 8, 3, 5, 7), (1, 2, 2), (1, 1, 2), (1, 2, 3), 2, "conv_tap_kstream"),
+    ("tap", (2, 3, 8, 64, 64), (64, 3, 3, 5, 7), 1, 1, 0, 1, "conv_tap"),
+    ("tap_conv1d", (2, 64, 3000), (128, 64, 3), 3, 4, 0, 1, "conv_tap"),
+    ("generic", (2, 5, 7, 9, 11), (6, 5, 2, 3, 2), (1, 2, 1), (2, 1, 1), (1, 0, 2), 1, "conv_mfma16"),
+]
+
+
+@pytest.mark.parametrize("case", NAN_CASES, ids=[c[0] for c in NAN_CASES])
+def test_nan_inputs_propagate_like_the_definition(case):
+    name, xs, ws, s, d, p, g, kernel = case
+    desc = ch.plan_describe(xs, ws, s, d, p, g)
+    assert f"kernel={kernel} " in desc + " ", desc
+    r = np.random.default_rng(zlib.crc32(name.encode()))
+    x, w, b = _int_inputs(r, xs, ws, bias=True)
+    flat = x.reshape(-1)
+    for i in r.choice(flat.size, size=3, replace=False):
+        flat[i] = np.nan
+    say(f"nan {name}: {desc}")
+    y = gpu_conv(x, w, b, s, d, p, g).astype(np.float64)
+    ref = oracle.conv(x, w, b, s, d, p, g)
+    nan_ref = np.isnan(ref)
+    assert nan_ref.any() and not nan_ref.all()
+    np.testing.assert_array_equal(np.isnan(y), nan_ref)
+    np.testing.assert_array_equal(y[~nan_ref], ref[~nan_ref])
+
+
+@pytest.mark.parametrize("min_dim", [2, 3])
+def test_fused_nan_inputs_propagate_like_torch_min(min_dim):
+    """min_dim 2 takes the depth-streamed kernel, 3 the generic one."""
+    xs, ws = (2, 3, 6, 32, 32), (24, 3, 3, 3, 3)
+    r = np.random.default_rng(77 + min_dim)
+    x, w, b = _float_inputs(r, xs, ws, True)
+    x[0, 1, 2, 5, 7] = np.nan
+    x[1, 0, 4, 20, 30] = np.nan
+    desc = ch.plan_describe(xs, ws, 1, 1, 0, 1, fused=True, min_dim=min_dim)
+    say(f"fused nan min_dim {min_dim}: {desc}")
+    y = gpu_fused(x, w, b, 1, 1, 0, 1, min_dim)
+    ref = oracle.conv3d_min_softmax(x, w, b, 1, 1, 0, 1, min_dim)
+    nan_ref = np.isnan(ref)
+    assert nan_ref.any() and not nan_ref.all()
+    np.testing.assert_array_equal(np.isnan(y), nan_ref)
+    assert float(np.abs(y[~nan_ref] - ref[~nan_ref]).max()) <= FUSED_ATOL
