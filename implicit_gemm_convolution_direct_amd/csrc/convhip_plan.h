@@ -144,8 +144,9 @@ constexpr bool split_pipe_fits(int NT, int NW, int wrow) {
   /* Conv3d 16->32, groups 2, kernel 3x5x7, stride (1,2,2), dilation (1,1,2):  \
      32x32 inputs (16x13 outputs, 13 tiles) */                                   \
   X(0, 8, 3, 5, 7, 1, 2, 2, 35, 20, 13)                                          \
-  /* the same on 24x24 inputs (12x9 outputs, 7 tiles) */                        \
-  X(1, 8, 3, 5, 7, 1, 2, 2, 35, 20, 7)
+  /* the same on 24x24 inputs (12x9 outputs, 7 tiles): the box of exactly      \
+     the rows and columns they read */                                           \
+  X(1, 8, 3, 5, 7, 1, 2, 2, 27, 15, 7)
 
 // Build-time specialisations of the direct kernel (conv_direct16) for small
 // convolutions: one wave per 16 output positions and all <= 16 output channels
