@@ -20,13 +20,24 @@
 //                   weights staged one depth tap at a time and held in VGPRs,
 //                   and the first tile batch's sum overlapped with the second
 //                   batch's products.
+// conv_tap_kstream  build-time specialised, few output channels per group: one
+//                   workgroup per (n, od) plane and group, whole tiles per
+//                   compute wave plus the remainder tiles split over the
+//                   waves by reduction blocks (stream-K inside the
+//                   workgroup), copy waves issuing every LDS DMA copy.
+// conv_direct16     small convolutions: one wave per 16 positions, operands
+//                   read from global memory straight into registers.
 // fused_stream      Conv3d -> min over depth -> softmax over channels for a
 //                   build-time geometry: depth planes streamed through a 4-slot
 //                   LDS ring, 4x4x1 MFMA with the weight operand broadcast.
-// fused_min_softmax_mfma4  the same fused op for any geometry (min over depth).
+// fused_min_softmax_mfma4  the same fused op for any geometry, min axis and
+//                   number of groups.
 //
 // Problem statements: POPCORNBENCH "Kimi-K2.6" pages l1_p60 (Conv3d), l1_p76
-// (Conv1d), l2_p24 (Conv3d + min + softmax), opening turns.
+// (Conv1d), l2_p24 (Conv3d + min + softmax), opening turns. The tiled direct
+// convolution with the input halo staged on chip and the weights cached next
+// to it follows the design monologue of l1_p60; the depth-streamed fused op
+// with its running minimum, turns 2 and 7 of l2_p24.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -1815,7 +1826,7 @@ __global__ __launch_bounds__(64) void conv_direct16_kernel(DirectArgs a) {
 // consumes them, several blocks ahead. Each copy wave waits for its own copies
 // and meets the compute waves at a barrier before the blocks that read them.
 // ---------------------------------------------------------------------------
-template <int CG, int KD, int KH, int KW, int DH, int DW, int F, int ROWS, int BW, int T>
+template <int CG, int KD, int KH, int KW, int DH, int DW, int F, int ROWS, int BW, int T, bool CLQ = false>
 struct KsGeo {
   static constexpr int KVOL = KD * KH * KW;
   static constexpr int KPP = KH * KW;           // reduction indices per box plane
@@ -1824,11 +1835,16 @@ struct KsGeo {
   static constexpr int NQ = (K + 15) / 16;      // 16-deep reduction blocks
   static constexpr int NS = 4 * NQ;             // 4-deep k-steps
   static constexpr int FF = F, BWC = BW, ROWSC = ROWS, KDC = KD, KHC = KH, KWC = KW, DHC = DH, DWC = DW, CGC = CG;
-  static constexpr int PLANE = ROWS * BW;       // box floats per (channel, depth tap)
+  // CLQ (channels-last input, C_in/groups a multiple of 4): a box plane holds
+  // one (channel quad, depth tap), 4 channels interleaved per site and copied
+  // 16 bytes per lane; otherwise one (channel, depth tap), 4 bytes per lane.
+  static_assert(!CLQ || CG % 4 == 0, "channel quads");
+  static constexpr int CH = CLQ ? 4 : 1;        // channels per plane
+  static constexpr int PLANE = ROWS * BW;       // box sites per plane
   static constexpr int PI = (PLANE + 63) / 64;  // copy instructions per plane
   static constexpr int PIW = (PI + 3) / 4;      // ... per wave (the rest pad to a multiple of 4)
-  static constexpr int PSLOT = PI * 64;         // floats per plane slot (whole copies)
-  static constexpr int NPL = CG * KD;           // planes in the box
+  static constexpr int PSLOT = PI * 64 * CH;    // floats per plane slot (whole copies)
+  static constexpr int NPL = CG / CH * KD;      // planes in the box
   static constexpr int FT = T / 4, R = T % 4;   // whole tiles per wave, split tiles
   static constexpr int NTW = FT + R;            // tiles a wave accumulates
   static constexpr int WQ = 4;                  // reduction blocks per weight stage (1 per copy wave)
@@ -1846,8 +1862,10 @@ struct KsGeo {
   static constexpr int koff(int k) {
     if (k >= K) return 0;
     const int c = k / KVOL, r = k % KVOL, td = r / KPP, r2 = r % KPP, th = r2 / KW, tw = r2 % KW;
-    return (c * KD + td) * PSLOT + th * DH * BW + tw * (DW / F);
+    return (c / CH * KD + td) * PSLOT + (th * DH * BW + tw * (DW / F)) * CH + c % CH;
   }
+  // First block that reads box plane p = (channel / CH) * KD + td.
+  static constexpr int plane_need(int p) { return ((p / KD) * CH * KVOL + (p % KD) * KPP) / 16; }
 };
 
 // Distinct per-step lane patterns koff(kidx(s, kg)) - koff(kidx(s, 0)).
@@ -1917,7 +1935,7 @@ struct KsSchedule {
   constexpr KsSchedule() {
     int n = 0;
     for (int r = 0; r < G::NWS; r++) { type[n] = 1; idx[n] = r; need[n] = r * G::WQ; cnt[n] = G::WQ / 4; n++; }
-    for (int p = 0; p < G::NPL; p++) { type[n] = 0; idx[n] = p; need[n] = (p * G::KPP) / 16; cnt[n] = G::PIW; n++; }
+    for (int p = 0; p < G::NPL; p++) { type[n] = 0; idx[n] = p; need[n] = G::plane_need(p); cnt[n] = G::PIW; n++; }
     // Stable insertion sort by first use (weights before planes on a tie).
     for (int i = 1; i < NST; i++)
       for (int j = i; j > 0 && need[j - 1] > need[j]; j--) {
@@ -2032,7 +2050,7 @@ __global__ __launch_bounds__(512) void conv_tap_kstream_kernel(ConvArgs a) {
       constexpr int st = decltype(stc)::value;
       if constexpr (SC.type[st] == 0) {
         constexpr int p = SC.idx[st];
-        constexpr int c = p / G::KDC, td = p % G::KDC;
+        constexpr int c = p / G::KDC * G::CH, td = p % G::KDC;  // first channel, depth tap
         const int id = id0 + td * D0;
         const bool dok = unsigned(id) < unsigned(L0);
         const float* pl = xg0 + c * c_step + int64_t(id) * d_step;
@@ -2041,7 +2059,10 @@ __global__ __launch_bounds__(512) void conv_tap_kstream_kernel(ConvArgs a) {
           const int ii = 4 * i + wave;  // copy instruction of the plane (wave-uniform)
           const bool real = ii < G::PI;
           const bool ok = real && dok && ((sok >> i) & 1);
-          lds_dma_f32(ok ? pl + soff[i] : kZeroWord, real ? box + p * G::PSLOT + ii * 64 : dummy);
+          if constexpr (G::CH == 4)
+            lds_dma_f32x4(ok ? pl + soff[i] : kZeroWord, real ? box + p * G::PSLOT + ii * 256 : dummy);
+          else
+            lds_dma_f32(ok ? pl + soff[i] : kZeroWord, real ? box + p * G::PSLOT + ii * 64 : dummy);
         }
       } else {
         constexpr int r = SC.idx[st];
@@ -2096,14 +2117,14 @@ __global__ __launch_bounds__(512) void conv_tap_kstream_kernel(ConvArgs a) {
   // tiles 4FT .. T-1. Lane li's position in tile t is 16t + li.
   int nb[NTW];
   {
-    OffStep os(16 * wave * G::FT + li, O2, 0, S1 * G::BWC, S2 / G::FF);
+    OffStep os(16 * wave * G::FT + li, O2, 0, S1 * G::BWC * G::CH, S2 / G::FF * G::CH);
 #pragma unroll
     for (int i = 0; i < G::FT; i++) {
       nb[i] = 16 * (wave * G::FT + i) + li < plane_out ? os.off : 0;
       os.next();
     }
     if constexpr (G::R > 0) {
-      OffStep os2(16 * 4 * G::FT + li, O2, 0, S1 * G::BWC, S2 / G::FF);
+      OffStep os2(16 * 4 * G::FT + li, O2, 0, S1 * G::BWC * G::CH, S2 / G::FF * G::CH);
 #pragma unroll
       for (int i = 0; i < G::R; i++) {
         nb[G::FT + i] = 16 * (4 * G::FT + i) + li < plane_out ? os2.off : 0;
@@ -3043,7 +3064,7 @@ static int launch_split_spec(const ConvArgs& args, const ConvPlan& p, hipStream_
 
 template <int CG, int KD, int KH, int KW, int DH, int DW, int F, int ROWS, int BW, int T, bool CL>
 static int launch_kstream(const ConvArgs& args, const ConvPlan& p, hipStream_t stream) {
-  using G = KsGeo<CG, KD, KH, KW, DH, DW, F, ROWS, BW, T>;
+  using G = KsGeo<CG, KD, KH, KW, DH, DW, F, ROWS, BW, T, CL>;
   static_assert(4 * G::LDS <= kLdsLimit, "stream-K specialisation exceeds LDS");
   if (int64_t(4) * G::LDS != p.lds_bytes) return CONV_ERR_UNSUPPORTED;
   hipLaunchKernelGGL((conv_tap_kstream_kernel<G, CL>), dim3(unsigned(p.grid[0])), dim3(512), 0, stream, args);

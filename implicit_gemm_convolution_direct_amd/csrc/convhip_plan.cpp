@@ -200,6 +200,8 @@ static bool plan_kstream(const Geom& g, const KsSpecDesc& d, ConvPlan* p) {
   if (g.K[0] != d.KD || g.K[1] != d.KH || g.K[2] != d.KW) return false;
   if (g.Dl[1] != d.DH || g.Dl[2] != d.DW) return false;
   if (g.S[2] % d.F != 0 || d.DW % d.F != 0) return false;
+  // Channels-last: the box is copied as 16-byte channel quads.
+  if (g.cl && (d.CG % 4 != 0 || g.Cin % 4 != 0 || !g.x_aligned16)) return false;
   if ((int64_t(d.CG) * d.KD * d.KH * d.KW) % 4 != 0) return false;
   if ((g.plane_out() + 15) / 16 != d.T) return false;
   const int64_t rows = (g.O[1] - 1) * g.S[1] + (g.K[1] - 1) * g.Dl[1] + 1;
