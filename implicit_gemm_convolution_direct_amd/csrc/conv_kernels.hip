@@ -2656,7 +2656,22 @@ struct StreamArgs {
   int dsplit;      // waves per (sample, tile): the depth range is split over them
   int ods;         // output depths per wave (the last range may be shorter)
   int units;       // N * tiles_per_plane * dsplit
+  // Element strides of x along the kernel's axes 0 and 1 (axis 2 is W,
+  // contiguous), and of w along kernel axes 0 and 1 (axis 2 stride 1): the
+  // host permutes D and H for a minimum over H.
+  int plane_stride, row_stride;
+  int ws0, ws1;
 };
+
+// Index in w's [C_in, kD, kH, kW] block of reduction index k = (c, axis-0
+// tap, axis-1 tap, axis-2 tap) in the kernel's axis order (k < KRED).
+template <class G>
+__device__ __forceinline__ int stream_widx(int k, const StreamArgs& a) {
+  const int c = k / G::KVOL, r = k - c * G::KVOL;
+  const int t0 = r / G::KHW, r2 = r - t0 * G::KHW;
+  const int t1 = r2 / G::KW, t2 = r2 - t1 * G::KW;
+  return c * G::KVOL + t0 * a.ws0 + t1 * a.ws1 + t2;
+}
 
 template <class G>
 __global__ __launch_bounds__(256, 4) void fused_stream_kernel(StreamArgs a) {
@@ -2692,7 +2707,7 @@ __global__ __launch_bounds__(256, 4) void fused_stream_kernel(StreamArgs a) {
     const int pair = 16 * r + (lane >> 2);
     const int gq = pair / G::KRED, k = pair - gq * G::KRED;
     const int co = G::CO4 + 4 * gq + (lane & 3);
-    aw[r] = (live && pair < G::NPAIR && co < a.Cout) ? a.w[co * G::KRED + k] : 0.0f;
+    aw[r] = (live && pair < G::NPAIR && co < a.Cout) ? a.w[co * G::KRED + stream_widx<G>(k, a)] : 0.0f;
   }
   // Weights of the 16x16x1 form: register j, lane 16b + m holds w[m][4j + b].
   float a16[G::MIX ? G::NA16 : 1];
@@ -2700,7 +2715,7 @@ __global__ __launch_bounds__(256, 4) void fused_stream_kernel(StreamArgs a) {
 #pragma unroll
     for (int j = 0; j < G::NA16; j++) {
       const int k = 4 * j + (lane >> 4), m = lane & 15;
-      a16[j] = (live && k < G::KRED && m < a.Cout) ? a.w[m * G::KRED + k] : 0.0f;
+      a16[j] = (live && k < G::KRED && m < a.Cout) ? a.w[m * G::KRED + stream_widx<G>(k, a)] : 0.0f;
     }
   }
 
@@ -2719,10 +2734,13 @@ __global__ __launch_bounds__(256, 4) void fused_stream_kernel(StreamArgs a) {
     const int r = rem / (G::BW / 4), q = rem - r * (G::BW / 4);
     const int ih = ih0 + r;
     const bool ok = unsigned(ih) < unsigned(a.L1);
-    soff[i] = ok ? int(c * chan_stride) + ih * G::BW + 4 * q : 0;
+    soff[i] = ok ? int(c * chan_stride) + ih * a.row_stride + 4 * q : 0;
     sok |= uint32_t(ok) << i;
   }
-  const int plane_elems = a.L1 * G::BW;
+  // Pinned in a scalar register: a kernel-argument load inside the depth loop
+  // would come with a wait that drains the LDS reads in flight.
+  int plane_elems = a.plane_stride;
+  pin_sgpr(plane_elems);
   // Plane z (input depth z - P0) -> slot z % 4. Planes past od1 + 1 are copied
   // as zeros so every wave issues the same number of copies per step; lanes
   // past the plane's last chunk copy nothing.
@@ -3300,7 +3318,7 @@ int conv_plan_describe(int nd, const int64_t* x_shape, const int64_t* w_shape, c
     if (nd != 3) return CONV_ERR_RANK;
     const int min_dim = fused == 1 ? 2 : fused;
     FusedPlan p;
-    rc = plan_fused(fused_geom(g, min_dim), min_dim, &p, use_tap() != 0 && min_dim == 2);
+    rc = plan_fused(fused_geom(g, min_dim), min_dim, &p, use_tap() != 0 && min_dim != 4);
     if (rc != CONV_OK) return rc;
     s = describe(fused_geom(g, min_dim), p);
   } else {
@@ -3375,7 +3393,9 @@ int conv3d_min_softmax(const float* x, const int64_t* x_shape, const float* w, c
   FusedPlan p;
   // The depth-streamed kernel copies input rows in 16-byte chunks.
   const bool aligned = (reinterpret_cast<uintptr_t>(x) & 15) == 0;
-  rc = plan_fused(g, min_dim, &p, use_tap() != 0 && aligned && min_dim == 2);
+  // The depth-streamed kernel streams over the min axis and copies input rows
+  // along W in 16-byte chunks: a minimum over D or H (W stays the row axis).
+  rc = plan_fused(g, min_dim, &p, use_tap() != 0 && aligned && min_dim != 4);
   if (rc != CONV_OK) return rc;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (p.spec >= 0) {
@@ -3390,6 +3410,10 @@ int conv3d_min_softmax(const float* x, const int64_t* x_shape, const float* w, c
     sa.dsplit = p.dsplit;
     sa.ods = int((g.O[0] + p.dsplit - 1) / p.dsplit);
     sa.units = int(p.units);
+    sa.plane_stride = int(xst[perm[0]]);
+    sa.row_stride = int(xst[perm[1]]);
+    sa.ws0 = int(wst[perm[0]]);
+    sa.ws1 = int(wst[perm[1]]);
     return launch_stream_spec(sa, p, s);
   }
   FusedArgs a;

@@ -93,14 +93,16 @@ def test_conv_fwd_channels_last_validation_errors():
 
 
 def test_fused_plan_per_min_axis():
-    """conv_plan_describe's fused modes: min over depth takes the depth-streamed
-    specialisation at the fused workload's geometry; min over H or W the generic
-    fused kernel on the permuted axes (whose box then spans the min axis)."""
+    """conv_plan_describe's fused modes: min over depth or H takes the
+    depth-streamed specialisation at the fused workload's geometry (streaming
+    over the min axis, rows along W); min over W the generic fused kernel on
+    the permuted axes (whose box then spans the min axis)."""
     xs, ws = (128, 3, 24, 32, 32), (24, 3, 3, 3, 3)
-    assert "kernel=fused_stream" in ch.plan_describe(xs, ws, fused=True, min_dim=2)
-    for md in (3, 4):
+    for md in (2, 3):
         d = ch.plan_describe(xs, ws, fused=True, min_dim=md)
-        assert "kernel=fused_min_softmax_mfma4" in d, d
+        assert "kernel=fused_stream" in d, d
+    d = ch.plan_describe(xs, ws, fused=True, min_dim=4)
+    assert "kernel=fused_min_softmax_mfma4" in d, d
     one, zero = I32(1, 1, 1), I32(0, 0, 0)
     buf = ctypes.create_string_buffer(256)
     assert ch.lib().conv_plan_describe(1, I64(1, 8, 40), I64(4, 8, 3), one, one, zero, 1, 3, buf, 256) == -2
@@ -156,7 +158,7 @@ def test_fused_generic_groups_are_native():
     for ws, g, kred in [((24, 3, 3, 3, 3), 1, 81), ((24, 1, 3, 3, 3), 3, 27), ((12, 1, 3, 3, 3), 3, 27),
                         ((6, 2, 3, 3, 3), 3, 54)]:
         xg = (xs[0], ws[1] * g) + xs[2:]
-        desc = ch.plan_describe(xg, ws, 1, 1, 0, g, fused=True, min_dim=3)
+        desc = ch.plan_describe(xg, ws, 1, 1, 0, g, fused=True, min_dim=4)
         f = dict(t.split("=", 1) for t in desc.split() if "=" in t)
         assert f["kernel"] == "fused_min_softmax_mfma4" and int(f["groups"]) == g and int(f["kred"]) == kred, desc
         coutg = ws[0] // g

@@ -294,6 +294,32 @@ def test_fused_min_over_h_or_w(case):
     assert err <= FUSED_ATOL
 
 
+# Minimum over H on the depth-streamed kernel: it streams over H (the min
+# axis) with rows along D, at the fused workload's channel, kernel and W extents.
+STREAM_MIN_H_CASES = [
+    ("two_samples", (2, 3, 6, 32, 32), True),
+    ("ragged_d_tiles", (1, 3, 5, 20, 32), False),
+    ("workload_slice", (2, 3, 24, 32, 32), True),
+]
+
+
+@pytest.mark.parametrize("case", STREAM_MIN_H_CASES, ids=[c[0] for c in STREAM_MIN_H_CASES])
+def test_fused_stream_min_over_h(case):
+    name, xs, bias = case
+    ws = (24, 3, 3, 3, 3)
+    desc = ch.plan_describe(xs, ws, 1, 1, 0, 1, fused=True, min_dim=3)
+    assert "kernel=fused_stream" in desc, desc
+    r = np.random.default_rng(zlib.crc32(name.encode()))
+    x, w, b = _float_inputs(r, xs, ws, bias)
+    say(f"stream min over H {name}: {desc}")
+    y = gpu_fused(x, w, b, 1, 1, 0, 1, 3)
+    ref = oracle.conv3d_min_softmax(x, w, b, 1, 1, 0, 1, 3)
+    assert y.shape == ref.shape, (y.shape, ref.shape)
+    err = float(np.abs(y - ref).max())
+    say(f"  max|err| = {err:.3e}")
+    assert err <= FUSED_ATOL
+
+
 GROUPED_FUSED_CASES = [
     ("groups2_min_d", (2, 4, 6, 8, 9), (6, 2, 3, 3, 3), 1, 1, 0, 2, 2),
     ("groups3_min_h_strided", (1, 6, 5, 9, 8), (9, 2, 2, 3, 2), (1, 2, 1), 1, (1, 1, 0), 3, 3),
@@ -699,9 +725,9 @@ def test_nan_inputs_propagate_like_the_definition(case):
     np.testing.assert_array_equal(y[~nan_ref], ref[~nan_ref])
 
 
-@pytest.mark.parametrize("min_dim", [2, 3])
+@pytest.mark.parametrize("min_dim", [2, 3, 4])
 def test_fused_nan_inputs_propagate_like_torch_min(min_dim):
-    """min_dim 2 takes the depth-streamed kernel, 3 the generic one."""
+    """min_dim 2 and 3 take the depth-streamed kernel, 4 the generic one."""
     xs, ws = (2, 3, 6, 32, 32), (24, 3, 3, 3, 3)
     r = np.random.default_rng(77 + min_dim)
     x, w, b = _float_inputs(r, xs, ws, True)
