@@ -8,6 +8,9 @@ this package. The HIP library and its Python binding never do.
                            (x [N, spatial..., C_in] -> y [N, out..., C_out]): a
                            pure change of memory order around ``conv``.
 * ``conv3d_min_softmax`` -- conv (composed) -> min over one axis -> softmax over channels.
+* ``min_axis``           -- the minimum over one axis of a 5-D tensor (the fused op's
+                           second step on its own).
+* ``softmax_channels``   -- softmax over dim 1 (the fused op's last step on its own).
 * ``out_len``            -- the output-length formula of one axis.
 * ``brute``              -- a second, pure-Python statement of the same definition
                            for tiny inputs (pins oracle.c by brute force).
@@ -38,6 +41,10 @@ def _lib():
         lib.oracle_conv3d_min_softmax.restype = ctypes.c_int
         lib.oracle_conv3d_min_softmax.argtypes = [fp, i64p, fp, i64p, fp, ip, ip, ip, ctypes.c_int,
                                                   ctypes.c_int, fp]
+        lib.oracle_min_axis.restype = ctypes.c_int
+        lib.oracle_min_axis.argtypes = [fp, i64p, ctypes.c_int, fp]
+        lib.oracle_softmax_channels.restype = ctypes.c_int
+        lib.oracle_softmax_channels.argtypes = [fp, i64p, fp]
         _LIB = lib
     return _LIB
 
@@ -113,4 +120,29 @@ def conv3d_min_softmax(x, w, bias=None, stride=1, dilation=1, padding=0, groups=
                                           out.ctypes.data)
     if rc != 0:
         raise ValueError(f"oracle_conv3d_min_softmax rejected the arguments (code {rc})")
+    return out
+
+
+def min_axis(y, dim):
+    """Minimum of a 5-D float32 array over axis ``dim`` (2, 3 or 4); float32, exact."""
+    y = np.ascontiguousarray(y, dtype=np.float32)
+    if y.ndim != 5:
+        raise ValueError("min_axis takes a 5-D array")
+    out = np.empty(tuple(v for a, v in enumerate(y.shape) if a != dim), dtype=np.float32)
+    rc = _lib().oracle_min_axis(y.ctypes.data, _i64(y.shape), int(dim), out.ctypes.data)
+    if rc != 0:
+        raise ValueError(f"oracle_min_axis rejected the arguments (code {rc})")
+    return out
+
+
+def softmax_channels(z):
+    """Softmax over axis 1 of a float32 array [N, C, ...], computed in float64."""
+    z = np.ascontiguousarray(z, dtype=np.float32)
+    if z.ndim < 2:
+        raise ValueError("softmax_channels takes an array [N, C, ...]")
+    S = int(np.prod(z.shape[2:])) if z.ndim > 2 else 1
+    out = np.empty(z.shape, dtype=np.float64)
+    rc = _lib().oracle_softmax_channels(z.ctypes.data, _i64((z.shape[0], z.shape[1], S)), out.ctypes.data)
+    if rc != 0:
+        raise ValueError(f"oracle_softmax_channels rejected the arguments (code {rc})")
     return out

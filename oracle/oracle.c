@@ -199,3 +199,64 @@ int oracle_conv3d_min_softmax(const float *x, const int64_t *xs, const float *w,
     free(conv);
     return OR_OK;
 }
+
+/* The fused op's last two steps on their own, as the unfused form runs them
+ * after a separate conv (page l2_p24, opening turns: torch.min over `dim` of
+ * the conv output, then torch.softmax over dim 1).
+ *
+ * oracle_min_axis: y is a 5-D fp32 tensor [N, C, D, H, W] (ys: 5 entries),
+ * dim in {2, 3, 4}; out (fp32) is y's shape with that axis removed and holds
+ * the minimum along it. A minimum rounds nothing, so fp32 is exact. A NaN
+ * anywhere along the axis makes the result NaN (torch.min propagates it). */
+int oracle_min_axis(const float *y, const int64_t *ys, int dim, float *out) {
+    if (dim < 2 || dim > 4) return OR_ERR_ARG;
+    for (int a = 0; a < 5; a++) if (ys[a] < 1) return OR_ERR_ARG;
+    /* y viewed as [outer, R, inner] with R the reduced axis */
+    int64_t outer = 1, inner = 1;
+    for (int a = 0; a < dim; a++) outer *= ys[a];
+    for (int a = dim + 1; a < 5; a++) inner *= ys[a];
+    const int64_t R = ys[dim];
+#pragma omp parallel for
+    for (int64_t o = 0; o < outer; o++)
+        for (int64_t i = 0; i < inner; i++) {
+            const float *p = y + o * R * inner + i;
+            float v = p[0];
+            for (int64_t j = 1; j < R && !isnan(v); j++) {
+                const float u = p[j * inner];
+                if (u < v || isnan(u)) v = u;
+            }
+            out[o * inner + i] = v;
+        }
+    return OR_OK;
+}
+
+/* oracle_softmax_channels: z [N, C, S] fp32 (zs: 3 entries; S is the product
+ * of the trailing axes), out (double) the same shape:
+ *   out[n,c,s] = exp(z[n,c,s] - M) / sum_c' exp(z[n,c',s] - M),  M = max_c z[n,c,s]
+ * in double precision. A NaN among a position's channels makes all of its
+ * outputs NaN, as torch.softmax gives. */
+int oracle_softmax_channels(const float *z, const int64_t *zs, double *out) {
+    for (int a = 0; a < 3; a++) if (zs[a] < 1) return OR_ERR_ARG;
+    const int64_t N = zs[0], C = zs[1], S = zs[2];
+#pragma omp parallel for collapse(2)
+    for (int64_t n = 0; n < N; n++)
+        for (int64_t s = 0; s < S; s++) {
+            const float *p = z + n * C * S + s;
+            double *q = out + n * C * S + s;
+            int has_nan = 0;
+            double mx = -INFINITY;
+            for (int64_t c = 0; c < C; c++) {
+                const double v = p[c * S];
+                if (isnan(v)) has_nan = 1;
+                else if (v > mx) mx = v;
+            }
+            if (has_nan) {
+                for (int64_t c = 0; c < C; c++) q[c * S] = NAN;
+                continue;
+            }
+            double sum = 0.0;
+            for (int64_t c = 0; c < C; c++) sum += exp((double)p[c * S] - mx);
+            for (int64_t c = 0; c < C; c++) q[c * S] = exp((double)p[c * S] - mx) / sum;
+        }
+    return OR_OK;
+}

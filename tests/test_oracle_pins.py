@@ -6,7 +6,8 @@ independent pure-Python reading of the definition), a library routine the
 definition reduces to (torch's float64 CPU convolution), closed forms and
 invariants (delta kernel, linearity, bias additivity, group decomposition,
 dilation / stride equivalences, 1-D = 3-D with unit axes, the exactly-once
-input use of the stride-3 dilation-4 Conv1d, softmax rows summing to one).
+input use of the stride-3 dilation-4 Conv1d, softmax rows summing to one,
+the logistic form of a two-channel softmax, numpy's and torch's minima).
 A dropped term, a flipped sign or index, a transposed operand or a wrong
 padding offset in oracle.c fails at least the brute-force and delta tests.
 """
@@ -359,3 +360,78 @@ def test_fused_nan_propagates_like_torch_min():
         np.testing.assert_array_equal(np.isnan(yo), np.isnan(t))
         ok = ~np.isnan(t)
         np.testing.assert_allclose(yo[ok], t[ok], rtol=1e-12, atol=1e-15)
+
+
+# ------------------------------------------------ the unfused steps on their own
+@pytest.mark.parametrize("dim", [2, 3, 4])
+def test_min_axis_matches_numpy_and_brute_force(dim):
+    """numpy's reduction (a library routine) on a ragged shape, and a pure-Python
+    scan of the axis on a tiny one; both are exact, so equality is bitwise."""
+    r = _rng(40 + dim)
+    y = r.standard_normal((3, 5, 7, 6, 9)).astype(np.float32)
+    np.testing.assert_array_equal(oracle.min_axis(y, dim), y.min(axis=dim))
+    t = r.standard_normal((2, 2, 3, 2, 4)).astype(np.float32)
+    got = oracle.min_axis(t, dim)
+    for idx in itertools.product(*[range(v) for a, v in enumerate(t.shape) if a != dim]):
+        vals = [float(t[idx[:dim] + (j,) + idx[dim:]]) for j in range(t.shape[dim])]
+        assert got[idx] == min(vals)
+
+
+def test_min_axis_nan_and_unit_axis():
+    """A NaN anywhere along the axis gives NaN (numpy and torch.min both propagate
+    it; np.fmin would drop it); an axis of length 1 is the identity."""
+    r = _rng(44)
+    y = r.standard_normal((2, 3, 4, 5, 6)).astype(np.float32)
+    y[1, 2, 3, 0, 5] = np.nan
+    y[0, 0, 0, 4, 1] = np.nan
+    for dim in (2, 3, 4):
+        got = oracle.min_axis(y, dim)
+        ref = torch.min(torch.from_numpy(y), dim=dim)[0].numpy()
+        np.testing.assert_array_equal(np.isnan(got), np.isnan(ref))
+        assert np.isnan(got).sum() == 2
+        np.testing.assert_array_equal(got[~np.isnan(got)], ref[~np.isnan(ref)])
+    u = r.standard_normal((2, 3, 1, 4, 5)).astype(np.float32)
+    np.testing.assert_array_equal(oracle.min_axis(u, 2), u[:, :, 0])
+
+
+def test_softmax_channels_closed_forms():
+    """Two channels give the logistic function of their difference; equal channels
+    give 1/C; adding a constant to every channel changes nothing; rows sum to 1."""
+    r = _rng(45)
+    a = r.standard_normal((3, 1, 11)).astype(np.float32) * 4
+    b = r.standard_normal((3, 1, 11)).astype(np.float32) * 4
+    s = oracle.softmax_channels(np.concatenate([a, b], axis=1))
+    np.testing.assert_allclose(s[:, 0], 1.0 / (1.0 + np.exp(b[:, 0].astype(np.float64) - a[:, 0])),
+                               rtol=1e-14, atol=1e-300)
+    e = np.repeat(a, 7, axis=1)
+    np.testing.assert_allclose(oracle.softmax_channels(e), 1.0 / 7.0, rtol=1e-14)
+    z = (np.round(r.standard_normal((2, 24, 5, 6)) * 1024) / 1024).astype(np.float32)  # z + 8 exact in fp32
+    s = oracle.softmax_channels(z)
+    assert s.shape == z.shape
+    np.testing.assert_allclose(s.sum(axis=1), 1.0, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(oracle.softmax_channels(z + np.float32(8.0)), s, rtol=1e-12, atol=1e-15)
+
+
+def test_softmax_channels_matches_torch_float64_and_nan_rows():
+    r = _rng(46)
+    z = (r.standard_normal((3, 40, 7, 5)) * 6).astype(np.float32)
+    z[2, 17, 3, 1] = np.nan
+    got = oracle.softmax_channels(z)
+    ref = torch.softmax(torch.from_numpy(z).double(), dim=1).numpy()
+    np.testing.assert_array_equal(np.isnan(got), np.isnan(ref))
+    assert np.isnan(got).sum() == 40
+    ok = ~np.isnan(ref)
+    np.testing.assert_allclose(got[ok], ref[ok], rtol=1e-12, atol=1e-300)
+
+
+def test_unfused_steps_compose_to_the_fused_oracle():
+    """softmax_channels(min_axis(conv)) is the fused op; the only difference is the
+    fp32 rounding of the conv output before the minimum (the unfused chain stores
+    it in fp32), so the two agree to fp32 rounding of the logits."""
+    r = _rng(47)
+    x, w, b = _fused_case(r, N=2, C_in=3, C_out=24, D=7, H=6, W=8, k=(3, 3, 3))
+    for min_dim in (2, 3, 4):
+        y = oracle.conv(x, w, b).astype(np.float32)
+        got = oracle.softmax_channels(oracle.min_axis(y, min_dim))
+        ref = oracle.conv3d_min_softmax(x, w, b, 1, 1, 0, 1, min_dim)
+        np.testing.assert_allclose(got, ref, rtol=0, atol=1e-6)
