@@ -383,9 +383,9 @@ def main():
     ap.add_argument("--warm-seconds", type=float, default=WARM_S,
                     help="minimum seconds of back-to-back warm-up calls per workload")
     ap.add_argument("--unfused-chain", action="store_true",
-                    help="only run the fused workload as three separate steps (conv_fwd writing the 5-D result, "
-                         "torch.amin over depth, torch.softmax over channels) and time it; for measuring the "
-                         "HBM traffic the fused kernel avoids")
+                    help="only run the fused workload as three separate launches (conv_fwd writing the 5-D "
+                         "result, min_over_axis over depth, softmax_over_channels) and time the chain and each "
+                         "step; for measuring the HBM traffic the fused kernel avoids")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device-to-device copy of this many bytes per step "
                          "(calibrates rocprofv3's FETCH_SIZE / WRITE_SIZE against a known traffic)")
@@ -425,24 +425,45 @@ def main():
         name = "conv3d_min_softmax"
         cfg, x, w, b = make_device_inputs(name, torch, ch, synth)
         args4 = (cfg["stride"], cfg["dilation"], cfg["padding"], cfg["groups"])
+        y5 = ch.conv_fwd(x, w, b, *args4)
+        m = ch.min_over_axis(y5, 2)
+        sm = ch.softmax_over_channels(m)
+        steps = {
+            "conv_fwd": lambda: ch.conv_fwd(x, w, b, *args4, out=y5),
+            "min_over_axis": lambda: ch.min_over_axis(y5, 2, out=m),
+            "softmax_over_channels": lambda: ch.softmax_over_channels(m, out=sm),
+        }
 
         def chain():
-            y5 = ch.conv_fwd(x, w, b, *args4)
-            return torch.softmax(torch.amin(y5, dim=2), dim=1)
+            for f in steps.values():
+                f()
 
         fused = ch.conv3d_min_softmax(x, w, b, *args4)
-        err = float((chain() - fused).abs().max())
-        for _ in range(args.warmup):
-            chain()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(torch.cuda.current_stream())
-        for _ in range(args.steps):
-            chain()
-        e1.record(torch.cuda.current_stream())
-        torch.cuda.synchronize()
+        chain()
+        err = float((sm - fused).abs().max())
+        stream = torch.cuda.current_stream()
+
+        def timed(f):
+            for _ in range(args.warmup):
+                f()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(args.steps):
+                f()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / args.steps
+
+        nbytes = {"conv_fwd": 4 * (x.numel() + w.numel() + (b.numel() if b is not None else 0) + y5.numel()),
+                  "min_over_axis": 4 * (y5.numel() + m.numel()),
+                  "softmax_over_channels": 4 * 2 * m.numel()}
+        per = {}
+        for k, f in steps.items():
+            ms = timed(f)
+            per[k] = {"ms": round(ms, 5), "alg_bytes": nbytes[k], "gbs": round(nbytes[k] / ms / 1e6, 1)}
         print(json.dumps({"unfused_chain": name, "steps": args.steps, "warmup": args.warmup,
-                          "ms_per_chain": round(e0.elapsed_time(e1) / args.steps, 5),
+                          "ms_per_chain": round(timed(chain), 5), "per_step": per,
                           "max_abs_diff_vs_fused": err}), flush=True)
         return
 

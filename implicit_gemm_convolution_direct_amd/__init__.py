@@ -12,6 +12,8 @@ Operations (POPCORNBENCH "Kimi-K2.6" pages l1_p60, l1_p76, l2_p24, opening turns
 * ``conv3d_min_softmax(x, w, bias, stride, dilation, padding, groups, min_dim=2)`` --
   softmax over channels of the minimum over depth of Conv3d, without writing the
   5-D conv result.
+* ``min_over_axis(y, dim)``, ``softmax_over_channels(z)`` -- that op's last two
+  steps as separate launches (its unfused form, measured beside it).
 """
 import ctypes
 import os
@@ -27,8 +29,9 @@ STATUS_NAMES = {
     -5: "CONV_ERR_PARAM", -6: "CONV_ERR_EMPTY_OUTPUT", -7: "CONV_ERR_UNSUPPORTED", -8: "CONV_ERR_OVERFLOW",
     -9: "CONV_ERR_HIP",
 }
-EXPORTED = ["conv_out_shape", "conv_fwd", "conv_fwd_channels_last", "conv3d_min_softmax", "conv_status_string",
-            "conv_plan_describe", "convhip_synth_fill", "convhip_peak_probe"]
+EXPORTED = ["conv_out_shape", "conv_fwd", "conv_fwd_channels_last", "conv3d_min_softmax", "min_over_axis",
+            "softmax_over_channels", "conv_status_string", "conv_plan_describe", "convhip_synth_fill",
+            "convhip_peak_probe"]
 
 
 class ConvError(RuntimeError):
@@ -60,6 +63,10 @@ def lib():
         L.conv_fwd_channels_last.argtypes = [ctypes.c_int, vp, i64p, vp, i64p, vp, ip, ip, ip, ctypes.c_int, vp, vp]
         L.conv3d_min_softmax.restype = ctypes.c_int
         L.conv3d_min_softmax.argtypes = [vp, i64p, vp, i64p, vp, ip, ip, ip, ctypes.c_int, ctypes.c_int, vp, vp]
+        L.min_over_axis.restype = ctypes.c_int
+        L.min_over_axis.argtypes = [vp, i64p, ctypes.c_int, vp, vp]
+        L.softmax_over_channels.restype = ctypes.c_int
+        L.softmax_over_channels.argtypes = [vp, i64p, vp, vp]
         L.conv_status_string.restype = ctypes.c_char_p
         L.conv_status_string.argtypes = [ctypes.c_int]
         L.conv_plan_describe.restype = ctypes.c_int
@@ -254,6 +261,47 @@ def conv3d_min_softmax(x, w, bias=None, stride=1, dilation=1, padding=0, groups=
                                   s, d, p, int(groups), int(min_dim), out.data_ptr(), _stream_handle(x.device))
     if rc != CONV_OK:
         raise ConvError(rc, "conv3d_min_softmax")
+    return out
+
+
+def _check_out(out, shape, like):
+    if out is None:
+        return torch.empty(shape, dtype=torch.float32, device=like.device)
+    _check_tensor(out, "out")
+    if out.device != like.device:
+        raise ValueError(f"out is on {out.device}, the input on {like.device}")
+    if tuple(out.shape) != tuple(shape):
+        raise ValueError(f"out has shape {tuple(out.shape)}, expected {tuple(shape)}")
+    return out
+
+
+def min_over_axis(y, dim, out=None):
+    """torch.amin(y, dim) of a 5-D fp32 GPU tensor for dim 2, 3 or 4 (NaN-propagating)."""
+    _check_tensor(y, "y")
+    if y.dim() != 5:
+        raise ValueError("y must be 5-D")
+    if dim not in (2, 3, 4):
+        raise ValueError("dim must be 2, 3 or 4")
+    out = _check_out(out, tuple(v for a, v in enumerate(y.shape) if a != dim), y)
+    rc = lib().min_over_axis(y.data_ptr(), _i64(y.shape), int(dim), out.data_ptr(), _stream_handle(y.device))
+    if rc != CONV_OK:
+        raise ConvError(rc, "min_over_axis")
+    return out
+
+
+def softmax_over_channels(z, out=None):
+    """torch.softmax(z, dim=1) of an fp32 GPU tensor [N, C, ...]."""
+    _check_tensor(z, "z")
+    if z.dim() < 2:
+        raise ValueError("z must be [N, C, ...]")
+    out = _check_out(out, tuple(z.shape), z)
+    S = 1
+    for v in z.shape[2:]:
+        S *= int(v)
+    rc = lib().softmax_over_channels(z.data_ptr(), _i64((z.shape[0], z.shape[1], S)), out.data_ptr(),
+                                     _stream_handle(z.device))
+    if rc != CONV_OK:
+        raise ConvError(rc, "softmax_over_channels")
     return out
 
 

@@ -7,6 +7,7 @@
  *
  *   conv_fwd            y = Conv{1,3}d(x, w, bias; stride, dilation, zero padding, groups)
  *   conv3d_min_softmax  y = softmax over channels of (min over depth of Conv3d(x, w, bias))
+ *   min_over_axis, softmax_over_channels   that op's last two steps, unfused
  *
  * Conventions shared by every entry point
  *   - Tensors are fp32, contiguous, row-major (NCL / NCDHW). Pointers named x, w,
@@ -128,6 +129,34 @@ int conv3d_min_softmax(const float *x, const int64_t *x_shape,
                        const float *w, const int64_t *w_shape, const float *bias,
                        const int *stride, const int *dilation, const int *padding, int groups,
                        int min_dim, float *y, convhip_stream_t stream);
+
+/*
+ * The fused op's last two steps on their own, for running it unfused after
+ * conv_fwd (page l2_p24, opening turns: torch.min over the chosen axis of the
+ * Conv3d output, then torch.softmax over channels; the page also weighs writing
+ * only these two steps as kernels over the library conv's output). The library
+ * uses them to measure that chain beside conv3d_min_softmax. Both read their
+ * input once and write their output once (HBM-bound).
+ *
+ * min_over_axis: y [N, C, D, H, W] (y_shape: 5 host entries), dim in {2, 3, 4};
+ * out is y's shape with axis `dim` removed, out = the minimum along that axis.
+ * Exact (a minimum rounds nothing). A NaN anywhere along the axis gives NaN, as
+ * torch.min does. y and out are device pointers; out must not overlap y.
+ * Returns CONV_OK, CONV_ERR_NULL, CONV_ERR_SHAPE (an entry < 1), CONV_ERR_PARAM
+ * (dim outside 2..4), CONV_ERR_OVERFLOW (more than 2^40 elements) or CONV_ERR_HIP.
+ */
+int min_over_axis(const float *y, const int64_t *y_shape, int dim, float *out, convhip_stream_t stream);
+
+/*
+ * softmax_over_channels: z [N, C, S] (z_shape: 3 host entries; S is the product
+ * of the trailing axes of an [N, C, ...] tensor), out the same shape:
+ *   out[n,c,s] = exp(z[n,c,s] - M) / sum_c' exp(z[n,c',s] - M),  M = max_c z[n,c,s]
+ * in fp32 (expf, one division per output). A NaN among a position's channels
+ * makes that position's outputs NaN, as torch.softmax does; infinities:
+ * unspecified. z and out are device pointers; out must not overlap z.
+ * Returns CONV_OK, CONV_ERR_NULL, CONV_ERR_SHAPE, CONV_ERR_OVERFLOW or CONV_ERR_HIP.
+ */
+int softmax_over_channels(const float *z, const int64_t *z_shape, float *out, convhip_stream_t stream);
 
 /*
  * Static text for a status code (never NULL). The codes name the failure

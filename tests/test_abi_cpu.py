@@ -263,3 +263,21 @@ def test_general_conv3d_kernel_choice(monkeypatch):
     # a plane of 12 tiles (16 x 12 outputs) is not the specialisation's 13
     d = ch.plan_describe((2, 16, 8, 32, 24), cfg["w"], *args[2:])
     assert "kernel=conv_tap_kstream" not in d, d
+
+
+def test_unfused_steps_validation_errors():
+    lib = ch.lib()
+    ys = I64(2, 24, 22, 30, 30)
+    assert lib.min_over_axis(FAKE, None, 2, FAKE, None) == -1
+    assert lib.min_over_axis(None, ys, 2, FAKE, None) == -1
+    assert lib.min_over_axis(FAKE, ys, 2, None, None) == -1
+    assert lib.min_over_axis(FAKE, ys, 1, FAKE, None) == -5
+    assert lib.min_over_axis(FAKE, ys, 5, FAKE, None) == -5
+    assert lib.min_over_axis(FAKE, I64(2, 24, 0, 30, 30), 2, FAKE, None) == -3
+    assert lib.min_over_axis(FAKE, I64(1 << 20, 1 << 10, 1 << 10, 4, 4), 2, FAKE, None) == -8
+    zs = I64(2, 24, 900)
+    assert lib.softmax_over_channels(FAKE, None, FAKE, None) == -1
+    assert lib.softmax_over_channels(None, zs, FAKE, None) == -1
+    assert lib.softmax_over_channels(FAKE, zs, None, None) == -1
+    assert lib.softmax_over_channels(FAKE, I64(2, 0, 900), FAKE, None) == -3
+    assert lib.softmax_over_channels(FAKE, I64(1 << 20, 1 << 12, 1 << 12), FAKE, None) == -8
