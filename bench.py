@@ -12,6 +12,9 @@ also times every other workload and reports it under "shapes":
   conv_fwd_channels_last ("<workload>_channels_last");
 * the five workloads on the generic kernels, with the build-time
   specialisations switched off ("<workload>_generic", CONVHIP_TAP=0);
+* the four plain convolutions on the vector-ALU direct kernel
+  ("<workload>_valu", CONVHIP_VALU=1): the per-shape comparison of the vector
+  ALU with the matrix cores;
 * neighbouring shapes that no specialisation was built for, and the fused op
   with the minimum over H or W and with groups (synth.VARIANTS).
 
@@ -50,14 +53,17 @@ HEADLINE = "long_conv1d"
 HEADLINE_SLICE = (0, 63)  # batch samples the oracle computes for the CPU baseline and parity
 CL_SUFFIX = "_channels_last"
 GEN_SUFFIX = "_generic"
+VALU_SUFFIX = "_valu"
+VALU_WORKLOADS = ("tiny_conv3d", "general_conv3d", "asym_conv3d", "long_conv1d")
 WORKLOAD_NAMES = ["tiny_conv3d", "general_conv3d", "conv3d_min_softmax", "asym_conv3d", "long_conv1d"]
 ORDER = (WORKLOAD_NAMES
          + [n + CL_SUFFIX for n in ("tiny_conv3d", "general_conv3d", "asym_conv3d", "long_conv1d")]
          + [n + GEN_SUFFIX for n in WORKLOAD_NAMES]
+         + [n + VALU_SUFFIX for n in VALU_WORKLOADS]
          + ["asym_conv3d_48", "general_conv3d_24", "long_conv1d_c96_d2", "conv3d_min_softmax_min_h",
             "conv3d_min_softmax_min_w", "conv3d_min_softmax_groups3"])
 KERNEL_SOURCES = [os.path.join(ROOT, "implicit_gemm_convolution_direct_amd", "csrc", f)
-                  for f in ("conv_kernels.hip", "convhip_plan.cpp", "convhip_plan.h")]
+                  for f in ("conv_kernels.hip", "valu_kernels.hip", "convhip_plan.cpp", "convhip_plan.h")]
 
 
 def kernel_source_hash():
@@ -111,20 +117,26 @@ def read_traffic(name):
 
 
 def split_name(name):
-    """(workload, channels_last, generic): a "<workload>_channels_last" entry times
+    """(workload, channels_last, mode): a "<workload>_channels_last" entry times
     the same workload with x [N, spatial..., C_in] and y [N, out..., C_out]; a
-    "<workload>_generic" entry times it with the build-time specialisations off."""
+    "<workload>_generic" entry (mode "generic") times it with the build-time
+    specialisations off; a "<workload>_valu" entry (mode "valu") on the
+    vector-ALU direct kernel. mode is None otherwise."""
     if name.endswith(CL_SUFFIX):
-        return name[:-len(CL_SUFFIX)], True, False
+        return name[:-len(CL_SUFFIX)], True, None
     if name.endswith(GEN_SUFFIX):
-        return name[:-len(GEN_SUFFIX)], False, True
-    return name, False, False
+        return name[:-len(GEN_SUFFIX)], False, "generic"
+    if name.endswith(VALU_SUFFIX):
+        return name[:-len(VALU_SUFFIX)], False, "valu"
+    return name, False, None
 
 
 def roofline(tflops, name, latency_bound=False):
-    """The roofline object of one entry: every workload here contracts on the
-    fp32 matrix cores (tiny Conv3d: launch latency binds before either peak)."""
-    rec = {"bound": "mfma", "achieved": tflops, "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
+    """The roofline object of one entry: the fp32 matrix cores, or for "_valu"
+    entries the vector ALU ("alu"; its fp32 peak is the same 157.3 TFLOP/s);
+    tiny Conv3d: launch latency binds before either peak."""
+    bound = "alu" if split_name(name)[2] == "valu" else "mfma"
+    rec = {"bound": bound, "achieved": tflops, "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
            "frac": round(tflops / PEAK_FP32_TFLOPS, 4), "traffic": read_traffic(name)}
     if latency_bound:
         rec["limited_by"] = "launch latency"
@@ -151,18 +163,20 @@ def make_device_inputs(name, torch, ch, synth, channels_last=False):
 
 
 def time_workload(name, steps, warmup, torch, ch, synth, flush=None, warm_s=WARM_S):
-    base, cl, generic = split_name(name)
-    saved_tap = os.environ.get("CONVHIP_TAP")
-    if generic:
-        os.environ["CONVHIP_TAP"] = "0"  # read by the library at every call
+    base, cl, mode = split_name(name)
+    # Switches read by the library at every call.
+    var = {"generic": ("CONVHIP_TAP", "0"), "valu": ("CONVHIP_VALU", "1")}.get(mode)
+    saved = os.environ.get(var[0]) if var else None
+    if var:
+        os.environ[var[0]] = var[1]
     try:
         return _time_workload(name, base, cl, steps, warmup, torch, ch, synth, flush, warm_s)
     finally:
-        if generic:
-            if saved_tap is None:
-                del os.environ["CONVHIP_TAP"]
+        if var:
+            if saved is None:
+                del os.environ[var[0]]
             else:
-                os.environ["CONVHIP_TAP"] = saved_tap
+                os.environ[var[0]] = saved
 
 
 def _time_workload(name, base, cl, steps, warmup, torch, ch, synth, flush, warm_s):

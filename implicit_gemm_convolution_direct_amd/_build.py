@@ -6,7 +6,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libconvhip.so")
 SOURCES = [os.path.join(CSRC, "conv_kernels.hip"), os.path.join(CSRC, "unfused_kernels.hip"),
-           os.path.join(CSRC, "convhip_plan.cpp")]
+           os.path.join(CSRC, "valu_kernels.hip"), os.path.join(CSRC, "convhip_plan.cpp")]
 HEADERS = [os.path.join(CSRC, "convhip_plan.h"),
            os.path.join(os.path.dirname(HERE), "include", "convhip.h")]
 

@@ -3047,6 +3047,13 @@ static int split_spin_cap() {
 // fits, else the pipelined channel-split kernel); CONVHIP_SPLIT_PIPE=1 forces
 // the pipelined channel-split kernel, =0 the one whose cross-wave sum follows
 // all products (tests and A/B timings run each).
+// CONVHIP_VALU=1: conv_fwd runs the vector-ALU direct kernel wherever it fits
+// (for measuring it against the matrix-core kernels, and for its tests).
+static bool force_valu() {
+  const char* s = std::getenv("CONVHIP_VALU");
+  return s && *s && std::atoi(s) != 0;
+}
+
 static int split_kernel_choice() {
   const char* s = std::getenv("CONVHIP_SPLIT_PIPE");
   if (!s || !*s) return 0;
@@ -3322,10 +3329,22 @@ int conv_plan_describe(int nd, const int64_t* x_shape, const int64_t* w_shape, c
     if (rc != CONV_OK) return rc;
     s = describe(fused_geom(g, min_dim), p);
   } else {
+    ValuPlan vp;
     ConvPlan p;
-    rc = plan_conv(g, &p, forced_conv_cfg(), 256, use_tap(), split_kernel_choice());
-    if (rc != CONV_OK) return rc;
-    s = describe(g, p);
+    bool valu = fused == 0 && force_valu() && plan_valu(g, &vp) == CONV_OK;
+    if (!valu) {
+      rc = plan_conv(g, &p, forced_conv_cfg(), 256, use_tap(), split_kernel_choice());
+      valu = fused == 0 && rc == CONV_ERR_UNSUPPORTED && plan_valu(g, &vp) == CONV_OK;
+      if (!valu && rc != CONV_OK) return rc;
+    }
+    if (valu) {
+      char t[256];
+      std::snprintf(t, sizeof t, "conv_valu co=%d pp=%d threads=%d pairs=%d grid=%lldx%lld lds=%d", vp.co,
+                    vp.pp, vp.threads, vp.pps, (long long)vp.grid[0], (long long)vp.grid[1], vp.lds_bytes);
+      s = t;
+    } else {
+      s = describe(g, p);
+    }
   }
   std::snprintf(buf, size_t(buflen), "%s", s.c_str());
   return CONV_OK;
@@ -3338,12 +3357,17 @@ int conv_fwd(int nd, const float* x, const int64_t* x_shape, const float* w, con
   int rc = make_geom(nd, x_shape, w_shape, stride, dilation, padding, groups, &g);
   if (rc != CONV_OK) return rc;
   if (!x || !w || !y) return CONV_ERR_NULL;
+  ValuPlan vp;
+  if (force_valu() && plan_valu(g, &vp) == CONV_OK) return launch_valu(g, vp, x, w, bias, y, stream);
   ConvPlan p;
   // The specialised kernels copy weights (and 1-D input rows) in 16-byte chunks:
   // they need 16-byte aligned pointers (any tensor allocation is; a sliced view
   // may not be).
   const bool aligned = ((reinterpret_cast<uintptr_t>(w) | reinterpret_cast<uintptr_t>(x)) & 15) == 0;
   rc = plan_conv(g, &p, forced_conv_cfg(), device_num_cu(), aligned ? use_tap() : 0, split_kernel_choice());
+  // Geometries whose tiles the matrix-core kernels cannot stage in LDS (large
+  // kernels over many channels) run on the vector-ALU kernel.
+  if (rc == CONV_ERR_UNSUPPORTED && plan_valu(g, &vp) == CONV_OK) return launch_valu(g, vp, x, w, bias, y, stream);
   if (rc != CONV_OK) return rc;
   ConvArgs a = conv_args(g, p, x, w, bias, y);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);

@@ -209,6 +209,24 @@ const TapClSpecDesc* tap_cl_specs(int* count);
 int plan_conv(const Geom& g, ConvPlan* p, int force_cfg = -1, int num_cu = 256, int use_tap = -1,
               int split_kernel = 0);
 
+// Direct convolution on the vector ALU (conv_valu_kernel, valu_kernels.hip):
+// any NCDHW geometry whose weights of one (input channel, depth tap) pair,
+// double-buffered (2 x kH x kW x CO floats), fit in 64 KiB of LDS. CO output
+// channels and pp positions per lane, `threads` lanes per workgroup; grid[0]
+// position blocks, grid[1] = groups x ncob channel blocks. conv_fwd takes it for geometries the
+// matrix-core kernels cannot stage, and when CONVHIP_VALU=1 forces it.
+struct ValuPlan {
+  int co = 0, pp = 0, ncob = 0;
+  int threads = 256;
+  int pps = 1;  // (input channel, depth tap) pairs per staged LDS buffer
+  int64_t grid[2] = {0, 0};
+  int lds_bytes = 0;
+};
+int plan_valu(const Geom& g, ValuPlan* p);
+// Enqueue the kernel on `stream` (a hipStream_t). Returns a conv_status.
+int launch_valu(const Geom& g, const ValuPlan& p, const float* x, const float* w, const float* bias, float* y,
+                void* stream);
+
 // Build-time specialisations of the depth-streamed fused kernel (stride 1,
 // dilation 1, groups 1, kD = 3, min over depth): X(id, CIN, KH, KW, NG, O2, ROWS, RT)
 // with NG groups of 4 output channels, W_out = O2 and at most ROWS staged input

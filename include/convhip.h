@@ -79,6 +79,10 @@ int conv_out_shape(int nd, const int64_t *in_spatial, const int64_t *k_spatial,
  * fp32 products and fp32 accumulation in an unspecified order. A NaN input
  * makes NaN every output whose receptive field holds it; infinite inputs give
  * unspecified results (a padded zero-weight term may turn them into NaN).
+ * Kernels: fp32 matrix cores wherever a tile's input box fits in LDS; other
+ * geometries (large kernels over many channels) run on a vector-ALU direct
+ * kernel. CONV_ERR_UNSUPPORTED only if neither fits: the vector kernel needs
+ * 2 * kH * kW * CO * 4 bytes <= 64 KiB (CO = 8 if C_out/groups <= 8, else 16).
  */
 int conv_fwd(int nd,
              const float *x, const int64_t *x_shape,

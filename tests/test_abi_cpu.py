@@ -281,3 +281,29 @@ def test_unfused_steps_validation_errors():
     assert lib.softmax_over_channels(FAKE, zs, None, None) == -1
     assert lib.softmax_over_channels(FAKE, I64(2, 0, 900), FAKE, None) == -3
     assert lib.softmax_over_channels(FAKE, I64(1 << 20, 1 << 12, 1 << 12), FAKE, None) == -8
+
+
+def test_valu_switch_plans_the_vector_kernel(monkeypatch):
+    """CONVHIP_VALU=1 routes conv_fwd to the vector-ALU direct kernel (8 or 16
+    output channels per lane); channels-last and the fused op are unaffected."""
+    monkeypatch.setenv("CONVHIP_VALU", "1")
+    d = ch.plan_describe((2, 3, 16, 16, 16), (8, 3, 3, 3, 3))
+    assert d.startswith("conv_valu co=8 pp=1 threads=64 pairs=9 grid=86x1"), d
+    d = ch.plan_describe((4, 16, 32, 32, 32), (32, 8, 3, 5, 7), (1, 2, 2), (1, 1, 2), (1, 2, 3), 2)
+    assert d.startswith("conv_valu co=16 pp=1 threads=64 pairs=1 grid=416x2"), d
+    d = ch.plan_describe((16, 3, 64, 64, 64), (64, 3, 3, 5, 7))
+    assert d.startswith("conv_valu co=16 pp=2 threads=256 pairs=7 grid=6743x4"), d
+    with pytest.raises(ch.ConvError) as e:  # 2 x 92 x 92 x 8 x 4 B > 64 KiB of LDS, and no box fits either
+        ch.plan_describe((1, 16, 4, 96, 96), (8, 16, 3, 92, 92))
+    assert e.value.status == -7
+    assert "conv_valu" not in ch.plan_describe((2, 16, 16, 16, 3), (8, 3, 3, 3, 3), channels_last=True)
+    assert "conv_valu" not in ch.plan_describe((128, 3, 24, 32, 32), (24, 3, 3, 3, 3), fused=True)
+
+
+def test_large_kernels_plan_the_vector_fallback():
+    """The matrix-core kernels cannot stage an 11^3 kernel over 16 channels; the
+    vector-ALU kernel takes it (weights of one channel and depth tap in LDS)."""
+    d = ch.plan_describe((2, 16, 16, 16, 16), (8, 16, 11, 11, 11))
+    assert d.startswith("conv_valu co=8 pp=1"), d
+    d = ch.plan_describe((1, 4, 24, 24, 24), (20, 2, 9, 9, 9), (2, 1, 1), (1, 2, 1), (3, 4, 4), 2)
+    assert d.startswith("conv_valu co=16 pp=1"), d
