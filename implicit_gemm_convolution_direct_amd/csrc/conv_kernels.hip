@@ -2604,9 +2604,13 @@ __global__ __launch_bounds__(256) void fused_min_softmax_mfma4_kernel(FusedArgs 
 //   partial minima of the depth ranges meet in LDS first.
 // ---------------------------------------------------------------------------
 
-template <int CIN, int KH, int KW_, int NG, int O2, int ROWS, int RT>
+template <int CIN, int KH, int KW_, int NG, int O2, int ROWS, int RT, int GRP>
 struct StreamGeo {
   static constexpr int CIN_ = CIN, NG_ = NG, O2_ = O2, KW = KW_;
+  // Conv groups: a channel block of group gq reduces over input channels
+  // gq*CG .. gq*CG + CG - 1 only; NQG blocks per group.
+  static constexpr int GRP_ = GRP, CG = CIN / GRP, NQG = NG / GRP;
+  static_assert(CIN % GRP == 0 && NG % GRP == 0, "whole channel blocks per group");
   static constexpr int RT_ = RT;  // > 0: a wave tile is RT whole output rows; 0: 64 flattened positions
   static_assert(RT * O2 <= 64, "a row tile fits the wave");
   static constexpr int KD = 3;
@@ -2621,15 +2625,16 @@ struct StreamGeo {
   static constexpr int KHW = KH * KW_;
   static constexpr int KVOL = KD * KHW;
   static constexpr int KRED = CIN * KVOL;
+  static constexpr int KREDG = CG * KVOL;        // reduction length of one output channel
   static constexpr int NT = CIN * KHW;           // staged values read per plane
   // With 16 or more output channels, channels 0..15 run on the 16x16x1 4-block
   // form (A broadcast from one block: one instruction per input value) and the
   // rest on the 4x4x1 16-block form; else every channel on the 4x4x1 form.
-  static constexpr bool MIX = NG >= 4;
+  static constexpr bool MIX = NG >= 4 && GRP == 1;
   static constexpr int NA16 = (KRED + 3) / 4;     // 16x16 weights: register j holds k = 4j .. 4j+3
   static constexpr int NG4 = MIX ? NG - 4 : NG;   // 4-channel groups on the 4x4x1 form
   static constexpr int CO4 = MIX ? 16 : 0;        // their first channel
-  static constexpr int NPAIR = NG4 * KRED;        // (channel group, reduction index) pairs
+  static constexpr int NPAIR = NG4 * KREDG;       // (channel block, reduction index) pairs
   static constexpr int NAREG = (NPAIR + 15) / 16;
   static constexpr int WAVES = 4;                // waves per workgroup
   // The rings; after the depth loop (depth range split over waves) the partial
@@ -2699,15 +2704,15 @@ __global__ __launch_bounds__(256, 4) void fused_stream_kernel(StreamArgs a) {
   const int od1 = live ? min(a.O0, od0 + a.ods) : od0;
   float* ring = smem + wave * (G::NSLOT * G::SLOT);
 
-  // Weights of the 4x4x1 form: register r, lane 4b + i holds w[CO4 + 4g + i][k]
-  // for pair 16r + b = g * KRED + k.
+  // Weights of the 4x4x1 form: register r, lane 4b + i holds w[CO4 + 4q + i][k]
+  // for pair 16r + b = q * KREDG + k (k within the block's group).
   float aw[G::NAREG];
 #pragma unroll
   for (int r = 0; r < G::NAREG; r++) {
     const int pair = 16 * r + (lane >> 2);
-    const int gq = pair / G::KRED, k = pair - gq * G::KRED;
+    const int gq = pair / G::KREDG, k = pair - gq * G::KREDG;
     const int co = G::CO4 + 4 * gq + (lane & 3);
-    aw[r] = (live && pair < G::NPAIR && co < a.Cout) ? a.w[co * G::KRED + stream_widx<G>(k, a)] : 0.0f;
+    aw[r] = (live && pair < G::NPAIR && co < a.Cout) ? a.w[co * G::KREDG + stream_widx<G>(k, a)] : 0.0f;
   }
   // Weights of the 16x16x1 form: register j, lane 16b + m holds w[m][4j + b].
   float a16[G::MIX ? G::NA16 : 1];
@@ -2816,12 +2821,15 @@ __global__ __launch_bounds__(256, 4) void fused_stream_kernel(StreamArgs a) {
         }
         static_for<G::NG4>([&](auto QQ) {
           constexpr int q = decltype(QQ)::value;
-          constexpr int pair = q * G::KRED + k;
-          constexpr int r = pair / 16, ab = pair % 16;
-          if constexpr (g == 0 && hw == 0)
-            acc[q] = __builtin_amdgcn_mfma_f32_4x4x1f32(aw[r], bv[cur][hw], v4f{0.f, 0.f, 0.f, 0.f}, 4, ab, 0);
-          else
-            acc[q] = __builtin_amdgcn_mfma_f32_4x4x1f32(aw[r], bv[cur][hw], acc[q], 4, ab, 0);
+          // Only the blocks of input channel c's group (all of them without groups).
+          if constexpr (G::GRP_ == 1 || q / G::NQG == c / G::CG) {
+            constexpr int pair = q * G::KREDG + (k - (c / G::CG) * G::CG * G::KVOL);
+            constexpr int r = pair / 16, ab = pair % 16;
+            if constexpr (kd == 0 && c % G::CG == 0 && hw == 0)
+              acc[q] = __builtin_amdgcn_mfma_f32_4x4x1f32(aw[r], bv[cur][hw], v4f{0.f, 0.f, 0.f, 0.f}, 4, ab, 0);
+            else
+              acc[q] = __builtin_amdgcn_mfma_f32_4x4x1f32(aw[r], bv[cur][hw], acc[q], 4, ab, 0);
+          }
         });
       });
       __builtin_amdgcn_sched_barrier(0);
@@ -3166,9 +3174,9 @@ static int launch_fused_ng(const FusedArgs& args, const FusedPlan& p, hipStream_
   return hipGetLastError() == hipSuccess ? CONV_OK : CONV_ERR_HIP;
 }
 
-template <int CIN, int KH, int KW, int NG, int O2, int ROWS, int RT>
+template <int CIN, int KH, int KW, int NG, int O2, int ROWS, int RT, int GRP>
 static int launch_stream(const StreamArgs& args, const FusedPlan& p, hipStream_t stream) {
-  using G = StreamGeo<CIN, KH, KW, NG, O2, ROWS, RT>;
+  using G = StreamGeo<CIN, KH, KW, NG, O2, ROWS, RT, GRP>;
   if (int64_t(4) * G::LDS_FLOATS != p.lds_bytes || G::WAVES % p.dsplit != 0) return CONV_ERR_UNSUPPORTED;
   hipLaunchKernelGGL(fused_stream_kernel<G>, dim3(unsigned(p.grid[0])), dim3(64 * G::WAVES), 0, stream, args);
   return hipGetLastError() == hipSuccess ? CONV_OK : CONV_ERR_HIP;
@@ -3176,9 +3184,9 @@ static int launch_stream(const StreamArgs& args, const FusedPlan& p, hipStream_t
 
 static int launch_stream_spec(const StreamArgs& args, const FusedPlan& p, hipStream_t stream) {
   switch (p.spec) {
-#define CONVHIP_FUSED_CASE(id, CIN, KH, KW, NG, O2, ROWS, RT) \
-  case id:                                                  \
-    return launch_stream<CIN, KH, KW, NG, O2, ROWS, RT>(args, p, stream);
+#define CONVHIP_FUSED_CASE(id, CIN, KH, KW, NG, O2, ROWS, RT, GRP) \
+  case id:                                                       \
+    return launch_stream<CIN, KH, KW, NG, O2, ROWS, RT, GRP>(args, p, stream);
     CONVHIP_FUSED_SPECS(CONVHIP_FUSED_CASE)
 #undef CONVHIP_FUSED_CASE
     default: return CONV_ERR_UNSUPPORTED;

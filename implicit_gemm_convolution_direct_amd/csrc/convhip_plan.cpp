@@ -573,7 +573,7 @@ int plan_conv(const Geom& g, ConvPlan* out, int force_cfg, int num_cu, int use_t
   return CONV_OK;
 }
 
-#define CONVHIP_FUSED_DESC(id, CIN, KH, KW, NG, O2, ROWS, RT) {id, CIN, KH, KW, NG, O2, ROWS, RT},
+#define CONVHIP_FUSED_DESC(id, CIN, KH, KW, NG, O2, ROWS, RT, GRP) {id, CIN, KH, KW, NG, O2, ROWS, RT, GRP},
 static const FusedSpecDesc kFusedSpecs[] = {CONVHIP_FUSED_SPECS(CONVHIP_FUSED_DESC)};
 #undef CONVHIP_FUSED_DESC
 
@@ -584,7 +584,9 @@ const FusedSpecDesc* fused_specs(int* count) {
 
 // Plan of a depth-streamed specialisation if the geometry is the one it was built for.
 static bool plan_fused_stream(const Geom& g, const FusedSpecDesc& d, FusedPlan* p) {
-  if (g.G != 1 || g.Cin != d.CIN || g.K[0] != 3 || g.K[1] != d.KH || g.K[2] != d.KW) return false;
+  if (g.G != d.GRP || g.Cin != d.CIN || g.K[0] != 3 || g.K[1] != d.KH || g.K[2] != d.KW) return false;
+  // A block of 4 output channels lies inside one group.
+  if (d.GRP > 1 && g.Coutg % 4 != 0) return false;
   for (int i = 0; i < 3; i++)
     if (g.S[i] != 1 || g.Dl[i] != 1) return false;
   if ((g.Cout + 3) / 4 != d.NG || g.O[2] != d.O2) return false;
@@ -748,9 +750,10 @@ std::string describe(const Geom& g, const FusedPlan& p) {
   char buf[512];
   if (p.spec >= 0) {
     std::snprintf(buf, sizeof buf,
-                  "kernel=fused_stream spec=%d ng=%d cpad=%d planes=%d rows=%d bw=%d tiles=%lld dsplit=%d units=%lld "
-                  "grid=%lldx%lldx%lld lds=%lld macs=%lld",
-                  p.spec, p.ng, p.cpad, p.dspan, p.rows, p.bw, (long long)p.tiles_per_plane, p.dsplit, (long long)p.units,
+                  "kernel=fused_stream spec=%d ng=%d cpad=%d groups=%lld planes=%d rows=%d bw=%d tiles=%lld dsplit=%d "
+                  "units=%lld grid=%lldx%lldx%lld lds=%lld macs=%lld",
+                  p.spec, p.ng, p.cpad, (long long)g.G, p.dspan, p.rows, p.bw, (long long)p.tiles_per_plane, p.dsplit,
+                  (long long)p.units,
                   (long long)p.grid[0], (long long)p.grid[1], (long long)p.grid[2], (long long)p.lds_bytes,
                   (long long)g.macs());
     return buf;

@@ -228,17 +228,21 @@ int launch_valu(const Geom& g, const ValuPlan& p, const float* x, const float* w
                 void* stream);
 
 // Build-time specialisations of the depth-streamed fused kernel (stride 1,
-// dilation 1, groups 1, kD = 3, min over depth): X(id, CIN, KH, KW, NG, O2, ROWS, RT)
-// with NG groups of 4 output channels, W_out = O2 and at most ROWS staged input
-// rows per wave tile. RT > 0: a wave tile is RT whole output rows (RT * O2 <= 64
-// positions, lanes past them idle; ROWS = RT + KH - 1); RT = 0: 64 consecutive
-// positions of the flattened plane.
+// dilation 1, kD = 3, streamed over the min axis): X(id, CIN, KH, KW, NG, O2,
+// ROWS, RT, GRP) with NG blocks of 4 output channels, W_out = O2, at most ROWS
+// staged input rows per wave tile and GRP conv groups (each channel block
+// reduces over its own group's CIN/GRP input channels only; with GRP > 1 a
+// block may not straddle two groups: C_out/GRP a multiple of 4). RT > 0: a
+// wave tile is RT whole output rows (RT * O2 <= 64 positions, lanes past them
+// idle; ROWS = RT + KH - 1); RT = 0: 64 consecutive positions of the plane.
 #define CONVHIP_FUSED_SPECS(X)                                                    \
   /* Conv3d 3->24, kernel 3x3x3, 32x32 planes (W_out 30): tiles of 2 rows */ \
-  X(0, 3, 3, 3, 6, 30, 4, 2)
+  X(0, 3, 3, 3, 6, 30, 4, 2, 1)                                                  \
+  /* the same with 3 groups (1 input and 8 output channels per group) */       \
+  X(1, 3, 3, 3, 6, 30, 4, 2, 3)
 
 struct FusedSpecDesc {
-  int id, CIN, KH, KW, NG, O2, ROWS, RT;
+  int id, CIN, KH, KW, NG, O2, ROWS, RT, GRP;
 };
 const FusedSpecDesc* fused_specs(int* count);
 

@@ -307,3 +307,17 @@ def test_large_kernels_plan_the_vector_fallback():
     assert d.startswith("conv_valu co=8 pp=1"), d
     d = ch.plan_describe((1, 4, 24, 24, 24), (20, 2, 9, 9, 9), (2, 1, 1), (1, 2, 1), (3, 4, 4), 2)
     assert d.startswith("conv_valu co=16 pp=1"), d
+
+
+def test_fused_stream_plans_native_groups():
+    """The depth-streamed fused kernel takes the grouped workload (3 groups of 1
+    input and 8 output channels) on its own specialisation; a group size that is
+    not a whole number of 4-channel blocks stays on the generic fused kernel."""
+    xs = (128, 3, 24, 32, 32)
+    for md in (2, 3):
+        d = ch.plan_describe(xs, (24, 1, 3, 3, 3), 1, 1, 0, 3, fused=True, min_dim=md)
+        assert "kernel=fused_stream spec=1" in d and "groups=3" in d, d
+    d = ch.plan_describe(xs, (24, 3, 3, 3, 3), fused=True)
+    assert "kernel=fused_stream spec=0" in d and "groups=1" in d, d
+    d = ch.plan_describe(xs, (18, 1, 3, 3, 3), 1, 1, 0, 3, fused=True)
+    assert "kernel=fused_min_softmax_mfma4" in d, d

@@ -341,19 +341,64 @@ def test_fused_grouped(case):
     assert err <= FUSED_ATOL
 
 
-def test_fused_grouped_workload_slice():
+@pytest.mark.parametrize("generic", [False, True])
+def test_fused_grouped_workload_slice(generic, monkeypatch):
     """The fused workload's shape with groups 3 (w [24, 1, 3, 3, 3]) on a
-    two-sample slice, against the oracle."""
+    two-sample slice, against the oracle: on the depth-streamed kernel (each
+    channel block reducing over its own group's input channel) and, with the
+    specialisations off, on the generic fused kernel."""
+    if generic:
+        monkeypatch.setenv("CONVHIP_TAP", "0")
     cfg = synth.VARIANTS["conv3d_min_softmax_groups3"]
     x, w, b = synth.make_inputs("conv3d_min_softmax_groups3", n_samples=2, sample_start=5)
     desc = ch.plan_describe(x.shape, w.shape, 1, 1, 0, cfg["groups"], fused=True)
-    assert "groups=3 kred=27" in desc, desc
+    if generic:
+        assert "groups=3 kred=27" in desc, desc
+    else:
+        assert "kernel=fused_stream spec=1" in desc and "groups=3" in desc, desc
     say(f"fused groups3 slice: {desc}")
     y = gpu_fused(x, w, b, 1, 1, 0, cfg["groups"], 2)
     ref = oracle.conv3d_min_softmax(x, w, b, 1, 1, 0, cfg["groups"], 2)
     err = float(np.abs(y - ref).max())
     say(f"  max|err| = {err:.3e}")
     assert err <= FUSED_ATOL
+
+
+# Conv groups on the depth-streamed kernel: 3 groups of 1 input and 8 output
+# channels (each 4-channel block reduces over its own group's channel only).
+STREAM_GROUP_CASES = [
+    ("groups3_two_samples", (2, 3, 6, 32, 32), 0, True, 2),
+    ("groups3_padded", (1, 3, 5, 9, 32), (1, 2, 0), False, 2),
+    ("groups3_ragged_units", (3, 3, 8, 21, 32), 0, True, 2),
+    ("groups3_min_over_h", (2, 3, 6, 20, 32), 0, True, 3),
+]
+
+
+@pytest.mark.parametrize("case", STREAM_GROUP_CASES, ids=[c[0] for c in STREAM_GROUP_CASES])
+def test_fused_stream_groups(case):
+    name, xs, p, bias, md = case
+    ws = (24, 1, 3, 3, 3)
+    desc = ch.plan_describe(xs, ws, 1, 1, p, 3, fused=True, min_dim=md)
+    assert "kernel=fused_stream spec=1" in desc, desc
+    r = np.random.default_rng(zlib.crc32(name.encode()))
+    x, w, b = _float_inputs(r, xs, ws, bias)
+    say(f"stream groups {name}: {desc}")
+    y = gpu_fused(x, w, b, 1, 1, p, 3, md)
+    ref = oracle.conv3d_min_softmax(x, w, b, 1, 1, p, 3, md)
+    err = float(np.abs(y - ref).max())
+    say(f"  max|err| = {err:.3e}")
+    assert err <= FUSED_ATOL
+
+
+def test_fused_stream_groups_integer_minimum_exact():
+    """Integer inputs keep every conv sum exact, so the minimum is exact and the
+    softmax error alone remains."""
+    r = np.random.default_rng(1750)
+    xs, ws = (2, 3, 5, 12, 32), (24, 1, 3, 3, 3)
+    x, w, b = _int_inputs(r, xs, ws, True)
+    y = gpu_fused(x, w, b, 1, 1, 0, 3, 2)
+    ref = oracle.conv3d_min_softmax(x, w, b, 1, 1, 0, 3, 2)
+    assert float(np.abs(y - ref).max()) <= FUSED_ATOL
 
 
 CONV2D_CASES = [
