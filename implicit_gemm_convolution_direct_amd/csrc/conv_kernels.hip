@@ -2604,7 +2604,7 @@ __global__ __launch_bounds__(256) void fused_min_softmax_mfma4_kernel(FusedArgs 
 //   partial minima of the depth ranges meet in LDS first.
 // ---------------------------------------------------------------------------
 
-template <int CIN, int KH, int KW_, int NG, int O2, int ROWS, int RT, int GRP>
+template <int CIN, int KH, int KW_, int NG, int O2, int ROWS, int RT, int GRP, int E4>
 struct StreamGeo {
   static constexpr int CIN_ = CIN, NG_ = NG, O2_ = O2, KW = KW_;
   // Conv groups: a channel block of group gq reduces over input channels
@@ -2617,8 +2617,11 @@ struct StreamGeo {
   static constexpr int BW = O2 + KW_ - 1;       // input columns per staged row
   static constexpr int CH = ROWS * BW;           // floats per channel of a plane
   static constexpr int PLANE = CIN * CH;         // floats of one staged plane
-  static_assert(BW % 4 == 0, "rows are copied in 16-byte chunks");
-  static constexpr int CHUNKS = PLANE / 4;       // 16-byte chunks per plane
+  // Floats per copy: 4 (16-byte chunks along contiguous rows) or 1 (E4: one
+  // element per lane, the column axis strided).
+  static constexpr int UNIT = E4 ? 1 : 4;
+  static_assert(BW % UNIT == 0, "rows are copied in whole chunks");
+  static constexpr int CHUNKS = PLANE / UNIT;    // copies' elements per plane
   static constexpr int PI = (CHUNKS + 63) / 64;  // 64-lane copies per plane (the last one partial)
   static constexpr int SLOT = PLANE;
   static constexpr int NSLOT = 4;
@@ -2661,11 +2664,11 @@ struct StreamArgs {
   int dsplit;      // waves per (sample, tile): the depth range is split over them
   int ods;         // output depths per wave (the last range may be shorter)
   int units;       // N * tiles_per_plane * dsplit
-  // Element strides of x along the kernel's axes 0 and 1 (axis 2 is W,
-  // contiguous), and of w along kernel axes 0 and 1 (axis 2 stride 1): the
-  // host permutes D and H for a minimum over H.
-  int plane_stride, row_stride;
-  int ws0, ws1;
+  // Element strides of x and of w along the kernel's axes 0, 1 and 2 (the
+  // streamed, row and column axes): the host permutes D, H and W so that the
+  // min axis is streamed.
+  int plane_stride, row_stride, col_stride;
+  int ws0, ws1, ws2;
 };
 
 // Index in w's [C_in, kD, kH, kW] block of reduction index k = (c, axis-0
@@ -2675,7 +2678,7 @@ __device__ __forceinline__ int stream_widx(int k, const StreamArgs& a) {
   const int c = k / G::KVOL, r = k - c * G::KVOL;
   const int t0 = r / G::KHW, r2 = r - t0 * G::KHW;
   const int t1 = r2 / G::KW, t2 = r2 - t1 * G::KW;
-  return c * G::KVOL + t0 * a.ws0 + t1 * a.ws1 + t2;
+  return c * G::KVOL + t0 * a.ws0 + t1 * a.ws1 + t2 * a.ws2;
 }
 
 template <class G>
@@ -2724,9 +2727,10 @@ __global__ __launch_bounds__(256, 4) void fused_stream_kernel(StreamArgs a) {
     }
   }
 
-  // Copy sources: copy i, lane l moves 16-byte chunk e = 64i + l = (c, row, q) of
-  // the slot from input (c, ih0 + row, 4q .. 4q+3) of the plane being staged
-  // (input rows are exactly BW wide: no padding along W).
+  // Copy sources: copy i, lane l moves element e = 64i + l = (c, row, q) of the
+  // slot (UNIT floats: 16 bytes, or 4 with E4) from input (c, ih0 + row,
+  // columns UNIT*q ..) of the plane being staged (input rows are exactly BW
+  // wide: no padding along the column axis).
   const int ih0 = oh_first - a.P1;
   const int64_t chan_stride = int64_t(a.L0) * a.L1 * a.L2;
   const float* xn = a.x + int64_t(n) * G::CIN_ * chan_stride;
@@ -2735,11 +2739,11 @@ __global__ __launch_bounds__(256, 4) void fused_stream_kernel(StreamArgs a) {
 #pragma unroll
   for (int i = 0; i < G::PI; i++) {
     const int e = 64 * i + lane;
-    const int c = e / (G::CH / 4), rem = e - c * (G::CH / 4);
-    const int r = rem / (G::BW / 4), q = rem - r * (G::BW / 4);
+    const int c = e / (G::CH / G::UNIT), rem = e - c * (G::CH / G::UNIT);
+    const int r = rem / (G::BW / G::UNIT), q = rem - r * (G::BW / G::UNIT);
     const int ih = ih0 + r;
     const bool ok = unsigned(ih) < unsigned(a.L1);
-    soff[i] = ok ? int(c * chan_stride) + ih * a.row_stride + 4 * q : 0;
+    soff[i] = ok ? int(c * chan_stride) + ih * a.row_stride + G::UNIT * q * a.col_stride : 0;
     sok |= uint32_t(ok) << i;
   }
   // Pinned in a scalar register: a kernel-argument load inside the depth loop
@@ -2757,7 +2761,10 @@ __global__ __launch_bounds__(256, 4) void fused_stream_kernel(StreamArgs a) {
 #pragma unroll
     for (int i = 0; i < G::PI; i++) {
       const bool ok = pok && ((sok >> i) & 1);
-      if (64 * i + lane < G::CHUNKS) lds_dma_f32x4(ok ? xp + soff[i] : kZeroWord, dst + 256 * i);
+      if (64 * i + lane < G::CHUNKS) {
+        if constexpr (G::UNIT == 4) lds_dma_f32x4(ok ? xp + soff[i] : kZeroWord, dst + 256 * i);
+        else lds_dma_f32(ok ? xp + soff[i] : kZeroWord, dst + 64 * i);
+      }
     }
   };
 
@@ -3174,9 +3181,9 @@ static int launch_fused_ng(const FusedArgs& args, const FusedPlan& p, hipStream_
   return hipGetLastError() == hipSuccess ? CONV_OK : CONV_ERR_HIP;
 }
 
-template <int CIN, int KH, int KW, int NG, int O2, int ROWS, int RT, int GRP>
+template <int CIN, int KH, int KW, int NG, int O2, int ROWS, int RT, int GRP, int E4>
 static int launch_stream(const StreamArgs& args, const FusedPlan& p, hipStream_t stream) {
-  using G = StreamGeo<CIN, KH, KW, NG, O2, ROWS, RT, GRP>;
+  using G = StreamGeo<CIN, KH, KW, NG, O2, ROWS, RT, GRP, E4>;
   if (int64_t(4) * G::LDS_FLOATS != p.lds_bytes || G::WAVES % p.dsplit != 0) return CONV_ERR_UNSUPPORTED;
   hipLaunchKernelGGL(fused_stream_kernel<G>, dim3(unsigned(p.grid[0])), dim3(64 * G::WAVES), 0, stream, args);
   return hipGetLastError() == hipSuccess ? CONV_OK : CONV_ERR_HIP;
@@ -3184,9 +3191,9 @@ static int launch_stream(const StreamArgs& args, const FusedPlan& p, hipStream_t
 
 static int launch_stream_spec(const StreamArgs& args, const FusedPlan& p, hipStream_t stream) {
   switch (p.spec) {
-#define CONVHIP_FUSED_CASE(id, CIN, KH, KW, NG, O2, ROWS, RT, GRP) \
-  case id:                                                       \
-    return launch_stream<CIN, KH, KW, NG, O2, ROWS, RT, GRP>(args, p, stream);
+#define CONVHIP_FUSED_CASE(id, CIN, KH, KW, NG, O2, ROWS, RT, GRP, E4) \
+  case id:                                                           \
+    return launch_stream<CIN, KH, KW, NG, O2, ROWS, RT, GRP, E4>(args, p, stream);
     CONVHIP_FUSED_SPECS(CONVHIP_FUSED_CASE)
 #undef CONVHIP_FUSED_CASE
     default: return CONV_ERR_UNSUPPORTED;
@@ -3333,7 +3340,7 @@ int conv_plan_describe(int nd, const int64_t* x_shape, const int64_t* w_shape, c
     if (nd != 3) return CONV_ERR_RANK;
     const int min_dim = fused == 1 ? 2 : fused;
     FusedPlan p;
-    rc = plan_fused(fused_geom(g, min_dim), min_dim, &p, use_tap() != 0 && min_dim != 4);
+    rc = plan_fused(fused_geom(g, min_dim), min_dim, &p, use_tap() != 0);
     if (rc != CONV_OK) return rc;
     s = describe(fused_geom(g, min_dim), p);
   } else {
@@ -3423,11 +3430,11 @@ int conv3d_min_softmax(const float* x, const int64_t* x_shape, const float* w, c
   const int64_t xst[3] = {g0.L[1] * g0.L[2], g0.L[2], 1};
   const int64_t wst[3] = {g0.K[1] * g0.K[2], g0.K[2], 1};
   FusedPlan p;
-  // The depth-streamed kernel copies input rows in 16-byte chunks.
+  // The depth-streamed kernel streams over the min axis. For a minimum over D
+  // or H it copies input rows along W in 16-byte chunks (x 16-byte aligned);
+  // for a minimum over W it copies single elements.
   const bool aligned = (reinterpret_cast<uintptr_t>(x) & 15) == 0;
-  // The depth-streamed kernel streams over the min axis and copies input rows
-  // along W in 16-byte chunks: a minimum over D or H (W stays the row axis).
-  rc = plan_fused(g, min_dim, &p, use_tap() != 0 && aligned && min_dim != 4);
+  rc = plan_fused(g, min_dim, &p, use_tap() != 0 && (aligned || min_dim == 4));
   if (rc != CONV_OK) return rc;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (p.spec >= 0) {
@@ -3444,8 +3451,10 @@ int conv3d_min_softmax(const float* x, const int64_t* x_shape, const float* w, c
     sa.units = int(p.units);
     sa.plane_stride = int(xst[perm[0]]);
     sa.row_stride = int(xst[perm[1]]);
+    sa.col_stride = int(xst[perm[2]]);
     sa.ws0 = int(wst[perm[0]]);
     sa.ws1 = int(wst[perm[1]]);
+    sa.ws2 = int(wst[perm[2]]);
     return launch_stream_spec(sa, p, s);
   }
   FusedArgs a;

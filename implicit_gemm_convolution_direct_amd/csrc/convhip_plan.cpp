@@ -573,7 +573,7 @@ int plan_conv(const Geom& g, ConvPlan* out, int force_cfg, int num_cu, int use_t
   return CONV_OK;
 }
 
-#define CONVHIP_FUSED_DESC(id, CIN, KH, KW, NG, O2, ROWS, RT, GRP) {id, CIN, KH, KW, NG, O2, ROWS, RT, GRP},
+#define CONVHIP_FUSED_DESC(id, CIN, KH, KW, NG, O2, ROWS, RT, GRP, E4) {id, CIN, KH, KW, NG, O2, ROWS, RT, GRP, E4},
 static const FusedSpecDesc kFusedSpecs[] = {CONVHIP_FUSED_SPECS(CONVHIP_FUSED_DESC)};
 #undef CONVHIP_FUSED_DESC
 
@@ -583,15 +583,19 @@ const FusedSpecDesc* fused_specs(int* count) {
 }
 
 // Plan of a depth-streamed specialisation if the geometry is the one it was built for.
-static bool plan_fused_stream(const Geom& g, const FusedSpecDesc& d, FusedPlan* p) {
+static bool plan_fused_stream(const Geom& g, int min_dim, const FusedSpecDesc& d, FusedPlan* p) {
+  // Columns along W (16-byte row copies) for a minimum over D or H; along H
+  // (element copies) for a minimum over W.
+  if (d.E4 != (min_dim == 4 ? 1 : 0)) return false;
   if (g.G != d.GRP || g.Cin != d.CIN || g.K[0] != 3 || g.K[1] != d.KH || g.K[2] != d.KW) return false;
   // A block of 4 output channels lies inside one group.
   if (d.GRP > 1 && g.Coutg % 4 != 0) return false;
   for (int i = 0; i < 3; i++)
     if (g.S[i] != 1 || g.Dl[i] != 1) return false;
   if ((g.Cout + 3) / 4 != d.NG || g.O[2] != d.O2) return false;
-  // Input rows are copied whole in 16-byte chunks: no padding along W.
-  if (g.P[2] != 0 || g.L[2] != d.O2 + d.KW - 1 || g.L[2] % 4 != 0) return false;
+  // Input rows are copied whole (16-byte chunks unless E4): no padding along
+  // the column axis.
+  if (g.P[2] != 0 || g.L[2] != d.O2 + d.KW - 1 || (!d.E4 && g.L[2] % 4 != 0)) return false;
   const int64_t plane_out = g.plane_out();
   int64_t tiles;
   if (d.RT > 0) {
@@ -643,7 +647,7 @@ int plan_fused(const Geom& g, int min_dim, FusedPlan* out, bool allow_spec) {
     int ns = 0;
     const FusedSpecDesc* specs = fused_specs(&ns);
     for (int i = 0; i < ns; i++)
-      if (plan_fused_stream(g, specs[i], out)) return CONV_OK;
+      if (plan_fused_stream(g, min_dim, specs[i], out)) return CONV_OK;
   }
   FusedPlan p;
   p.cpad = int((g.Coutg + 3) / 4 * 4);

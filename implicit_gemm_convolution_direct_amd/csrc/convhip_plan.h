@@ -229,20 +229,25 @@ int launch_valu(const Geom& g, const ValuPlan& p, const float* x, const float* w
 
 // Build-time specialisations of the depth-streamed fused kernel (stride 1,
 // dilation 1, kD = 3, streamed over the min axis): X(id, CIN, KH, KW, NG, O2,
-// ROWS, RT, GRP) with NG blocks of 4 output channels, W_out = O2, at most ROWS
-// staged input rows per wave tile and GRP conv groups (each channel block
-// reduces over its own group's CIN/GRP input channels only; with GRP > 1 a
-// block may not straddle two groups: C_out/GRP a multiple of 4). RT > 0: a
-// wave tile is RT whole output rows (RT * O2 <= 64 positions, lanes past them
-// idle; ROWS = RT + KH - 1); RT = 0: 64 consecutive positions of the plane.
+// ROWS, RT, GRP, E4) with NG blocks of 4 output channels, O2 output columns,
+// at most ROWS staged input rows per wave tile and GRP conv groups (each
+// channel block reduces over its own group's CIN/GRP input channels only; with
+// GRP > 1 a block may not straddle two groups: C_out/GRP a multiple of 4).
+// E4 = 0: the column axis is W (contiguous), input rows copied in 16-byte
+// chunks (minimum over D or H); E4 = 1: columns run along H with W streamed
+// (minimum over W), every input element copied on its own (4 bytes). RT > 0:
+// a wave tile is RT whole output rows (RT * O2 <= 64 positions, lanes past
+// them idle; ROWS = RT + KH - 1); RT = 0: 64 consecutive positions.
 #define CONVHIP_FUSED_SPECS(X)                                                    \
-  /* Conv3d 3->24, kernel 3x3x3, 32x32 planes (W_out 30): tiles of 2 rows */ \
-  X(0, 3, 3, 3, 6, 30, 4, 2, 1)                                                  \
+  /* Conv3d 3->24, kernel 3x3x3, 32x32 planes (30 output columns): tiles of 2 rows */ \
+  X(0, 3, 3, 3, 6, 30, 4, 2, 1, 0)                                               \
   /* the same with 3 groups (1 input and 8 output channels per group) */       \
-  X(1, 3, 3, 3, 6, 30, 4, 2, 3)
+  X(1, 3, 3, 3, 6, 30, 4, 2, 3, 0)                                               \
+  /* the same streamed over W (minimum over W): columns along H */               \
+  X(2, 3, 3, 3, 6, 30, 4, 2, 1, 1)
 
 struct FusedSpecDesc {
-  int id, CIN, KH, KW, NG, O2, ROWS, RT, GRP;
+  int id, CIN, KH, KW, NG, O2, ROWS, RT, GRP, E4;
 };
 const FusedSpecDesc* fused_specs(int* count);
 

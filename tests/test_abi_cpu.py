@@ -92,15 +92,19 @@ def test_conv_fwd_channels_last_validation_errors():
     assert lib.conv_plan_describe(3, I64(1, 8, 8, 8, 4), I64(4, 4, 3, 3, 3), one, one, zero, 1, -1, buf, 256) == -5
 
 
-def test_fused_plan_per_min_axis():
-    """conv_plan_describe's fused modes: min over depth or H takes the
-    depth-streamed specialisation at the fused workload's geometry (streaming
-    over the min axis, rows along W); min over W the generic fused kernel on
-    the permuted axes (whose box then spans the min axis)."""
+def test_fused_plan_per_min_axis(monkeypatch):
+    """conv_plan_describe's fused modes: at the fused workload's geometry every
+    min axis takes a depth-streamed specialisation that streams over it (min
+    over D or H: columns along W, 16-byte row copies, spec 0; min over W:
+    columns along H, element copies, spec 2); with the specialisations off,
+    the generic fused kernel."""
     xs, ws = (128, 3, 24, 32, 32), (24, 3, 3, 3, 3)
-    for md in (2, 3):
+    for md, spec in ((2, 0), (3, 0), (4, 2)):
         d = ch.plan_describe(xs, ws, fused=True, min_dim=md)
-        assert "kernel=fused_stream" in d, d
+        assert f"kernel=fused_stream spec={spec} " in d, d
+    d = ch.plan_describe((128, 3, 24, 30, 32), ws, fused=True, min_dim=4)  # H = 30: no spec fits
+    assert "kernel=fused_min_softmax_mfma4" in d, d
+    monkeypatch.setenv("CONVHIP_TAP", "0")
     d = ch.plan_describe(xs, ws, fused=True, min_dim=4)
     assert "kernel=fused_min_softmax_mfma4" in d, d
     one, zero = I32(1, 1, 1), I32(0, 0, 0)
@@ -149,11 +153,13 @@ def test_direct_kernel_plans():
             assert fields["grid"] == f"{(n_pos + 15) // 16}x{g}x1" and fields["lds"] == "0", desc
 
 
-def test_fused_generic_groups_are_native():
+def test_fused_generic_groups_are_native(monkeypatch):
     """Grouped fused calls reduce over C_in/groups input channels per output
     channel: the multiply-adds issued exceed the algorithmic count only by the
     padding of positions to 64, of each group's channels to 4 and of its
-    reduction to 4, never by the number of groups."""
+    reduction to 4, never by the number of groups (the generic fused kernel,
+    specialisations off)."""
+    monkeypatch.setenv("CONVHIP_TAP", "0")
     xs = (128, 3, 24, 32, 32)
     for ws, g, kred in [((24, 3, 3, 3, 3), 1, 81), ((24, 1, 3, 3, 3), 3, 27), ((12, 1, 3, 3, 3), 3, 27),
                         ((6, 2, 3, 3, 3), 3, 54)]:

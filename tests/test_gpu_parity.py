@@ -320,6 +320,43 @@ def test_fused_stream_min_over_h(case):
     assert err <= FUSED_ATOL
 
 
+# Minimum over W on the depth-streamed kernel: it streams over W with rows
+# along D and columns along H, copying single input elements.
+STREAM_MIN_W_CASES = [
+    ("two_samples", (2, 3, 6, 32, 32), 0, True),
+    ("short_w_ragged_d", (1, 3, 5, 32, 9), 0, False),
+    ("padded_d_and_w", (1, 3, 7, 32, 12), (1, 0, 2), True),
+    ("workload_slice", (2, 3, 24, 32, 32), 0, True),
+]
+
+
+@pytest.mark.parametrize("case", STREAM_MIN_W_CASES, ids=[c[0] for c in STREAM_MIN_W_CASES])
+def test_fused_stream_min_over_w(case):
+    name, xs, p, bias = case
+    ws = (24, 3, 3, 3, 3)
+    desc = ch.plan_describe(xs, ws, 1, 1, p, 1, fused=True, min_dim=4)
+    assert "kernel=fused_stream spec=2" in desc, desc
+    r = np.random.default_rng(zlib.crc32(name.encode()))
+    x, w, b = _float_inputs(r, xs, ws, bias)
+    say(f"stream min over W {name}: {desc}")
+    y = gpu_fused(x, w, b, 1, 1, p, 1, 4)
+    ref = oracle.conv3d_min_softmax(x, w, b, 1, 1, p, 1, 4)
+    assert y.shape == ref.shape, (y.shape, ref.shape)
+    err = float(np.abs(y - ref).max())
+    say(f"  max|err| = {err:.3e}")
+    assert err <= FUSED_ATOL
+
+
+def test_fused_stream_min_over_w_integer_minimum_exact():
+    r = np.random.default_rng(1760)
+    xs, ws = (2, 3, 5, 32, 11), (24, 3, 3, 3, 3)
+    x, w, b = _int_inputs(r, xs, ws, True)
+    assert "kernel=fused_stream spec=2" in ch.plan_describe(xs, ws, fused=True, min_dim=4)
+    y = gpu_fused(x, w, b, 1, 1, 0, 1, 4)
+    ref = oracle.conv3d_min_softmax(x, w, b, 1, 1, 0, 1, 4)
+    assert float(np.abs(y - ref).max()) <= FUSED_ATOL
+
+
 GROUPED_FUSED_CASES = [
     ("groups2_min_d", (2, 4, 6, 8, 9), (6, 2, 3, 3, 3), 1, 1, 0, 2, 2),
     ("groups3_min_h_strided", (1, 6, 5, 9, 8), (9, 2, 2, 3, 2), (1, 2, 1), 1, (1, 1, 0), 3, 3),
