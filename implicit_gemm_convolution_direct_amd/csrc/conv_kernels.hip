@@ -3346,10 +3346,10 @@ int conv_plan_describe(int nd, const int64_t* x_shape, const int64_t* w_shape, c
   } else {
     ValuPlan vp;
     ConvPlan p;
-    bool valu = fused == 0 && force_valu() && plan_valu(g, &vp) == CONV_OK;
+    bool valu = force_valu() && plan_valu(g, &vp) == CONV_OK;
     if (!valu) {
       rc = plan_conv(g, &p, forced_conv_cfg(), 256, use_tap(), split_kernel_choice());
-      valu = fused == 0 && rc == CONV_ERR_UNSUPPORTED && plan_valu(g, &vp) == CONV_OK;
+      valu = rc == CONV_ERR_UNSUPPORTED && plan_valu(g, &vp) == CONV_OK;
       if (!valu && rc != CONV_OK) return rc;
     }
     if (valu) {
@@ -3404,8 +3404,12 @@ int conv_fwd_channels_last(int nd, const float* x, const int64_t* x_shape, const
   // copies an aligned w.
   g.x_aligned16 = (reinterpret_cast<uintptr_t>(x) & 15) == 0;
   g.w_aligned16 = (reinterpret_cast<uintptr_t>(w) & 15) == 0;
+  ValuPlan vp;
+  if (force_valu() && plan_valu(g, &vp) == CONV_OK) return launch_valu(g, vp, x, w, bias, y, stream);
   ConvPlan p;
   rc = plan_conv(g, &p, forced_conv_cfg(), device_num_cu(), use_tap(), split_kernel_choice());
+  // Geometries no matrix-core kernel can stage run on the vector-ALU kernel.
+  if (rc == CONV_ERR_UNSUPPORTED && plan_valu(g, &vp) == CONV_OK) return launch_valu(g, vp, x, w, bias, y, stream);
   if (rc != CONV_OK) return rc;
   ConvArgs a = conv_args(g, p, x, w, bias, y);
   a.vec_store = (g.Cout % 4 == 0 && g.Coutg % 4 == 0 && (reinterpret_cast<uintptr_t>(y) & 15) == 0) ? 1 : 0;

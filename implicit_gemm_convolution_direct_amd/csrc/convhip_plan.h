@@ -210,7 +210,7 @@ int plan_conv(const Geom& g, ConvPlan* p, int force_cfg = -1, int num_cu = 256, 
               int split_kernel = 0);
 
 // Direct convolution on the vector ALU (conv_valu_kernel, valu_kernels.hip):
-// any NCDHW geometry whose weights of one (input channel, depth tap) pair,
+// any geometry, channels-first or channels-last, whose weights of one (input channel, depth tap) pair,
 // double-buffered (2 x kH x kW x CO floats), fit in 64 KiB of LDS. CO output
 // channels and pp positions per lane, `threads` lanes per workgroup; grid[0]
 // position blocks, grid[1] = groups x ncob channel blocks. conv_fwd takes it for geometries the

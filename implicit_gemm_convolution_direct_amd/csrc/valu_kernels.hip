@@ -64,7 +64,9 @@ __device__ __forceinline__ void fma_tap(float (&acc)[PP][CO], const float (&xv)[
 // CO x kH x kW each, are staged transposed, [pair][tap][CO], in one of two LDS
 // buffers, one barrier per stage (a buffer is rewritten two stages later,
 // after every lane has passed the barrier that follows its use).
-template <int CO, int PP, int T>
+// CL: channels-last tensors, x [N, D, H, W, C_in] and y [N, D_out, H_out,
+// W_out, C_out]; otherwise NCDHW.
+template <int CO, int PP, int T, bool CL>
 __global__ __launch_bounds__(T) void conv_valu_kernel(ValuArgs a) {
   extern __shared__ float wl[];
   const int tid = threadIdx.x;
@@ -74,6 +76,10 @@ __global__ __launch_bounds__(T) void conv_valu_kernel(ValuArgs a) {
   const int kvol = a.K0 * khw;
   const int64_t plane_in = int64_t(a.L0) * a.L1 * a.L2;
   const int64_t plane_out = int64_t(a.O0) * a.O1 * a.O2;
+  // Element strides of x: between input channels and between sites (W steps).
+  const int64_t cstride = CL ? 1 : plane_in;
+  const int site = CL ? a.Cin : 1;
+  const int wstep = a.D2 * site;  // between a row's taps
 
   // This lane's positions: sample, window origin and input base (clamped into
   // range for invalid lanes; their stores are skipped).
@@ -97,7 +103,7 @@ __global__ __launch_bounds__(T) void conv_valu_kernel(ValuArgs a) {
     iw0[pp] = ow * a.S2 - a.P2;
     sp[pp] = (int64_t(od) * a.O1 + oh) * a.O2 + ow;
     nn[pp] = n;
-    xb[pp] = a.x + (int64_t(n) * a.Cin + int64_t(g) * a.Cg) * plane_in;
+    xb[pp] = a.x + int64_t(n) * a.Cin * plane_in + int64_t(g) * a.Cg * cstride;
   }
 
   float acc[PP][CO];
@@ -132,7 +138,7 @@ __global__ __launch_bounds__(T) void conv_valu_kernel(ValuArgs a) {
           const int zd = id0[pp] + td * a.D0, zh = ih0[pp] + th * a.D1;
           rowok[pp] = zd >= 0 && zd < a.L0 && zh >= 0 && zh < a.L1;
           // The row's first tap; dereferenced only where the tap is in range.
-          xrow[pp] = xb[pp] + int64_t(c) * plane_in + (int64_t(zd) * a.L1 + zh) * a.L2 + iw0[pp];
+          xrow[pp] = xb[pp] + int64_t(c) * cstride + ((int64_t(zd) * a.L1 + zh) * a.L2 + iw0[pp]) * int64_t(site);
         }
         const v4f* wr0 = reinterpret_cast<const v4f*>(wpair + th * a.K2 * CO);
         // Out-of-range taps load the plane's first element (always in range)
@@ -145,7 +151,7 @@ __global__ __launch_bounds__(T) void conv_valu_kernel(ValuArgs a) {
           for (int pp = 0; pp < PP; pp++) {
             const int zw = iw0[pp] + tw * a.D2;
             const bool ok = rowok[pp] && zw >= 0 && zw < a.L2;
-            const float v = *(ok ? xrow[pp] + tw * a.D2 : xb[pp]);
+            const float v = *(ok ? xrow[pp] + tw * wstep : xb[pp]);
             xv[pp] = ok ? v : 0.0f;
           }
           fma_tap<CO, PP>(acc, xv, wr0 + tw * (CO / 4));
@@ -162,7 +168,10 @@ __global__ __launch_bounds__(T) void conv_valu_kernel(ValuArgs a) {
     const float b = a.bias ? a.bias[cg] : 0.0f;
 #pragma unroll
     for (int pp = 0; pp < PP; pp++)
-      if (valid[pp]) a.y[(nn[pp] * a.Cout + cg) * plane_out + sp[pp]] = acc[pp][j] + b;
+      if (valid[pp]) {
+        const int64_t yi = CL ? (nn[pp] * plane_out + sp[pp]) * a.Cout + cg : (nn[pp] * a.Cout + cg) * plane_out + sp[pp];
+        a.y[yi] = acc[pp][j] + b;
+      }
   }
 }
 
@@ -174,7 +183,6 @@ constexpr int kMaxLdsBytes = 64 * 1024;
 }  // namespace
 
 int plan_valu(const Geom& g, ValuPlan* p) {
-  if (g.cl) return CONV_ERR_UNSUPPORTED;
   const int co = g.Coutg <= 8 ? 8 : 16;
   const int64_t psz = g.K[1] * g.K[2] * co;
   if (2 * psz * 4 > kMaxLdsBytes) return CONV_ERR_UNSUPPORTED;
@@ -224,15 +232,19 @@ int launch_valu(const Geom& g, const ValuPlan& p, const float* x, const float* w
   a.pps = p.pps;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const dim3 grid(unsigned(p.grid[0]), unsigned(p.grid[1]));
-#define CONVHIP_VALU_CASE(CO, PP, T)                                                     \
-  if (p.co == CO && p.pp == PP && p.threads == T) {                                      \
-    hipLaunchKernelGGL((conv_valu_kernel<CO, PP, T>), grid, dim3(T), p.lds_bytes, s, a); \
-    return hipGetLastError() == hipSuccess ? CONV_OK : CONV_ERR_HIP;                     \
+#define CONVHIP_VALU_CASE(CO, PP, T, CL)                                                     \
+  if (p.co == CO && p.pp == PP && p.threads == T && g.cl == CL) {                            \
+    hipLaunchKernelGGL((conv_valu_kernel<CO, PP, T, CL>), grid, dim3(T), p.lds_bytes, s, a); \
+    return hipGetLastError() == hipSuccess ? CONV_OK : CONV_ERR_HIP;                         \
   }
-  CONVHIP_VALU_CASE(8, 2, 256)
-  CONVHIP_VALU_CASE(16, 2, 256)
-  CONVHIP_VALU_CASE(8, 1, 64)
-  CONVHIP_VALU_CASE(16, 1, 64)
+  CONVHIP_VALU_CASE(8, 2, 256, false)
+  CONVHIP_VALU_CASE(16, 2, 256, false)
+  CONVHIP_VALU_CASE(8, 1, 64, false)
+  CONVHIP_VALU_CASE(16, 1, 64, false)
+  CONVHIP_VALU_CASE(8, 2, 256, true)
+  CONVHIP_VALU_CASE(16, 2, 256, true)
+  CONVHIP_VALU_CASE(8, 1, 64, true)
+  CONVHIP_VALU_CASE(16, 1, 64, true)
 #undef CONVHIP_VALU_CASE
   return CONV_ERR_UNSUPPORTED;
 }

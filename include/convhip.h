@@ -102,9 +102,10 @@ int conv_fwd(int nd,
  * x_shape: nd+2 host entries in the channels-last order above ([N, spatial..., C_in]).
  * w keeps the conv_fwd layout [C_out, C_in/groups, k...] (w_shape likewise);
  * bias [C_out] or NULL. y: device buffer of N*prod(out)*C_out floats. Status
- * codes, ownership and stream semantics as conv_fwd. Any pointer alignment is
- * accepted (16-byte aligned y with C_out and C_out/groups multiples of 4 takes
- * vector stores).
+ * codes, ownership, stream semantics and the kernel choice (matrix cores, or the
+ * vector-ALU direct kernel where no matrix-core kernel fits) as conv_fwd. Any
+ * pointer alignment is accepted (16-byte aligned y with C_out and C_out/groups
+ * multiples of 4 takes vector stores).
  */
 int conv_fwd_channels_last(int nd,
                            const float *x, const int64_t *x_shape,

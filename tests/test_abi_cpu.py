@@ -290,8 +290,9 @@ def test_unfused_steps_validation_errors():
 
 
 def test_valu_switch_plans_the_vector_kernel(monkeypatch):
-    """CONVHIP_VALU=1 routes conv_fwd to the vector-ALU direct kernel (8 or 16
-    output channels per lane); channels-last and the fused op are unaffected."""
+    """CONVHIP_VALU=1 routes conv_fwd and conv_fwd_channels_last to the
+    vector-ALU direct kernel (8 or 16 output channels per lane); the fused op is
+    unaffected."""
     monkeypatch.setenv("CONVHIP_VALU", "1")
     d = ch.plan_describe((2, 3, 16, 16, 16), (8, 3, 3, 3, 3))
     assert d.startswith("conv_valu co=8 pp=1 threads=64 pairs=9 grid=86x1"), d
@@ -302,7 +303,8 @@ def test_valu_switch_plans_the_vector_kernel(monkeypatch):
     with pytest.raises(ch.ConvError) as e:  # 2 x 92 x 92 x 8 x 4 B > 64 KiB of LDS, and no box fits either
         ch.plan_describe((1, 16, 4, 96, 96), (8, 16, 3, 92, 92))
     assert e.value.status == -7
-    assert "conv_valu" not in ch.plan_describe((2, 16, 16, 16, 3), (8, 3, 3, 3, 3), channels_last=True)
+    d = ch.plan_describe((2, 16, 16, 16, 3), (8, 3, 3, 3, 3), channels_last=True)
+    assert d.startswith("conv_valu co=8 pp=1"), d
     assert "conv_valu" not in ch.plan_describe((128, 3, 24, 32, 32), (24, 3, 3, 3, 3), fused=True)
 
 
@@ -327,3 +329,8 @@ def test_fused_stream_plans_native_groups():
     assert "kernel=fused_stream spec=0" in d and "groups=1" in d, d
     d = ch.plan_describe(xs, (18, 1, 3, 3, 3), 1, 1, 0, 3, fused=True)
     assert "kernel=fused_min_softmax_mfma4" in d, d
+
+
+def test_large_kernels_plan_the_vector_fallback_channels_last():
+    d = ch.plan_describe((2, 16, 16, 16, 16), (8, 16, 11, 11, 11), channels_last=True)
+    assert d.startswith("conv_valu co=8 pp=1"), d

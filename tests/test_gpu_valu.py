@@ -94,3 +94,35 @@ def test_large_kernels_fall_back_to_the_vector_kernel(monkeypatch):
            "fallback 11^3")
     _check((1, 4, 24, 24, 24), (20, 2, 9, 9, 9), (2, 1, 1), (1, 2, 1), (3, 4, 4), 2, False, 961,
            "fallback 9^3 groups")
+
+
+def _check_cl(xs_cl, ws, s, d, p, g, bias, seed, what):
+    desc = ch.plan_describe(xs_cl, ws, s, d, p, g, channels_last=True)
+    assert desc.startswith("conv_valu"), desc
+    r = np.random.default_rng(seed)
+    x, w, b = _int_inputs(r, xs_cl, ws, bias)
+    say(f"valu channels-last {what}: x={xs_cl} w={ws}: {desc}")
+    y = ch.conv_fwd_channels_last(to_dev(x), to_dev(w), to_dev(b), s, d, p, g)
+    torch.cuda.synchronize()
+    ref = oracle.conv_channels_last(x, w, b, s, d, p, g)
+    np.testing.assert_array_equal(y.cpu().numpy().astype(np.float64), ref)
+
+
+CL_CASES = [
+    ((2, 9, 8, 7, 3), (8, 3, 3, 3, 3), (1, 1, 1), (1, 1, 1), (0, 0, 0), 1, True),
+    ((1, 8, 9, 11, 4), (6, 2, 3, 2, 3), (2, 1, 3), (1, 2, 1), (1, 0, 2), 2, False),
+    ((2, 8, 10, 12, 16), (32, 8, 3, 5, 7), (1, 2, 2), (1, 1, 2), (1, 2, 3), 2, True),
+    ((8, 40, 40, 40, 3), (20, 3, 3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1), 1, True),   # 256-lane groups
+]
+
+
+@pytest.mark.parametrize("case", range(len(CL_CASES)))
+def test_valu_kernel_channels_last_integer_exact(case):
+    xs, ws, s, d, p, g, bias = CL_CASES[case]
+    _check_cl(xs, ws, s, d, p, g, bias, 970 + case, f"case {case}")
+
+
+def test_large_kernels_fall_back_to_the_vector_kernel_channels_last(monkeypatch):
+    monkeypatch.delenv("CONVHIP_VALU")
+    _check_cl((2, 16, 16, 16, 16), (8, 16, 11, 11, 11), (1, 1, 1), (1, 1, 1), (0, 0, 0), 1, True, 980,
+              "fallback 11^3")
