@@ -8,8 +8,9 @@ w[128,64,3], stride 3, dilation 4), the largest configuration. The same run
 also times every other workload and reports it under "shapes":
 
 * the tiny, general and asymmetric Conv3d and the fused Conv3d+min+softmax;
-* the four plain convolutions again on channels-last tensors through
-  conv_fwd_channels_last ("<workload>_channels_last");
+* the four plain convolutions and the fused op again on channels-last tensors
+  through conv_fwd_channels_last and conv3d_min_softmax_channels_last
+  ("<workload>_channels_last");
 * the five workloads on the generic kernels, with the build-time
   specialisations switched off ("<workload>_generic", CONVHIP_TAP=0);
 * the four plain convolutions on the vector-ALU direct kernel
@@ -57,7 +58,8 @@ VALU_SUFFIX = "_valu"
 VALU_WORKLOADS = ("tiny_conv3d", "general_conv3d", "asym_conv3d", "long_conv1d")
 WORKLOAD_NAMES = ["tiny_conv3d", "general_conv3d", "conv3d_min_softmax", "asym_conv3d", "long_conv1d"]
 ORDER = (WORKLOAD_NAMES
-         + [n + CL_SUFFIX for n in ("tiny_conv3d", "general_conv3d", "asym_conv3d", "long_conv1d")]
+         + [n + CL_SUFFIX for n in ("tiny_conv3d", "general_conv3d", "asym_conv3d", "long_conv1d",
+                                    "conv3d_min_softmax")]
          + [n + GEN_SUFFIX for n in WORKLOAD_NAMES]
          + [n + VALU_SUFFIX for n in VALU_WORKLOADS]
          + ["asym_conv3d_48", "general_conv3d_24", "long_conv1d_c96_d2", "conv3d_min_softmax_min_h",
@@ -184,7 +186,11 @@ def _time_workload(name, base, cl, steps, warmup, torch, ch, synth, flush, warm_
     out, macs, nbytes, conv_elems, y_elems = geometry(cfg)
     args = (cfg["stride"], cfg["dilation"], cfg["padding"], cfg["groups"])
     md = cfg.get("min_dim", 2)
-    if cl:
+    if cl and cfg["fused"]:
+        keep = [o for a, o in enumerate(out) if a != md - 2]
+        y = torch.empty((cfg["x"][0], *keep, cfg["w"][0]), dtype=torch.float32, device=x.device)
+        call = lambda: ch.conv3d_min_softmax_channels_last(x, w, b, *args, min_dim=md, out=y)
+    elif cl:
         y = torch.empty((cfg["x"][0], *out, cfg["w"][0]), dtype=torch.float32, device=x.device)
         call = lambda: ch.conv_fwd_channels_last(x, w, b, *args, out=y)
     elif cfg["fused"]:

@@ -12,6 +12,8 @@ Operations (POPCORNBENCH "Kimi-K2.6" pages l1_p60, l1_p76, l2_p24, opening turns
 * ``conv3d_min_softmax(x, w, bias, stride, dilation, padding, groups, min_dim=2)`` --
   softmax over channels of the minimum over depth of Conv3d, without writing the
   5-D conv result.
+* ``conv3d_min_softmax_channels_last(x, w, ...)`` -- the same on channels-last
+  tensors: x [N, D, H, W, C_in] -> y [N, kept axes..., C_out].
 * ``min_over_axis(y, dim)``, ``softmax_over_channels(z)`` -- that op's last two
   steps as separate launches (its unfused form, measured beside it).
 """
@@ -29,7 +31,8 @@ STATUS_NAMES = {
     -5: "CONV_ERR_PARAM", -6: "CONV_ERR_EMPTY_OUTPUT", -7: "CONV_ERR_UNSUPPORTED", -8: "CONV_ERR_OVERFLOW",
     -9: "CONV_ERR_HIP",
 }
-EXPORTED = ["conv_out_shape", "conv_fwd", "conv_fwd_channels_last", "conv3d_min_softmax", "min_over_axis",
+EXPORTED = ["conv_out_shape", "conv_fwd", "conv_fwd_channels_last", "conv3d_min_softmax",
+            "conv3d_min_softmax_channels_last", "min_over_axis",
             "softmax_over_channels", "conv_status_string", "conv_plan_describe", "convhip_synth_fill",
             "convhip_peak_probe"]
 
@@ -63,6 +66,9 @@ def lib():
         L.conv_fwd_channels_last.argtypes = [ctypes.c_int, vp, i64p, vp, i64p, vp, ip, ip, ip, ctypes.c_int, vp, vp]
         L.conv3d_min_softmax.restype = ctypes.c_int
         L.conv3d_min_softmax.argtypes = [vp, i64p, vp, i64p, vp, ip, ip, ip, ctypes.c_int, ctypes.c_int, vp, vp]
+        L.conv3d_min_softmax_channels_last.restype = ctypes.c_int
+        L.conv3d_min_softmax_channels_last.argtypes = [vp, i64p, vp, i64p, vp, ip, ip, ip, ctypes.c_int, ctypes.c_int,
+                                                       vp, vp]
         L.min_over_axis.restype = ctypes.c_int
         L.min_over_axis.argtypes = [vp, i64p, ctypes.c_int, vp, vp]
         L.softmax_over_channels.restype = ctypes.c_int
@@ -117,10 +123,13 @@ def out_shape(in_spatial, k_spatial, stride, dilation, padding):
 def plan_describe(x_shape, w_shape, stride=1, dilation=1, padding=0, groups=1, fused=False, channels_last=False,
                   min_dim=2):
     """The library's launch plan; channels_last=True takes x_shape as [N, spatial..., C_in];
-    fused=True describes conv3d_min_softmax with that min_dim."""
+    fused=True describes conv3d_min_softmax (or its channels-last form) with that min_dim."""
     nd = len(x_shape) - 2
     buf = ctypes.create_string_buffer(1024)
-    mode = 2 if channels_last else ((1 if min_dim == 2 else int(min_dim)) if fused else 0)
+    if fused:
+        mode = int(min_dim) + 3 if channels_last else (1 if min_dim == 2 else int(min_dim))
+    else:
+        mode = 2 if channels_last else 0
     rc = lib().conv_plan_describe(nd, _i64(x_shape), _i64(w_shape), _i32(_vec(stride, nd, "stride")),
                                   _i32(_vec(dilation, nd, "dilation")), _i32(_vec(padding, nd, "padding")),
                                   int(groups), mode, buf, 1024)
@@ -302,6 +311,31 @@ def softmax_over_channels(z, out=None):
                                      _stream_handle(z.device))
     if rc != CONV_OK:
         raise ConvError(rc, "softmax_over_channels")
+    return out
+
+
+def conv3d_min_softmax_channels_last(x, w, bias=None, stride=1, dilation=1, padding=0, groups=1, min_dim=2,
+                                     out=None):
+    """conv3d_min_softmax on channels-last tensors: x [N, D, H, W, C_in] -> y [N, kept axes..., C_out]
+    (min_dim 2, 3, 4 = D, H, W); w keeps [C_out, C_in/groups, kD, kH, kW]."""
+    _check_operands(x, w, bias, out)
+    if x.dim() != 5 or w.dim() != 5:
+        raise ValueError("x and w must be 5-D")
+    if min_dim not in (2, 3, 4):
+        raise ValueError("min_dim must be 2, 3 or 4")
+    logical = (x.shape[0], x.shape[4], x.shape[1], x.shape[2], x.shape[3])
+    _, _, ws, s, d, p, shape = _conv_args(tuple(logical), tuple(w.shape), stride, dilation, padding,
+                                          drop_axis=min_dim - 2)
+    shape = (shape[0], *shape[2:], shape[1])
+    if out is None:
+        out = torch.empty(shape, dtype=torch.float32, device=x.device)
+    elif tuple(out.shape) != shape:
+        raise ValueError(f"out has shape {tuple(out.shape)}, expected {shape}")
+    rc = lib().conv3d_min_softmax_channels_last(x.data_ptr(), _i64(x.shape), w.data_ptr(), ws,
+                                                bias.data_ptr() if bias is not None else None, s, d, p, int(groups),
+                                                int(min_dim), out.data_ptr(), _stream_handle(x.device))
+    if rc != CONV_OK:
+        raise ConvError(rc, "conv3d_min_softmax_channels_last")
     return out
 
 

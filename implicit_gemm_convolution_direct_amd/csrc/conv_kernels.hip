@@ -2334,6 +2334,9 @@ struct FusedArgs {
   // w (per kernel axis), in the kernel's axis order.
   int64_t xs_n, xs_c, xs0, xs1, xs2;
   int ws0, ws1, ws2;
+  // Element strides of y per sample, per output channel and per output
+  // position (y [N, C_out, positions] or channels-last [N, positions, C_out]).
+  int64_t ys_n, ys_c, ys_p;
   int Cg, Coutg, groups;  // input / output channels per group, groups
   int kg;                 // reduction length of one group: Cg * kvol
   int kgp;                // kg rounded up to 4 (zero weights past kg)
@@ -2464,8 +2467,7 @@ __global__ __launch_bounds__(256) void fused_min_softmax_mfma4_kernel(FusedArgs 
   const bool red_overlaps_box = a.red_off == 0;
   float* red = smem + a.red_off;
   float* fin = smem + a.fin_off;
-  const int64_t out_plane = int64_t(a.O1) * a.O2;
-  float* yp = a.y + int64_t(n) * a.Cout * out_plane + int64_t(oh) * a.O2 + ow;
+  float* yp = a.y + int64_t(n) * a.ys_n + (int64_t(oh) * a.O2 + ow) * a.ys_p;
 
   for (int g = 0; g < a.groups; g++) {
     const float4* wrow = reinterpret_cast<const float4*>(Wt + (g * a.cpadg + wlane) * a.kgs);
@@ -2554,7 +2556,7 @@ __global__ __launch_bounds__(256) void fused_min_softmax_mfma4_kernel(FusedArgs 
         const float inv_den = 1.0f / sum;
 #pragma unroll
         for (int c = 0; c < 4 * NG; c++)
-          if (c < a.Cout) yp[int64_t(c) * out_plane] = m[c] * inv_den;
+          if (c < a.Cout) yp[int64_t(c) * a.ys_c] = m[c] * inv_den;
       }
       return;
     }
@@ -2577,7 +2579,7 @@ __global__ __launch_bounds__(256) void fused_min_softmax_mfma4_kernel(FusedArgs 
     float sum = 0.0f;
     for (int c = 0; c < a.Cout; c++) sum += expf(fin[c * 64 + lane] - mx);
     const float inv_den = 1.0f / sum;
-    for (int c = 0; c < a.Cout; c++) yp[int64_t(c) * out_plane] = expf(fin[c * 64 + lane] - mx) * inv_den;
+    for (int c = 0; c < a.Cout; c++) yp[int64_t(c) * a.ys_c] = expf(fin[c * 64 + lane] - mx) * inv_den;
   }
 }
 
@@ -2669,6 +2671,10 @@ struct StreamArgs {
   // min axis is streamed.
   int plane_stride, row_stride, col_stride;
   int ws0, ws1, ws2;
+  // Element strides of x per sample and per input channel, and of y per
+  // sample, output channel and output position (NCDHW or channels-last).
+  int64_t xs_n, ys_n;
+  int xs_c, ys_c, ys_p;
 };
 
 // Index in w's [C_in, kD, kH, kW] block of reduction index k = (c, axis-0
@@ -2732,8 +2738,8 @@ __global__ __launch_bounds__(256, 4) void fused_stream_kernel(StreamArgs a) {
   // columns UNIT*q ..) of the plane being staged (input rows are exactly BW
   // wide: no padding along the column axis).
   const int ih0 = oh_first - a.P1;
-  const int64_t chan_stride = int64_t(a.L0) * a.L1 * a.L2;
-  const float* xn = a.x + int64_t(n) * G::CIN_ * chan_stride;
+  const int chan_stride = a.xs_c;
+  const float* xn = a.x + int64_t(n) * a.xs_n;
   int soff[G::PI];
   uint32_t sok = 0;
 #pragma unroll
@@ -2856,7 +2862,7 @@ __global__ __launch_bounds__(256, 4) void fused_stream_kernel(StreamArgs a) {
       }
   }
 
-  float* yp = a.y + int64_t(n) * a.Cout * a.plane_out + p;
+  float* yp = a.y + int64_t(n) * a.ys_n + int64_t(p) * a.ys_p;
   if (a.dsplit > 1) {
     // The parts of one (sample, tile) are consecutive waves of this workgroup:
     // part 0 takes the minimum over the others' partial minima. The ring is
@@ -2924,7 +2930,7 @@ __global__ __launch_bounds__(256, 4) void fused_stream_kernel(StreamArgs a) {
     const float inv = 1.0f / sum;
 #pragma unroll
     for (int c = 0; c < 4 * NG; c++)
-      if (c < a.Cout) yp[int64_t(c) * a.plane_out] = m[c] * inv;
+      if (c < a.Cout) yp[int64_t(c) * a.ys_c] = m[c] * inv;
   }
 }
 
@@ -3293,6 +3299,106 @@ static Geom fused_geom(const Geom& g0, int min_dim) {
   return g;
 }
 
+// The fused op on NCDHW tensors (g0.cl false) or channels-last ones (x [N, D,
+// H, W, C_in], y [N, kept axes, C_out]); g0 holds the logical geometry.
+static int fused_run(const Geom& g0, int min_dim, const float* x, const float* w, const float* bias, float* y,
+                     convhip_stream_t stream) {
+  if (min_dim < 2 || min_dim > 4) return CONV_ERR_PARAM;
+  const int* perm = kFusedPerm[min_dim - 2];
+  const Geom g = fused_geom(g0, min_dim);
+  // Element strides of x per logical spatial axis (D, H, W), per input channel
+  // and per sample; of w per kernel axis; of y per sample, output channel and
+  // output position (y [N, C_out, kept axes], or channels-last).
+  const int64_t vol = g0.L[0] * g0.L[1] * g0.L[2];
+  const bool cl = g0.cl;
+  const int64_t xst[3] = {g0.L[1] * g0.L[2] * (cl ? g0.Cin : 1), g0.L[2] * (cl ? g0.Cin : 1), cl ? g0.Cin : 1};
+  const int64_t xs_c = cl ? 1 : vol, xs_n = g0.Cin * vol;
+  const int64_t wst[3] = {g0.K[1] * g0.K[2], g0.K[2], 1};
+  const int64_t plane = g.plane_out();
+  const int64_t ys_n = g.Cout * plane, ys_c = cl ? 1 : plane, ys_p = cl ? g.Cout : 1;
+  FusedPlan p;
+  // The depth-streamed kernel streams over the min axis. With contiguous
+  // columns (W, in NCDHW, for a minimum over D or H) it copies input rows in
+  // 16-byte chunks (x 16-byte aligned); else single elements.
+  const bool aligned = (reinterpret_cast<uintptr_t>(x) & 15) == 0;
+  int rc = plan_fused(g, min_dim, &p, use_tap() != 0 && (aligned || min_dim == 4 || cl));
+  if (rc != CONV_OK) return rc;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (p.spec >= 0) {
+    StreamArgs sa;
+    sa.x = x; sa.w = w; sa.bias = bias; sa.y = y;
+    sa.Cout = int(g.Cout);
+    sa.L0 = int(g.L[0]); sa.L1 = int(g.L[1]); sa.L2 = int(g.L[2]);
+    sa.P0 = int(g.P[0]); sa.P1 = int(g.P[1]); sa.P2 = int(g.P[2]);
+    sa.O0 = int(g.O[0]); sa.O1 = int(g.O[1]);
+    sa.plane_out = int(g.plane_out());
+    sa.tiles_per_plane = int(p.tiles_per_plane);
+    sa.dsplit = p.dsplit;
+    sa.ods = int((g.O[0] + p.dsplit - 1) / p.dsplit);
+    sa.units = int(p.units);
+    sa.plane_stride = int(xst[perm[0]]);
+    sa.row_stride = int(xst[perm[1]]);
+    sa.col_stride = int(xst[perm[2]]);
+    sa.ws0 = int(wst[perm[0]]);
+    sa.ws1 = int(wst[perm[1]]);
+    sa.ws2 = int(wst[perm[2]]);
+    sa.xs_n = xs_n;
+    sa.xs_c = int(xs_c);
+    sa.ys_n = ys_n;
+    sa.ys_c = int(ys_c);
+    sa.ys_p = int(ys_p);
+    return launch_stream_spec(sa, p, s);
+  }
+  FusedArgs a;
+  a.x = x; a.w = w; a.bias = bias; a.y = y;
+  a.Cin = int(g.Cin); a.Cout = int(g.Cout);
+  a.L0 = int(g.L[0]); a.L1 = int(g.L[1]); a.L2 = int(g.L[2]);
+  a.K0 = int(g.K[0]); a.K1 = int(g.K[1]); a.K2 = int(g.K[2]);
+  a.S0 = int(g.S[0]); a.S1 = int(g.S[1]); a.S2 = int(g.S[2]);
+  a.D0 = int(g.Dl[0]); a.D1 = int(g.Dl[1]); a.D2 = int(g.Dl[2]);
+  a.P0 = int(g.P[0]); a.P1 = int(g.P[1]); a.P2 = int(g.P[2]);
+  a.O0 = int(g.O[0]); a.O1 = int(g.O[1]); a.O2 = int(g.O[2]);
+  a.kvol = int(g.kvol());
+  a.mode = p.mode; a.dspan = p.dspan; a.rows = p.rows; a.bw = p.bw; a.boxc = p.boxc; a.row_tiles = p.row_tiles;
+  a.plane_out = int(g.plane_out());
+  a.xs_c = xs_c;
+  a.xs_n = xs_n;
+  a.ys_n = ys_n;
+  a.ys_c = ys_c;
+  a.ys_p = ys_p;
+  a.xs0 = xst[perm[0]];
+  a.xs1 = xst[perm[1]];
+  a.xs2 = xst[perm[2]];
+  a.ws0 = int(wst[perm[0]]);
+  a.ws1 = int(wst[perm[1]]);
+  a.ws2 = int(wst[perm[2]]);
+  a.Cg = int(g.Cg);
+  a.Coutg = int(g.Coutg);
+  a.groups = int(g.G);
+  a.kg = p.kg; a.kgp = p.kgp; a.kgs = p.kgs; a.cpadg = p.cpad;
+  a.tile_pos = p.tile_pos;
+  a.nrows = p.nrows;
+  a.ko_off = p.ko_off; a.wt_off = p.wt_off; a.red_off = p.red_off; a.fin_off = p.fin_off;
+  switch (p.ng) {
+    case 1: return launch_fused_ng<1>(a, p, s);
+    case 2: return launch_fused_ng<2>(a, p, s);
+    case 3: return launch_fused_ng<3>(a, p, s);
+    case 4: return launch_fused_ng<4>(a, p, s);
+    case 5: return launch_fused_ng<5>(a, p, s);
+    case 6: return launch_fused_ng<6>(a, p, s);
+    case 7: return launch_fused_ng<7>(a, p, s);
+    case 8: return launch_fused_ng<8>(a, p, s);
+    case 9: return launch_fused_ng<9>(a, p, s);
+    case 10: return launch_fused_ng<10>(a, p, s);
+    case 11: return launch_fused_ng<11>(a, p, s);
+    case 12: return launch_fused_ng<12>(a, p, s);
+    case 13: return launch_fused_ng<13>(a, p, s);
+    case 14: return launch_fused_ng<14>(a, p, s);
+    case 15: return launch_fused_ng<15>(a, p, s);
+    default: return launch_fused_ng<16>(a, p, s);
+  }
+}
+
 extern "C" {
 
 int conv_out_shape(int nd, const int64_t* in_spatial, const int64_t* k_spatial, const int* stride,
@@ -3330,15 +3436,16 @@ int conv_plan_describe(int nd, const int64_t* x_shape, const int64_t* w_shape, c
                        const int* dilation, const int* padding, int groups, int fused, char* buf, int buflen) {
   if (!buf || buflen < 1) return CONV_ERR_NULL;
   buf[0] = 0;
-  if (fused < 0 || fused > 4) return CONV_ERR_PARAM;
+  if (fused < 0 || fused > 7) return CONV_ERR_PARAM;
   Geom g;
-  int rc = fused == 2 ? make_geom_channels_last(nd, x_shape, w_shape, stride, dilation, padding, groups, &g)
-                      : make_geom(nd, x_shape, w_shape, stride, dilation, padding, groups, &g);
+  const bool cl = fused == 2 || fused >= 5;
+  int rc = cl ? make_geom_channels_last(nd, x_shape, w_shape, stride, dilation, padding, groups, &g)
+              : make_geom(nd, x_shape, w_shape, stride, dilation, padding, groups, &g);
   if (rc != CONV_OK) return rc;
   std::string s;
   if (fused == 1 || fused >= 3) {
     if (nd != 3) return CONV_ERR_RANK;
-    const int min_dim = fused == 1 ? 2 : fused;
+    const int min_dim = fused == 1 ? 2 : fused >= 5 ? fused - 3 : fused;
     FusedPlan p;
     rc = plan_fused(fused_geom(g, min_dim), min_dim, &p, use_tap() != 0);
     if (rc != CONV_OK) return rc;
@@ -3427,85 +3534,17 @@ int conv3d_min_softmax(const float* x, const int64_t* x_shape, const float* w, c
   int rc = make_geom(3, x_shape, w_shape, stride, dilation, padding, groups, &g);
   if (rc != CONV_OK) return rc;
   if (!x || !w || !y) return CONV_ERR_NULL;
-  if (min_dim < 2 || min_dim > 4) return CONV_ERR_PARAM;
-  const int* perm = kFusedPerm[min_dim - 2];
-  const Geom g0 = g;
-  g = fused_geom(g0, min_dim);
-  const int64_t xst[3] = {g0.L[1] * g0.L[2], g0.L[2], 1};
-  const int64_t wst[3] = {g0.K[1] * g0.K[2], g0.K[2], 1};
-  FusedPlan p;
-  // The depth-streamed kernel streams over the min axis. For a minimum over D
-  // or H it copies input rows along W in 16-byte chunks (x 16-byte aligned);
-  // for a minimum over W it copies single elements.
-  const bool aligned = (reinterpret_cast<uintptr_t>(x) & 15) == 0;
-  rc = plan_fused(g, min_dim, &p, use_tap() != 0 && (aligned || min_dim == 4));
+  return fused_run(g, min_dim, x, w, bias, y, stream);
+}
+
+int conv3d_min_softmax_channels_last(const float* x, const int64_t* x_shape, const float* w, const int64_t* w_shape,
+                                     const float* bias, const int* stride, const int* dilation, const int* padding,
+                                     int groups, int min_dim, float* y, convhip_stream_t stream) {
+  Geom g;
+  int rc = make_geom_channels_last(3, x_shape, w_shape, stride, dilation, padding, groups, &g);
   if (rc != CONV_OK) return rc;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (p.spec >= 0) {
-    StreamArgs sa;
-    sa.x = x; sa.w = w; sa.bias = bias; sa.y = y;
-    sa.Cout = int(g.Cout);
-    sa.L0 = int(g.L[0]); sa.L1 = int(g.L[1]); sa.L2 = int(g.L[2]);
-    sa.P0 = int(g.P[0]); sa.P1 = int(g.P[1]); sa.P2 = int(g.P[2]);
-    sa.O0 = int(g.O[0]); sa.O1 = int(g.O[1]);
-    sa.plane_out = int(g.plane_out());
-    sa.tiles_per_plane = int(p.tiles_per_plane);
-    sa.dsplit = p.dsplit;
-    sa.ods = int((g.O[0] + p.dsplit - 1) / p.dsplit);
-    sa.units = int(p.units);
-    sa.plane_stride = int(xst[perm[0]]);
-    sa.row_stride = int(xst[perm[1]]);
-    sa.col_stride = int(xst[perm[2]]);
-    sa.ws0 = int(wst[perm[0]]);
-    sa.ws1 = int(wst[perm[1]]);
-    sa.ws2 = int(wst[perm[2]]);
-    return launch_stream_spec(sa, p, s);
-  }
-  FusedArgs a;
-  a.x = x; a.w = w; a.bias = bias; a.y = y;
-  a.Cin = int(g.Cin); a.Cout = int(g.Cout);
-  a.L0 = int(g.L[0]); a.L1 = int(g.L[1]); a.L2 = int(g.L[2]);
-  a.K0 = int(g.K[0]); a.K1 = int(g.K[1]); a.K2 = int(g.K[2]);
-  a.S0 = int(g.S[0]); a.S1 = int(g.S[1]); a.S2 = int(g.S[2]);
-  a.D0 = int(g.Dl[0]); a.D1 = int(g.Dl[1]); a.D2 = int(g.Dl[2]);
-  a.P0 = int(g.P[0]); a.P1 = int(g.P[1]); a.P2 = int(g.P[2]);
-  a.O0 = int(g.O[0]); a.O1 = int(g.O[1]); a.O2 = int(g.O[2]);
-  a.kvol = int(g.kvol());
-  a.mode = p.mode; a.dspan = p.dspan; a.rows = p.rows; a.bw = p.bw; a.boxc = p.boxc; a.row_tiles = p.row_tiles;
-  a.plane_out = int(g.plane_out());
-  a.xs_c = g0.L[0] * g0.L[1] * g0.L[2];
-  a.xs_n = g0.Cin * a.xs_c;
-  a.xs0 = xst[perm[0]];
-  a.xs1 = xst[perm[1]];
-  a.xs2 = xst[perm[2]];
-  a.ws0 = int(wst[perm[0]]);
-  a.ws1 = int(wst[perm[1]]);
-  a.ws2 = int(wst[perm[2]]);
-  a.Cg = int(g.Cg);
-  a.Coutg = int(g.Coutg);
-  a.groups = int(g.G);
-  a.kg = p.kg; a.kgp = p.kgp; a.kgs = p.kgs; a.cpadg = p.cpad;
-  a.tile_pos = p.tile_pos;
-  a.nrows = p.nrows;
-  a.ko_off = p.ko_off; a.wt_off = p.wt_off; a.red_off = p.red_off; a.fin_off = p.fin_off;
-  switch (p.ng) {
-    case 1: return launch_fused_ng<1>(a, p, s);
-    case 2: return launch_fused_ng<2>(a, p, s);
-    case 3: return launch_fused_ng<3>(a, p, s);
-    case 4: return launch_fused_ng<4>(a, p, s);
-    case 5: return launch_fused_ng<5>(a, p, s);
-    case 6: return launch_fused_ng<6>(a, p, s);
-    case 7: return launch_fused_ng<7>(a, p, s);
-    case 8: return launch_fused_ng<8>(a, p, s);
-    case 9: return launch_fused_ng<9>(a, p, s);
-    case 10: return launch_fused_ng<10>(a, p, s);
-    case 11: return launch_fused_ng<11>(a, p, s);
-    case 12: return launch_fused_ng<12>(a, p, s);
-    case 13: return launch_fused_ng<13>(a, p, s);
-    case 14: return launch_fused_ng<14>(a, p, s);
-    case 15: return launch_fused_ng<15>(a, p, s);
-    default: return launch_fused_ng<16>(a, p, s);
-  }
+  if (!x || !w || !y) return CONV_ERR_NULL;
+  return fused_run(g, min_dim, x, w, bias, y, stream);
 }
 
 int convhip_peak_probe(int kind, int64_t iters, float* sink, int64_t* flop, convhip_stream_t stream) {

@@ -584,9 +584,10 @@ const FusedSpecDesc* fused_specs(int* count) {
 
 // Plan of a depth-streamed specialisation if the geometry is the one it was built for.
 static bool plan_fused_stream(const Geom& g, int min_dim, const FusedSpecDesc& d, FusedPlan* p) {
-  // Columns along W (16-byte row copies) for a minimum over D or H; along H
-  // (element copies) for a minimum over W.
-  if (d.E4 != (min_dim == 4 ? 1 : 0)) return false;
+  // Columns along W, contiguous in NCDHW (16-byte row copies), for a minimum
+  // over D or H; element copies for a minimum over W (columns along H) and for
+  // channels-last input (columns C_in floats apart).
+  if (d.E4 != ((min_dim == 4 || g.cl) ? 1 : 0)) return false;
   if (g.G != d.GRP || g.Cin != d.CIN || g.K[0] != 3 || g.K[1] != d.KH || g.K[2] != d.KW) return false;
   // A block of 4 output channels lies inside one group.
   if (d.GRP > 1 && g.Coutg % 4 != 0) return false;

@@ -7,6 +7,7 @@
  *
  *   conv_fwd            y = Conv{1,3}d(x, w, bias; stride, dilation, zero padding, groups)
  *   conv3d_min_softmax  y = softmax over channels of (min over depth of Conv3d(x, w, bias))
+ *                       (and its channels-last form)
  *   min_over_axis, softmax_over_channels   that op's last two steps, unfused
  *
  * Conventions shared by every entry point
@@ -136,6 +137,21 @@ int conv3d_min_softmax(const float *x, const int64_t *x_shape,
                        int min_dim, float *y, convhip_stream_t stream);
 
 /*
+ * conv3d_min_softmax on channels-last tensors (the NDHWC layout that page
+ * l1_p60's monologue weighs for coalesced input reads): the same operation,
+ * with x stored [N, D, H, W, C_in] (x_shape in that order) and y stored with
+ * the channels innermost, [N, kept axes..., C_out] (min_dim 2: [N, H_out,
+ * W_out, C_out]; 3: [N, D_out, W_out, C_out]; 4: [N, D_out, H_out, C_out]).
+ * min_dim keeps its meaning (2, 3, 4 = D, H, W). w keeps [C_out, C_in/groups,
+ * kD, kH, kW]. Support, status codes and numerics as conv3d_min_softmax; any
+ * pointer alignment is accepted.
+ */
+int conv3d_min_softmax_channels_last(const float *x, const int64_t *x_shape,
+                                     const float *w, const int64_t *w_shape, const float *bias,
+                                     const int *stride, const int *dilation, const int *padding, int groups,
+                                     int min_dim, float *y, convhip_stream_t stream);
+
+/*
  * The fused op's last two steps on their own, for running it unfused after
  * conv_fwd (page l2_p24, opening turns: torch.min over the chosen axis of the
  * Conv3d output, then torch.softmax over channels; the page also weighs writing
@@ -182,7 +198,8 @@ const char *conv_status_string(int status);
  * truncated to buflen). fused = 0 for conv_fwd, 1 for conv3d_min_softmax with
  * min_dim 2, 3 or 4 for conv3d_min_softmax with that min_dim (then nd must be
  * 3, else CONV_ERR_RANK), 2 for conv_fwd_channels_last (x_shape in its
- * channels-last order); other values give CONV_ERR_PARAM. Host only; launches
+ * channels-last order), 5, 6 or 7 for conv3d_min_softmax_channels_last with
+ * min_dim 2, 3 or 4; other values give CONV_ERR_PARAM. Host only; launches
  * nothing.
  * Returns a conv_status.
  */

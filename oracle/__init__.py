@@ -8,6 +8,8 @@ this package. The HIP library and its Python binding never do.
                            (x [N, spatial..., C_in] -> y [N, out..., C_out]): a
                            pure change of memory order around ``conv``.
 * ``conv3d_min_softmax`` -- conv (composed) -> min over one axis -> softmax over channels.
+* ``conv3d_min_softmax_channels_last`` -- the same on channels-last tensors (a pure
+                           change of memory order around ``conv3d_min_softmax``).
 * ``min_axis``           -- the minimum over one axis of a 5-D tensor (the fused op's
                            second step on its own).
 * ``softmax_channels``   -- softmax over dim 1 (the fused op's last step on its own).
@@ -146,3 +148,12 @@ def softmax_channels(z):
     if rc != 0:
         raise ValueError(f"oracle_softmax_channels rejected the arguments (code {rc})")
     return out
+
+
+def conv3d_min_softmax_channels_last(x_cl, w, bias=None, stride=1, dilation=1, padding=0, groups=1, min_dim=2):
+    """conv3d_min_softmax for x stored [N, D, H, W, C_in]; returns float64 [N, kept axes..., C_out]:
+    the channel axis moved in on the way in and out on the way out (min_dim keeps its
+    meaning: 2, 3, 4 = D, H, W)."""
+    x = np.moveaxis(np.asarray(x_cl, dtype=np.float32), -1, 1)
+    y = conv3d_min_softmax(x, w, bias, stride, dilation, padding, groups, min_dim)
+    return np.ascontiguousarray(np.moveaxis(y, 1, -1))

@@ -88,7 +88,7 @@ def test_conv_fwd_channels_last_validation_errors():
     assert f(s=I32(1, 0, 1)) == -5
     assert f(nd=1, xs=(1, 8, 4), ws=(4, 4, 9)) == -6
     buf = ctypes.create_string_buffer(256)
-    assert lib.conv_plan_describe(3, I64(1, 8, 8, 8, 4), I64(4, 4, 3, 3, 3), one, one, zero, 1, 5, buf, 256) == -5
+    assert lib.conv_plan_describe(3, I64(1, 8, 8, 8, 4), I64(4, 4, 3, 3, 3), one, one, zero, 1, 8, buf, 256) == -5
     assert lib.conv_plan_describe(3, I64(1, 8, 8, 8, 4), I64(4, 4, 3, 3, 3), one, one, zero, 1, -1, buf, 256) == -5
 
 
@@ -334,3 +334,23 @@ def test_fused_stream_plans_native_groups():
 def test_large_kernels_plan_the_vector_fallback_channels_last():
     d = ch.plan_describe((2, 16, 16, 16, 16), (8, 16, 11, 11, 11), channels_last=True)
     assert d.startswith("conv_valu co=8 pp=1"), d
+
+
+def test_fused_channels_last_plans():
+    """The channels-last fused op (x [N, D, H, W, C]) takes the depth-streamed kernel's
+    element-copy specialisation at the workload's geometry for every min axis, and the
+    generic fused kernel elsewhere."""
+    xs, ws = (128, 24, 32, 32, 3), (24, 3, 3, 3, 3)
+    for md in (2, 3, 4):
+        d = ch.plan_describe(xs, ws, fused=True, channels_last=True, min_dim=md)
+        assert "kernel=fused_stream spec=2 " in d, d
+    d = ch.plan_describe((128, 24, 32, 32, 3), (24, 1, 3, 3, 3), 1, 1, 0, 3, fused=True, channels_last=True)
+    assert "kernel=fused_min_softmax_mfma4" in d, d
+    lib = ch.lib()
+    one, zero = I32(1, 1, 1), I32(0, 0, 0)
+    f = lambda xs=(1, 6, 8, 8, 3), ws=(4, 3, 3, 3, 3), md=2, x=FAKE, y=FAKE: \
+        lib.conv3d_min_softmax_channels_last(x, I64(*xs), FAKE, I64(*ws), None, one, one, zero, 1, md, y, None)
+    assert f(x=None) == -1 and f(y=None) == -1
+    assert f(md=5) == -5 and f(md=1) == -5
+    assert f(xs=(1, 6, 8, 8, 4)) == -3          # C_in (last entry) does not match w
+    assert f(xs=(1, 2, 8, 8, 3)) == -6          # empty output along D

@@ -5,6 +5,8 @@ Integer-valued inputs keep every partial sum an exact fp32 integer, so those
 cases compare bit for bit; uniform inputs use the conv tolerance
 1e-4 * sqrt(K_red) * max|y_ref|.
 """
+import zlib
+
 import numpy as np
 import pytest
 import torch
@@ -359,3 +361,50 @@ def test_channels_last_split_geometry_misaligned_weights_take_generic():
     y = ch.conv_fwd_channels_last(to_dev(x), wd, to_dev(b), s, d, p, g)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(y.cpu().numpy().astype(np.float64), oracle.conv_channels_last(x, w, b, s, d, p, g))
+
+
+# ------------------------------------------------- fused op, channels-last
+FUSED_ATOL = 1e-5
+FUSED_CL_CASES = [
+    # name, x [N, D, H, W, C], w, stride, dilation, padding, groups, min_dim, streamed kernel expected
+    ("workload_like_min_d", (2, 6, 32, 32, 3), (24, 3, 3, 3, 3), 1, 1, 0, 1, 2, True),
+    ("workload_like_min_h", (2, 6, 20, 32, 3), (24, 3, 3, 3, 3), 1, 1, 0, 1, 3, True),
+    ("workload_like_min_w", (1, 5, 32, 12, 3), (24, 3, 3, 3, 3), 1, 1, 0, 1, 4, True),
+    ("groups3_min_d", (2, 5, 9, 32, 3), (24, 1, 3, 3, 3), 1, 1, (1, 2, 0), 3, 2, False),
+    ("generic_strided_padded", (1, 7, 9, 11, 4), (10, 2, 2, 3, 2), (2, 1, 2), (1, 2, 1), (1, 1, 2), 2, 3, False),
+    ("generic_min_w", (2, 5, 6, 9, 3), (5, 3, 1, 2, 4), 1, (1, 1, 2), (0, 1, 1), 1, 4, False),
+]
+
+
+@pytest.mark.parametrize("case", FUSED_CL_CASES, ids=[c[0] for c in FUSED_CL_CASES])
+def test_fused_channels_last(case):
+    """conv3d_min_softmax on x [N, D, H, W, C_in], y [N, kept axes, C_out], against the
+    oracle on the same tensors with the channel axis moved."""
+    name, xs, ws, s, d, p, g, md, streamed = case
+    desc = ch.plan_describe(xs, ws, s, d, p, g, fused=True, channels_last=True, min_dim=md)
+    assert ("kernel=fused_stream spec=" in desc) == streamed, desc
+    r = np.random.default_rng(zlib.crc32(name.encode()))
+    x, w, b = _float_inputs(r, xs, ws, True)
+    say(f"fused channels-last {name}: {desc}")
+    y = ch.conv3d_min_softmax_channels_last(to_dev(x), to_dev(w), to_dev(b), s, d, p, g, md)
+    torch.cuda.synchronize()
+    ref = oracle.conv3d_min_softmax_channels_last(x, w, b, s, d, p, g, md)
+    assert tuple(y.shape) == ref.shape, (tuple(y.shape), ref.shape)
+    err = float(np.abs(y.cpu().numpy() - ref).max())
+    say(f"  max|err| = {err:.3e}")
+    assert err <= FUSED_ATOL
+
+
+def test_fused_channels_last_matches_ncdhw_entry_point():
+    """The fused workload's shape on two samples: the channels-last result is the
+    NCDHW entry point's result with the channel axis moved, to fp32 rounding."""
+    x, w, b = synth.make_inputs("conv3d_min_softmax", n_samples=2)
+    xd, wd, bd = to_dev(x), to_dev(w), to_dev(b)
+    x_cl = xd.permute(0, 2, 3, 4, 1).contiguous()
+    for md in (2, 3, 4):
+        y = ch.conv3d_min_softmax(xd, wd, bd, min_dim=md)
+        y_cl = ch.conv3d_min_softmax_channels_last(x_cl, wd, bd, min_dim=md)
+        torch.cuda.synchronize()
+        err = float((y_cl - y.permute(0, 2, 3, 1)).abs().max())
+        say(f"  min_dim {md}: channels-last vs NCDHW max|diff| = {err:.3e}")
+        assert err <= FUSED_ATOL

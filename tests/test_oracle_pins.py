@@ -435,3 +435,18 @@ def test_unfused_steps_compose_to_the_fused_oracle():
         got = oracle.softmax_channels(oracle.min_axis(y, min_dim))
         ref = oracle.conv3d_min_softmax(x, w, b, 1, 1, 0, 1, min_dim)
         np.testing.assert_allclose(got, ref, rtol=0, atol=1e-6)
+
+
+def test_fused_channels_last_oracle_matches_torch_on_moved_axes():
+    """The channels-last fused oracle: x stored [N, D, H, W, C], y [N, kept, C];
+    torch's float64 composition on the logical (permuted) tensor, for each min axis."""
+    r = _rng(48)
+    x_cl = r.standard_normal((2, 6, 5, 7, 3)).astype(np.float32)
+    w = (r.standard_normal((8, 3, 3, 2, 3)) * 0.5).astype(np.float32)
+    b = r.standard_normal(8).astype(np.float32)
+    xt = torch.from_numpy(x_cl).double().permute(0, 4, 1, 2, 3)
+    for md in (2, 3, 4):
+        got = oracle.conv3d_min_softmax_channels_last(x_cl, w, b, 1, 1, (1, 0, 1), 1, md)
+        t = F.conv3d(xt, torch.from_numpy(w).double(), torch.from_numpy(b).double(), padding=(1, 0, 1))
+        t = torch.softmax(torch.min(t, dim=md)[0], dim=1).permute(0, 2, 3, 1).numpy()
+        np.testing.assert_allclose(got, t, rtol=1e-12, atol=1e-15)
