@@ -2338,6 +2338,7 @@ struct FusedArgs {
   // position (y [N, C_out, positions] or channels-last [N, positions, C_out]).
   int64_t ys_n, ys_c, ys_p;
   int Cg, Coutg, groups;  // input / output channels per group, groups
+  int cchunks;            // output-channel chunks per group (cpadg channels each, the last ragged)
   int kg;                 // reduction length of one group: Cg * kvol
   int kgp;                // kg rounded up to 4 (zero weights past kg)
   int kgs;                // floats per weight row in LDS (kgp, or kgp + 4 against bank conflicts)
@@ -2427,8 +2428,9 @@ __global__ __launch_bounds__(256) void fused_min_softmax_mfma4_kernel(FusedArgs 
       while (zr >= a.rows) { zr -= a.rows; zd++; }
     }
   }
-  // Weights [group][channel][k], rows of kgs floats; zero past kg and Coutg.
-  const int w_total = a.groups * a.cpadg * a.kgs;
+  // Weights [group][chunk][channel][k], rows of kgs floats; zero past kg and
+  // past the group's Coutg channels.
+  const int w_total = a.groups * a.cchunks * a.cpadg * a.kgs;
   const float inv_kgs = 1.0f / float(a.kgs), inv_cpadg = 1.0f / float(a.cpadg), inv_kvol = 1.0f / float(a.kvol);
   const float inv_k12 = 1.0f / float(a.K1 * a.K2), inv_k2 = 1.0f / float(a.K2);
   for (int i = wave; i * 64 < w_total; i += 4) {
@@ -2436,7 +2438,9 @@ __global__ __launch_bounds__(256) void fused_min_softmax_mfma4_kernel(FusedArgs 
     if (e < w_total) {
       int k, c, cl, r, r2, th, tw;
       const int gc = divmod_small(e, a.kgs, inv_kgs, k);
-      const int g = divmod_small(gc, a.cpadg, inv_cpadg, c);
+      const int u = divmod_small(gc, a.cpadg, inv_cpadg, c);
+      const int g = u / a.cchunks;
+      c += (u - g * a.cchunks) * a.cpadg;  // channel within the group
       const bool ok = c < a.Coutg && k < a.kg;
       cl = divmod_small(ok ? k : 0, a.kvol, inv_kvol, r);
       const int td = divmod_small(r, a.K1 * a.K2, inv_k12, r2);
@@ -2469,8 +2473,11 @@ __global__ __launch_bounds__(256) void fused_min_softmax_mfma4_kernel(FusedArgs 
   float* fin = smem + a.fin_off;
   float* yp = a.y + int64_t(n) * a.ys_n + (int64_t(oh) * a.O2 + ow) * a.ys_p;
 
-  for (int g = 0; g < a.groups; g++) {
-    const float4* wrow = reinterpret_cast<const float4*>(Wt + (g * a.cpadg + wlane) * a.kgs);
+  const int units = a.groups * a.cchunks;
+  for (int u = 0; u < units; u++) {
+    const int g = u / a.cchunks;                    // conv group
+    const int cbase = (u - g * a.cchunks) * a.cpadg;  // first channel of the chunk within the group
+    const float4* wrow = reinterpret_cast<const float4*>(Wt + (u * a.cpadg + wlane) * a.kgs);
     const float* xg = Xs + g * a.Cg * a.boxc + noff;
     v4f mn[NG];
 #pragma unroll
@@ -2530,7 +2537,7 @@ __global__ __launch_bounds__(256) void fused_min_softmax_mfma4_kernel(FusedArgs 
 #pragma unroll
       for (int r = 0; r < 4; r++) red[(wave * a.cpadg + 4 * i + r) * 64 + lane] = mn[i][r];
     __syncthreads();
-    if (a.groups == 1) {
+    if (units == 1) {
       // One group: wave 0 merges and normalises in registers.
       if (wave == 0 && valid) {
         float m[4 * NG];
@@ -2562,12 +2569,12 @@ __global__ __launch_bounds__(256) void fused_min_softmax_mfma4_kernel(FusedArgs 
     }
     // Several groups: the waves merge a quarter of the group's channels each
     // into fin[channel][position], then free red for the next group.
-    for (int c = wave; c < a.Coutg; c += 4) {
+    for (int c = wave; c < a.cpadg && cbase + c < a.Coutg; c += 4) {
       float v = red[c * 64 + lane];
       v = min_nan(v, red[(a.cpadg + c) * 64 + lane]);
       v = min_nan(v, red[(2 * a.cpadg + c) * 64 + lane]);
       v = min_nan(v, red[(3 * a.cpadg + c) * 64 + lane]);
-      const int co = g * a.Coutg + c;
+      const int co = g * a.Coutg + cbase + c;
       fin[co * 64 + lane] = v + (a.bias ? a.bias[co] : 0.0f);
     }
     __syncthreads();
@@ -3375,6 +3382,7 @@ static int fused_run(const Geom& g0, int min_dim, const float* x, const float* w
   a.Cg = int(g.Cg);
   a.Coutg = int(g.Coutg);
   a.groups = int(g.G);
+  a.cchunks = p.cchunks;
   a.kg = p.kg; a.kgp = p.kgp; a.kgs = p.kgs; a.cpadg = p.cpad;
   a.tile_pos = p.tile_pos;
   a.nrows = p.nrows;

@@ -643,7 +643,7 @@ static bool plan_fused_stream(const Geom& g, int min_dim, const FusedSpecDesc& d
 int plan_fused(const Geom& g, int min_dim, FusedPlan* out, bool allow_spec) {
   if (g.nd != 3) return CONV_ERR_RANK;
   // g is in the kernels' axis order (the minimum over axis 0).
-  if (min_dim < 2 || min_dim > 4 || g.Cout > 64) return CONV_ERR_UNSUPPORTED;
+  if (min_dim < 2 || min_dim > 4) return CONV_ERR_UNSUPPORTED;
   if (allow_spec) {
     int ns = 0;
     const FusedSpecDesc* specs = fused_specs(&ns);
@@ -651,8 +651,13 @@ int plan_fused(const Geom& g, int min_dim, FusedPlan* out, bool allow_spec) {
       if (plan_fused_stream(g, min_dim, specs[i], out)) return CONV_OK;
   }
   FusedPlan p;
-  p.cpad = int((g.Coutg + 3) / 4 * 4);
+  // At most 64 output channels (16 blocks of 4) per pass over a group's
+  // reduction: more run as several channel chunks of the group, each reducing
+  // over the group's whole input, their minima merged in LDS before the softmax.
+  p.cchunks = int((g.Coutg + 63) / 64);
+  p.cpad = int(((g.Coutg + p.cchunks - 1) / p.cchunks + 3) / 4 * 4);
   p.ng = p.cpad / 4;
+  const int64_t units = g.G * p.cchunks;
   const int BN = 64;
   p.mode = (g.O[2] * 2 <= BN) ? TILE_FLAT : TILE_ROW;
   box_dims(g, p.mode, BN, &p.rows, &p.bw, &p.tiles_per_plane, &p.row_tiles);
@@ -675,17 +680,17 @@ int plan_fused(const Geom& g, int min_dim, FusedPlan* out, bool allow_spec) {
   p.kgs = ((p.kgp / 4) % 2 == 1) ? p.kgp : p.kgp + 4;
   const int64_t nrows = g.Cin * int64_t(p.dspan) * p.rows;
   const int64_t box = g.Cin * boxc;
-  const int64_t red = 4 * int64_t(p.cpad) * 64;  // per-wave minima of one group
-  // One group: the minima reuse the box space once it is read for the last time.
-  const int64_t region = g.G == 1 ? std::max(box, red) : box;
+  const int64_t red = 4 * int64_t(p.cpad) * 64;  // per-wave minima of one group (chunk)
+  // One pass: the minima reuse the box space once it is read for the last time.
+  const int64_t region = units == 1 ? std::max(box, red) : box;
   int64_t off = (region + 3) / 4 * 4;
   const int64_t ko_off = off;
   off += p.kgp;
   off = (off + 3) / 4 * 4;
   const int64_t wt_off = off;
-  off += g.G * int64_t(p.cpad) * p.kgs;
+  off += units * int64_t(p.cpad) * p.kgs;
   int64_t red_off = 0, fin_off = 0;
-  if (g.G > 1) {
+  if (units > 1) {
     red_off = off;
     off += red;
     fin_off = off;
@@ -766,11 +771,11 @@ std::string describe(const Geom& g, const FusedPlan& p) {
   // Multiply-adds the matrix cores perform: every tile's 64 positions, every
   // output depth, each group's channels rounded up to 4, over the group's
   // reduction rounded up to 4 (no products across groups).
-  const int64_t issued = int64_t(p.grid[0]) * p.grid[1] * 64 * g.O[0] * g.G * p.cpad * p.kgp;
+  const int64_t issued = int64_t(p.grid[0]) * p.grid[1] * 64 * g.O[0] * g.G * p.cchunks * p.cpad * p.kgp;
   std::snprintf(buf, sizeof buf,
-                "kernel=fused_min_softmax_mfma4 ng=%d cpad=%d groups=%lld kred=%d mode=%s tile=%d box=%dx%dx%dx%d "
-                "grid=%lldx%lldx%lld lds=%lld macs=%lld issued=%lld",
-                p.ng, p.cpad, (long long)g.G, p.kg, p.mode == TILE_FLAT ? "flat" : "row",
+                "kernel=fused_min_softmax_mfma4 ng=%d cpad=%d chunks=%d groups=%lld kred=%d mode=%s tile=%d "
+                "box=%dx%dx%dx%d grid=%lldx%lldx%lld lds=%lld macs=%lld issued=%lld",
+                p.ng, p.cpad, p.cchunks, (long long)g.G, p.kg, p.mode == TILE_FLAT ? "flat" : "row",
                 p.mode == TILE_FLAT ? p.tile_pos : 64, int(g.Cin), p.dspan, p.rows,
                 p.bw, (long long)p.grid[0], (long long)p.grid[1], (long long)p.grid[2], (long long)p.lds_bytes,
                 (long long)g.macs(), (long long)issued);

@@ -265,6 +265,7 @@ struct FusedPlan {
   // Generic kernel: reduction of one group (C_in/groups * kvol), rounded up to 4,
   // LDS weight row pitch; box rows; LDS float offsets of its regions.
   int kg = 0, kgp = 0, kgs = 0, nrows = 0;
+  int cchunks = 1;     // generic kernel: output-channel chunks of at most 64 per group
   int tile_pos = 64;   // generic kernel, TILE_FLAT: output positions per tile
   int ko_off = 0, wt_off = 0, red_off = 0, fin_off = 0;
   int64_t tiles_per_plane = 0;

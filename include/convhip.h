@@ -125,8 +125,10 @@ int conv_fwd_channels_last(int nd,
  *   min_dim 2: y [N, C_out, H_out, W_out],
  *              y[n,:,h,w] = softmax_c( min_{od} conv3d(x,w,bias)[n,c,od,h,w] );
  *   min_dim 3: y [N, C_out, D_out, W_out];  min_dim 4: y [N, C_out, D_out, H_out].
- * Supported: C_out <= 64, and the input box of one output tile over the whole
- * min axis must fit in LDS; other valid arguments return CONV_ERR_UNSUPPORTED.
+ * Supported while one output tile's input box over the whole min axis, the
+ * weights and the minima of all C_out channels at 64 positions fit in LDS
+ * (160 KiB; more than 64 channels per group run as channel chunks of at most
+ * 64); other valid arguments return CONV_ERR_UNSUPPORTED.
  * With groups > 1 each output channel reduces over its own group's C_in/groups
  * input channels only. A NaN input propagates as it does through the module's
  * torch.min (the minimum is NaN-propagating); infinite inputs: unspecified.

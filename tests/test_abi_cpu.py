@@ -181,11 +181,11 @@ def test_conv3d_min_softmax_validation_errors():
                                             kw.get("y", FAKE), None)
     assert f(y=None) == -1
     assert f(md=5) == -5
-    assert f(md=3, ws=I64(65, 3, 3, 3, 3)) == -7   # min over H: supported, but not C_out > 64
+    assert f(md=3, ws=I64(2048, 3, 3, 3, 3)) == -7  # min over H: the weights of 2048 channels exceed LDS
     assert f(md=4, xs=I64(2, 3, 6, 6, 2)) == -6    # min over W of an empty output
     assert f(g=3) == -4                                                # C_out % groups
-    assert f(ws=I64(66, 1, 3, 3, 3), xs=I64(2, 3, 6, 6, 6), g=3) == -7  # grouped, C_out > 64
-    assert f(ws=I64(65, 3, 3, 3, 3)) == -7                             # C_out > 64: unsupported
+    assert f(ws=I64(2046, 1, 3, 3, 3), xs=I64(2, 3, 6, 6, 6), g=3) == -7  # grouped: weights exceed LDS
+    assert f(ws=I64(2048, 3, 3, 3, 3)) == -7                             # weights exceed LDS
     assert f(xs=I64(2, 3, 2, 6, 6)) == -6
     assert f(s=I32(1, 0, 1)) == -5
 
@@ -354,3 +354,17 @@ def test_fused_channels_last_plans():
     assert f(md=5) == -5 and f(md=1) == -5
     assert f(xs=(1, 6, 8, 8, 4)) == -3          # C_in (last entry) does not match w
     assert f(xs=(1, 2, 8, 8, 3)) == -6          # empty output along D
+
+
+def test_fused_generic_channel_chunks():
+    """More than 64 output channels per group run as balanced chunks of at most 64
+    (each reducing over the group's whole input); the multiply-adds issued are the
+    algorithmic count times the padding of positions, chunks' channels and reduction."""
+    for xs, ws, g, chunks, cpad in [((2, 3, 6, 9, 10), (96, 3, 3, 3, 3), 1, 2, 48),
+                                    ((2, 3, 6, 9, 10), (150, 3, 3, 3, 3), 1, 3, 52),
+                                    ((2, 4, 6, 9, 10), (160, 2, 3, 3, 3), 2, 2, 40),
+                                    ((2, 3, 6, 9, 10), (64, 3, 3, 3, 3), 1, 1, 64)]:
+        desc = ch.plan_describe(xs, ws, 1, 1, 0, g, fused=True)
+        f = dict(t.split("=", 1) for t in desc.split() if "=" in t)
+        assert f["kernel"] == "fused_min_softmax_mfma4" and int(f["chunks"]) == chunks, desc
+        assert int(f["cpad"]) == cpad, desc

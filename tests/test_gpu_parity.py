@@ -438,6 +438,40 @@ def test_fused_stream_groups_integer_minimum_exact():
     assert float(np.abs(y - ref).max()) <= FUSED_ATOL
 
 
+# More than 64 output channels per group: the generic fused kernel runs them as
+# chunks of at most 64 channels and merges the chunks' minima before the softmax.
+FUSED_CHUNK_CASES = [
+    ("cout96_min_d", (2, 3, 6, 9, 10), (96, 3, 3, 3, 3), 1, 1, 0, 1, 2),
+    ("cout150_min_h_padded", (1, 3, 5, 8, 12), (150, 3, 2, 3, 3), 1, 1, (1, 1, 1), 1, 3),
+    ("groups2_cout160_min_w", (2, 4, 5, 7, 9), (160, 2, 2, 2, 3), (1, 1, 2), 1, 0, 2, 4),
+    ("cout128_two_tiles", (2, 3, 8, 12, 12), (128, 3, 3, 3, 3), 1, 1, 0, 1, 2),
+]
+
+
+@pytest.mark.parametrize("case", FUSED_CHUNK_CASES, ids=[c[0] for c in FUSED_CHUNK_CASES])
+def test_fused_channel_chunks(case):
+    name, xs, ws, s, d, p, g, md = case
+    desc = ch.plan_describe(xs, ws, s, d, p, g, fused=True, min_dim=md)
+    assert "kernel=fused_min_softmax_mfma4" in desc and "chunks=1 " not in desc, desc
+    r = np.random.default_rng(zlib.crc32(name.encode()))
+    x, w, b = _float_inputs(r, xs, ws, True)
+    say(f"fused channel chunks {name}: {desc}")
+    y = gpu_fused(x, w, b, s, d, p, g, md)
+    ref = oracle.conv3d_min_softmax(x, w, b, s, d, p, g, md)
+    err = float(np.abs(y - ref).max())
+    say(f"  max|err| = {err:.3e}")
+    assert err <= FUSED_ATOL
+
+
+def test_fused_channel_chunks_integer_minimum_exact():
+    r = np.random.default_rng(1780)
+    xs, ws = (2, 3, 5, 7, 9), (100, 3, 2, 3, 2)
+    x, w, b = _int_inputs(r, xs, ws, True)
+    y = gpu_fused(x, w, b, 1, 1, 0, 1, 2)
+    ref = oracle.conv3d_min_softmax(x, w, b, 1, 1, 0, 1, 2)
+    assert float(np.abs(y - ref).max()) <= FUSED_ATOL
+
+
 CONV2D_CASES = [
     ("conv2d_workload_like", (2, 16, 32, 32), (32, 8, 5, 7), (2, 2), (1, 2), (2, 3), 2),
     ("conv2d_3x3", (1, 3, 40, 50), (8, 3, 3, 3), 1, 1, 1, 1),
