@@ -193,6 +193,8 @@ int plan_valu(const Geom& g, ValuPlan* p) {
   const int64_t npairs = g.Cg * g.K[0];
   if (g.Cin >= (int64_t(1) << 30) || g.Cout >= (int64_t(1) << 30) || npairs >= (int64_t(1) << 30))
     return CONV_ERR_OVERFLOW;
+  // The kernel steps along a row's taps in 32-bit element offsets.
+  if (g.K[2] * g.Dl[2] * (g.cl ? g.Cin : 1) >= (int64_t(1) << 31)) return CONV_ERR_OVERFLOW;
   p->co = co;
   p->ncob = int((g.Coutg + co - 1) / co);
   // 256 lanes x 2 positions per workgroup where that still gives 4 workgroups
