@@ -1,8 +1,7 @@
 """Host logic of bench.py (CPU only): the work it credits each workload with,
 its entry names and roofline objects, the committed traffic summaries it reads,
 and the one-GPU guard. The MAC counts are checked against the sizes the pages
-print and against
-an independent count from the output shapes."""
+print and against a count written out from the output shapes."""
 import os
 import subprocess
 import sys
